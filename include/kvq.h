@@ -1,0 +1,178 @@
+/*
+ * kvq.h -- paged quantized KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * Two steps of LLM decoding over a paged KV cache whose K and V sides are each
+ * stored in one of five formats (any K/V pairing):
+ *   1. kvq_reshape_and_cache: write new K/V rows into the paged pools;
+ *   2. kvq_paged_decode:      one query token per sequence attends to its pages.
+ * kvq_pool_layout gives the byte layout the caller allocates the pools with.
+ *
+ * Sources (web pages, cited by title and item):
+ *   [kv_cache.rs]  "spark_runtime/kv_cache.rs" -- KvCacheDtype catalogue,
+ *                  kv_pair / is_wht_rotated, KvCacheConfig::block_bytes_dims,
+ *                  LayerPool (separate K / V block strides).
+ *   [bf16k_turbov] "metrale_model_layers/layers/ops/kv_cache_bf16k_turbov.rs" --
+ *                  module invariants (pool layout, code section then scales)
+ *                  and the reshape_and_cache_* / paged_decode_attn_* launchers.
+ *   [kv.rs]        "combs_models/kv.rs" -- repeat_kv (GQA), attend (scaled
+ *                  softmax attention; decode needs no mask), paged gather.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers; "host" ones are host
+ *     memory read before the call returns.  The library allocates nothing,
+ *     keeps no state between calls (apart from constant tables built once per
+ *     process) and never synchronizes the host: work is queued on `stream`
+ *     (a hipStream_t, NULL = the default stream) in call order.
+ *   - Every argument is checked on the host before anything is launched; a
+ *     failed check returns a negative kvq_status and launches nothing.  The
+ *     checks cannot see device memory: slot ids, block ids and sequence
+ *     lengths must lie in range (caller contract; an out-of-range id is a
+ *     memory fault).
+ *   - Functions are thread-safe.  Concurrent calls that write the same pool
+ *     slots or the same workspace race.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage format of one side (K or V) of the cache.  [kv_cache.rs] KvCacheDtype:
+ *   KVQ_BF16      2 bytes per element, the bf16 bit pattern.
+ *   KVQ_FP8_E4M3  1 byte per element: OCP E4M3FN of x / scale, one fp32 scale
+ *                 per tensor supplied by the caller (clamped to +-448, round
+ *                 to nearest even).
+ *   KVQ_TURBO{2,3,4}  TurboQuant: the row (head_dim values) is rotated by the
+ *                 orthonormal Walsh-Hadamard transform, re-rounded to bf16, and
+ *                 every group of 16 elements is stored as 2/3/4-bit indices into
+ *                 the Lloyd-Max codebook of a standard Gaussian, with one E4M3
+ *                 scale byte (group absmax / largest centroid) per group.
+ * Rotated sides (turbo) make decode rotate the query (K side) and rotate the
+ * output back (V side) -- [kv_cache.rs] is_wht_rotated. */
+typedef enum kvq_format {
+  KVQ_BF16 = 0,
+  KVQ_FP8_E4M3 = 1,
+  KVQ_TURBO2 = 2,
+  KVQ_TURBO3 = 3,
+  KVQ_TURBO4 = 4
+} kvq_format;
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = -1,  /* a size, count, scale or pointer is invalid  */
+  KVQ_ERR_UNSUPPORTED = -2,  /* valid, but outside what the kernels handle  */
+  KVQ_ERR_ALIGNMENT = -3,    /* a pointer or stride is not 16-byte aligned  */
+  KVQ_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required  */
+  KVQ_ERR_LAUNCH = -5        /* the HIP runtime rejected a kernel launch    */
+} kvq_status;
+
+/* Byte layout of the two pools of one attention layer.
+ * Pool element order [bf16k_turbov, module invariants]:
+ *   [num_blocks, block_size, num_kv_heads, head_dim]; inside a block the flat
+ *   element index of (offset, head, d) is e = (offset*num_kv_heads + head)*head_dim + d.
+ * A block of one side is its code section (data_section_bytes) followed, for
+ * turbo sides, by one E4M3 scale byte per group of 16 elements (byte e/16 of
+ * the scale section).  Codes of b bits occupy bits [e*b, e*b+b) of the code
+ * section read as a little-endian bit stream.  Blocks are block_stride_bytes
+ * apart: the block's size [kv_cache.rs block_bytes_dims] rounded up to 16.
+ * K and V have separate strides [kv_cache.rs LayerPool]. */
+typedef struct kvq_layout {
+  int32_t k_format;            /* kvq_format of the K side                     */
+  int32_t v_format;            /* kvq_format of the V side                     */
+  uint32_t block_size;         /* token positions per block                    */
+  uint32_t num_kv_heads;
+  uint32_t head_dim;
+  uint32_t k_rotated;          /* 1 if the K side is stored WHT-rotated         */
+  uint32_t v_rotated;          /* 1 if the V side is stored WHT-rotated         */
+  uint32_t reserved;           /* 0                                            */
+  uint64_t k_data_section_bytes;
+  uint64_t k_block_stride_bytes;
+  uint64_t v_data_section_bytes;
+  uint64_t v_block_stride_bytes;
+} kvq_layout;
+
+/* Fill *out (host) with the pool layout for a (K format, V format) pair.
+ * [kv_cache.rs] block_bytes_dims, k/v_block_bytes_for_layer.
+ * Supported: block_size a power of two in [1, 1024]; num_kv_heads in [1, 256];
+ * head_dim in {64, 128, 256}.  Pools hold num_blocks * *_block_stride_bytes
+ * bytes; their base pointers must be 16-byte aligned.
+ * Returns KVQ_OK, KVQ_ERR_INVALID_ARG (unknown format, zero size, out == NULL)
+ * or KVQ_ERR_UNSUPPORTED (a size outside the supported set). */
+int kvq_pool_layout(int32_t k_format, int32_t v_format, uint32_t block_size,
+                    uint32_t num_kv_heads, uint32_t head_dim, kvq_layout* out);
+
+/* Write num_tokens new K/V rows into the pools.
+ * [bf16k_turbov] reshape_and_cache_bf16k_turbo{2,3,4}v; [kv_cache.rs] write path
+ * (turbo sides rotated by wht before quantizing).
+ *   layout        host; as filled by kvq_pool_layout (re-checked here).
+ *   key, value    device bf16 [num_tokens, num_kv_heads, head_dim]; token t's
+ *                 row of head h starts at element t*key_stride + h*head_dim
+ *                 (value_stride for value).  16-byte aligned; strides are
+ *                 multiples of 8 and >= num_kv_heads*head_dim.
+ *   k_cache, v_cache  device pools (see kvq_layout).
+ *   slot_mapping  device int64 [num_tokens]: slot = block*block_size + offset;
+ *                 a negative slot skips the token.  Slots must be distinct.
+ *   k_scale, v_scale  per-tensor scales of fp8 sides (finite, > 0); ignored
+ *                 for other formats.
+ * num_tokens == 0 returns KVQ_OK with nothing launched. */
+int kvq_reshape_and_cache(const kvq_layout* layout, const void* key, const void* value,
+                          void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                          uint32_t num_tokens, uint32_t key_stride, uint32_t value_stride,
+                          float k_scale, float v_scale, void* stream);
+
+/* Paged decode attention: for every sequence s and query head h (kv head
+ * g = h / (num_q_heads/num_kv_heads), [kv.rs] repeat_kv):
+ *   L = seq_lens[s] (counts the token just written); window start
+ *   j0 = sliding_window ? max(0, L - sliding_window) : 0;
+ *   score_j = inv_sqrt_d * <q, K_j> over j in [j0, L), K_j read from page
+ *   block_tables[s][j / block_size] at offset j % block_size;
+ *   p = softmax(score) over the window;
+ *   out[s][h] = sum over j with p_j > sparse_v_threshold of p_j * V_j
+ *   (no renormalization; threshold 0 = dense).
+ * [bf16k_turbov] paged_decode_attn_bf16k_turbo{2,3,4}v (argument list, sparse-V
+ * skip of a position's V "when its attention weight is at most" the threshold);
+ * [kv.rs] attend.  Rotated K: the query is rotated first; rotated V: the
+ * output is rotated back ([kv_cache.rs] is_wht_rotated).  An empty sequence
+ * (L == 0) gives a zero row.
+ *   q             device bf16 [num_seqs, num_q_heads, head_dim]; sequence s
+ *                 starts at element s*q_stride (multiple of 8, >= Hq*head_dim).
+ *   out           device fp32 [num_seqs, num_q_heads, head_dim], contiguous.
+ *   block_tables  device int32 [num_seqs, max_blocks_per_seq]; entries past a
+ *                 sequence's last page are never read.
+ *   seq_lens      device int32 [num_seqs], each <= max_blocks_per_seq*block_size.
+ *   num_q_heads   a multiple of num_kv_heads; the group size
+ *                 num_q_heads/num_kv_heads must be 1, 2, 4 or 8.
+ *   inv_sqrt_d    the score scale (finite, > 0), used as given.
+ *   k_scale, v_scale  fp8 per-tensor scales (as passed to the write).
+ *   workspace     device scratch of *workspace_bytes bytes (16-byte aligned),
+ *                 overwritten by the call.  With workspace == NULL the call
+ *                 only stores the required size in *workspace_bytes (host)
+ *                 and returns KVQ_OK without launching; the size depends on
+ *                 every size argument and on whether the threshold is 0.
+ * Returns KVQ_OK or a negative kvq_status (nothing launched on error). */
+int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cache,
+                     const void* v_cache, float* out, const int32_t* block_tables,
+                     const int32_t* seq_lens, uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                     uint32_t num_q_heads, float inv_sqrt_d, uint32_t q_stride,
+                     uint32_t sliding_window, float sparse_v_threshold, float k_scale,
+                     float v_scale, void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Introspection (host only): the fp32 Lloyd-Max tables the turbo format uses.
+ * centroids[0..L-1] ascending, thresholds[1..L-1] (midpoints; [0] = 0),
+ * *inv_cmax = 1/largest centroid, *levels = L = 2^bits.  Buffers hold 16 floats.
+ * Returns KVQ_ERR_INVALID_ARG for a non-turbo format or a NULL pointer. */
+int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax,
+                 uint32_t* levels);
+
+/* Static, human-readable name of a kvq_status value. */
+const char* kvq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,205 @@
+"""Python binding of libkvq (paged quantized KV cache for MI355X / gfx950).
+
+Argument marshalling only: every step of the write and of the decode runs in
+the HIP kernels of libkvq.so, reached through its C ABI (include/kvq.h) with
+ctypes.  torch supplies device memory and the current HIP stream.  There is
+no CPU fallback: without the built library every call raises.
+
+    import paged_quantized_kv_kvq_amd as kvq
+    lay = kvq.pool_layout("bf16", "turbo4", block_size=16, num_kv_heads=8, head_dim=128)
+    k_pool = kvq.alloc_pool(lay, "k", num_blocks)
+    kvq.reshape_and_cache(lay, key, value, k_pool, v_pool, slot_mapping)
+    out = kvq.paged_decode(lay, q, k_pool, v_pool, block_tables, seq_lens, inv_sqrt_d,
+                           sparse_v_threshold=1e-3)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
+           "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
+           "library_path"]
+
+FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4}
+_NAMES = {v: k for k, v in FORMATS.items()}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvq.so")
+_lib = None
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        msg = _lib.kvq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+class Layout(ctypes.Structure):
+    """Mirror of struct kvq_layout."""
+    _fields_ = [("k_format", ctypes.c_int32), ("v_format", ctypes.c_int32),
+                ("block_size", ctypes.c_uint32), ("num_kv_heads", ctypes.c_uint32),
+                ("head_dim", ctypes.c_uint32), ("k_rotated", ctypes.c_uint32),
+                ("v_rotated", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("k_data_section_bytes", ctypes.c_uint64), ("k_block_stride_bytes", ctypes.c_uint64),
+                ("v_data_section_bytes", ctypes.c_uint64), ("v_block_stride_bytes", ctypes.c_uint64)]
+
+    @property
+    def k_fmt(self) -> str:
+        return _NAMES[self.k_format]
+
+    @property
+    def v_fmt(self) -> str:
+        return _NAMES[self.v_format]
+
+    def __repr__(self):
+        return (f"Layout({self.k_fmt}/{self.v_fmt}, bs={self.block_size}, Hkv={self.num_kv_heads}, "
+                f"hd={self.head_dim}, K stride {self.k_block_stride_bytes} B, V stride "
+                f"{self.v_block_stride_bytes} B)")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkvq.so (built in-tree by ``python -m paged_quantized_kv_kvq_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m paged_quantized_kv_kvq_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, U32, I32, F32, SZ = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kvq_pool_layout.argtypes = [I32, I32, U32, U32, U32, ctypes.POINTER(Layout)]
+    lib.kvq_reshape_and_cache.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, U32, U32, U32, F32, F32, P]
+    lib.kvq_paged_decode.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, U32, U32, U32, F32, U32, U32,
+                                     F32, F32, F32, P, ctypes.POINTER(SZ), P]
+    lib.kvq_codebook.argtypes = [I32, ctypes.POINTER(F32), ctypes.POINTER(F32), ctypes.POINTER(F32),
+                                 ctypes.POINTER(U32)]
+    lib.kvq_status_string.argtypes = [ctypes.c_int]
+    lib.kvq_status_string.restype = ctypes.c_char_p
+    for f in ("kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode", "kvq_codebook"):
+        getattr(lib, f).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise KvqError(status, what)
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+def pool_layout(k_format, v_format, block_size: int, num_kv_heads: int, head_dim: int) -> Layout:
+    lib = load()
+    lay = Layout()
+    _check(lib.kvq_pool_layout(_fmt(k_format), _fmt(v_format), block_size, num_kv_heads, head_dim,
+                               ctypes.byref(lay)), "kvq_pool_layout")
+    return lay
+
+
+def alloc_pool(layout: Layout, side: str, num_blocks: int, device="cuda", fill: Optional[int] = None):
+    """uint8 device tensor holding num_blocks blocks of one side's pool."""
+    stride = layout.k_block_stride_bytes if side == "k" else layout.v_block_stride_bytes
+    if fill is None:
+        return torch.empty(num_blocks * stride, dtype=torch.uint8, device=device)
+    return torch.full((num_blocks * stride,), fill, dtype=torch.uint8, device=device)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _row_stride(t: torch.Tensor, name: str) -> int:
+    """Elements between rows of [rows, heads, head_dim] with contiguous heads."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{name} must be [rows, heads, head_dim] with contiguous heads")
+    return t.stride(0)
+
+
+def reshape_and_cache(layout: Layout, key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
+                      v_scale: float = 1.0, stream=None) -> None:
+    """Write key/value rows ([T, Hkv, hd] bf16) into the pools at slot_mapping (int64 [T])."""
+    lib = load()
+    T = key.shape[0]
+    if value.shape[0] != T or slot_mapping.numel() != T:
+        raise ValueError("key, value and slot_mapping disagree on the number of tokens")
+    _check(lib.kvq_reshape_and_cache(
+        ctypes.byref(layout), _dev(key, torch.bfloat16, "key"), _dev(value, torch.bfloat16, "value"),
+        _dev(k_cache, torch.uint8, "k_cache"), _dev(v_cache, torch.uint8, "v_cache"),
+        _dev(slot_mapping, torch.int64, "slot_mapping"), T, _row_stride(key, "key"),
+        _row_stride(value, "value"), k_scale, v_scale, _stream(stream)), "kvq_reshape_and_cache")
+
+
+def decode_workspace_bytes(layout: Layout, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                           sliding_window: int = 0, sparse_v_threshold: float = 0.0) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.kvq_paged_decode(ctypes.byref(layout), None, None, None, None, None, None,
+                                max_blocks_per_seq, num_seqs, num_q_heads, 1.0,
+                                num_q_heads * layout.head_dim, sliding_window, sparse_v_threshold,
+                                1.0, 1.0, None, ctypes.byref(n), None), "kvq_paged_decode (size)")
+    return n.value
+
+
+def paged_decode(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 block_tables: torch.Tensor, seq_lens: torch.Tensor, inv_sqrt_d: float,
+                 sliding_window: int = 0, sparse_v_threshold: float = 0.0, k_scale: float = 1.0,
+                 v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """fp32 [S, Hq, hd] attention output for bf16 q [S, Hq, hd]."""
+    lib = load()
+    S, Hq, hd = q.shape
+    if q.stride(2) != 1 or q.stride(1) != hd:
+        raise ValueError("q must be [S, Hq, head_dim] with contiguous heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((S, Hq, hd), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (S, Hq, hd):
+        raise ValueError("out must be contiguous fp32 [S, Hq, head_dim]")
+    need = decode_workspace_bytes(layout, S, Hq, mb, sliding_window, sparse_v_threshold)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib.kvq_paged_decode(
+        ctypes.byref(layout), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.uint8, "k_cache"),
+        _dev(v_cache, torch.uint8, "v_cache"), _dev(out, torch.float32, "out"),
+        _dev(block_tables, torch.int32, "block_tables"), _dev(seq_lens, torch.int32, "seq_lens"),
+        mb, S, Hq, inv_sqrt_d, q.stride(0), sliding_window, sparse_v_threshold, k_scale, v_scale,
+        _dev(workspace, torch.uint8, "workspace"), ctypes.byref(n), _stream(stream)), "kvq_paged_decode")
+    return out
+
+
+def codebook(fmt) -> dict:
+    """The library's fp32 Lloyd-Max tables for a turbo format."""
+    lib = load()
+    c = (ctypes.c_float * 16)()
+    t = (ctypes.c_float * 16)()
+    inv = ctypes.c_float()
+    L = ctypes.c_uint32()
+    _check(lib.kvq_codebook(_fmt(fmt), c, t, ctypes.byref(inv), ctypes.byref(L)), "kvq_codebook")
+    n = L.value
+    import numpy as np
+    return {"levels": n, "centroids": np.array(c[:n], dtype=np.float32),
+            "thresholds": np.array(t[:n], dtype=np.float32), "inv_cmax": np.float32(inv.value)}

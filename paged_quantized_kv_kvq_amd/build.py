@@ -1,0 +1,91 @@
+"""Build libkvq.so (HIP kernels + C ABI) for gfx950 with hipcc.
+
+    python -m paged_quantized_kv_kvq_amd.build [--jobs N] [--verbose]
+
+Every .hip file under csrc/ is compiled to an object in csrc/../_build/, in
+parallel, and linked into paged_quantized_kv_kvq_amd/libkvq.so.  The cache
+write is compiled with -ffp-contract=off: its codes must match a plain fp32
+reference bit for bit, so no multiply-add may be fused.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libkvq.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the kvq library)")
+
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # packed fp32 VALU forms stay off (not needed; avoided on this target)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Wno-unused-command-line-argument",
+]
+EXACT = ["-ffp-contract=off"]          # bit-exact quantization
+FAST = ["-ffp-contract=fast"]          # decode: fused multiply-adds allowed
+
+
+def sources():
+    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def compile_one(src: str, verbose: bool) -> tuple:
+    obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
+    flags = EXACT if src in ("kvq_write.hip", "kvq_api.hip") else FAST
+    cmd = [hipcc()] + COMMON + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+    t0 = time.time()
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or r.returncode:
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+    return src, obj, r.returncode, time.time() - t0
+
+
+def build(jobs: int = 0, verbose: bool = False) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    jobs = jobs or max(1, min(8, os.cpu_count() or 1))
+    objs = []
+    failed = []
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        for src, obj, rc, dt in ex.map(lambda s: compile_one(s, verbose), sources()):
+            if verbose:
+                sys.stderr.write(f"  {src}: {dt:.1f}s\n")
+            (failed if rc else objs).append(src if rc else obj)
+    if failed:
+        raise RuntimeError(f"hipcc failed for {failed}")
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--verbose", action="store_true")
+    a = ap.parse_args()
+    t0 = time.time()
+    print(build(a.jobs, a.verbose), f"({time.time() - t0:.1f}s)")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,346 @@
+// The exported C ABI: argument checks, pool layout, Lloyd-Max tables, decode
+// planning and kernel dispatch.  Nothing here touches device memory.
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr uint32_t kMaxSplitLen = 4096;
+constexpr uint32_t kMaxSparseSplitLen = 1024;  // scores of a split live in LDS
+constexpr uint32_t kPagesPerSplit = 512;       // page ids of a split live in LDS
+constexpr uint64_t kTargetWorkgroups = 4096;
+
+bool valid_format(int32_t f) { return f >= KVQ_BF16 && f <= KVQ_TURBO4; }
+bool is_turbo(int32_t f) { return f >= KVQ_TURBO2; }
+uint32_t format_bits(int32_t f) { return f == KVQ_BF16 ? 16u : f == KVQ_FP8_E4M3 ? 8u : uint32_t(f); }
+bool pow2(uint64_t x) { return x && !(x & (x - 1)); }
+uint32_t log2u(uint64_t x) {
+  uint32_t r = 0;
+  while ((1ull << r) < x) ++r;
+  return r;
+}
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Lloyd-Max quantizer of N(0,1) with L levels: iterate the two optimality
+// conditions (thresholds at centroid midpoints; centroids at the conditional
+// mean (pdf(a) - pdf(b)) / (cdf(b) - cdf(a)) of their cell) over all L cells,
+// mirroring the result after every sweep to keep it exactly symmetric.
+double gauss_pdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.3989422804014327; }
+
+// cdf(b) - cdf(a) without cancellation in either tail
+double gauss_mass(double a, double b) {
+  const double r = 0.7071067811865476;
+  if (a >= 0.0) return 0.5 * (std::erfc(a * r) - std::erfc(b * r));
+  if (b <= 0.0) return 0.5 * (std::erfc(-b * r) - std::erfc(-a * r));
+  return 1.0 - 0.5 * std::erfc(-a * r) - 0.5 * std::erfc(b * r);
+}
+
+void lloyd_max(int L, double* c) {
+  for (int k = 0; k < L; ++k) c[k] = -3.0 + 6.0 * (k + 0.5) / L;
+  int settle = 2000;
+  for (int it = 0; it < 100000; ++it) {
+    double t[17];
+    t[0] = -INFINITY;
+    t[L] = INFINITY;
+    for (int k = 1; k < L; ++k) t[k] = 0.5 * (c[k - 1] + c[k]);
+    double nc[16], delta = 0.0;
+    for (int k = 0; k < L; ++k) nc[k] = (gauss_pdf(t[k]) - gauss_pdf(t[k + 1])) / gauss_mass(t[k], t[k + 1]);
+    for (int k = 0; k < L / 2; ++k) {
+      const double v = 0.5 * (nc[L - 1 - k] - nc[k]);
+      nc[k] = -v;
+      nc[L - 1 - k] = v;
+    }
+    for (int k = 0; k < L; ++k) {
+      delta = std::fmax(delta, std::fabs(nc[k] - c[k]));
+      c[k] = nc[k];
+    }
+    if (delta <= 1e-15 && (--settle < 0 || delta == 0.0)) break;
+  }
+}
+
+Codebooks build_codebooks() {
+  Codebooks cb;
+  std::memset(&cb, 0, sizeof(cb));
+  for (int bits = 2; bits <= 4; ++bits) {
+    const int L = 1 << bits;
+    double c[16];
+    lloyd_max(L, c);
+    for (int k = 0; k < L; ++k) cb.centroid[bits - 2][k] = float(c[k]);
+    for (int k = 1; k < L; ++k) cb.threshold[bits - 2][k] = float(0.5 * (c[k - 1] + c[k]));
+    cb.inv_cmax[bits - 2] = float(1.0 / c[L - 1]);
+  }
+  return cb;
+}
+
+int layout_impl(int32_t kf, int32_t vf, uint32_t bs, uint32_t nkv, uint32_t hd, kvq_layout* out) {
+  if (!out || !valid_format(kf) || !valid_format(vf) || bs == 0 || nkv == 0 || hd == 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (!pow2(bs) || bs > 1024 || nkv > 256 || (hd != 64 && hd != 128 && hd != 256)) return KVQ_ERR_UNSUPPORTED;
+  const uint64_t e = uint64_t(bs) * nkv * hd;
+  kvq_layout l;
+  std::memset(&l, 0, sizeof(l));
+  l.k_format = kf;
+  l.v_format = vf;
+  l.block_size = bs;
+  l.num_kv_heads = nkv;
+  l.head_dim = hd;
+  l.k_rotated = is_turbo(kf) ? 1u : 0u;
+  l.v_rotated = is_turbo(vf) ? 1u : 0u;
+  const int32_t fmts[2] = {kf, vf};
+  uint64_t data[2], stride[2];
+  for (int i = 0; i < 2; ++i) {
+    data[i] = e * format_bits(fmts[i]) / 8;
+    const uint64_t bytes = data[i] + (is_turbo(fmts[i]) ? e / 16 : 0);
+    stride[i] = (bytes + 15) / 16 * 16;
+  }
+  l.k_data_section_bytes = data[0];
+  l.k_block_stride_bytes = stride[0];
+  l.v_data_section_bytes = data[1];
+  l.v_block_stride_bytes = stride[1];
+  *out = l;
+  return KVQ_OK;
+}
+
+// A layout handed back by the caller must be exactly one this library made.
+int check_layout(const kvq_layout* l) {
+  if (!l) return KVQ_ERR_INVALID_ARG;
+  kvq_layout ref;
+  const int st = layout_impl(l->k_format, l->v_format, l->block_size, l->num_kv_heads, l->head_dim, &ref);
+  if (st != KVQ_OK) return st;
+  return std::memcmp(&ref, l, sizeof(ref)) == 0 ? KVQ_OK : KVQ_ERR_INVALID_ARG;
+}
+
+bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+
+struct Plan {
+  uint32_t split_len, nsplit;
+  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cs, bytes;
+};
+
+uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+// Split length: the smallest power of two >= 256 giving about
+// kTargetWorkgroups workgroups over the longest possible window.
+Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
+               uint32_t window, bool sparse) {
+  uint64_t span = uint64_t(max_blocks) * bs;
+  if (window && window < span) span = window;
+  const uint64_t work = span * S * nkv;
+  uint32_t sl = 256;
+  while (sl < kMaxSplitLen && uint64_t(sl) * kTargetWorkgroups < work) sl <<= 1;
+  if (sparse && sl > kMaxSparseSplitLen) sl = kMaxSparseSplitLen;
+  while (sl > 16 && sl / bs + 2 > kPagesPerSplit) sl >>= 1;
+  Plan p;
+  p.split_len = sl;
+  p.nsplit = uint32_t(span == 0 ? 1 : (span + sl - 1) / sl);
+  const uint64_t units = uint64_t(S) * nkv * p.nsplit;
+  uint64_t off = 0;
+  p.off_ml = off;
+  off = up256(off + units * G * 2 * sizeof(float));
+  if (!sparse) {
+    p.off_part = off;
+    off = up256(off + units * G * hd * sizeof(float));
+    p.off_cnt = p.off_cidx = p.off_cs = 0;
+  } else {
+    p.off_part = 0;
+    p.off_cnt = off;
+    off = up256(off + units * sizeof(int32_t));
+    p.off_cidx = off;
+    off = up256(off + units * sl * sizeof(int32_t));
+    p.off_cs = off;
+    off = up256(off + units * sl * G * sizeof(float));
+  }
+  p.bytes = off;
+  return p;
+}
+
+}  // namespace
+
+const Codebooks& codebooks() {
+  static Codebooks cb;
+  static std::once_flag once;
+  std::call_once(once, [] { cb = build_codebooks(); });
+  return cb;
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int kvq_pool_layout(int32_t k_format, int32_t v_format, uint32_t block_size, uint32_t num_kv_heads,
+                    uint32_t head_dim, kvq_layout* out) {
+  return layout_impl(k_format, v_format, block_size, num_kv_heads, head_dim, out);
+}
+
+int kvq_reshape_and_cache(const kvq_layout* layout, const void* key, const void* value, void* k_cache,
+                          void* v_cache, const int64_t* slot_mapping, uint32_t num_tokens, uint32_t key_stride,
+                          uint32_t value_stride, float k_scale, float v_scale, void* stream) {
+  const int st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (num_tokens == 0) return KVQ_OK;
+  const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return KVQ_ERR_INVALID_ARG;
+  if (uint64_t(num_tokens) * nkv * 2 >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  if (key_stride < nkv * hd || value_stride < nkv * hd) return KVQ_ERR_INVALID_ARG;
+  if (key_stride % 8 || value_stride % 8) return KVQ_ERR_ALIGNMENT;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return KVQ_ERR_ALIGNMENT;
+  if (layout->k_format == KVQ_FP8_E4M3 && !good_scale(k_scale)) return KVQ_ERR_INVALID_ARG;
+  if (layout->v_format == KVQ_FP8_E4M3 && !good_scale(v_scale)) return KVQ_ERR_INVALID_ARG;
+  WriteArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.key = static_cast<const uint16_t*>(key);
+  a.value = static_cast<const uint16_t*>(value);
+  a.k_cache = static_cast<uint8_t*>(k_cache);
+  a.v_cache = static_cast<uint8_t*>(v_cache);
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = nkv;
+  a.log2_bs = log2u(layout->block_size);
+  a.key_stride = key_stride;
+  a.value_stride = value_stride;
+  a.k_format = layout->k_format;
+  a.v_format = layout->v_format;
+  a.k_stride = layout->k_block_stride_bytes;
+  a.k_data = layout->k_data_section_bytes;
+  a.v_stride = layout->v_block_stride_bytes;
+  a.v_data = layout->v_data_section_bytes;
+  a.k_scale = layout->k_format == KVQ_FP8_E4M3 ? k_scale : 1.0f;
+  a.v_scale = layout->v_format == KVQ_FP8_E4M3 ? v_scale : 1.0f;
+  a.wht_scale = float(1.0 / std::sqrt(double(hd)));
+  a.cb = codebooks();
+  return launch_write(int(hd), a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
+                     float* out, const int32_t* block_tables, const int32_t* seq_lens,
+                     uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, float inv_sqrt_d,
+                     uint32_t q_stride, uint32_t sliding_window, float sparse_v_threshold, float k_scale,
+                     float v_scale, void* workspace, size_t* workspace_bytes, void* stream) {
+  const int st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (!workspace_bytes) return KVQ_ERR_INVALID_ARG;
+  const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim;
+  if (num_q_heads == 0 || num_q_heads % nkv) return KVQ_ERR_INVALID_ARG;
+  const uint32_t G = num_q_heads / nkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+  if (!std::isfinite(inv_sqrt_d) || inv_sqrt_d <= 0.0f) return KVQ_ERR_INVALID_ARG;
+  if (!std::isfinite(sparse_v_threshold) || sparse_v_threshold < 0.0f) return KVQ_ERR_INVALID_ARG;
+  if (layout->k_format == KVQ_FP8_E4M3 && !good_scale(k_scale)) return KVQ_ERR_INVALID_ARG;
+  if (layout->v_format == KVQ_FP8_E4M3 && !good_scale(v_scale)) return KVQ_ERR_INVALID_ARG;
+  if (num_seqs && max_blocks_per_seq == 0) return KVQ_ERR_INVALID_ARG;
+  if (q_stride < num_q_heads * hd) return KVQ_ERR_INVALID_ARG;
+  if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
+  if (uint64_t(max_blocks_per_seq) * layout->block_size >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  const bool sparse = sparse_v_threshold > 0.0f;
+  const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse);
+  const uint64_t nwg = uint64_t(num_seqs) * nkv * p.nsplit;
+  if (nwg >= (1ull << 31) || uint64_t(num_seqs) * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  if (!workspace) {
+    *workspace_bytes = size_t(p.bytes);
+    return KVQ_OK;
+  }
+  if (*workspace_bytes < p.bytes) return KVQ_ERR_WORKSPACE;
+  if (num_seqs == 0) return KVQ_OK;
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 16))
+    return KVQ_ERR_ALIGNMENT;
+
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.out = out;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.ml = reinterpret_cast<float*>(ws + p.off_ml);
+  if (sparse) {
+    a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
+    a.cidx = reinterpret_cast<int32_t*>(ws + p.off_cidx);
+    a.cscore = reinterpret_cast<float*>(ws + p.off_cs);
+  } else {
+    a.part = reinterpret_cast<float*>(ws + p.off_part);
+  }
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = nkv;
+  a.log2_bs = log2u(layout->block_size);
+  a.q_stride = q_stride;
+  a.window = sliding_window;
+  a.split_len = p.split_len;
+  a.nsplit = p.nsplit;
+  a.k_stride = layout->k_block_stride_bytes;
+  a.k_data = layout->k_data_section_bytes;
+  a.v_stride = layout->v_block_stride_bytes;
+  a.v_data = layout->v_data_section_bytes;
+  const float log2e = 1.4426950408889634f;
+  a.qk_scale = inv_sqrt_d * log2e * (layout->k_format == KVQ_FP8_E4M3 ? k_scale : 1.0f);
+  a.v_scale = layout->v_format == KVQ_FP8_E4M3 ? v_scale : 1.0f;
+  a.thr = sparse_v_threshold;
+  a.wht_scale = float(1.0 / std::sqrt(double(hd)));
+  a.cb = codebooks();
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int kf = layout->k_format, vf = layout->v_format;
+  hipError_t e;
+  if (!sparse) {
+    switch (kf) {
+      case KVQ_BF16: e = launch_split_bf16(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+    }
+    if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
+  } else {
+    switch (kf) {
+      case KVQ_BF16: e = launch_scores_bf16(int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_FP8_E4M3: e = launch_scores_fp8(int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO2: e = launch_scores_turbo2(int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO3: e = launch_scores_turbo3(int(hd), int(G), a, uint32_t(nwg), s); break;
+      default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
+    }
+    if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, s);
+  }
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax, uint32_t* levels) {
+  if (!is_turbo(format) || !valid_format(format) || !centroids || !thresholds || !inv_cmax || !levels)
+    return KVQ_ERR_INVALID_ARG;
+  const Codebooks& cb = codebooks();
+  const int b = format;
+  const int L = 1 << b;
+  for (int k = 0; k < 16; ++k) {
+    centroids[k] = k < L ? cb.centroid[b - 2][k] : 0.0f;
+    thresholds[k] = k < L ? cb.threshold[b - 2][k] : 0.0f;
+  }
+  *inv_cmax = cb.inv_cmax[b - 2];
+  *levels = uint32_t(L);
+  return KVQ_OK;
+}
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported size or format";
+    case KVQ_ERR_ALIGNMENT: return "misaligned pointer or stride";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// Decode kernels that depend only on the V side: the sparse-V pass and the
+// split merge (with the inverse rotation of a rotated V side).
+#include "kvq_decode.h"
+
+namespace kvq {
+namespace {
+
+template <int VF, int HD>
+hipError_t sparse_g(int g, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_seqs * a.num_kv_heads), block(kWaves * kWave);
+  switch (g) {
+    case 1: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 1>), grid, block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 2>), grid, block, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 4>), grid, block, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 8>), grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int VF>
+hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, hipStream_t st) {
+  switch (hd) {
+    case 64: return sparse_g<VF, 64>(g, a, st);
+    case 128: return sparse_g<VF, 128>(g, a, st);
+    case 256: return sparse_g<VF, 256>(g, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int HD>
+hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_seqs * a.num_q_heads), block(kWaves * kWave);
+  if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true>), grid, block, 0, st, a, g);
+  else hipLaunchKernelGGL((merge_kernel<HD, false>), grid, block, 0, st, a, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+  switch (vf) {
+    case KVQ_BF16: return sparse_hd<KVQ_BF16>(hd, g, a, st);
+    case KVQ_FP8_E4M3: return sparse_hd<KVQ_FP8_E4M3>(hd, g, a, st);
+    case KVQ_TURBO2: return sparse_hd<KVQ_TURBO2>(hd, g, a, st);
+    case KVQ_TURBO3: return sparse_hd<KVQ_TURBO3>(hd, g, a, st);
+    case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+  switch (hd) {
+    case 64: return merge_hd<64>(v_rotated, g, a, st);
+    case 128: return merge_hd<128>(v_rotated, g, a, st);
+    case 256: return merge_hd<256>(v_rotated, g, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq

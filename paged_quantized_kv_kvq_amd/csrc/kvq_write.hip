@@ -1,0 +1,186 @@
+// Cache write: quantize new K/V rows and scatter them into the paged pools.
+//
+// "metrale_model_layers/layers/ops/kv_cache_bf16k_turbov.rs",
+// reshape_and_cache_bf16k_turbo{2,3,4}v (slot_mapping scatter of [tokens,
+// kv_heads, head_dim] rows); "spark_runtime/kv_cache.rs", KvCacheDtype
+// (bf16 copy, fp8 E4M3 with a per-tensor scale, turbo: wht_bf16_inplace then
+// Lloyd-Max codes with one E4M3 scale per 16 elements).
+//
+// One wave64 writes one (token, kv head) row of one side: head_dim/64 values
+// per lane.  The rotation is done in registers: butterfly strides below the
+// per-lane count stay in the lane, the rest are lane-xor exchanges.  Group
+// absmax and code packing are lane reductions; nothing touches LDS.
+//
+// Bit-exactness: every rounding step is a single IEEE fp32 operation in a
+// fixed order (file compiled with -ffp-contract=off):
+//   butterflies (ascending stride) -> * RN32(1/sqrt(d)) -> round to bf16 ->
+//   group absmax -> s = absmax * RN32(1/c_max) -> E4M3(s) = sigma, s_q ->
+//   code = #{k : y >= s_q * t_k} -> little-endian bit packing.
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+template <int E>
+__device__ __forceinline__ void load_bf16(const uint16_t* __restrict__ p, int lane, uint32_t (&raw)[E]) {
+  if constexpr (E == 1) {
+    raw[0] = p[lane];
+  } else if constexpr (E == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(p)[lane];
+    raw[0] = w & 0xFFFFu;
+    raw[1] = w >> 16;
+  } else {
+    const uint2 w = reinterpret_cast<const uint2*>(p)[lane];
+    raw[0] = w.x & 0xFFFFu;
+    raw[1] = w.x >> 16;
+    raw[2] = w.y & 0xFFFFu;
+    raw[3] = w.y >> 16;
+  }
+}
+
+// Store E bytes (packed little-endian in `v`) at dst + lane*E.
+template <int E>
+__device__ __forceinline__ void store_bytes(uint8_t* __restrict__ dst, int lane, uint32_t v) {
+  if constexpr (E == 1) dst[lane] = uint8_t(v);
+  else if constexpr (E == 2) reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(v);
+  else reinterpret_cast<uint32_t*>(dst)[lane] = v;
+}
+
+template <int HD, int BITS>
+__device__ __forceinline__ void write_turbo(const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
+                                            uint32_t row, uint64_t data_bytes, const WriteArgs& a,
+                                            int lane) {
+  constexpr int E = HD / 64;
+  constexpr int L = 1 << BITS;
+  float y[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) y[e] = bf16_bits_to_float(raw[e]);
+  // in-lane butterflies (stride < E)
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if ((e & h) == 0) {
+        const float lo = y[e], hi = y[e + h];
+        y[e] = lo + hi;
+        y[e + h] = lo - hi;
+      }
+    }
+  }
+  // cross-lane butterflies: element stride h = m*E pairs lane with lane ^ m
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float other = __shfl_xor(y[e], m);
+      y[e] = (lane & m) ? (other - y[e]) : (y[e] + other);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    y[e] = round_to_bf16(y[e] * a.wht_scale);
+    amax = fmaxf(amax, fabsf(y[e]));
+  }
+  amax = group_max<16 / E>(amax);  // one group of 16 elements = 16/E lanes
+  const float s = amax * a.cb.inv_cmax[BITS - 2];
+  const uint32_t sigma = e4m3_encode(s);
+  const float sq = e4m3_decode(sigma);
+  float t[L];
+#pragma unroll
+  for (int k = 1; k < L; ++k) t[k] = sq * a.cb.threshold[BITS - 2][k];
+  // pack: a unit of U elements fills whole bytes (4 bytes, or 3 for 3-bit)
+  constexpr int U = (BITS == 3) ? 8 : 32 / BITS;
+  constexpr int LU = U / E;  // lanes per unit
+  uint32_t part = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 1; k < L; ++k) c += (y[e] >= t[k]) ? 1u : 0u;
+    part |= c << (BITS * ((lane * E + e) % U));
+  }
+#pragma unroll
+  for (int m = 1; m < LU; m <<= 1) part |= uint32_t(__shfl_xor(int(part), m));
+  uint8_t* codes = blk + uint64_t(row) * (HD * BITS / 8);
+  if ((lane % LU) == 0) {
+    const int unit = lane / LU;
+    if constexpr (BITS == 3) {
+      uint8_t* d = codes + unit * 3;
+      d[0] = uint8_t(part);
+      d[1] = uint8_t(part >> 8);
+      d[2] = uint8_t(part >> 16);
+    } else {
+      reinterpret_cast<uint32_t*>(codes)[unit] = part;
+    }
+  }
+  if ((lane % (16 / E)) == 0) {
+    blk[data_bytes + uint64_t(row) * (HD / 16) + lane / (16 / E)] = uint8_t(sigma);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ src, uint8_t* __restrict__ blk,
+                                          uint32_t row, uint64_t data_bytes, float scale,
+                                          const WriteArgs& a, int lane) {
+  constexpr int E = HD / 64;
+  uint32_t raw[E];
+  load_bf16<E>(src, lane, raw);
+  if (fmt == KVQ_BF16) {
+    uint8_t* dst = blk + uint64_t(row) * HD * 2;
+    if constexpr (E == 1) reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(raw[0]);
+    else if constexpr (E == 2) reinterpret_cast<uint32_t*>(dst)[lane] = raw[0] | (raw[1] << 16);
+    else reinterpret_cast<uint2*>(dst)[lane] = make_uint2(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16));
+  } else if (fmt == KVQ_FP8_E4M3) {
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) packed |= e4m3_encode(bf16_bits_to_float(raw[e]) / scale) << (8 * e);
+    store_bytes<E>(blk + uint64_t(row) * HD, lane, packed);
+  } else if (fmt == KVQ_TURBO2) {
+    write_turbo<HD, 2>(raw, blk, row, data_bytes, a, lane);
+  } else if (fmt == KVQ_TURBO3) {
+    write_turbo<HD, 3>(raw, blk, row, data_bytes, a, lane);
+  } else {
+    write_turbo<HD, 4>(raw, blk, row, data_bytes, a, lane);
+  }
+}
+
+// Work item w = (token, kv head, side) with side fastest; one wave per item.
+template <int HD>
+__global__ __launch_bounds__(256) void write_kernel(const WriteArgs a) {
+  const uint32_t item = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t per_token = a.num_kv_heads * 2u;
+  if (item >= a.num_tokens * per_token) return;
+  const uint32_t t = item / per_token;
+  const uint32_t rem = item - t * per_token;
+  const uint32_t h = rem >> 1;
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  const uint64_t blk = uint64_t(slot) >> a.log2_bs;
+  const uint32_t off = uint32_t(slot) & ((1u << a.log2_bs) - 1u);
+  const uint32_t row = off * a.num_kv_heads + h;
+  if ((rem & 1u) == 0) {
+    write_row<HD>(a.k_format, a.key + uint64_t(t) * a.key_stride + h * HD, a.k_cache + blk * a.k_stride,
+                  row, a.k_data, a.k_scale, a, lane);
+  } else {
+    write_row<HD>(a.v_format, a.value + uint64_t(t) * a.value_stride + h * HD, a.v_cache + blk * a.v_stride,
+                  row, a.v_data, a.v_scale, a, lane);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_write(int head_dim, const WriteArgs& a, hipStream_t st) {
+  const uint64_t items = uint64_t(a.num_tokens) * a.num_kv_heads * 2u;
+  const dim3 grid(uint32_t((items + 3) / 4)), block(256);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(write_kernel<64>, grid, block, 0, st, a); break;
+    case 128: hipLaunchKernelGGL(write_kernel<128>, grid, block, 0, st, a); break;
+    case 256: hipLaunchKernelGGL(write_kernel<256>, grid, block, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -57,6 +57,7 @@ class Workload:
     sliding_window: int = 0
     pool_blocks: Optional[int] = None  # None: exactly the blocks the sequences need
     write_tail: int = 1               # positions per sequence written by the timed step
+    fixed_lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths
 
     @property
     def group(self) -> int:
@@ -90,6 +91,8 @@ def _gen(wid: int, stream: int, idx: int, device) -> torch.Generator:
 
 
 def seq_lens(w: Workload) -> np.ndarray:
+    if w.fixed_lens is not None:
+        return np.asarray(w.fixed_lens, dtype=np.int32)
     lo, hi = w.seq_len
     if lo == hi:
         return np.full(w.num_seqs, lo, dtype=np.int32)
@@ -109,7 +112,8 @@ def block_tables(w: Workload, lens: np.ndarray, max_blocks_per_seq: Optional[int
     num_blocks = total if w.pool_blocks is None else max(w.pool_blocks, total)
     g = _gen(w.wid, _S_PERM, 0, "cpu")
     perm = torch.randperm(num_blocks, generator=g).numpy().astype(np.int32)
-    mb = max_blocks_per_seq or max(1, (w.seq_len[1] + bs - 1) // bs)
+    longest = max([int(x) for x in lens] + [w.seq_len[1]])
+    mb = max_blocks_per_seq or max(1, (longest + bs - 1) // bs)
     bt = np.full((len(lens), mb), -1, dtype=np.int32)
     o = 0
     for s, n in enumerate(need):
@@ -212,3 +216,14 @@ def make_case(w: Workload, device="cpu", seqs: Optional[Sequence[int]] = None) -
     vmax = max((float(t.abs().max().float()) for t in v if t.numel()), default=1.0)
     return Case(w, lens, bt, nb, queries(w, device), k, v,
                 fp8_scale_from_absmax(kmax), fp8_scale_from_absmax(vmax))
+
+
+def small(wid: int, *, lens, num_q_heads, num_kv_heads, head_dim, block_size, k_format, v_format,
+          dist="normal", outliers=True, sparse_v_threshold=0.0, sliding_window=0,
+          extra_blocks=3) -> Workload:
+    """A test-sized workload with explicit sequence lengths (ragged, empty, ...)."""
+    need = sum((int(L) + block_size - 1) // block_size for L in lens)
+    return Workload(wid, f"small-{wid}", len(lens), num_q_heads, num_kv_heads, head_dim, block_size,
+                    k_format, v_format, (max(lens), max(lens)), dist=dist, outliers=outliers,
+                    sparse_v_threshold=sparse_v_threshold, sliding_window=sliding_window,
+                    pool_blocks=need + extra_blocks, fixed_lens=tuple(int(L) for L in lens))

@@ -1,0 +1,158 @@
+"""The C-ABI library on the host: it loads, exports what include/kvq.h
+declares, and its host-only parts (layout, tables, argument checks, workspace
+size query) behave as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_quantized_kv_kvq_amd as kvq
+from oracle import codebook as ocb
+from oracle import layout as olayout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvq.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = os.popen(f"nm -D --defined-only {kvq.library_path()}").read()
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    assert set(names) <= exported
+
+
+@pytest.mark.parametrize("kf", list(kvq.FORMATS))
+@pytest.mark.parametrize("vf", list(kvq.FORMATS))
+def test_layout_matches_oracle(kf, vf):
+    for bs, nkv, hd in [(16, 8, 128), (16, 2, 64), (16, 4, 256), (32, 8, 128), (1, 1, 64), (1024, 256, 256)]:
+        lay = kvq.pool_layout(kf, vf, bs, nkv, hd)
+        ks, vs = olayout.pool_layout(kf, vf, bs, nkv, hd)
+        assert (lay.k_data_section_bytes, lay.k_block_stride_bytes) == (ks.data_section_bytes, ks.block_stride_bytes)
+        assert (lay.v_data_section_bytes, lay.v_block_stride_bytes) == (vs.data_section_bytes, vs.block_stride_bytes)
+        assert lay.k_rotated == olayout.is_rotated(kf) and lay.v_rotated == olayout.is_rotated(vf)
+
+
+def test_layout_rejects(lib):
+    lay = kvq.Layout()
+    assert lib.kvq_pool_layout(5, 0, 16, 8, 128, ctypes.byref(lay)) == INVALID
+    assert lib.kvq_pool_layout(0, -1, 16, 8, 128, ctypes.byref(lay)) == INVALID
+    assert lib.kvq_pool_layout(0, 0, 0, 8, 128, ctypes.byref(lay)) == INVALID
+    assert lib.kvq_pool_layout(0, 0, 16, 8, 128, None) == INVALID
+    assert lib.kvq_pool_layout(0, 0, 12, 8, 128, ctypes.byref(lay)) == UNSUPPORTED
+    assert lib.kvq_pool_layout(0, 0, 2048, 8, 128, ctypes.byref(lay)) == UNSUPPORTED
+    assert lib.kvq_pool_layout(2, 2, 16, 8, 96, ctypes.byref(lay)) == UNSUPPORTED
+    assert lib.kvq_pool_layout(2, 2, 16, 300, 128, ctypes.byref(lay)) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt,bits", [("turbo2", 2), ("turbo3", 3), ("turbo4", 4)])
+def test_codebook_tables_bit_equal_to_oracle(fmt, bits):
+    lib_t = kvq.codebook(fmt)
+    ora = ocb.turbo_tables(bits)
+    assert lib_t["levels"] == ora["levels"]
+    assert np.array_equal(lib_t["centroids"].view(np.uint32), ora["centroids"].view(np.uint32))
+    assert np.array_equal(lib_t["thresholds"].view(np.uint32), ora["thresholds"].view(np.uint32))
+    assert lib_t["inv_cmax"].view(np.uint32) == ora["inv_cmax"].view(np.uint32)
+
+
+def test_codebook_rejects_non_turbo():
+    with pytest.raises(kvq.KvqError):
+        kvq.codebook("bf16")
+
+
+# ---------------------------------------------------------------- argument checks
+# Fake, suitably aligned addresses: every call below must fail on the host
+# before anything is launched.
+A = 0x7F0000000000
+
+
+def _write(lib, lay, key=A, value=A, kc=A, vc=A, slots=A, T=4, ks=None, vs=None, k_scale=1.0, v_scale=1.0):
+    n = lay.num_kv_heads * lay.head_dim
+    ks = n if ks is None else ks
+    vs = n if vs is None else vs
+    return lib.kvq_reshape_and_cache(ctypes.byref(lay), key, value, kc, vc, slots, T, ks, vs,
+                                     k_scale, v_scale, None)
+
+
+def test_write_checks(lib):
+    lay = kvq.pool_layout("fp8", "turbo3", 16, 8, 128)
+    assert _write(lib, lay, T=0) == OK                     # nothing to do
+    assert _write(lib, lay, key=0) == INVALID
+    assert _write(lib, lay, ks=8 * 128 - 8) == INVALID     # rows overlap
+    assert _write(lib, lay, ks=8 * 128 + 4) == ALIGN
+    assert _write(lib, lay, key=A + 8) == ALIGN
+    assert _write(lib, lay, kc=A + 4) == ALIGN
+    assert _write(lib, lay, slots=A + 4) == ALIGN
+    assert _write(lib, lay, k_scale=0.0) == INVALID        # fp8 K needs a scale
+    assert _write(lib, lay, k_scale=float("nan")) == INVALID
+    bad = kvq.pool_layout("fp8", "turbo3", 16, 8, 128)
+    bad.v_block_stride_bytes += 16                         # not a layout the library made
+    assert _write(lib, bad) == INVALID
+    assert lib.kvq_reshape_and_cache(None, A, A, A, A, A, 4, 1024, 1024, 1.0, 1.0, None) == INVALID
+
+
+def _decode(lib, lay, Hq=32, S=2, mb=8, thr=0.0, win=0, inv=0.1, qs=None, ks=1.0, vs=1.0, ws=A, wsb=1 << 40,
+            q=A, out=A, bt=A, sl=A, kc=A):
+    qs = Hq * lay.head_dim if qs is None else qs
+    n = ctypes.c_size_t(wsb)
+    st = lib.kvq_paged_decode(ctypes.byref(lay), q, kc, A, out, bt, sl, mb, S, Hq, inv, qs, win, thr, ks, vs,
+                              ws, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_decode_checks(lib):
+    lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
+    assert _decode(lib, lay, Hq=12)[0] == INVALID           # Hq not a multiple of Hkv
+    assert _decode(lib, lay, Hq=24)[0] == UNSUPPORTED       # G = 3
+    assert _decode(lib, lay, Hq=128)[0] == UNSUPPORTED      # G = 16
+    assert _decode(lib, lay, inv=0.0)[0] == INVALID
+    assert _decode(lib, lay, thr=-1e-3)[0] == INVALID
+    assert _decode(lib, lay, thr=float("inf"))[0] == INVALID
+    assert _decode(lib, lay, qs=32 * 128 - 8)[0] == INVALID
+    assert _decode(lib, lay, qs=32 * 128 + 4)[0] == ALIGN
+    assert _decode(lib, lay, mb=0)[0] == INVALID
+    assert _decode(lib, lay, wsb=16)[0] == WORKSPACE
+    assert _decode(lib, lay, q=A + 2)[0] == ALIGN
+    assert _decode(lib, lay, out=A + 4)[0] == ALIGN
+    assert _decode(lib, lay, bt=A + 2)[0] == ALIGN
+    assert _decode(lib, lay, q=0)[0] == INVALID
+    fp8 = kvq.pool_layout("fp8", "turbo2", 16, 8, 128)
+    assert _decode(lib, fp8, ks=0.0)[0] == INVALID
+
+
+def test_decode_workspace_query(lib):
+    lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
+    st, dense = _decode(lib, lay, ws=0, wsb=0, S=64, mb=512)
+    assert st == OK and dense > 0
+    st, sparse = _decode(lib, lay, ws=0, wsb=0, S=64, mb=512, thr=1e-3)
+    assert st == OK and sparse > 0 and sparse != dense
+    # binding helper agrees
+    assert kvq.decode_workspace_bytes(lay, 64, 32, 512, 0, 1e-3) == sparse
+    # a window bounds the work, so the workspace shrinks
+    st, win = _decode(lib, lay, ws=0, wsb=0, S=64, mb=512, win=256)
+    assert st == OK and win < dense
+    # zero sequences: a valid, launch-free call
+    st, _ = _decode(lib, lay, S=0, ws=A, wsb=1 << 20)
+    assert st == OK
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5, 99):
+        assert lib.kvq_status_string(code)

@@ -1,0 +1,124 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Write: pool bytes (slots, packed codes, scale bytes) bit-exact.  Decode:
+max-abs <= 2e-3 and rel-L2 <= 1e-3 against the fp64 oracle, on the same
+seeded inputs.  Pools are poison-filled and unused page-table entries point
+at a poison block, and the decode workspace starts as NaN, so a stray read
+shows up as a non-finite output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.gpu import stage
+from kvq_testlib import OracleCache, check_decode, say, timed
+
+pytestmark = pytest.mark.gpu
+
+FMTS = list(synth.FORMATS)
+ALL_PAIRS = [(k, v) for k in FMTS for v in FMTS]
+
+
+def _decode(kvq, st, out=None):
+    w = st.w
+    need = kvq.decode_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, st.bt.shape[1], w.sliding_window,
+                                      w.sparse_v_threshold)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+    return kvq.paged_decode(st.layout, st.q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev,
+                            synth.inv_sqrt_d(w.head_dim), w.sliding_window, w.sparse_v_threshold,
+                            st.k_scale, st.v_scale, out=out, workspace=ws)
+
+
+def run(kvq, w, seqs=None, tail=None, label="", from_window=False, check_pools=True):
+    seqs = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    say(f"case {label}: {w}")
+    st = stage(w, kvq, "cuda", keep_host=seqs, write_tail=tail)
+    if st.tail_slots.numel():
+        kvq.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool, st.tail_slots,
+                              st.k_scale, st.v_scale)
+    out = _decode(kvq, st)
+    torch.cuda.synchronize()
+    out_np = out.cpu().numpy()
+    ora = OracleCache(st, seqs, from_window=from_window)
+    if check_pools:
+        ora.compare_pools(st)
+    ref = ora.decode(st, synth.inv_sqrt_d(w.head_dim))
+    e, rel, namb = check_decode(out_np, ref, seqs, label)
+    say(f"  ok {label}: max-abs {e:.2e} rel-L2 {rel:.2e} ambiguous {namb}")
+    return st, out
+
+
+LENS = [0, 1, 15, 16, 17, 300, 1100]
+
+
+@pytest.mark.parametrize("kf,vf", ALL_PAIRS)
+def test_pairs_dense(gpu_lib, kf, vf):
+    w = synth.small(1000 + FMTS.index(kf) * 5 + FMTS.index(vf), lens=LENS, num_q_heads=8, num_kv_heads=2,
+                    head_dim=128, block_size=16, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=3, label=f"{kf}/{vf} dense")
+
+
+@pytest.mark.parametrize("hd", [64, 256])
+@pytest.mark.parametrize("kf,vf", [("bf16", "bf16"), ("fp8", "turbo2"), ("turbo3", "turbo3"),
+                                   ("turbo4", "turbo3"), ("bf16", "turbo4"), ("turbo2", "fp8")])
+def test_head_dims(gpu_lib, kf, vf, hd):
+    w = synth.small(2000 + hd + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[5, 64, 700], num_q_heads=4,
+                    num_kv_heads=2, head_dim=hd, block_size=16, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=2, label=f"{kf}/{vf} hd{hd}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 8])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3")])
+def test_group_sizes(gpu_lib, kf, vf, g):
+    w = synth.small(3000 + g * 10 + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[33, 517, 260], num_q_heads=2 * g,
+                    num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=1, label=f"{kf}/{vf} G{g}")
+
+
+@pytest.mark.parametrize("bs", [1, 2, 32, 128])
+def test_block_sizes(gpu_lib, bs):
+    w = synth.small(4000 + bs, lens=[1, 77, 600, 257], num_q_heads=8, num_kv_heads=4, head_dim=128,
+                    block_size=bs, k_format="fp8", v_format="turbo4")
+    run(gpu_lib, w, tail=2, label=f"bs{bs}")
+
+
+@pytest.mark.parametrize("thr", [1e-3, 0.05])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo3", "turbo3"), ("fp8", "fp8"), ("bf16", "bf16"),
+                                   ("turbo4", "turbo2")])
+def test_sparse_v(gpu_lib, kf, vf, thr):
+    w = synth.small(5000 + int(thr * 1e4) + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[0, 1, 40, 1500, 2100],
+                    num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf,
+                    sparse_v_threshold=thr)
+    run(gpu_lib, w, tail=2, label=f"{kf}/{vf} thr{thr}")
+
+
+@pytest.mark.parametrize("win,thr", [(1, 0.0), (100, 0.0), (700, 1e-3), (5000, 0.0)])
+def test_sliding_window(gpu_lib, win, thr):
+    w = synth.small(6000 + win, lens=[0, 50, 333, 1600], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    block_size=16, k_format="turbo3", v_format="turbo4", sliding_window=win,
+                    sparse_v_threshold=thr)
+    run(gpu_lib, w, tail=1, label=f"window {win} thr {thr}")
+
+
+def test_student_t_values(gpu_lib):
+    w = synth.small(7000, lens=[900, 31], num_q_heads=16, num_kv_heads=4, head_dim=256, block_size=16,
+                    k_format="turbo3", v_format="turbo3", dist="student_t5", outliers=False,
+                    sparse_v_threshold=1e-3, sliding_window=512)
+    run(gpu_lib, w, tail=4, label="student-t turbo3")
+
+
+def test_decode_is_deterministic(gpu_lib):
+    w = synth.small(8000, lens=[1000, 3000], num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                    k_format="bf16", v_format="turbo4", sparse_v_threshold=1e-3)
+    st = stage(w, gpu_lib, "cuda", write_tail=0)
+    a = _decode(gpu_lib, st).clone()
+    b = _decode(gpu_lib, st)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all() and torch.equal(a, b)
+    w2 = w.scaled(sparse_v_threshold=0.0)
+    st.w = w2
+    a = _decode(gpu_lib, st).clone()
+    b = _decode(gpu_lib, st)
+    torch.cuda.synchronize()
+    assert torch.isfinite(a).all() and torch.equal(a, b)
