@@ -1,0 +1,277 @@
+"""Benchmark: paged quantized KV write + paged decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one pass of the whole hot path over one batch: every sequence's new
+token is written into the paged pools (kvq_reshape_and_cache, scattered slots)
+and then every sequence decodes one token over its pages (kvq_paged_decode).
+Inputs are seeded synthetic data of the workload's shapes, staged in HBM
+before the timed region.  Prints one JSON line.
+
+value      effective KV GB/s: K+V bytes of every attended (position, kv head)
+           at the storage formats' sizes, per step time (sparse V skips some
+           of those bytes; the roofline below counts only what must move).
+roofline   the decode call (its two kernels: score/candidate pass and V pass,
+           or split pass and merge) timed with HIP events on the stream the
+           library launches on; algorithmic bytes = K of every attended
+           position + V of every position some head keeps + q + out + the
+           page-table entries and lengths read.
+cpu_baseline  the CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from synth.gpu import stage  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+ROW_BYTES = {"bf16": lambda hd: 2 * hd, "fp8": lambda hd: hd, "turbo4": lambda hd: hd // 2 + hd // 16,
+             "turbo3": lambda hd: hd * 3 // 8 + hd // 16, "turbo2": lambda hd: hd // 4 + hd // 16}
+METRIC = "paged-decode effective KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_quantized_kv_kvq_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kept_rows(st, w) -> int:
+    """(position, kv head) pairs whose V some query head of the group keeps.
+
+    Measurement bookkeeping only (plain torch on the device): scores from the
+    stored K, exact for bf16 K; for other K formats the dense count is used.
+    """
+    S, G, Hkv, hd = w.num_seqs, w.group, w.num_kv_heads, w.head_dim
+    P = _attended(st, w)
+    if w.sparse_v_threshold <= 0.0 or w.k_format != "bf16":
+        return int(P.sum()) * Hkv
+    bs = w.block_size
+    kp = st.k_pool.view(torch.bfloat16)
+    blk_elems = bs * Hkv * hd
+    total = 0
+    inv = synth.inv_sqrt_d(hd)
+    for s in range(S):
+        L = int(st.lens[s])
+        j0 = max(0, L - w.sliding_window) if w.sliding_window else 0
+        if L <= j0:
+            continue
+        j = torch.arange(j0, L, device="cuda")
+        pages = st.bt_dev[s, (j // bs)].long()
+        base = pages * blk_elems + (j % bs) * Hkv * hd
+        idx = base[:, None, None] + torch.arange(Hkv, device="cuda")[None, :, None] * hd + \
+            torch.arange(hd, device="cuda")[None, None, :]
+        K = kp[idx].float().permute(1, 2, 0).contiguous()       # [Hkv, hd, P]
+        q = st.q[s].float().view(Hkv, G, hd).contiguous()
+        sc = torch.matmul(q, K) * inv                            # [Hkv, G, P]
+        p = torch.softmax(sc, dim=-1)
+        total += int((p > w.sparse_v_threshold).any(dim=1).sum())
+    return total
+
+
+def _attended(st, w) -> np.ndarray:
+    L = st.lens.astype(np.int64)
+    if w.sliding_window:
+        return np.minimum(L, w.sliding_window)
+    return L
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_decode:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(st, w, n_seqs: int):
+    """Oracle (plain numpy, fp64 attention) on the first n_seqs sequences."""
+    from oracle import decode as odecode
+    from oracle import layout as olayout
+    from oracle import write as owrite
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_baseline(st, w, n_seqs, odecode, olayout, owrite)
+
+
+def _cpu_baseline(st, w, n_seqs, odecode, olayout, owrite):
+    seqs = list(range(n_seqs))
+    ks, vs = olayout.pool_layout(w.k_format, w.v_format, w.block_size, w.num_kv_heads, w.head_dim)
+    bs = w.block_size
+    remap = {}
+    for s in seqs:
+        for b in st.bt[s, :(int(st.lens[s]) + bs - 1) // bs]:
+            remap.setdefault(int(b), len(remap))
+    n = len(remap) + 1
+    kp = np.zeros(n * ks.block_stride_bytes, np.uint8)
+    vp = np.zeros(n * vs.block_stride_bytes, np.uint8)
+    bt = np.full_like(st.bt, -1)
+    for s in seqs:
+        nb = (int(st.lens[s]) + bs - 1) // bs
+        bt[s, :nb] = [remap[int(b)] for b in st.bt[s, :nb]]
+    tail = w.write_tail
+    pre = {}
+    for s in seqs:  # cache contents before the step (untimed)
+        K, V = st.host_kv[s]
+        L = int(st.lens[s])
+        pos = np.arange(max(0, L - tail))
+        slots = bt[s, pos // bs].astype(np.int64) * bs + pos % bs
+        owrite.reshape_and_cache(ks, vs, K[pos], V[pos], kp, vp, slots, st.k_scale, st.v_scale)
+        pre[s] = L
+    q = st.q.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    t0 = time.perf_counter()
+    for s in seqs:  # the step: write the new tokens, then decode
+        K, V = st.host_kv[s]
+        L = int(st.lens[s])
+        pos = np.arange(max(0, L - tail), L)
+        slots = bt[s, pos // bs].astype(np.int64) * bs + pos % bs
+        owrite.reshape_and_cache(ks, vs, K[pos], V[pos], kp, vp, slots, st.k_scale, st.v_scale)
+    odecode.paged_decode(ks, vs, q, kp, vp, bt, st.lens, synth.inv_sqrt_d(w.head_dim), w.sliding_window,
+                         w.sparse_v_threshold, st.k_scale, st.v_scale, seqs=seqs)
+    dt = time.perf_counter() - t0
+    att = _attended(st, w)[seqs].sum()
+    kv_bytes = att * w.num_kv_heads * (ROW_BYTES[w.k_format](w.head_dim) + ROW_BYTES[w.v_format](w.head_dim))
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seqs} of {w.num_seqs} sequences ({int(att)} attended positions): write of their "
+                      f"new token + fp64 decode of all {w.num_q_heads} q heads, one thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-seqs", type=int, default=24, help="sequences in the oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU: this path has no multi-GPU step (asked for {args.gpus}); "
+              "each GPU would serve its own sequences or kv heads with no exchange", file=sys.stderr)
+        sys.exit(2)
+    import paged_quantized_kv_kvq_amd as kvq
+    kvq.load()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    keep = range(min(args.cpu_seqs, w.num_seqs)) if args.cpu_seqs else ()
+    t0 = time.time()
+    st = stage(w, kvq, "cuda", keep_host=keep, log=log)
+    log(f"staged {w.name} in {time.time() - t0:.1f}s: {int(st.lens.sum())} positions, "
+        f"{st.num_blocks} blocks, tail batch {st.tail_slots.numel()} tokens")
+    hd, Hkv = w.head_dim, w.num_kv_heads
+    inv = synth.inv_sqrt_d(hd)
+    mb = st.bt.shape[1]
+    ws = torch.empty(max(16, kvq.decode_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, mb,
+                                                        w.sliding_window, w.sparse_v_threshold)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.num_seqs, w.num_q_heads, hd), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def write():
+        kvq.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool, st.tail_slots,
+                              st.k_scale, st.v_scale, stream=stream)
+
+    def decode():
+        kvq.paged_decode(st.layout, st.q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev, inv, w.sliding_window,
+                         w.sparse_v_threshold, st.k_scale, st.v_scale, out=out, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        write()
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_step = elapsed * 1e3 / args.steps
+    assert torch.isfinite(out).all(), "non-finite decode output"
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    att = _attended(st, w)
+    positions = int(att.sum())
+    kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
+    kv_dense = positions * Hkv * (kb + vb)
+    kept = kept_rows(st, w)
+    alg = (positions * Hkv * kb + kept * vb + w.num_seqs * w.num_q_heads * hd * (2 + 4)
+           + sum(int(math.ceil(int(L) / w.block_size)) for L in att) * 4 + w.num_seqs * 4)
+    achieved = alg / (dec_ms * 1e-3) / 1e9
+    value = kv_dense / (ms_step * 1e-3) / 1e9
+    traffic = traffic_from_profile(w.name)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "k_format": w.k_format, "v_format": w.v_format,
+                   "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": Hkv, "head_dim": hd,
+                   "block_size": w.block_size, "seq_lens": list(w.seq_len), "attended_positions": positions,
+                   "sparse_v_threshold": w.sparse_v_threshold, "sliding_window": w.sliding_window,
+                   "write_tokens_per_step": int(st.tail_slots.numel()), "parallelism": "1 GPU"},
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "decode_ms": round(dec_ms, 4),
+        "kept_v_fraction": round(kept / max(1, positions * Hkv), 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic, 0),
+                     "kernel": "kvq_paged_decode (both kernels)", "algorithmic_bytes": alg},
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    if args.cpu_seqs:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = cpu_baseline(st, w, min(args.cpu_seqs, w.num_seqs))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -118,7 +118,7 @@ bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
   uint32_t split_len, nsplit;
-  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cs, bytes;
+  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cpage, off_cs, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -141,16 +141,17 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
+  p.off_part = p.off_cnt = p.off_cidx = p.off_cpage = p.off_cs = 0;
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
-    p.off_cnt = p.off_cidx = p.off_cs = 0;
   } else {
-    p.off_part = 0;
     p.off_cnt = off;
     off = up256(off + units * sizeof(int32_t));
     p.off_cidx = off;
     off = up256(off + units * sl * sizeof(int32_t));
+    p.off_cpage = off;
+    off = up256(off + units * sl * sizeof(uint64_t));
     p.off_cs = off;
     off = up256(off + units * sl * G * sizeof(float));
   }
@@ -264,12 +265,13 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.ml = reinterpret_cast<float*>(ws + p.off_ml);
-  if (sparse) {
+  if (!sparse) {
+    a.part = reinterpret_cast<float*>(ws + p.off_part);
+  } else {
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     a.cidx = reinterpret_cast<int32_t*>(ws + p.off_cidx);
+    a.cvbase = reinterpret_cast<uint64_t*>(ws + p.off_cpage);
     a.cscore = reinterpret_cast<float*>(ws + p.off_cs);
-  } else {
-    a.part = reinterpret_cast<float*>(ws + p.off_part);
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -311,7 +313,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO3: e = launch_scores_turbo3(int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
-    if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, s);
+    if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, num_seqs * nkv, s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

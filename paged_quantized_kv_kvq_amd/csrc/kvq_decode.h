@@ -3,8 +3,8 @@
 //
 // "metrale_model_layers/layers/ops/kv_cache_bf16k_turbov.rs",
 // paged_decode_attn_bf16k_turbo{2,3,4}v: block_tables / seq_lens walk, GQA,
-// inv_sqrt_d, sliding_window, and the sparse-V skip ("skips a position's V
-// load and dequant when its attention weight is at most" the threshold).
+// inv_sqrt_d, sliding_window, and the sparse-V skip (a position's V is not
+// loaded or dequantized when its attention weight is at most the threshold).
 // "combs_models/kv.rs", attend: softmax(q K^T * scale) V, no mask for a single
 // decode query.  "spark_runtime/kv_cache.rs", is_wht_rotated: rotated K sides
 // are scored against WHT(q); rotated V sides give WHT(out), rotated back.
@@ -13,19 +13,25 @@
 //   * split-K over positions: a workgroup handles (sequence, kv head, split of
 //     split_len positions) and ALL G = Hq/Hkv query heads of that kv head, so
 //     every K/V byte is read once, not G times;
-//   * inside a wave, T = head_dim/8 lanes share one position (8 dims per
-//     lane) and 64/T positions are in flight per step, kUnroll steps deep;
-//     a score is a T-lane DPP sum;
-//   * every lane-slot keeps its own online softmax state (log2 domain), merged
-//     across slots and waves at the end of the split;
+//   * a wave walks 16-position chunks.  When block_size >= 16 a chunk lies in
+//     one block, so its page base is a scalar and every lane address is a
+//     32-bit offset from it; the next chunk's loads are issued before the
+//     current chunk is computed (two register buffers);
+//   * inside a chunk, T = head_dim/D lanes share one position (D = 16 dims
+//     per lane, 8 for G = 8) and 64/T positions are side by side; a score is
+//     a T-lane DPP sum of bf16 dot products (v_dot2_f32_bf16 for bf16 K and
+//     for fp8 K widened exactly to bf16) or fp32 FMAs (rotated turbo K);
+//   * every lane slot keeps its own online softmax state (log2 domain),
+//     merged across slots and waves at the end of the split;
 //   * dense (threshold 0): partial (max, sum, unnormalized output) per split,
-//     combined by merge_kernel (which also applies the iWHT);
-//   * sparse (threshold > 0): scores_kernel stores only candidate positions
-//     (split-local weight above thr: an upper bound on the global weight), then
-//     sparse_v_kernel recomputes the exact global softmax weight of each
-//     candidate and loads V only where some head of the group keeps it.
-//   * workgroup ids are remapped so the kv heads of one (sequence, split) run
-//     on the same XCD and share L2 lines (heads of a page are interleaved).
+//     combined by merge_kernel (which also applies the inverse rotation);
+//   * sparse (threshold > 0): scores_kernel keeps only candidate positions
+//     (split-local weight above thr: an upper bound on the global weight);
+//     sparse_v_kernel, one workgroup per (sequence, kv head), recomputes each
+//     candidate's exact global weight, loads V only where some head of the
+//     group keeps it, and writes the output;
+//   * workgroup ids are renumbered so the kv heads of one (sequence, split)
+//     run on the same XCD and share L2 lines (the heads of a page interleave).
 #pragma once
 
 #include "kvq_device.h"
@@ -33,119 +39,178 @@
 namespace kvq {
 
 constexpr int kWaves = 4;        // waves per workgroup
-constexpr int kDims = 8;         // head_dim elements per lane
-constexpr int kUnroll = 4;       // positions in flight per lane slot
+constexpr int kChunk = 16;       // positions per wave iteration
 constexpr int kMaxPages = 512;   // page ids of one split staged in LDS
 constexpr int kMaxSparseSplit = 1024;
+constexpr int kCandUnroll = 4;   // kept V rows in flight per lane slot (sparse V)
 
 template <int F>
 struct Fmt {
   static constexpr int bits = (F == KVQ_BF16) ? 16 : (F == KVQ_FP8_E4M3) ? 8 : F;
   static constexpr bool turbo = F >= KVQ_TURBO2;
-  static constexpr int words = (bits == 16) ? 4 : (bits == 8) ? 2 : 1;
 };
 
-template <int F>
+// Lane geometry for a head size and group size.
+template <int HD, int G>
+struct Geo {
+  static constexpr int D = (G <= 4) ? 16 : 8;  // dims per lane
+  static constexpr int T = HD / D;             // lanes per position
+  static constexpr int P = kWave / T;          // positions side by side in a wave
+  static constexpr int U = kChunk / P;         // steps per chunk
+  static_assert(P >= 1 && P <= kChunk && kChunk % P == 0, "chunk geometry");
+};
+
+// One lane's bytes of one position: D elements (+ the group scale byte).
+template <int F, int D>
 struct Raw {
-  uint32_t w[Fmt<F>::words];
+  static constexpr int bytes = D * Fmt<F>::bits / 8;
+  static constexpr int words = (bytes + 3) / 4;
+  uint32_t w[words];
   uint32_t sc;
 };
 
-// Bytes of one lane's 8 elements of row `row` (8 elements = `bits` bytes).
-template <int F, int HD>
-__device__ __forceinline__ void load_chunk(const uint8_t* __restrict__ blk, uint32_t row, int t,
-                                           uint64_t data_bytes, Raw<F>& r) {
-  constexpr int bits = Fmt<F>::bits;
-  const uint8_t* p = blk + uint64_t(row) * (HD * bits / 8) + t * bits;
-  if constexpr (bits == 16) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
-  } else if constexpr (bits == 8) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    r.w[0] = v.x; r.w[1] = v.y;
-  } else if constexpr (bits == 4) {
+template <int F, int HD, int D>
+__device__ __forceinline__ void load_lane(const uint8_t* __restrict__ blk, uint32_t row, int t,
+                                          uint64_t data_bytes, Raw<F, D>& r) {
+  constexpr int B = Raw<F, D>::bytes;
+  const uint8_t* p = blk + uint64_t(row) * (HD * Fmt<F>::bits / 8) + t * B;
+  if constexpr (B == 32) {
+    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+    r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  } else if constexpr (B == 16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  } else if constexpr (B == 8) {
+    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = a.x; r.w[1] = a.y;
+  } else if constexpr (B == 4) {
     r.w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else if constexpr (bits == 2) {
+  } else if constexpr (B == 2) {
     r.w[0] = *reinterpret_cast<const uint16_t*>(p);
   } else {
-    r.w[0] = uint32_t(p[0]) | (uint32_t(p[1]) << 8) | (uint32_t(p[2]) << 16);
+    // 3-bit codes: 3 or 6 bytes at any alignment.  Read the two aligned
+    // dwords that cover them (at most 2 bytes past the row end, still inside
+    // the block: the scale section follows the codes) and shift.
+    const uintptr_t ad = reinterpret_cast<uintptr_t>(p);
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(ad & ~uintptr_t(3));
+    const uint64_t v = (uint64_t(q[1]) << 32 | q[0]) >> ((ad & 3u) * 8u);
+    r.w[0] = uint32_t(v);
+    if constexpr (Raw<F, D>::words > 1) r.w[1] = uint32_t(v >> 32) & 0xFFFFu;
   }
-  if constexpr (Fmt<F>::turbo) r.sc = blk[data_bytes + uint64_t(row) * (HD / 16) + (t >> 1)];
+  if constexpr (Fmt<F>::turbo) r.sc = blk[data_bytes + uint64_t(row) * (HD / 16) + (t * D) / 16];
   else r.sc = 0;
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <int F, int D>
+__device__ __forceinline__ void zero_raw(Raw<F, D>& r) {
+#pragma unroll
+  for (int i = 0; i < Raw<F, D>::words; ++i) r.w[i] = 0;
+  r.sc = 0;
+}
 
-// Raw chunk -> 8 fp32 values.  bf16: exact; fp8: the E4M3 value (the tensor
-// scale is applied by the caller); turbo: the codebook centroid (the group
-// scale is returned in `sq`).
-template <int F>
-__device__ __forceinline__ void dequant(const Raw<F>& r, const float* __restrict__ cen, float (&v)[kDims],
-                                        float& sq) {
-  constexpr int bits = Fmt<F>::bits;
-  sq = 1.0f;
-  if constexpr (bits == 16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(r.w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
-    }
-  } else if constexpr (bits == 8) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(r.w[i]), false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(r.w[i]), true);
-      v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
-    }
+// code i of a lane's turbo chunk
+template <int BITS, int D>
+__device__ __forceinline__ uint32_t code_at(const uint32_t* w, int i) {
+  if constexpr (BITS == 3 && D == 16) {
+    return uint32_t(((uint64_t(w[1]) << 32) | w[0]) >> (3 * i)) & 7u;
+  } else if constexpr (BITS == 3) {
+    return (w[0] >> (3 * i)) & 7u;
   } else {
-    constexpr uint32_t mask = (1u << bits) - 1u;
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) v[i] = cen[(r.w[0] >> (bits * i)) & mask];
-    sq = e4m3_decode(r.sc);
+    const int bit = BITS * i;
+    return (w[bit / 32] >> (bit % 32)) & ((1u << BITS) - 1u);
   }
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// two E4M3 bytes (low or high half of w) -> two bf16 (exact: every E4M3 value is a bf16 value)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, HI));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Shared prologue: q rows of the G heads in LDS (rotated when K is), the
-// codebook(s) and the split's page ids.
-template <int KF, int VF, int HD, int G>
-struct Smem {
-  float q[G][HD];
-  float kcen[16];
-  float vcen[16];
-  int32_t pages[kMaxPages];
+// Query registers of one lane: packed bf16 pairs (bf16 / fp8 K) or the rotated
+// fp32 query (turbo K), for the lane's D dims of each of the G heads.
+template <int KF, int D, int G>
+struct QReg {
+  static constexpr bool packed = !Fmt<KF>::turbo;
+  uint32_t qp[packed ? G : 1][packed ? D / 2 : 1];
+  float qf[packed ? 1 : G][packed ? 1 : D];
 };
 
-template <int KF, int VF, int HD, int G>
-__device__ __forceinline__ void prologue(const DecodeArgs& a, Smem<KF, VF, HD, G>& sm, uint32_t s, uint32_t g,
-                                         int pb, int pe) {
-  const int tid = threadIdx.x;
-  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
-  for (int i = tid; i < G * HD; i += kWaves * kWave) sm.q[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
-  if (tid < 16) {
-    if constexpr (Fmt<KF>::turbo) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
-    if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
-  }
-  if (pe > pb) {
-    const int first = pb >> a.log2_bs;
-    const int n = ((pe - 1) >> a.log2_bs) - first + 1;
-    const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks + first;
-    for (int i = tid; i < n; i += kWaves * kWave) sm.pages[i] = bt[i];
-  }
-  __syncthreads();
-  if constexpr (Fmt<KF>::turbo) {
-    // unnormalized WHT of every q row (the 1/sqrt(d) goes into the score scale)
-    for (int h2 = 1; h2 < HD; h2 <<= 1) {
-      for (int i = tid; i < G * HD / 2; i += kWaves * kWave) {
-        const int hh = i / (HD / 2), k = i % (HD / 2);
-        const int lo = (k / h2) * 2 * h2 + (k % h2);
-        const float x = sm.q[hh][lo], y = sm.q[hh][lo + h2];
-        sm.q[hh][lo] = x + y;
-        sm.q[hh][lo + h2] = x - y;
-      }
-      __syncthreads();
+// Partial score of one lane for every head (before the T-lane sum).
+template <int KF, int D, int G>
+__device__ __forceinline__ void lane_scores(const QReg<KF, D, G>& q, const Raw<KF, D>& k,
+                                            const float* __restrict__ kcen, float (&part)[G]) {
+  if constexpr (KF == KVQ_BF16) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D / 2; ++i) s = dot2_bf16(q.qp[h][i], k.w[i], s);
+      part[h] = s;
     }
+  } else if constexpr (KF == KVQ_FP8_E4M3) {
+    uint32_t kb[D / 2];
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      kb[2 * i] = fp8x2_to_bf16x2<false>(k.w[i]);
+      kb[2 * i + 1] = fp8x2_to_bf16x2<true>(k.w[i]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D / 2; ++i) s = dot2_bf16(q.qp[h][i], kb[i], s);
+      part[h] = s;
+    }
+  } else {
+    float kv[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) kv[i] = kcen[code_at<Fmt<KF>::bits, D>(k.w, i)];
+    const float sq = e4m3_decode(k.sc);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) s = fmaf(q.qf[h][i], kv[i], s);
+      part[h] = s * sq;
+    }
+  }
+}
+
+// V chunk -> D fp32 values (bf16 exact, fp8 the E4M3 value, turbo the
+// centroid with the group scale in `sq`).
+template <int VF, int D>
+__device__ __forceinline__ void v_values(const Raw<VF, D>& v, const float* __restrict__ vcen, float (&x)[D],
+                                         float& sq) {
+  sq = 1.0f;
+  if constexpr (VF == KVQ_BF16) {
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) {
+      x[2 * i] = __uint_as_float(v.w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(v.w[i] & 0xFFFF0000u);
+    }
+  } else if constexpr (VF == KVQ_FP8_E4M3) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v.w[i]), false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v.w[i]), true);
+      x[4 * i] = lo.x; x[4 * i + 1] = lo.y; x[4 * i + 2] = hi.x; x[4 * i + 3] = hi.y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) x[i] = vcen[code_at<Fmt<VF>::bits, D>(v.w, i)];
+    sq = e4m3_decode(v.sc);
   }
 }
 
@@ -162,49 +227,128 @@ __device__ __forceinline__ SeqSpan split_span(const DecodeArgs& a, uint32_t s, u
   return r;
 }
 
-// Scores of up to kUnroll positions of one lane slot (log2 units; -inf when
-// the position is past the end), with their K chunks loaded in one batch.
-template <int KF, int VF, int HD, int G, bool LOAD_V>
-__device__ __forceinline__ void score_step(const DecodeArgs& a, const Smem<KF, VF, HD, G>& sm,
-                                           const float (&qr)[G][kDims], int c0, int pb, int pe, uint32_t g,
-                                           int t, int r, float (&sc)[kUnroll][G], Raw<VF> (&vr)[kUnroll],
-                                           bool (&valid)[kUnroll]) {
-  constexpr int T = HD / kDims;
-  constexpr int P = kWave / T;
-  const int first = pb >> a.log2_bs;
-  const uint32_t bmask = (1u << a.log2_bs) - 1u;
-  Raw<KF> kr[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int j = c0 + u * P + r;
-    valid[u] = j < pe;
-    if (valid[u]) {
-      const uint64_t page = uint64_t(uint32_t(sm.pages[(j >> a.log2_bs) - first]));
-      const uint32_t row = (uint32_t(j) & bmask) * a.num_kv_heads + g;
-      load_chunk<KF, HD>(a.k_cache + page * a.k_stride, row, t, a.k_data, kr[u]);
-      if constexpr (LOAD_V) load_chunk<VF, HD>(a.v_cache + page * a.v_stride, row, t, a.v_data, vr[u]);
-    } else {
-      // past the end: zero bytes decode to finite values, so p = 0 times them stays 0
-#pragma unroll
-      for (int k = 0; k < Fmt<KF>::words; ++k) kr[u].w[k] = 0;
-      kr[u].sc = 0;
-#pragma unroll
-      for (int k = 0; k < Fmt<VF>::words; ++k) vr[u].w[k] = 0;
-      vr[u].sc = 0;
+struct Tile {
+  uint32_t s, g, split;
+};
+
+__device__ __forceinline__ Tile split_tile(const DecodeArgs& a) {
+  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+  Tile t;
+  t.g = tile % a.num_kv_heads;
+  t.split = (tile / a.num_kv_heads) % a.nsplit;
+  t.s = tile / (a.num_kv_heads * a.nsplit);
+  return t;
+}
+
+template <int KF, int HD, int G>
+struct PrologueSmem {
+  float q[Fmt<KF>::turbo ? G : 1][Fmt<KF>::turbo ? HD : 1];
+  float kcen[16];
+  float vcen[16];
+  uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
+  uint64_t vbase[kMaxPages];  // ... and in the V pool
+};
+
+// Page ids of the split, codebooks, and (turbo K) the rotated query in LDS;
+// then the lane's query registers.
+template <int KF, int VF, int HD, int G>
+__device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, HD, G>& sm, uint32_t s,
+                                         uint32_t g, int pb, int pe, int t, QReg<KF, Geo<HD, G>::D, G>& q) {
+  constexpr int D = Geo<HD, G>::D;
+  const int tid = threadIdx.x;
+  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
+  if (tid < 16) {
+    if constexpr (Fmt<KF>::turbo) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
+    if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
+  }
+  {
+    const int first = pb >> a.log2_bs;
+    const int n = ((pe - 1) >> a.log2_bs) - first + 1;
+    const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks + first;
+    for (int i = tid; i < n; i += kWaves * kWave) {
+      const uint64_t page = uint64_t(uint32_t(bt[i]));
+      sm.kbase[i] = page * a.k_stride;
+      sm.vbase[i] = page * a.v_stride;
     }
   }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    float kv[kDims], sq;
-    dequant<KF>(kr[u], sm.kcen, kv, sq);
+  if constexpr (!Fmt<KF>::turbo) {
+    // bf16 query pairs straight from memory (the score scale is applied later)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float part = 0.0f;
+      const uint4* src = reinterpret_cast<const uint4*>(qg + h * HD + t * D);
 #pragma unroll
-      for (int i = 0; i < kDims; ++i) part = fmaf(qr[h][i], kv[i], part);
-      if constexpr (Fmt<KF>::turbo) part *= sq;
-      part = group_sum<T>(part);
-      sc[u][h] = valid[u] ? part : -INFINITY;
+      for (int i = 0; i < D / 8; ++i) {
+        const uint4 v = src[i];
+        q.qp[h][4 * i] = v.x; q.qp[h][4 * i + 1] = v.y; q.qp[h][4 * i + 2] = v.z; q.qp[h][4 * i + 3] = v.w;
+      }
+    }
+    __syncthreads();
+  } else {
+    for (int i = tid; i < G * HD; i += kWaves * kWave) sm.q[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
+    __syncthreads();
+    // unnormalized WHT of every q row (1/sqrt(d) goes into the score scale)
+    for (int h2 = 1; h2 < HD; h2 <<= 1) {
+      for (int i = tid; i < G * HD / 2; i += kWaves * kWave) {
+        const int hh = i / (HD / 2), k = i % (HD / 2);
+        const int lo = (k / h2) * 2 * h2 + (k % h2);
+        const float x = sm.q[hh][lo], y = sm.q[hh][lo + h2];
+        sm.q[hh][lo] = x + y;
+        sm.q[hh][lo + h2] = x - y;
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < D; ++i) q.qf[h][i] = sm.q[h][t * D + i];
+  }
+}
+
+// Load one 16-position chunk (starting at c, a multiple of 16) for a lane.
+// Every load is issued unconditionally: a position outside [pb, pe) reads
+// the clamped position's bytes (always inside a page of this split) and is
+// masked afterwards.  Loads without branches let the compiler keep the next
+// chunk's loads in flight while the current chunk is computed.
+template <int KF, int VF, int HD, int G, bool LOAD_V>
+__device__ __forceinline__ void load_chunk(const DecodeArgs& a, const PrologueSmem<KF, HD, G>& sm, int first, int c,
+                                           int pb, int pe, uint32_t g, int t, int r,
+                                           Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
+                                           Raw<VF, Geo<HD, G>::D> (&vr)[Geo<HD, G>::U], bool (&ok)[Geo<HD, G>::U]) {
+  using GE = Geo<HD, G>;
+  const uint32_t bmask = (1u << a.log2_bs) - 1u;
+#pragma unroll
+  for (int u = 0; u < GE::U; ++u) {
+    const int j = c + u * GE::P + r;
+    ok[u] = j >= pb && j < pe;
+    const int jc = min(max(j, pb), pe - 1);
+    const int bi = (jc >> a.log2_bs) - first;
+    const uint32_t row = (uint32_t(jc) & bmask) * a.num_kv_heads + g;
+    load_lane<KF, HD, GE::D>(a.k_cache + sm.kbase[bi], row, t, a.k_data, kr[u]);
+    if constexpr (LOAD_V) load_lane<VF, HD, GE::D>(a.v_cache + sm.vbase[bi], row, t, a.v_data, vr[u]);
+  }
+}
+
+template <int F, int D>
+__device__ __forceinline__ void mask_raw(Raw<F, D>& r, bool ok) {
+#pragma unroll
+  for (int i = 0; i < Raw<F, D>::words; ++i) r.w[i] = ok ? r.w[i] : 0u;
+  r.sc = ok ? r.sc : 0u;
+}
+
+// Scores (log2 units, -inf outside the split) of a loaded chunk.
+template <int KF, int VF, int HD, int G>
+__device__ __forceinline__ void chunk_scores(const QReg<KF, Geo<HD, G>::D, G>& q, const float* kcen, float qscale,
+                                             const Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
+                                             const bool (&ok)[Geo<HD, G>::U], float (&sc)[Geo<HD, G>::U][G]) {
+  using GE = Geo<HD, G>;
+#pragma unroll
+  for (int u = 0; u < GE::U; ++u) {
+    float part[G];
+    lane_scores<KF, GE::D, G>(q, kr[u], kcen, part);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = group_sum<GE::T>(part[h]) * qscale;
+      sc[u][h] = ok[u] ? v : -INFINITY;
     }
   }
 }
@@ -213,104 +357,130 @@ __device__ __forceinline__ void score_step(const DecodeArgs& a, const Smem<KF, V
 
 template <int KF, int VF, int HD, int G>
 struct SplitSmem {
-  Smem<KF, VF, HD, G> base;
+  PrologueSmem<KF, HD, G> pro;
   float red[kWaves][G][HD + 2];
 };
 
 template <int KF, int VF, int HD, int G>
-__global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs a) {
-  constexpr int T = HD / kDims;
-  constexpr int P = kWave / T;
-  constexpr int CH = P * kUnroll;
-  __shared__ SplitSmem<KF, VF, HD, G> sm;
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t g = tile % a.num_kv_heads;
-  const uint32_t split = (tile / a.num_kv_heads) % a.nsplit;
-  const uint32_t s = tile / (a.num_kv_heads * a.nsplit);
-  const SeqSpan sp = split_span(a, s, split);
-  if (sp.pb >= sp.L) return;
-  prologue<KF, VF, HD, G>(a, sm.base, s, g, sp.pb, sp.pe);
+struct DenseState {
+  float m[G], l[G], acc[G][Geo<HD, G>::D];
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t = lane % T, r = lane / T;
-  const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
-  float qr[G][kDims];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) qr[h][i] = sm.base.q[h][t * kDims + i] * qscale;
-
-  float m[G], l[G], acc[G][kDims];
+template <int KF, int VF, int HD, int G>
+__device__ __forceinline__ void dense_chunk(const Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
+                                            const Raw<VF, Geo<HD, G>::D> (&vr)[Geo<HD, G>::U],
+                                            const bool (&ok)[Geo<HD, G>::U], const QReg<KF, Geo<HD, G>::D, G>& q,
+                                            const float* kcen, const float* vcen, float qscale,
+                                            DenseState<KF, VF, HD, G>& st) {
+  using GE = Geo<HD, G>;
+  float sc[GE::U][G];
+  chunk_scores<KF, VF, HD, G>(q, kcen, qscale, kr, ok, sc);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+    float mx = sc[0][h];
 #pragma unroll
-    for (int i = 0; i < kDims; ++i) acc[h][i] = 0.0f;
+    for (int u = 1; u < GE::U; ++u) mx = fmaxf(mx, sc[u][h]);
+    if (mx > st.m[h]) {
+      const float alpha = fast_exp2(st.m[h] - mx);  // 0 while m is -inf
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int i = 0; i < GE::D; ++i) st.acc[h][i] *= alpha;
+      st.m[h] = mx;
+    }
   }
-
-  for (int c0 = sp.pb + w * CH; c0 < sp.pe; c0 += kWaves * CH) {
-    float sc[kUnroll][G];
-    Raw<VF> vr[kUnroll];
-    bool valid[kUnroll];
-    score_step<KF, VF, HD, G, true>(a, sm.base, qr, c0, sp.pb, sp.pe, g, t, r, sc, vr, valid);
+#pragma unroll
+  for (int u = 0; u < GE::U; ++u) {
+    Raw<VF, GE::D> vm = vr[u];
+    mask_raw(vm, ok[u]);  // a masked position adds 0 * (finite value)
+    float x[GE::D], sq;
+    v_values<VF, GE::D>(vm, vcen, x, sq);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = sc[0][h];
+      const float p = ok[u] ? fast_exp2(sc[u][h] - st.m[h]) : 0.0f;
+      st.l[h] += p;
+      const float pw = p * sq;
 #pragma unroll
-      for (int u = 1; u < kUnroll; ++u) mx = fmaxf(mx, sc[u][h]);
-      if (mx > m[h]) {
-        const float alpha = fast_exp2(m[h] - mx);  // 0 while m is -inf
-        l[h] *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDims; ++i) acc[h][i] *= alpha;
-        m[h] = mx;
-      }
+      for (int i = 0; i < GE::D; ++i) st.acc[h][i] = fmaf(pw, x[i], st.acc[h][i]);
     }
+  }
+}
+
+template <int KF, int VF, int HD, int G>
+__global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs a) {
+  using GE = Geo<HD, G>;
+  constexpr int D = GE::D, T = GE::T;
+  __shared__ SplitSmem<KF, VF, HD, G> sm;
+  const Tile tl = split_tile(a);
+  const SeqSpan sp = split_span(a, tl.s, tl.split);
+  if (sp.pb >= sp.L) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+  const int t = lane % T, r = lane / T;
+  QReg<KF, D, G> q;
+  prologue<KF, VF, HD, G>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
+  const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
+  const int first = sp.pb >> a.log2_bs;
+
+  DenseState<KF, VF, HD, G> st;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float vv[kDims], sq;
-      dequant<VF>(vr[u], sm.base.vcen, vv, sq);
+  for (int h = 0; h < G; ++h) {
+    st.m[h] = -INFINITY;
+    st.l[h] = 0.0f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = valid[u] ? fast_exp2(sc[u][h] - m[h]) : 0.0f;
-        l[h] += p;
-        const float pw = p * sq;
-#pragma unroll
-        for (int i = 0; i < kDims; ++i) acc[h][i] = fmaf(pw, vv[i], acc[h][i]);
-      }
+    for (int i = 0; i < D; ++i) st.acc[h][i] = 0.0f;
+  }
+
+  Raw<KF, D> kA[GE::U], kB[GE::U];
+  Raw<VF, D> vA[GE::U], vB[GE::U];
+  bool oA[GE::U], oB[GE::U];
+  constexpr int step = kWaves * kChunk;
+  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;
+  // The next chunk is always loaded (past the end: this chunk again, an L2
+  // hit, never used) so that no branch sits between a load and its use.
+  if (c < sp.pe) {
+    load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
+    for (;;) {
+      const int cb = c + step;
+      load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB, vB, oB);
+      dense_chunk<KF, VF, HD, G>(kA, vA, oA, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
+      if (cb >= sp.pe) break;
+      const int ca = cb + step;
+      load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
+      dense_chunk<KF, VF, HD, G>(kB, vB, oB, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
+      if (ca >= sp.pe) break;
+      c = ca;
     }
   }
 
-  // merge the P lane slots of the wave (same dims, different positions)
+  // merge the lane slots of the wave (same dims, different positions)
 #pragma unroll
   for (int off = T; off < kWave; off <<= 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float M = fmaxf(m[h], mo);
-      const float a1 = m[h] > -INFINITY ? fast_exp2(m[h] - M) : 0.0f;
+      const float mo = __shfl_xor(st.m[h], off);
+      const float lo = __shfl_xor(st.l[h], off);
+      const float M = fmaxf(st.m[h], mo);
+      const float a1 = st.m[h] > -INFINITY ? fast_exp2(st.m[h] - M) : 0.0f;
       const float a2 = mo > -INFINITY ? fast_exp2(mo - M) : 0.0f;
-      l[h] = l[h] * a1 + lo * a2;
+      st.l[h] = st.l[h] * a1 + lo * a2;
 #pragma unroll
-      for (int i = 0; i < kDims; ++i) acc[h][i] = acc[h][i] * a1 + __shfl_xor(acc[h][i], off) * a2;
-      m[h] = M;
+      for (int i = 0; i < D; ++i) st.acc[h][i] = st.acc[h][i] * a1 + __shfl_xor(st.acc[h][i], off) * a2;
+      st.m[h] = M;
     }
   }
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int i = 0; i < kDims; ++i) sm.red[w][h][t * kDims + i] = acc[h][i];
+      for (int i = 0; i < D; ++i) sm.red[w][h][t * D + i] = st.acc[h][i];
       if (t == 0) {
-        sm.red[w][h][HD] = m[h];
-        sm.red[w][h][HD + 1] = l[h];
+        sm.red[w][h][HD] = st.m[h];
+        sm.red[w][h][HD + 1] = st.l[h];
       }
     }
   }
   __syncthreads();
-  const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit + split;
+  const uint64_t base = (uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split;
   for (int i = tid; i < G * HD; i += kWaves * kWave) {
     const int h = i / HD, d = i % HD;
     float M = -INFINITY;
@@ -340,8 +510,8 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
 
 // ------------------------------------------------------------------ merge
 
-// Rotate an LDS row of HD values by the orthonormal WHT (used to bring a
-// rotated V side's output back).  All threads of the block take part.
+// Rotate an LDS row of HD values by the orthonormal WHT (brings a rotated V
+// side's output back).  All threads of the block take part.
 template <int HD>
 __device__ __forceinline__ void lds_wht(float* x, float scale) {
   const int tid = threadIdx.x;
@@ -358,7 +528,8 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
   __syncthreads();
 }
 
-// One workgroup per (sequence, q head): combine the split partials.
+// One workgroup per (sequence, q head): combine the dense split partials with
+// log-sum-exp weights, apply the fp8 V scale and the inverse rotation.
 template <int HD, bool VROT>
 __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs a, int G) {
   __shared__ float o[HD];
@@ -396,7 +567,7 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
 
 template <int KF, int HD, int G>
 struct ScoreSmem {
-  Smem<KF, KVQ_BF16, HD, G> base;
+  PrologueSmem<KF, HD, G> pro;
   float sc[kMaxSparseSplit * G];
   float wred[kWaves][G];
   float stat[G][2];
@@ -404,48 +575,60 @@ struct ScoreSmem {
 };
 
 // Scores of one split; stores the split's (max, sum) and the candidate
-// positions whose split-local weight exceeds thr * (1 - 1e-4).  Since the
-// global normalizer is at least the split's, a position that is not a
-// candidate has global weight <= thr and is provably skipped.
+// positions whose split-local weight exceeds thr * (1 - 1e-4).  The global
+// normalizer is at least the split's, so a position that is not a candidate
+// has global weight <= thr and is provably skipped.
 template <int KF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs a) {
-  constexpr int T = HD / kDims;
-  constexpr int P = kWave / T;
-  constexpr int CH = P * kUnroll;
+  using GE = Geo<HD, G>;
+  constexpr int D = GE::D, T = GE::T;
   __shared__ ScoreSmem<KF, HD, G> sm;
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
-  const uint32_t g = tile % a.num_kv_heads;
-  const uint32_t split = (tile / a.num_kv_heads) % a.nsplit;
-  const uint32_t s = tile / (a.num_kv_heads * a.nsplit);
-  const SeqSpan sp = split_span(a, s, split);
+  const Tile tl = split_tile(a);
+  const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
-  prologue<KF, KVQ_BF16, HD, G>(a, sm.base, s, g, sp.pb, sp.pe);
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int t = lane % T, r = lane / T;
+  QReg<KF, D, G> q;
+  prologue<KF, KVQ_BF16, HD, G>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
   const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
-  float qr[G][kDims];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int i = 0; i < kDims; ++i) qr[h][i] = sm.base.q[h][t * kDims + i] * qscale;
+  const int first = sp.pb >> a.log2_bs;
 
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-  for (int c0 = sp.pb + w * CH; c0 < sp.pe; c0 += kWaves * CH) {
-    float sc[kUnroll][G];
-    Raw<KVQ_BF16> vr[kUnroll];
-    bool valid[kUnroll];
-    score_step<KF, KVQ_BF16, HD, G, false>(a, sm.base, qr, c0, sp.pb, sp.pe, g, t, r, sc, vr, valid);
+  auto consume = [&](int c, const Raw<KF, D>(&kr)[GE::U], const bool(&ok)[GE::U]) {
+    float sc[GE::U][G];
+    chunk_scores<KF, KVQ_BF16, HD, G>(q, sm.pro.kcen, qscale, kr, ok, sc);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int j = c0 + u * P + r;
+    for (int u = 0; u < GE::U; ++u) {
+      const int j = c + u * GE::P + r;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         mloc[h] = fmaxf(mloc[h], sc[u][h]);
-        if (valid[u] && t == 0) sm.sc[(j - sp.pb) * G + h] = sc[u][h];
+        if (ok[u] && t == 0) sm.sc[(j - sp.pb) * G + h] = sc[u][h];
       }
+    }
+  };
+  Raw<KF, D> kA[GE::U], kB[GE::U];
+  Raw<KVQ_BF16, D> vdummy[GE::U];
+  bool oA[GE::U], oB[GE::U];
+  constexpr int step = kWaves * kChunk;
+  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;
+  if (c < sp.pe) {
+    load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vdummy, oA);
+    for (;;) {
+      const int cb = c + step;
+      load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB,
+                                             vdummy, oB);
+      consume(c, kA, oA);
+      if (cb >= sp.pe) break;
+      const int ca = cb + step;
+      load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA,
+                                             vdummy, oA);
+      consume(cb, kB, oB);
+      if (ca >= sp.pe) break;
+      c = ca;
     }
   }
 #pragma unroll
@@ -480,7 +663,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
     sm.stat[tid][1] = sum;
   }
   __syncthreads();
-  const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit + split;
+  const uint64_t base = (uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split;
   if (tid < G) {
     a.ml[(base * G + tid) * 2] = sm.stat[tid][0];
     a.ml[(base * G + tid) * 2 + 1] = sm.stat[tid][1];
@@ -490,10 +673,11 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
 #pragma unroll
   for (int h = 0; h < G; ++h) cut[h] = a.thr * (1.0f - 1e-4f) * sm.stat[h][1];
   int32_t* cidx = a.cidx + base * a.split_len;
+  uint64_t* cvb = a.cvbase + base * a.split_len;
   float* cs = a.cscore + base * a.split_len * G;
   int total = 0;
-  for (int c = 0; c < n; c += kWaves * kWave) {
-    const int i = c + tid;
+  for (int c0 = 0; c0 < n; c0 += kWaves * kWave) {
+    const int i = c0 + tid;
     bool cand = false;
     if (i < n) {
 #pragma unroll
@@ -507,7 +691,9 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
     for (int ww = 0; ww < w; ++ww) off += sm.wcount[ww];
     if (cand) {
       const int k = off + before;
-      cidx[k] = sp.pb + i;
+      const int j = sp.pb + i;
+      cidx[k] = j;
+      cvb[k] = sm.pro.vbase[(j >> a.log2_bs) - first];
 #pragma unroll
       for (int h = 0; h < G; ++h) cs[k * G + h] = sm.sc[i * G + h];
     }
@@ -517,99 +703,155 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   if (tid == 0) a.cnt[base] = total;
 }
 
+constexpr int kRecPerLane = 2;  // candidate records read per lane per round (sparse V)
+
 template <int VF, int HD, int G>
 struct SparseSmem {
-  float mz[G][2];
   float vcen[16];
+  struct Kept {
+    uint64_t vb;   // byte offset of the V page
+    uint32_t row;  // row (offset * Hkv + kv head) in the page
+    float p[G];    // kept weights (0 for heads that drop the position)
+  } kept[kWaves][kWave * kRecPerLane];
   float red[kWaves][G][HD];
 };
 
-// One workgroup per (sequence, kv head): exact global weights of the
-// candidates, V loaded only where some head of the group keeps the position.
+// One workgroup per (sequence, kv head): every candidate of every split of the
+// sequence gets its exact global weight; V is loaded only where some head of
+// the group keeps the position, and the workgroup writes the final output.
+// Each lane reads whole candidate records (coalesced: 128 records per wave
+// per round, one memory latency) and decides keep/drop for every head; a
+// ballot compacts the kept ones into LDS, and the wave's lane slots then
+// stream their V rows.  The global (max, sum) per head and the per-split
+// candidate counts come from uniform loads.
 template <int VF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeArgs a) {
-  constexpr int T = HD / kDims;
-  constexpr int P = kWave / T;
-  constexpr int NS = kWaves * P;  // lane slots per workgroup
+  using GE = Geo<HD, G>;
+  constexpr int D = GE::D, T = GE::T, P = GE::P;
+  constexpr int RW = kWave * kRecPerLane;  // records per wave per round
   __shared__ SparseSmem<VF, HD, G> sm;
   const uint32_t g = blockIdx.x % a.num_kv_heads;
   const uint32_t s = blockIdx.x / a.num_kv_heads;
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint64_t sbase = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane % T, r = lane / T;
-  const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * G + tid) * 2]);
-    float z = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const float mk = a.ml[((base + k) * G + tid) * 2];
-      if (mk > -INFINITY) z += fast_exp2(mk - M) * a.ml[((base + k) * G + tid) * 2 + 1];
-    }
-    sm.mz[tid][0] = M;
-    sm.mz[tid][1] = z > 0.0f ? 1.0f / z : 0.0f;
-  }
   if (tid < 16) {
     if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
-  __syncthreads();
   float M[G], iz[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    M[h] = sm.mz[h][0];
-    iz[h] = sm.mz[h][1];
+    float mx = -INFINITY;
+    for (int k = 0; k < ns; ++k) mx = fmaxf(mx, a.ml[((sbase + k) * G + h) * 2]);
+    float z = 0.0f;
+    for (int k = 0; k < ns; ++k) {
+      const float mk = a.ml[((sbase + k) * G + h) * 2];
+      if (mk > -INFINITY) z += fast_exp2(mk - mx) * a.ml[((sbase + k) * G + h) * 2 + 1];
+    }
+    M[h] = mx;
+    iz[h] = z > 0.0f ? 1.0f / z : 0.0f;
   }
-  float acc[G][kDims];
+  int total = 0;
+  for (int k = 0; k < ns; ++k) total += a.cnt[sbase + k];
+  __syncthreads();
+  float acc[G][D];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int i = 0; i < kDims; ++i) acc[h][i] = 0.0f;
-  const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks;
+    for (int i = 0; i < D; ++i) acc[h][i] = 0.0f;
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
-  const int slot = w * P + r;
-  for (int k = 0; k < ns; ++k) {
-    const int cnt = a.cnt[base + k];
-    const int32_t* cidx = a.cidx + (base + k) * a.split_len;
-    const float* cs = a.cscore + (base + k) * a.split_len * G;
-    for (int i = slot; i < cnt; i += NS) {
-      const int j = cidx[i];
+  auto& kept = sm.kept[w];
+  for (int i0 = w * RW; i0 < total; i0 += kWaves * RW) {
+    // 1. records -> keep decisions, compacted into the wave's LDS list
+    int nk = 0;
+#pragma unroll
+    for (int q = 0; q < kRecPerLane; ++q) {
+      const int gi = i0 + q * kWave + lane;
+      const bool ok = gi < total;
+      // locate the record: split k with prefix(k) <= gi < prefix(k+1)
+      int k = 0, before = 0;
+      bool found = false;
+      for (int kk = 0; kk < ns; ++kk) {
+        const int c = a.cnt[sbase + kk];
+        if (!found) {
+          if (gi < before + c) {
+            found = true;
+            k = kk;
+          } else {
+            before += c;
+          }
+        }
+      }
+      const int kc = ok ? k : 0;
+      const uint64_t rec = (sbase + kc) * a.split_len + (ok ? gi - before : 0);
+      const uint32_t row = (uint32_t(a.cidx[rec]) & bmask) * a.num_kv_heads + g;
+      const uint64_t vb = a.cvbase[rec];
       float p[G];
       bool any = false;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        p[h] = fast_exp2(cs[i * G + h] - M[h]) * iz[h];
-        p[h] = p[h] > a.thr ? p[h] : 0.0f;
+        const float pv = fast_exp2(a.cscore[rec * G + h] - M[h]) * iz[h];
+        p[h] = (ok && pv > a.thr) ? pv : 0.0f;
         any |= p[h] > 0.0f;
       }
+      const uint64_t bal = __ballot(any);
       if (any) {
-        const uint64_t page = uint64_t(uint32_t(bt[j >> a.log2_bs]));
-        const uint32_t row = (uint32_t(j) & bmask) * a.num_kv_heads + g;
-        Raw<VF> vr;
-        load_chunk<VF, HD>(a.v_cache + page * a.v_stride, row, t, a.v_data, vr);
-        float vv[kDims], sq;
-        dequant<VF>(vr, sm.vcen, vv, sq);
+        const int kk = nk + __popcll(bal & ((1ull << lane) - 1ull));
+        kept[kk].vb = vb;
+        kept[kk].row = row;
+#pragma unroll
+        for (int h = 0; h < G; ++h) kept[kk].p[h] = p[h];
+      }
+      nk += __popcll(bal);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 2. lane slots stream the kept V rows, kCandUnroll in flight
+    for (int k0 = r; k0 < nk; k0 += P * kCandUnroll) {
+      Raw<VF, D> vr[kCandUnroll];
+      float pk[kCandUnroll][G];
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {
+        const int k = k0 + u * P;
+        const bool ok = k < nk;
+        const int kc = ok ? k : 0;
+        load_lane<VF, HD, D>(a.v_cache + kept[kc].vb, kept[kc].row, t, a.v_data, vr[u]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) pk[u][h] = ok ? kept[kc].p[h] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kCandUnroll; ++u) {
+        mask_raw(vr[u], k0 + u * P < nk);
+        float x[D], sq;
+        v_values<VF, D>(vr[u], sm.vcen, x, sq);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float pw = p[h] * sq;
+          const float pw = pk[u][h] * sq;
 #pragma unroll
-          for (int i2 = 0; i2 < kDims; ++i2) acc[h][i2] = fmaf(pw, vv[i2], acc[h][i2]);
+          for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 #pragma unroll
   for (int off = T; off < kWave; off <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < kDims; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
+      for (int i = 0; i < D; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < kDims; ++i) sm.red[w][h][t * kDims + i] = acc[h][i];
+      for (int i = 0; i < D; ++i) sm.red[w][h][t * D + i] = acc[h][i];
   }
   __syncthreads();
   for (int i = tid; i < G * HD; i += kWaves * kWave) {

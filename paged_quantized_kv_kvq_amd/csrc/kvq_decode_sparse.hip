@@ -1,13 +1,14 @@
-// Decode kernels that depend only on the V side: the sparse-V pass and the
-// split merge (with the inverse rotation of a rotated V side).
+// Decode kernels that depend only on the V side: the sparse-V pass (one
+// workgroup per (sequence, kv head)) and the dense split merge (with the
+// inverse rotation of a rotated V side).
 #include "kvq_decode.h"
 
 namespace kvq {
 namespace {
 
 template <int VF, int HD>
-hipError_t sparse_g(int g, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_seqs * a.num_kv_heads), block(kWaves * kWave);
+hipError_t sparse_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
+  const dim3 grid(nwg), block(kWaves * kWave);
   switch (g) {
     case 1: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 1>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 2>), grid, block, 0, st, a); break;
@@ -19,11 +20,11 @@ hipError_t sparse_g(int g, const DecodeArgs& a, hipStream_t st) {
 }
 
 template <int VF>
-hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (hd) {
-    case 64: return sparse_g<VF, 64>(g, a, st);
-    case 128: return sparse_g<VF, 128>(g, a, st);
-    case 256: return sparse_g<VF, 256>(g, a, st);
+    case 64: return sparse_g<VF, 64>(g, a, nwg, st);
+    case 128: return sparse_g<VF, 128>(g, a, nwg, st);
+    case 256: return sparse_g<VF, 256>(g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -38,13 +39,13 @@ hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (vf) {
-    case KVQ_BF16: return sparse_hd<KVQ_BF16>(hd, g, a, st);
-    case KVQ_FP8_E4M3: return sparse_hd<KVQ_FP8_E4M3>(hd, g, a, st);
-    case KVQ_TURBO2: return sparse_hd<KVQ_TURBO2>(hd, g, a, st);
-    case KVQ_TURBO3: return sparse_hd<KVQ_TURBO3>(hd, g, a, st);
-    case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, st);
+    case KVQ_BF16: return sparse_hd<KVQ_BF16>(hd, g, a, nwg, st);
+    case KVQ_FP8_E4M3: return sparse_hd<KVQ_FP8_E4M3>(hd, g, a, nwg, st);
+    case KVQ_TURBO2: return sparse_hd<KVQ_TURBO2>(hd, g, a, nwg, st);
+    case KVQ_TURBO3: return sparse_hd<KVQ_TURBO3>(hd, g, a, nwg, st);
+    case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -51,10 +51,12 @@ struct DecodeArgs {
   float* out;
   const int32_t* block_tables;
   const int32_t* seq_lens;
-  float* part;     // dense: [S][Hkv][nsplit][G][hd] unnormalized partial outputs
-  float* ml;       // [S][Hkv][nsplit][G][2] (running max in log2 units, sum)
+  float* part;     // dense: [S][Hkv][nsplit][G][hd] unnormalized partial
+                   // outputs of each split (relative to the split max)
+  float* ml;       // [S][Hkv][nsplit][G][2] (max in log2 units, sum of exp2)
   int32_t* cnt;    // sparse: [S][Hkv][nsplit] candidate counts
   int32_t* cidx;   // sparse: [S][Hkv][nsplit][split_len] candidate positions
+  uint64_t* cvbase; // sparse: [S][Hkv][nsplit][split_len] byte offset of their V page
   float* cscore;   // sparse: [S][Hkv][nsplit][split_len][G] their log2 scores
   uint32_t max_blocks;
   uint32_t num_seqs;
@@ -92,7 +94,7 @@ hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, h
 hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);  // one workgroup per (seq, kv head)
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq
