@@ -21,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the public C-ABI header
 ARCH = "gfx950"
 
 
@@ -46,10 +47,11 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def compile_one(src: str, verbose: bool) -> tuple:
-    obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
+def compile_one(src: str, verbose: bool, out_dir: str = OUT_DIR, defines=()) -> tuple:
+    obj = os.path.join(out_dir, src.replace(".hip", ".o"))
     flags = EXACT if src in ("kvq_write.hip", "kvq_api.hip") else FAST
-    cmd = [hipcc()] + COMMON + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + COMMON + flags + [f"-I{INCLUDE}"] + [f"-D{d}" for d in defines] + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or r.returncode:
@@ -57,25 +59,27 @@ def compile_one(src: str, verbose: bool) -> tuple:
     return src, obj, r.returncode, time.time() - t0
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(jobs: int = 0, verbose: bool = False, lib: str = LIB, out_dir: str = OUT_DIR, defines=()) -> str:
+    """Compile and link.  `defines` (NAME=VALUE) override the tuning constants of
+    csrc/kvq_internal.h; `lib` / `out_dir` place a variant build elsewhere."""
+    os.makedirs(out_dir, exist_ok=True)
     jobs = jobs or max(1, min(8, os.cpu_count() or 1))
     objs = []
     failed = []
     with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, dt in ex.map(lambda s: compile_one(s, verbose), sources()):
+        for src, obj, rc, dt in ex.map(lambda s: compile_one(s, verbose, out_dir, defines), sources()):
             if verbose:
                 sys.stderr.write(f"  {src}: {dt:.1f}s\n")
             (failed if rc else objs).append(src if rc else obj)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def main() -> None:

@@ -1,5 +1,6 @@
 // The exported C ABI: argument checks, pool layout, Lloyd-Max tables, decode
 // planning and kernel dispatch.  Nothing here touches device memory.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -10,9 +11,9 @@ namespace kvq {
 namespace {
 
 constexpr uint32_t kMaxSplitLen = 4096;
-constexpr uint32_t kMaxSparseSplitLen = 1024;  // scores of a split live in LDS
-constexpr uint32_t kPagesPerSplit = 512;       // page ids of a split live in LDS
-constexpr uint64_t kTargetWorkgroups = 4096;
+constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a split live in LDS
+constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
+constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 
 bool valid_format(int32_t f) { return f >= KVQ_BF16 && f <= KVQ_TURBO4; }
 bool is_turbo(int32_t f) { return f >= KVQ_TURBO2; }
@@ -117,8 +118,8 @@ int check_layout(const kvq_layout* l) {
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
-  uint32_t split_len, nsplit;
-  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cpage, off_cs, bytes;
+  uint32_t split_len, nsplit, vsplits, nparts;
+  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cpage, off_cs, off_vpart, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -141,7 +142,9 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
-  p.off_part = p.off_cnt = p.off_cidx = p.off_cpage = p.off_cs = 0;
+  p.off_part = p.off_cnt = p.off_cidx = p.off_cpage = p.off_cs = p.off_vpart = 0;
+  p.vsplits = std::min<uint32_t>(64, std::max<uint32_t>(1, KVQ_VPART_POSITIONS / sl));  // <= kMaxStatSplits
+  p.nparts = (p.nsplit + p.vsplits - 1) / p.vsplits;
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
@@ -154,6 +157,8 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     off = up256(off + units * sl * sizeof(uint64_t));
     p.off_cs = off;
     off = up256(off + units * sl * G * sizeof(float));
+    p.off_vpart = off;
+    off = up256(off + uint64_t(S) * nkv * p.nparts * G * hd * sizeof(float));
   }
   p.bytes = off;
   return p;
@@ -242,8 +247,11 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   if (uint64_t(max_blocks_per_seq) * layout->block_size >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const bool sparse = sparse_v_threshold > 0.0f;
   const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse);
-  const uint64_t nwg = uint64_t(num_seqs) * nkv * p.nsplit;
-  if (nwg >= (1ull << 31) || uint64_t(num_seqs) * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
+  const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
+  const uint64_t nwg_v = (uint64_t(num_seqs) * p.nparts + 7) / 8 * 8 * nkv;
+  if (nwg >= (1ull << 31) || nwg_v >= (1ull << 31) || uint64_t(num_seqs) * num_q_heads >= (1ull << 31))
+    return KVQ_ERR_UNSUPPORTED;
   if (!workspace) {
     *workspace_bytes = size_t(p.bytes);
     return KVQ_OK;
@@ -272,6 +280,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
     a.cidx = reinterpret_cast<int32_t*>(ws + p.off_cidx);
     a.cvbase = reinterpret_cast<uint64_t*>(ws + p.off_cpage);
     a.cscore = reinterpret_cast<float*>(ws + p.off_cs);
+    a.vpart = reinterpret_cast<float*>(ws + p.off_vpart);
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -282,6 +291,8 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   a.window = sliding_window;
   a.split_len = p.split_len;
   a.nsplit = p.nsplit;
+  a.vsplits = p.vsplits;
+  a.nparts = p.nparts;
   a.k_stride = layout->k_block_stride_bytes;
   a.k_data = layout->k_data_section_bytes;
   a.v_stride = layout->v_block_stride_bytes;
@@ -304,7 +315,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
     }
-    if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
+    if (e == hipSuccess) e = launch_merge(false, layout->v_rotated != 0, int(hd), int(G), a, s);
   } else {
     switch (kf) {
       case KVQ_BF16: e = launch_scores_bf16(int(hd), int(G), a, uint32_t(nwg), s); break;
@@ -313,7 +324,8 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO3: e = launch_scores_turbo3(int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
-    if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, num_seqs * nkv, s);
+    if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);
+    if (e == hipSuccess) e = launch_merge(true, layout->v_rotated != 0, int(hd), int(G), a, s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

@@ -27,9 +27,9 @@
 //     combined by merge_kernel (which also applies the inverse rotation);
 //   * sparse (threshold > 0): scores_kernel keeps only candidate positions
 //     (split-local weight above thr: an upper bound on the global weight);
-//     sparse_v_kernel, one workgroup per (sequence, kv head), recomputes each
-//     candidate's exact global weight, loads V only where some head of the
-//     group keeps it, and writes the output;
+//     sparse_v_kernel, one workgroup per (sequence, kv head, part of a few
+//     splits), recomputes each candidate's exact global weight, loads V only
+//     where some head of the group keeps it; merge_kernel sums the parts;
 //   * workgroup ids are renumbered so the kv heads of one (sequence, split)
 //     run on the same XCD and share L2 lines (the heads of a page interleave).
 #pragma once
@@ -38,10 +38,10 @@
 
 namespace kvq {
 
-constexpr int kWaves = 4;        // waves per workgroup
-constexpr int kChunk = 16;       // positions per wave iteration
-constexpr int kMaxPages = 512;   // page ids of one split staged in LDS
-constexpr int kMaxSparseSplit = 1024;
+constexpr int kWaves = KVQ_WAVES;  // waves per workgroup
+constexpr int kChunk = 16;         // positions per wave iteration
+constexpr int kMaxPages = 160;     // page offsets of one split staged in LDS
+constexpr int kMaxSparseSplit = KVQ_MAX_SPARSE_SPLIT;
 constexpr int kCandUnroll = 4;   // kept V rows in flight per lane slot (sparse V)
 
 template <int F>
@@ -69,24 +69,52 @@ struct Raw {
   uint32_t sc;
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Cache rows are streamed once per decode: optionally tag the loads non-temporal.
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#if KVQ_NT_LOADS
+  return __builtin_nontemporal_load(q);
+#else
+  return *q;
+#endif
+}
+__device__ __forceinline__ u32x2 load8(const uint8_t* p) {
+  const u32x2* q = reinterpret_cast<const u32x2*>(p);
+#if KVQ_NT_LOADS
+  return __builtin_nontemporal_load(q);
+#else
+  return *q;
+#endif
+}
+__device__ __forceinline__ uint32_t load4(const uint8_t* p) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#if KVQ_NT_LOADS
+  return __builtin_nontemporal_load(q);
+#else
+  return *q;
+#endif
+}
+
 template <int F, int HD, int D>
 __device__ __forceinline__ void load_lane(const uint8_t* __restrict__ blk, uint32_t row, int t,
                                           uint64_t data_bytes, Raw<F, D>& r) {
   constexpr int B = Raw<F, D>::bytes;
   const uint8_t* p = blk + uint64_t(row) * (HD * Fmt<F>::bits / 8) + t * B;
   if constexpr (B == 32) {
-    const uint4 a = reinterpret_cast<const uint4*>(p)[0];
-    const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+    const u32x4 a = load16(p), b = load16(p + 16);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
     r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
   } else if constexpr (B == 16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const u32x4 a = load16(p);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
   } else if constexpr (B == 8) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
+    const u32x2 a = load8(p);
     r.w[0] = a.x; r.w[1] = a.y;
   } else if constexpr (B == 4) {
-    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    r.w[0] = load4(p);
   } else if constexpr (B == 2) {
     r.w[0] = *reinterpret_cast<const uint16_t*>(p);
   } else {
@@ -229,14 +257,20 @@ __device__ __forceinline__ SeqSpan split_span(const DecodeArgs& a, uint32_t s, u
 
 struct Tile {
   uint32_t s, g, split;
+  bool valid;
 };
 
-__device__ __forceinline__ Tile split_tile(const DecodeArgs& a) {
-  const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+// (sequence, split, kv head) of this workgroup; `per_seq` units per sequence.
+// Units are numbered split-major (unit = split * S + sequence): the units of
+// one split index rotate over the XCDs, and so do the (fewer) later splits
+// that only long sequences have.
+__device__ __forceinline__ Tile unit_tile(const DecodeArgs& a, uint32_t per_seq) {
+  uint32_t unit, head;
   Tile t;
-  t.g = tile % a.num_kv_heads;
-  t.split = (tile / a.num_kv_heads) % a.nsplit;
-  t.s = tile / (a.num_kv_heads * a.nsplit);
+  t.valid = xcd_unit_tile(blockIdx.x, a.num_seqs * per_seq, a.num_kv_heads, unit, head);
+  t.g = head;
+  t.s = unit % a.num_seqs;
+  t.split = unit / a.num_seqs;
   return t;
 }
 
@@ -410,7 +444,8 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
   using GE = Geo<HD, G>;
   constexpr int D = GE::D, T = GE::T;
   __shared__ SplitSmem<KF, VF, HD, G> sm;
-  const Tile tl = split_tile(a);
+  const Tile tl = unit_tile(a, a.nsplit);
+  if (!tl.valid) return;
   const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -528,9 +563,10 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
   __syncthreads();
 }
 
-// One workgroup per (sequence, q head): combine the dense split partials with
-// log-sum-exp weights, apply the fp8 V scale and the inverse rotation.
-template <int HD, bool VROT>
+// One workgroup per (sequence, q head).  Dense: combine the split partials
+// with log-sum-exp weights.  Sparse: sum the V-pass parts (already divided by
+// the global softmax sum).  Then the fp8 V scale and the inverse rotation.
+template <int HD, bool VROT, bool SPARSE>
 __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs a, int G) {
   __shared__ float o[HD];
   const uint32_t hq = blockIdx.x % a.num_q_heads;
@@ -540,22 +576,32 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
   const int tid = threadIdx.x;
-  const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * G + h) * 2]);
-  float sum = 0.0f;
-  for (int k = 0; k < ns; ++k) {
-    const float mk = a.ml[((base + k) * G + h) * 2];
-    if (mk > -INFINITY) sum += fast_exp2(mk - M) * a.ml[((base + k) * G + h) * 2 + 1];
-  }
-  const float inv = sum > 0.0f ? a.v_scale / sum : 0.0f;
-  for (int d = tid; d < HD; d += kWaves * kWave) {
-    float acc = 0.0f;
+  if constexpr (SPARSE) {
+    const int nact = ns > 0 ? (ns + int(a.vsplits) - 1) / int(a.vsplits) : 1;
+    const uint64_t pbase = (uint64_t(s) * a.num_kv_heads + g) * a.nparts;
+    for (int d = tid; d < HD; d += kWaves * kWave) {
+      float acc = 0.0f;
+      for (int p = 0; p < nact; ++p) acc += a.vpart[((pbase + p) * G + h) * HD + d];
+      o[d] = acc * a.v_scale;
+    }
+  } else {
+    const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * G + h) * 2]);
+    float sum = 0.0f;
     for (int k = 0; k < ns; ++k) {
       const float mk = a.ml[((base + k) * G + h) * 2];
-      if (mk > -INFINITY) acc += fast_exp2(mk - M) * a.part[((base + k) * G + h) * HD + d];
+      if (mk > -INFINITY) sum += fast_exp2(mk - M) * a.ml[((base + k) * G + h) * 2 + 1];
     }
-    o[d] = acc * inv;
+    const float inv = sum > 0.0f ? a.v_scale / sum : 0.0f;
+    for (int d = tid; d < HD; d += kWaves * kWave) {
+      float acc = 0.0f;
+      for (int k = 0; k < ns; ++k) {
+        const float mk = a.ml[((base + k) * G + h) * 2];
+        if (mk > -INFINITY) acc += fast_exp2(mk - M) * a.part[((base + k) * G + h) * HD + d];
+      }
+      o[d] = acc * inv;
+    }
   }
   __syncthreads();
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
@@ -583,7 +629,8 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   using GE = Geo<HD, G>;
   constexpr int D = GE::D, T = GE::T;
   __shared__ ScoreSmem<KF, HD, G> sm;
-  const Tile tl = split_tile(a);
+  const Tile tl = unit_tile(a, a.nsplit);
+  if (!tl.valid) return;
   const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -703,11 +750,23 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   if (tid == 0) a.cnt[base] = total;
 }
 
-constexpr int kRecPerLane = 2;  // candidate records read per lane per round (sparse V)
+constexpr int kRecPerLane = 2;    // candidate records read per lane per round (sparse V)
+constexpr int kMaxStatSplits = 64;  // splits whose stats the V pass stages in LDS at once
+
+// The V pass uses 8 dims per lane (more rows side by side, fewer registers).
+template <int HD>
+struct VGeo {
+  static constexpr int D = 8;
+  static constexpr int T = HD / D;
+  static constexpr int P = kWave / T;
+};
 
 template <int VF, int HD, int G>
 struct SparseSmem {
   float vcen[16];
+  float mz[G][2];                     // global (max, 1/sum) per head
+  float st[kMaxStatSplits][G][2];     // split stats being reduced
+  int cnt[kMaxStatSplits];            // candidate counts of the part's splits
   struct Kept {
     uint64_t vb;   // byte offset of the V page
     uint32_t row;  // row (offset * Hkv + kv head) in the page
@@ -716,48 +775,75 @@ struct SparseSmem {
   float red[kWaves][G][HD];
 };
 
-// One workgroup per (sequence, kv head): every candidate of every split of the
-// sequence gets its exact global weight; V is loaded only where some head of
-// the group keeps the position, and the workgroup writes the final output.
-// Each lane reads whole candidate records (coalesced: 128 records per wave
-// per round, one memory latency) and decides keep/drop for every head; a
-// ballot compacts the kept ones into LDS, and the wave's lane slots then
-// stream their V rows.  The global (max, sum) per head and the per-split
-// candidate counts come from uniform loads.
+// One workgroup per (sequence, kv head, part), a part being `vsplits`
+// consecutive splits: every candidate of those splits gets its exact global
+// weight; V is loaded only where some head of the group keeps the position.
+// The split stats (for the global max and sum per head) and the part's
+// candidate counts are staged in LDS with one parallel load.  Each lane reads
+// whole candidate records (coalesced: 128 records per wave per round, one
+// memory latency) and decides keep/drop for every head; a ballot compacts the
+// kept ones into LDS, and the wave's lane slots then stream their V rows.
+// Each part stores its partial output; the merge kernel sums the parts.
 template <int VF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeArgs a) {
-  using GE = Geo<HD, G>;
+  using GE = VGeo<HD>;
   constexpr int D = GE::D, T = GE::T, P = GE::P;
   constexpr int RW = kWave * kRecPerLane;  // records per wave per round
   __shared__ SparseSmem<VF, HD, G> sm;
-  const uint32_t g = blockIdx.x % a.num_kv_heads;
-  const uint32_t s = blockIdx.x / a.num_kv_heads;
+  const Tile tl = unit_tile(a, a.nparts);
+  if (!tl.valid) return;
+  const uint32_t s = tl.s, g = tl.g, part = tl.split;
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
+  const int nact = ns > 0 ? (ns + int(a.vsplits) - 1) / int(a.vsplits) : 1;
+  if (int(part) >= nact) return;
   const uint64_t sbase = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane % T, r = lane / T;
+  const int k0 = int(part * a.vsplits);
+  const int k1 = min(ns, k0 + int(a.vsplits));
   if (tid < 16) {
     if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
+  // global (max, sum) per head over all splits, staged kMaxStatSplits at a time
+  float runm = -INFINITY, runz = 0.0f;  // (threads < G) running stats of head tid
+  for (int kb = 0; kb < ns; kb += kMaxStatSplits) {
+    const int nk = min(kMaxStatSplits, ns - kb);
+    for (int i = tid; i < nk * G; i += kWaves * kWave) {
+      const int k = i / G, h = i % G;
+      sm.st[k][h][0] = a.ml[((sbase + kb + k) * G + h) * 2];
+      sm.st[k][h][1] = a.ml[((sbase + kb + k) * G + h) * 2 + 1];
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mx = runm;
+      for (int k = 0; k < nk; ++k) mx = fmaxf(mx, sm.st[k][tid][0]);
+      float z = runm > -INFINITY ? runz * fast_exp2(runm - mx) : 0.0f;
+      for (int k = 0; k < nk; ++k) {
+        const float mk = sm.st[k][tid][0];
+        if (mk > -INFINITY) z += fast_exp2(mk - mx) * sm.st[k][tid][1];
+      }
+      runm = mx;
+      runz = z;
+    }
+    __syncthreads();
+  }
+  if (tid < G) {
+    sm.mz[tid][0] = runm;
+    sm.mz[tid][1] = runz > 0.0f ? 1.0f / runz : 0.0f;
+  }
+  for (int k = k0 + tid; k < k1; k += kWaves * kWave) sm.cnt[k - k0] = a.cnt[sbase + k];
+  __syncthreads();
   float M[G], iz[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mx = -INFINITY;
-    for (int k = 0; k < ns; ++k) mx = fmaxf(mx, a.ml[((sbase + k) * G + h) * 2]);
-    float z = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const float mk = a.ml[((sbase + k) * G + h) * 2];
-      if (mk > -INFINITY) z += fast_exp2(mk - mx) * a.ml[((sbase + k) * G + h) * 2 + 1];
-    }
-    M[h] = mx;
-    iz[h] = z > 0.0f ? 1.0f / z : 0.0f;
+    M[h] = sm.mz[h][0];
+    iz[h] = sm.mz[h][1];
   }
   int total = 0;
-  for (int k = 0; k < ns; ++k) total += a.cnt[sbase + k];
-  __syncthreads();
+  for (int k = k0; k < k1; ++k) total += sm.cnt[k - k0];
   float acc[G][D];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -772,11 +858,11 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     for (int q = 0; q < kRecPerLane; ++q) {
       const int gi = i0 + q * kWave + lane;
       const bool ok = gi < total;
-      // locate the record: split k with prefix(k) <= gi < prefix(k+1)
-      int k = 0, before = 0;
+      // locate the record: the first split k >= k0 with prefix(k+1) > gi
+      int k = k0, before = 0;
       bool found = false;
-      for (int kk = 0; kk < ns; ++kk) {
-        const int c = a.cnt[sbase + kk];
+      for (int kk = k0; kk < k1; ++kk) {
+        const int c = sm.cnt[kk - k0];
         if (!found) {
           if (gi < before + c) {
             found = true;
@@ -786,8 +872,7 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
           }
         }
       }
-      const int kc = ok ? k : 0;
-      const uint64_t rec = (sbase + kc) * a.split_len + (ok ? gi - before : 0);
+      const uint64_t rec = (sbase + (ok ? k : k0)) * a.split_len + (ok ? gi - before : 0);
       const uint32_t row = (uint32_t(a.cidx[rec]) & bmask) * a.num_kv_heads + g;
       const uint64_t vb = a.cvbase[rec];
       float p[G];
@@ -812,21 +897,21 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // 2. lane slots stream the kept V rows, kCandUnroll in flight
-    for (int k0 = r; k0 < nk; k0 += P * kCandUnroll) {
+    for (int q0 = r; q0 < nk; q0 += P * kCandUnroll) {
       Raw<VF, D> vr[kCandUnroll];
       float pk[kCandUnroll][G];
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
-        const int k = k0 + u * P;
-        const bool ok = k < nk;
-        const int kc = ok ? k : 0;
-        load_lane<VF, HD, D>(a.v_cache + kept[kc].vb, kept[kc].row, t, a.v_data, vr[u]);
+        const int q = q0 + u * P;
+        const bool ok = q < nk;
+        const int qc = ok ? q : 0;
+        load_lane<VF, HD, D>(a.v_cache + kept[qc].vb, kept[qc].row, t, a.v_data, vr[u]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) pk[u][h] = ok ? kept[kc].p[h] : 0.0f;
+        for (int h = 0; h < G; ++h) pk[u][h] = ok ? kept[qc].p[h] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
-        mask_raw(vr[u], k0 + u * P < nk);
+        mask_raw(vr[u], q0 + u * P < nk);
         float x[D], sq;
         v_values<VF, D>(vr[u], sm.vcen, x, sq);
 #pragma unroll
@@ -854,20 +939,13 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
       for (int i = 0; i < D; ++i) sm.red[w][h][t * D + i] = acc[h][i];
   }
   __syncthreads();
+  const uint64_t pbase = (uint64_t(s) * a.num_kv_heads + g) * a.nparts;
   for (int i = tid; i < G * HD; i += kWaves * kWave) {
     const int h = i / HD, d = i % HD;
     float o = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) o += sm.red[ww][h][d];
-    sm.red[0][h][d] = o * a.v_scale;
-  }
-  __syncthreads();
-  if constexpr (Fmt<VF>::turbo) {
-    for (int h = 0; h < G; ++h) lds_wht<HD>(sm.red[0][h], a.wht_scale);
-  }
-  for (int i = tid; i < G * HD; i += kWaves * kWave) {
-    const int h = i / HD, d = i % HD;
-    a.out[(uint64_t(s) * a.num_q_heads + g * G + h) * HD + d] = sm.red[0][h][d];
+    a.vpart[(pbase + part) * G * HD + i] = o;
   }
 }
 

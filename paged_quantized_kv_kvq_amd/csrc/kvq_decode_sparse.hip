@@ -1,6 +1,6 @@
-// Decode kernels that depend only on the V side: the sparse-V pass (one
-// workgroup per (sequence, kv head)) and the dense split merge (with the
-// inverse rotation of a rotated V side).
+// Decode kernels that depend only on the V side: the sparse-V pass and the
+// merge (dense: log-sum-exp over splits; sparse: sum over V-pass parts; both
+// with the inverse rotation of a rotated V side).
 #include "kvq_decode.h"
 
 namespace kvq {
@@ -30,10 +30,15 @@ hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream
 }
 
 template <int HD>
-hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t merge_hd(bool sparse, bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_seqs * a.num_q_heads), block(kWaves * kWave);
-  if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true>), grid, block, 0, st, a, g);
-  else hipLaunchKernelGGL((merge_kernel<HD, false>), grid, block, 0, st, a, g);
+  if (sparse) {
+    if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true, true>), grid, block, 0, st, a, g);
+    else hipLaunchKernelGGL((merge_kernel<HD, false, true>), grid, block, 0, st, a, g);
+  } else {
+    if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true, false>), grid, block, 0, st, a, g);
+    else hipLaunchKernelGGL((merge_kernel<HD, false, false>), grid, block, 0, st, a, g);
+  }
   return hipGetLastError();
 }
 
@@ -50,11 +55,11 @@ hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t 
   }
 }
 
-hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_merge(bool sparse, bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return merge_hd<64>(v_rotated, g, a, st);
-    case 128: return merge_hd<128>(v_rotated, g, a, st);
-    case 256: return merge_hd<256>(v_rotated, g, a, st);
+    case 64: return merge_hd<64>(sparse, v_rotated, g, a, st);
+    case 128: return merge_hd<128>(sparse, v_rotated, g, a, st);
+    case 256: return merge_hd<256>(sparse, v_rotated, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -90,12 +90,18 @@ __device__ __forceinline__ float group_max(float x) {
 // ---------------------------------------------------------------- launch mapping
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup i runs on XCD
-// i % 8, each XCD with its own L2).  Renumber them so that consecutive logical
-// tiles land on the same XCD: tiles that read neighbouring bytes of the same
-// cache lines (the kv heads of one page) then share one L2.
-__device__ __forceinline__ uint32_t xcd_tile(uint32_t i, uint32_t n) {
-  const uint32_t x = i & 7u, k = i >> 3, q = n >> 3, r = n & 7u;
-  return x * q + (x < r ? x : r) + k;
+// i % 8, each XCD with its own L2).  A tile is a (unit, kv head) pair, a unit
+// being a (sequence, split).  All kv heads of a unit go to one XCD, dispatched
+// back to back, so they share the L2 lines their interleaved rows live in;
+// consecutive units rotate over the XCDs, which keeps the XCDs evenly loaded
+// when sequence lengths differ.  The grid has ceil(units/8)*8*heads
+// workgroups; the padding ones get valid == false.
+__device__ __forceinline__ bool xcd_unit_tile(uint32_t i, uint32_t nunits, uint32_t nheads, uint32_t& unit,
+                                              uint32_t& head) {
+  const uint32_t x = i & 7u, rest = i >> 3;
+  head = rest % nheads;
+  unit = (rest / nheads) * 8u + x;
+  return unit < nunits;
 }
 
 }  // namespace kvq

@@ -6,7 +6,24 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
+
+// Tuning constants (compile-time; the defaults are the measured best on MI355X).
+#ifndef KVQ_WAVES
+#define KVQ_WAVES 4              // waves per decode workgroup
+#endif
+#ifndef KVQ_TARGET_WORKGROUPS
+#define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many
+#endif
+#ifndef KVQ_MAX_SPARSE_SPLIT
+#define KVQ_MAX_SPARSE_SPLIT 2048  // positions per split on the sparse path (scores kept in LDS)
+#endif
+#ifndef KVQ_VPART_POSITIONS
+#define KVQ_VPART_POSITIONS 2048  // positions whose candidates one sparse-V workgroup takes
+#endif
+#ifndef KVQ_NT_LOADS
+#define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
+#endif
 
 namespace kvq {
 
@@ -58,6 +75,7 @@ struct DecodeArgs {
   int32_t* cidx;   // sparse: [S][Hkv][nsplit][split_len] candidate positions
   uint64_t* cvbase; // sparse: [S][Hkv][nsplit][split_len] byte offset of their V page
   float* cscore;   // sparse: [S][Hkv][nsplit][split_len][G] their log2 scores
+  float* vpart;    // sparse: [S][Hkv][nparts][G][hd] output partials of the V-pass parts
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
@@ -67,7 +85,8 @@ struct DecodeArgs {
   uint32_t window;
   uint32_t split_len;
   uint32_t nsplit;
-  uint32_t pad0;
+  uint32_t vsplits;  // sparse: splits per V-pass part
+  uint32_t nparts;   // sparse: V-pass parts per (sequence, kv head) = ceil(nsplit / vsplits)
   uint64_t k_stride;
   uint64_t k_data;
   uint64_t v_stride;
@@ -94,7 +113,7 @@ hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, h
 hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);  // one workgroup per (seq, kv head)
-hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_merge(bool sparse, bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq
