@@ -50,14 +50,23 @@ struct Fmt {
   static constexpr bool turbo = F >= KVQ_TURBO2;
 };
 
-// Lane geometry for a head size and group size.
-template <int HD, int G>
+// Lane geometry for a head size and a number of dims per lane.
+template <int HD, int DIMS>
 struct Geo {
-  static constexpr int D = (G <= 4) ? 16 : 8;  // dims per lane
-  static constexpr int T = HD / D;             // lanes per position
-  static constexpr int P = kWave / T;          // positions side by side in a wave
-  static constexpr int U = kChunk / P;         // steps per chunk
+  static constexpr int D = DIMS;          // dims per lane
+  static constexpr int T = HD / D;        // lanes per position
+  static constexpr int P = kWave / T;     // positions side by side in a wave
+  static constexpr int U = kChunk / P;    // steps per chunk
   static_assert(P >= 1 && P <= kChunk && kChunk % P == 0, "chunk geometry");
+};
+
+// Dims per lane of the dense split kernel and of the sparse score kernel:
+// 16 (fewer lanes per position, cheaper sums) unless the G accumulators or
+// query registers of 16 dims would cost too many registers.
+template <int G>
+struct LaneDims {
+  static constexpr int dense = (G <= 4) ? 16 : 8;
+  static constexpr int score = KVQ_SCORE_DIMS > 0 ? KVQ_SCORE_DIMS : dense;
 };
 
 // One lane's bytes of one position: D elements (+ the group scale byte).
@@ -285,10 +294,9 @@ struct PrologueSmem {
 
 // Page ids of the split, codebooks, and (turbo K) the rotated query in LDS;
 // then the lane's query registers.
-template <int KF, int VF, int HD, int G>
+template <int KF, int VF, int HD, int G, int D>
 __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, HD, G>& sm, uint32_t s,
-                                         uint32_t g, int pb, int pe, int t, QReg<KF, Geo<HD, G>::D, G>& q) {
-  constexpr int D = Geo<HD, G>::D;
+                                         uint32_t g, int pb, int pe, int t, QReg<KF, D, G>& q) {
   const int tid = threadIdx.x;
   const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
   if (tid < 16) {
@@ -343,12 +351,12 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
 // the clamped position's bytes (always inside a page of this split) and is
 // masked afterwards.  Loads without branches let the compiler keep the next
 // chunk's loads in flight while the current chunk is computed.
-template <int KF, int VF, int HD, int G, bool LOAD_V>
+template <int KF, int VF, int HD, int G, int D, bool LOAD_V>
 __device__ __forceinline__ void load_chunk(const DecodeArgs& a, const PrologueSmem<KF, HD, G>& sm, int first, int c,
                                            int pb, int pe, uint32_t g, int t, int r,
-                                           Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
-                                           Raw<VF, Geo<HD, G>::D> (&vr)[Geo<HD, G>::U], bool (&ok)[Geo<HD, G>::U]) {
-  using GE = Geo<HD, G>;
+                                           Raw<KF, D> (&kr)[Geo<HD, D>::U], Raw<VF, D> (&vr)[Geo<HD, D>::U],
+                                           bool (&ok)[Geo<HD, D>::U]) {
+  using GE = Geo<HD, D>;
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
 #pragma unroll
   for (int u = 0; u < GE::U; ++u) {
@@ -370,11 +378,11 @@ __device__ __forceinline__ void mask_raw(Raw<F, D>& r, bool ok) {
 }
 
 // Scores (log2 units, -inf outside the split) of a loaded chunk.
-template <int KF, int VF, int HD, int G>
-__device__ __forceinline__ void chunk_scores(const QReg<KF, Geo<HD, G>::D, G>& q, const float* kcen, float qscale,
-                                             const Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
-                                             const bool (&ok)[Geo<HD, G>::U], float (&sc)[Geo<HD, G>::U][G]) {
-  using GE = Geo<HD, G>;
+template <int KF, int HD, int G, int D>
+__device__ __forceinline__ void chunk_scores(const QReg<KF, D, G>& q, const float* kcen, float qscale,
+                                             const Raw<KF, D> (&kr)[Geo<HD, D>::U], const bool (&ok)[Geo<HD, D>::U],
+                                             float (&sc)[Geo<HD, D>::U][G]) {
+  using GE = Geo<HD, D>;
 #pragma unroll
   for (int u = 0; u < GE::U; ++u) {
     float part[G];
@@ -395,20 +403,20 @@ struct SplitSmem {
   float red[kWaves][G][HD + 2];
 };
 
-template <int KF, int VF, int HD, int G>
+template <int G, int D>
 struct DenseState {
-  float m[G], l[G], acc[G][Geo<HD, G>::D];
+  float m[G], l[G], acc[G][D];
 };
 
-template <int KF, int VF, int HD, int G>
-__device__ __forceinline__ void dense_chunk(const Raw<KF, Geo<HD, G>::D> (&kr)[Geo<HD, G>::U],
-                                            const Raw<VF, Geo<HD, G>::D> (&vr)[Geo<HD, G>::U],
-                                            const bool (&ok)[Geo<HD, G>::U], const QReg<KF, Geo<HD, G>::D, G>& q,
+template <int KF, int VF, int HD, int G, int D>
+__device__ __forceinline__ void dense_chunk(const Raw<KF, D> (&kr)[Geo<HD, D>::U],
+                                            const Raw<VF, D> (&vr)[Geo<HD, D>::U],
+                                            const bool (&ok)[Geo<HD, D>::U], const QReg<KF, D, G>& q,
                                             const float* kcen, const float* vcen, float qscale,
-                                            DenseState<KF, VF, HD, G>& st) {
-  using GE = Geo<HD, G>;
+                                            DenseState<G, D>& st) {
+  using GE = Geo<HD, D>;
   float sc[GE::U][G];
-  chunk_scores<KF, VF, HD, G>(q, kcen, qscale, kr, ok, sc);
+  chunk_scores<KF, HD, G, D>(q, kcen, qscale, kr, ok, sc);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float mx = sc[0][h];
@@ -441,8 +449,9 @@ __device__ __forceinline__ void dense_chunk(const Raw<KF, Geo<HD, G>::D> (&kr)[G
 
 template <int KF, int VF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs a) {
-  using GE = Geo<HD, G>;
-  constexpr int D = GE::D, T = GE::T;
+  constexpr int D = LaneDims<G>::dense;
+  using GE = Geo<HD, D>;
+  constexpr int T = GE::T;
   __shared__ SplitSmem<KF, VF, HD, G> sm;
   const Tile tl = unit_tile(a, a.nsplit);
   if (!tl.valid) return;
@@ -452,11 +461,11 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int t = lane % T, r = lane / T;
   QReg<KF, D, G> q;
-  prologue<KF, VF, HD, G>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
+  prologue<KF, VF, HD, G, D>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
   const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
   const int first = sp.pb >> a.log2_bs;
 
-  DenseState<KF, VF, HD, G> st;
+  DenseState<G, D> st;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     st.m[h] = -INFINITY;
@@ -473,15 +482,15 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
   // The next chunk is always loaded (past the end: this chunk again, an L2
   // hit, never used) so that no branch sits between a load and its use.
   if (c < sp.pe) {
-    load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
+    load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
     for (;;) {
       const int cb = c + step;
-      load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB, vB, oB);
-      dense_chunk<KF, VF, HD, G>(kA, vA, oA, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
+      load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB, vB, oB);
+      dense_chunk<KF, VF, HD, G, D>(kA, vA, oA, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
       if (cb >= sp.pe) break;
       const int ca = cb + step;
-      load_chunk<KF, VF, HD, G, true>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
-      dense_chunk<KF, VF, HD, G>(kB, vB, oB, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
+      load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
+      dense_chunk<KF, VF, HD, G, D>(kB, vB, oB, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
       if (ca >= sp.pe) break;
       c = ca;
     }
@@ -626,8 +635,9 @@ struct ScoreSmem {
 // has global weight <= thr and is provably skipped.
 template <int KF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs a) {
-  using GE = Geo<HD, G>;
-  constexpr int D = GE::D, T = GE::T;
+  constexpr int D = LaneDims<G>::score;
+  using GE = Geo<HD, D>;
+  constexpr int T = GE::T;
   __shared__ ScoreSmem<KF, HD, G> sm;
   const Tile tl = unit_tile(a, a.nsplit);
   if (!tl.valid) return;
@@ -637,7 +647,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int t = lane % T, r = lane / T;
   QReg<KF, D, G> q;
-  prologue<KF, KVQ_BF16, HD, G>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
+  prologue<KF, KVQ_BF16, HD, G, D>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
   const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
   const int first = sp.pb >> a.log2_bs;
 
@@ -646,7 +656,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
   auto consume = [&](int c, const Raw<KF, D>(&kr)[GE::U], const bool(&ok)[GE::U]) {
     float sc[GE::U][G];
-    chunk_scores<KF, KVQ_BF16, HD, G>(q, sm.pro.kcen, qscale, kr, ok, sc);
+    chunk_scores<KF, HD, G, D>(q, sm.pro.kcen, qscale, kr, ok, sc);
 #pragma unroll
     for (int u = 0; u < GE::U; ++u) {
       const int j = c + u * GE::P + r;
@@ -663,15 +673,15 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   constexpr int step = kWaves * kChunk;
   int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;
   if (c < sp.pe) {
-    load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vdummy, oA);
+    load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vdummy, oA);
     for (;;) {
       const int cb = c + step;
-      load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB,
+      load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB,
                                              vdummy, oB);
       consume(c, kA, oA);
       if (cb >= sp.pe) break;
       const int ca = cb + step;
-      load_chunk<KF, KVQ_BF16, HD, G, false>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA,
+      load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA,
                                              vdummy, oA);
       consume(cb, kB, oB);
       if (ca >= sp.pe) break;

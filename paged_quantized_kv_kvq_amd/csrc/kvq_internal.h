@@ -21,6 +21,9 @@
 #ifndef KVQ_VPART_POSITIONS
 #define KVQ_VPART_POSITIONS 2048  // positions whose candidates one sparse-V workgroup takes
 #endif
+#ifndef KVQ_SCORE_DIMS
+#define KVQ_SCORE_DIMS 0         // dims per lane in the sparse score kernel (0: as the dense kernel)
+#endif
 #ifndef KVQ_NT_LOADS
 #define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
 #endif

@@ -1,0 +1,81 @@
+"""GPU parity at the benchmark workloads' full sizes.
+
+Each workload is staged exactly as the benchmark stages it (whole pool, all
+sequences, the timed step's write batch in its shuffled slot order) and
+decoded through the same C-ABI call with the same arguments.  The oracle then
+rebuilds only a few sampled sequences (shortest, longest, one seeded pick;
+for the sliding-window workload only the pages inside the window) and checks
+them element by element: written pool bytes bit-exact, decode outputs to the
+same max-abs / relative-L2 bar as the small cases.  Properties that hold at
+any size are checked on every sequence: all outputs finite, the decode
+repeatable bit for bit, and the write idempotent (writing the same batch
+again leaves the pool bytes unchanged).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.gpu import stage
+from kvq_testlib import OracleCache, check_decode, say, timed
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(lens: np.ndarray, wid: int, extra: int = 1):
+    picks = {int(np.argmin(lens)), int(np.argmax(lens))}
+    want = len(picks) + extra
+    rng = np.random.default_rng(wid)
+    for s in rng.permutation(len(lens)):
+        if len(picks) >= want:
+            break
+        picks.add(int(s))
+    return sorted(picks)
+
+
+def _decode(kvq, st):
+    w = st.w
+    need = kvq.decode_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, st.bt.shape[1], w.sliding_window,
+                                      w.sparse_v_threshold)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bytes
+    return kvq.paged_decode(st.layout, st.q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev,
+                            synth.inv_sqrt_d(w.head_dim), w.sliding_window, w.sparse_v_threshold,
+                            st.k_scale, st.v_scale, workspace=ws)
+
+
+# sequences the oracle rebuilds per workload (its cost grows with their length)
+EXTRA = {1: 0, 2: 1, 3: 0, 4: 1, 5: 1}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wid", sorted(synth.WORKLOADS))
+def test_workload_full_size(gpu_lib, wid):
+    w = synth.WORKLOADS[wid]
+    lens = synth.seq_lens(w)
+    seqs = _sample(lens, wid, EXTRA[wid])
+    say(f"workload {wid} ({w.name}): {w.num_seqs} seqs, lens {lens.min()}..{lens.max()}, oracle seqs {seqs}")
+    with timed(f"stage workload {wid}"):
+        st = stage(w, gpu_lib, "cuda", keep_host=seqs)
+    with timed(f"write {st.tail_slots.numel()} tokens + decode"):
+        if st.tail_slots.numel():
+            gpu_lib.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool,
+                                      st.tail_slots, st.k_scale, st.v_scale)
+        out = _decode(gpu_lib, st).clone()
+        again = _decode(gpu_lib, st)
+        torch.cuda.synchronize()
+    assert torch.isfinite(out).all(), "non-finite decode output"
+    assert torch.equal(out, again), "decode is not repeatable"
+    if st.tail_slots.numel():
+        kb, vb = st.k_pool.clone(), st.v_pool.clone()
+        gpu_lib.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool,
+                                  st.tail_slots, st.k_scale, st.v_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(kb, st.k_pool) and torch.equal(vb, st.v_pool), "rewrite changed the pool"
+        del kb, vb
+    out_np = out.cpu().numpy()
+    with timed(f"oracle for {len(seqs)} sequences"):
+        ora = OracleCache(st, seqs, from_window=bool(w.sliding_window))
+        ora.compare_pools(st)
+        ref = ora.decode(st, synth.inv_sqrt_d(w.head_dim))
+    e, rel, namb = check_decode(out_np, ref, seqs, f"workload {wid}")
+    say(f"  ok workload {wid}: max-abs {e:.2e} rel-L2 {rel:.2e} ambiguous {namb}")
