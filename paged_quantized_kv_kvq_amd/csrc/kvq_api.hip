@@ -118,8 +118,8 @@ int check_layout(const kvq_layout* l) {
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
-  uint32_t split_len, nsplit, vsplits, nparts;
-  uint64_t off_part, off_ml, off_cnt, off_cidx, off_cpage, off_cs, off_vpart, bytes;
+  uint32_t split_len, nsplit, vsplits, nparts, seg_cap;
+  uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -142,21 +142,19 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
-  p.off_part = p.off_cnt = p.off_cidx = p.off_cpage = p.off_cs = p.off_vpart = 0;
+  p.off_part = p.off_cnt = p.off_crec = p.off_vpart = 0;
+  p.seg_cap = 0;
   p.vsplits = std::min<uint32_t>(64, std::max<uint32_t>(1, KVQ_VPART_POSITIONS / sl));  // <= kMaxStatSplits
   p.nparts = (p.nsplit + p.vsplits - 1) / p.vsplits;
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
   } else {
+    p.seg_cap = cand_segment_cap(sl);
     p.off_cnt = off;
-    off = up256(off + units * sizeof(int32_t));
-    p.off_cidx = off;
-    off = up256(off + units * sl * sizeof(int32_t));
-    p.off_cpage = off;
-    off = up256(off + units * sl * sizeof(uint64_t));
-    p.off_cs = off;
-    off = up256(off + units * sl * G * sizeof(float));
+    off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
+    p.off_crec = off;
+    off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
     p.off_vpart = off;
     off = up256(off + uint64_t(S) * nkv * p.nparts * G * hd * sizeof(float));
   }
@@ -277,9 +275,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
     a.part = reinterpret_cast<float*>(ws + p.off_part);
   } else {
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
-    a.cidx = reinterpret_cast<int32_t*>(ws + p.off_cidx);
-    a.cvbase = reinterpret_cast<uint64_t*>(ws + p.off_cpage);
-    a.cscore = reinterpret_cast<float*>(ws + p.off_cs);
+    a.crec = reinterpret_cast<uint32_t*>(ws + p.off_crec);
     a.vpart = reinterpret_cast<float*>(ws + p.off_vpart);
   }
   a.max_blocks = max_blocks_per_seq;
@@ -293,6 +289,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   a.nsplit = p.nsplit;
   a.vsplits = p.vsplits;
   a.nparts = p.nparts;
+  a.seg_cap = p.seg_cap;
   a.k_stride = layout->k_block_stride_bytes;
   a.k_data = layout->k_data_section_bytes;
   a.v_stride = layout->v_block_stride_bytes;

@@ -136,8 +136,18 @@ __device__ __forceinline__ void load_lane(const uint8_t* __restrict__ blk, uint3
     r.w[0] = uint32_t(v);
     if constexpr (Raw<F, D>::words > 1) r.w[1] = uint32_t(v >> 32) & 0xFFFFu;
   }
-  if constexpr (Fmt<F>::turbo) r.sc = blk[data_bytes + uint64_t(row) * (HD / 16) + (t * D) / 16];
-  else r.sc = 0;
+  // The scale byte is read as the aligned dword that holds it (scale_shift
+  // selects it at the use), so no byte extension sits next to the load.
+  if constexpr (Fmt<F>::turbo)
+    r.sc = *reinterpret_cast<const uint32_t*>(blk + data_bytes + uint64_t(row) * (HD / 16) + (((t * D) / 16) & ~3));
+  else
+    r.sc = 0;
+}
+
+// Bit offset of a lane's scale byte inside the dword load_lane reads.
+template <int D>
+__device__ __forceinline__ uint32_t scale_shift(int t) {
+  return 8u * uint32_t(((t * D) / 16) & 3);
 }
 
 template <int F, int D>
@@ -182,6 +192,7 @@ struct QReg {
   static constexpr bool packed = !Fmt<KF>::turbo;
   uint32_t qp[packed ? G : 1][packed ? D / 2 : 1];
   float qf[packed ? 1 : G][packed ? 1 : D];
+  uint32_t scsh;  // scale_shift of the lane (turbo K)
 };
 
 // Partial score of one lane for every head (before the T-lane sum).
@@ -214,7 +225,7 @@ __device__ __forceinline__ void lane_scores(const QReg<KF, D, G>& q, const Raw<K
     float kv[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) kv[i] = kcen[code_at<Fmt<KF>::bits, D>(k.w, i)];
-    const float sq = e4m3_decode(k.sc);
+    const float sq = e4m3_decode(k.sc >> q.scsh);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float s = 0.0f;
@@ -229,7 +240,7 @@ __device__ __forceinline__ void lane_scores(const QReg<KF, D, G>& q, const Raw<K
 // centroid with the group scale in `sq`).
 template <int VF, int D>
 __device__ __forceinline__ void v_values(const Raw<VF, D>& v, const float* __restrict__ vcen, float (&x)[D],
-                                         float& sq) {
+                                         float& sq, uint32_t scsh) {
   sq = 1.0f;
   if constexpr (VF == KVQ_BF16) {
 #pragma unroll
@@ -247,7 +258,7 @@ __device__ __forceinline__ void v_values(const Raw<VF, D>& v, const float* __res
   } else {
 #pragma unroll
     for (int i = 0; i < D; ++i) x[i] = vcen[code_at<Fmt<VF>::bits, D>(v.w, i)];
-    sq = e4m3_decode(v.sc);
+    sq = e4m3_decode(v.sc >> scsh);
   }
 }
 
@@ -273,10 +284,21 @@ struct Tile {
 // Units are numbered split-major (unit = split * S + sequence): the units of
 // one split index rotate over the XCDs, and so do the (fewer) later splits
 // that only long sequences have.
+//
+// MODE 1 keeps the kv heads of a unit on one XCD; MODE 0 numbers workgroups
+// unit-major (wg = unit * Hkv + head), so that with 8 kv heads each XCD takes
+// one head of every unit.
+template <int MODE>
 __device__ __forceinline__ Tile unit_tile(const DecodeArgs& a, uint32_t per_seq) {
   uint32_t unit, head;
   Tile t;
-  t.valid = xcd_unit_tile(blockIdx.x, a.num_seqs * per_seq, a.num_kv_heads, unit, head);
+  if constexpr (MODE == 1) {
+    t.valid = xcd_unit_tile(blockIdx.x, a.num_seqs * per_seq, a.num_kv_heads, unit, head);
+  } else {
+    unit = blockIdx.x / a.num_kv_heads;
+    head = blockIdx.x % a.num_kv_heads;
+    t.valid = unit < a.num_seqs * per_seq;
+  }
   t.g = head;
   t.s = unit % a.num_seqs;
   t.split = unit / a.num_seqs;
@@ -290,6 +312,7 @@ struct PrologueSmem {
   float vcen[16];
   uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
   uint64_t vbase[kMaxPages];  // ... and in the V pool
+  uint32_t page[kMaxPages];   // page ids (for candidate records)
 };
 
 // Page ids of the split, codebooks, and (turbo K) the rotated query in LDS;
@@ -299,6 +322,20 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
                                          uint32_t g, int pb, int pe, int t, QReg<KF, D, G>& q) {
   const int tid = threadIdx.x;
   const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
+  q.scsh = scale_shift<D>(t);
+  if constexpr (!Fmt<KF>::turbo) {
+    // bf16 query pairs straight from memory (the score scale is applied
+    // later); requested first so that their latency overlaps the page table's
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const uint4* src = reinterpret_cast<const uint4*>(qg + h * HD + t * D);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        const uint4 v = src[i];
+        q.qp[h][4 * i] = v.x; q.qp[h][4 * i + 1] = v.y; q.qp[h][4 * i + 2] = v.z; q.qp[h][4 * i + 3] = v.w;
+      }
+    }
+  }
   if (tid < 16) {
     if constexpr (Fmt<KF>::turbo) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
     if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
@@ -311,19 +348,14 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
       const uint64_t page = uint64_t(uint32_t(bt[i]));
       sm.kbase[i] = page * a.k_stride;
       sm.vbase[i] = page * a.v_stride;
+      sm.page[i] = uint32_t(page);
     }
   }
   if constexpr (!Fmt<KF>::turbo) {
-    // bf16 query pairs straight from memory (the score scale is applied later)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const uint4* src = reinterpret_cast<const uint4*>(qg + h * HD + t * D);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const uint4 v = src[i];
-        q.qp[h][4 * i] = v.x; q.qp[h][4 * i + 1] = v.y; q.qp[h][4 * i + 2] = v.z; q.qp[h][4 * i + 3] = v.w;
-      }
-    }
+    // Every load so far is complete before the chunk loop starts: the loop
+    // then begins with only chunk loads outstanding on every path, and the
+    // compiler's wait counts inside it stay exact.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   } else {
     for (int i = tid; i < G * HD; i += kWaves * kWave) sm.q[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
@@ -435,7 +467,7 @@ __device__ __forceinline__ void dense_chunk(const Raw<KF, D> (&kr)[Geo<HD, D>::U
     Raw<VF, GE::D> vm = vr[u];
     mask_raw(vm, ok[u]);  // a masked position adds 0 * (finite value)
     float x[GE::D], sq;
-    v_values<VF, GE::D>(vm, vcen, x, sq);
+    v_values<VF, GE::D>(vm, vcen, x, sq, q.scsh);  // V lanes hold the same dims as K lanes
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = ok[u] ? fast_exp2(sc[u][h] - st.m[h]) : 0.0f;
@@ -453,7 +485,7 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
   using GE = Geo<HD, D>;
   constexpr int T = GE::T;
   __shared__ SplitSmem<KF, VF, HD, G> sm;
-  const Tile tl = unit_tile(a, a.nsplit);
+  const Tile tl = unit_tile<KVQ_TILE_DENSE>(a, a.nsplit);
   if (!tl.valid) return;
   const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
@@ -474,25 +506,34 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
     for (int i = 0; i < D; ++i) st.acc[h][i] = 0.0f;
   }
 
-  Raw<KF, D> kA[GE::U], kB[GE::U];
-  Raw<VF, D> vA[GE::U], vB[GE::U];
-  bool oA[GE::U], oB[GE::U];
+  // Chunk n of the wave sits in buffer n % NB and is loaded NB - 1 chunks
+  // ahead, every load inside the loop (the first NB - 1 uses are of empty,
+  // all-masked buffers); whole rounds of NB chunks, one exit at the bottom (a
+  // chunk past the end is all masked and reads the clamped last position).
+  constexpr int NB = KVQ_DENSE_BUFS;
+  Raw<KF, D> kb[NB][GE::U];
+  Raw<VF, D> vb[NB][GE::U];
+  bool ob[NB][GE::U];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int u = 0; u < GE::U; ++u) {
+      zero_raw(kb[i][u]);
+      zero_raw(vb[i][u]);
+      ob[i][u] = false;
+    }
   constexpr int step = kWaves * kChunk;
-  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;
-  // The next chunk is always loaded (past the end: this chunk again, an L2
-  // hit, never used) so that no branch sits between a load and its use.
+  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;  // next chunk to load
   if (c < sp.pe) {
-    load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
-    for (;;) {
-      const int cb = c + step;
-      load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB, vB, oB);
-      dense_chunk<KF, VF, HD, G, D>(kA, vA, oA, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
-      if (cb >= sp.pe) break;
-      const int ca = cb + step;
-      load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA, vA, oA);
-      dense_chunk<KF, VF, HD, G, D>(kB, vB, oB, q, sm.pro.kcen, sm.pro.vcen, qscale, st);
-      if (ca >= sp.pe) break;
-      c = ca;
+    const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;  // covers chunks + NB - 1 uses
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        load_chunk<KF, VF, HD, G, D, true>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kb[(i + NB - 1) % NB],
+                                           vb[(i + NB - 1) % NB], ob[(i + NB - 1) % NB]);
+        dense_chunk<KF, VF, HD, G, D>(kb[i], vb[i], ob[i], q, sm.pro.kcen, sm.pro.vcen, qscale, st);
+        c += step;
+      }
     }
   }
 
@@ -624,22 +665,33 @@ template <int KF, int HD, int G>
 struct ScoreSmem {
   PrologueSmem<KF, HD, G> pro;
   float sc[kMaxSparseSplit * G];
-  float wred[kWaves][G];
-  float stat[G][2];
-  int wcount[kWaves];
+  float wm[kWaves][G];  // per-wave max and sum of exp2(score - max)
+  float wz[kWaves][G];
 };
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // Scores of one split; stores the split's (max, sum) and the candidate
 // positions whose split-local weight exceeds thr * (1 - 1e-4).  The global
 // normalizer is at least the split's, so a position that is not a candidate
 // has global weight <= thr and is provably skipped.
+//
+// Wave w scores chunks w, w + kWaves, ... of 16 positions; after the loop it
+// reduces its own scores (max, sum), one barrier combines the waves, and each
+// wave then compacts its own candidates into its own segment of the record
+// list (no further barriers).  A record is (page id, position, G log2 scores).
 template <int KF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs a) {
   constexpr int D = LaneDims<G>::score;
   using GE = Geo<HD, D>;
   constexpr int T = GE::T;
+  constexpr int RS = cand_record_words(G);
   __shared__ ScoreSmem<KF, HD, G> sm;
-  const Tile tl = unit_tile(a, a.nsplit);
+  const Tile tl = unit_tile<KVQ_TILE_SCORES>(a, a.nsplit);
   if (!tl.valid) return;
   const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
@@ -667,100 +719,123 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
       }
     }
   };
-  Raw<KF, D> kA[GE::U], kB[GE::U];
+  // The wave's chunks c, c + step, ...; chunk n sits in buffer n % NB and is
+  // loaded NB - 1 chunks ahead of its use.  Every load is issued inside the
+  // loop (the first NB - 1 uses are of empty, all-masked buffers), and the
+  // loop runs whole rounds of NB chunks with one exit at the bottom; a chunk
+  // past the end is all masked (its loads read the clamped last position, an
+  // L2 hit).  With one loop entry state and no early exit the compiler keeps
+  // NB - 1 chunks in flight across the back edge.
+  constexpr int NB = KVQ_SCORE_BUFS;
+  Raw<KF, D> kb[NB][GE::U];
   Raw<KVQ_BF16, D> vdummy[GE::U];
-  bool oA[GE::U], oB[GE::U];
+  bool ob[NB][GE::U];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int u = 0; u < GE::U; ++u) {
+      zero_raw(kb[i][u]);
+      ob[i][u] = false;
+    }
   constexpr int step = kWaves * kChunk;
-  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;
+  const int cs = sp.pb & ~(kChunk - 1);
+  int c = cs + w * kChunk;  // next chunk to load; the one used trails by NB - 1
   if (c < sp.pe) {
-    load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r, kA, vdummy, oA);
-    for (;;) {
-      const int cb = c + step;
-      load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, cb < sp.pe ? cb : c, sp.pb, sp.pe, tl.g, t, r, kB,
-                                             vdummy, oB);
-      consume(c, kA, oA);
-      if (cb >= sp.pe) break;
-      const int ca = cb + step;
-      load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, ca < sp.pe ? ca : cb, sp.pb, sp.pe, tl.g, t, r, kA,
-                                             vdummy, oA);
-      consume(cb, kB, oB);
-      if (ca >= sp.pe) break;
-      c = ca;
+    const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;  // covers chunks + NB - 1 uses
+    for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r,
+                                               kb[(i + NB - 1) % NB], vdummy, ob[(i + NB - 1) % NB]);
+        consume(c - (NB - 1) * step, kb[i], ob[i]);
+        c += step;
+      }
+    }
+  }
+  // the wave's own scores: lane (sub, pos) visits position pos of every
+  // kSubs-th chunk the wave scored
+  wave_lds_sync();
+  constexpr int kSubs = kWave / kChunk;
+  constexpr int lap = kSubs * step;
+  const int sub = lane / kChunk, pos = lane % kChunk;
+  float mw[G], zl[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    mw[h] = group_max<kWave>(mloc[h]);
+    zl[h] = 0.0f;
+  }
+  for (int cw = cs + w * kChunk; cw < sp.pe; cw += lap) {
+    const int j = cw + sub * step + pos;
+    if (j >= sp.pb && j < sp.pe) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) zl[h] += fast_exp2(sm.sc[(j - sp.pb) * G + h] - mw[h]);
     }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mw = group_max<kWave>(mloc[h]);
-    if (lane == 0) sm.wred[w][h] = mw;
+    const float zw = group_sum<kWave>(zl[h]);
+    if (lane == 0) {
+      sm.wm[w][h] = mw[h];
+      sm.wz[w][h] = zw;
+    }
   }
   __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.wred[ww][tid]);
-    sm.stat[tid][0] = M;
-  }
-  __syncthreads();
-  const int n = sp.pe - sp.pb;
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lsum[h] = 0.0f;
-  for (int i = tid; i < n; i += kWaves * kWave) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) lsum[h] += fast_exp2(sm.sc[i * G + h] - sm.stat[h][0]);
-  }
+  float M[G], cut[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float lw = group_sum<kWave>(lsum[h]);
-    if (lane == 0) sm.wred[w][h] = lw;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float sum = 0.0f;
-    for (int ww = 0; ww < kWaves; ++ww) sum += sm.wred[ww][tid];
-    sm.stat[tid][1] = sum;
-  }
-  __syncthreads();
-  const uint64_t base = (uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split;
-  if (tid < G) {
-    a.ml[(base * G + tid) * 2] = sm.stat[tid][0];
-    a.ml[(base * G + tid) * 2 + 1] = sm.stat[tid][1];
-  }
-  // candidates, compacted in position order
-  float cut[G];
+    float m = -INFINITY;
 #pragma unroll
-  for (int h = 0; h < G; ++h) cut[h] = a.thr * (1.0f - 1e-4f) * sm.stat[h][1];
-  int32_t* cidx = a.cidx + base * a.split_len;
-  uint64_t* cvb = a.cvbase + base * a.split_len;
-  float* cs = a.cscore + base * a.split_len * G;
-  int total = 0;
-  for (int c0 = 0; c0 < n; c0 += kWaves * kWave) {
-    const int i = c0 + tid;
+    for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, sm.wm[ww][h]);
+    float z = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float mk = sm.wm[ww][h];
+      if (mk > -INFINITY) z += fast_exp2(mk - m) * sm.wz[ww][h];
+    }
+    M[h] = m;
+    cut[h] = a.thr * (1.0f - 1e-4f) * z;
+    if (tid == h) {
+      const uint64_t base = (uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split;
+      a.ml[(base * G + h) * 2] = m;
+      a.ml[(base * G + h) * 2 + 1] = z;
+    }
+  }
+  // candidates of this wave, compacted in its own segment
+  const uint64_t seg = ((uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split) * kWaves + w;
+  uint32_t* rec = a.crec + seg * a.seg_cap * RS;
+  int nw = 0;
+  for (int cw = cs + w * kChunk; cw < sp.pe; cw += lap) {
+    const int j = cw + sub * step + pos;
     bool cand = false;
-    if (i < n) {
+    float sv[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) cand |= fast_exp2(sm.sc[i * G + h] - sm.stat[h][0]) > cut[h];
+    for (int h = 0; h < G; ++h) sv[h] = 0.0f;
+    if (j >= sp.pb && j < sp.pe) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sv[h] = sm.sc[(j - sp.pb) * G + h];
+        cand |= fast_exp2(sv[h] - M[h]) > cut[h];
+      }
     }
-    const uint64_t ballot = __ballot(cand);
-    const int before = __popcll(ballot & ((1ull << lane) - 1ull));
-    if (lane == 0) sm.wcount[w] = __popcll(ballot);
-    __syncthreads();
-    int off = total;
-    for (int ww = 0; ww < w; ++ww) off += sm.wcount[ww];
+    const uint64_t bal = __ballot(cand);
     if (cand) {
-      const int k = off + before;
-      const int j = sp.pb + i;
-      cidx[k] = j;
-      cvb[k] = sm.pro.vbase[(j >> a.log2_bs) - first];
+      const int k = nw + __popcll(bal & ((1ull << lane) - 1ull));
+      uint32_t rw[RS];
+      rw[0] = sm.pro.page[(j >> a.log2_bs) - first];
+      rw[1] = uint32_t(j);
 #pragma unroll
-      for (int h = 0; h < G; ++h) cs[k * G + h] = sm.sc[i * G + h];
+      for (int h = 0; h < G; ++h) rw[2 + h] = __float_as_uint(sv[h]);
+#pragma unroll
+      for (int i = 2 + G; i < RS; ++i) rw[i] = 0u;
+      uint4* dst = reinterpret_cast<uint4*>(rec + uint64_t(k) * RS);
+#pragma unroll
+      for (int i = 0; i < RS / 4; ++i) dst[i] = make_uint4(rw[4 * i], rw[4 * i + 1], rw[4 * i + 2], rw[4 * i + 3]);
     }
-    for (int ww = 0; ww < kWaves; ++ww) total += sm.wcount[ww];
-    __syncthreads();
+    nw += __popcll(bal);
   }
-  if (tid == 0) a.cnt[base] = total;
+  if (lane == 0) a.cnt[seg] = nw;
 }
 
-constexpr int kRecPerLane = 2;    // candidate records read per lane per round (sparse V)
 constexpr int kMaxStatSplits = 64;  // splits whose stats the V pass stages in LDS at once
 
 // The V pass uses 8 dims per lane (more rows side by side, fewer registers).
@@ -771,36 +846,53 @@ struct VGeo {
   static constexpr int P = kWave / T;
 };
 
+template <int G>
+__device__ __forceinline__ void load_record(const uint32_t* src, uint32_t (&rw)[cand_record_words(G)]) {
+  const uint4* p = reinterpret_cast<const uint4*>(src);
+#pragma unroll
+  for (int i = 0; i < int(cand_record_words(G)) / 4; ++i) {
+    const uint4 v = p[i];
+    rw[4 * i] = v.x;
+    rw[4 * i + 1] = v.y;
+    rw[4 * i + 2] = v.z;
+    rw[4 * i + 3] = v.w;
+  }
+}
+
 template <int VF, int HD, int G>
 struct SparseSmem {
   float vcen[16];
   float mz[G][2];                     // global (max, 1/sum) per head
   float st[kMaxStatSplits][G][2];     // split stats being reduced
-  int cnt[kMaxStatSplits];            // candidate counts of the part's splits
+  int pre[kWaves][kMaxStatSplits];    // per wave: inclusive prefix of its segment counts
   struct Kept {
     uint64_t vb;   // byte offset of the V page
     uint32_t row;  // row (offset * Hkv + kv head) in the page
     float p[G];    // kept weights (0 for heads that drop the position)
-  } kept[kWaves][kWave * kRecPerLane];
-  float red[kWaves][G][HD];
+  };
+  union {
+    Kept kept[kWaves][kWave];
+    float red[kWaves][G][HD];
+  } u;
 };
 
 // One workgroup per (sequence, kv head, part), a part being `vsplits`
 // consecutive splits: every candidate of those splits gets its exact global
 // weight; V is loaded only where some head of the group keeps the position.
-// The split stats (for the global max and sum per head) and the part's
-// candidate counts are staged in LDS with one parallel load.  Each lane reads
-// whole candidate records (coalesced: 128 records per wave per round, one
-// memory latency) and decides keep/drop for every head; a ballot compacts the
-// kept ones into LDS, and the wave's lane slots then stream their V rows.
-// Each part stores its partial output; the merge kernel sums the parts.
+// Wave w of this kernel takes the records that wave w of the score kernel
+// wrote (its segments of the part's splits), so the waves share the work
+// evenly.  The wave's segment counts, a first record per lane (read ahead,
+// before the counts are known) and the split stats are all requested at once.
+// A ballot compacts the kept records of a round of 64 into LDS, and the
+// wave's lane slots then stream their V rows, kCandUnroll rows per slot in
+// flight.  Each part stores its partial output; the merge kernel sums them.
 template <int VF, int HD, int G>
 __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeArgs a) {
   using GE = VGeo<HD>;
   constexpr int D = GE::D, T = GE::T, P = GE::P;
-  constexpr int RW = kWave * kRecPerLane;  // records per wave per round
+  constexpr int RS = cand_record_words(G);
   __shared__ SparseSmem<VF, HD, G> sm;
-  const Tile tl = unit_tile(a, a.nparts);
+  const Tile tl = unit_tile<KVQ_TILE_SPARSE_V>(a, a.nparts);
   if (!tl.valid) return;
   const uint32_t s = tl.s, g = tl.g, part = tl.split;
   const SeqSpan sp = split_span(a, s, 0);
@@ -814,6 +906,11 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
   const int t = lane % T, r = lane / T;
   const int k0 = int(part * a.vsplits);
   const int k1 = min(ns, k0 + int(a.vsplits));
+  const int nseg = k1 - k0;  // 0 only for an empty sequence
+  // requests that do not depend on each other go out first
+  const int myc = lane < nseg ? a.cnt[(sbase + k0 + lane) * kWaves + w] : 0;
+  uint32_t spec[RS];
+  load_record<G>(a.crec + (((sbase + k0) * kWaves + w) * a.seg_cap + lane) * RS, spec);
   if (tid < 16) {
     if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
@@ -844,7 +941,16 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     sm.mz[tid][0] = runm;
     sm.mz[tid][1] = runz > 0.0f ? 1.0f / runz : 0.0f;
   }
-  for (int k = k0 + tid; k < k1; k += kWaves * kWave) sm.cnt[k - k0] = a.cnt[sbase + k];
+  // the wave's segments: inclusive prefix of their counts
+  int pre = myc;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(pre, off);
+    if (lane >= off) pre += v;
+  }
+  if (lane < nseg) sm.pre[w][lane] = pre;
+  const int total = nseg > 0 ? __shfl(pre, nseg - 1) : 0;
+  const int c0 = __shfl(myc, 0);
   __syncthreads();
   float M[G], iz[G];
 #pragma unroll
@@ -852,78 +958,69 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     M[h] = sm.mz[h][0];
     iz[h] = sm.mz[h][1];
   }
-  int total = 0;
-  for (int k = k0; k < k1; ++k) total += sm.cnt[k - k0];
   float acc[G][D];
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[h][i] = 0.0f;
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
-  auto& kept = sm.kept[w];
-  for (int i0 = w * RW; i0 < total; i0 += kWaves * RW) {
-    // 1. records -> keep decisions, compacted into the wave's LDS list
-    int nk = 0;
+  const uint32_t vsh = scale_shift<D>(t);
+  auto& kept = sm.u.kept[w];
+  for (int i0 = 0; i0 < total; i0 += kWave) {
+    // 1. one record per lane -> keep decisions, compacted into the wave's LDS list
+    const int gi = i0 + lane;
+    const bool ok = gi < total;
+    uint32_t rw[RS];
 #pragma unroll
-    for (int q = 0; q < kRecPerLane; ++q) {
-      const int gi = i0 + q * kWave + lane;
-      const bool ok = gi < total;
-      // locate the record: the first split k >= k0 with prefix(k+1) > gi
-      int k = k0, before = 0;
-      bool found = false;
-      for (int kk = k0; kk < k1; ++kk) {
-        const int c = sm.cnt[kk - k0];
-        if (!found) {
-          if (gi < before + c) {
-            found = true;
-            k = kk;
-          } else {
-            before += c;
-          }
-        }
-      }
-      const uint64_t rec = (sbase + (ok ? k : k0)) * a.split_len + (ok ? gi - before : 0);
-      const uint32_t row = (uint32_t(a.cidx[rec]) & bmask) * a.num_kv_heads + g;
-      const uint64_t vb = a.cvbase[rec];
-      float p[G];
-      bool any = false;
+    for (int i = 0; i < RS; ++i) rw[i] = 0u;
+    if (i0 == 0 && lane < c0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pv = fast_exp2(a.cscore[rec * G + h] - M[h]) * iz[h];
-        p[h] = (ok && pv > a.thr) ? pv : 0.0f;
-        any |= p[h] > 0.0f;
-      }
-      const uint64_t bal = __ballot(any);
-      if (any) {
-        const int kk = nk + __popcll(bal & ((1ull << lane) - 1ull));
-        kept[kk].vb = vb;
-        kept[kk].row = row;
+      for (int i = 0; i < RS; ++i) rw[i] = spec[i];
+    } else if (ok) {
+      // segment k: the number of segments whose inclusive prefix is <= gi
+      int k = 0;
 #pragma unroll
-        for (int h = 0; h < G; ++h) kept[kk].p[h] = p[h];
-      }
-      nk += __popcll(bal);
+      for (int b = kMaxStatSplits / 2; b > 0; b >>= 1)
+        if (k + b < nseg && sm.pre[w][k + b - 1] <= gi) k += b;
+      const int off = gi - (k > 0 ? sm.pre[w][k - 1] : 0);
+      load_record<G>(a.crec + (((sbase + k0 + k) * kWaves + w) * a.seg_cap + off) * RS, rw);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float p[G];
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pv = fast_exp2(__uint_as_float(rw[2 + h]) - M[h]) * iz[h];
+      p[h] = (ok && pv > a.thr) ? pv : 0.0f;
+      any |= p[h] > 0.0f;
+    }
+    const uint64_t bal = __ballot(any);
+    if (any) {
+      const int kk = __popcll(bal & ((1ull << lane) - 1ull));
+      kept[kk].vb = uint64_t(rw[0]) * a.v_stride;
+      kept[kk].row = (rw[1] & bmask) * a.num_kv_heads + g;
+#pragma unroll
+      for (int h = 0; h < G; ++h) kept[kk].p[h] = p[h];
+    }
+    const int nk = __popcll(bal);
+    wave_lds_sync();
     // 2. lane slots stream the kept V rows, kCandUnroll in flight
     for (int q0 = r; q0 < nk; q0 += P * kCandUnroll) {
       Raw<VF, D> vr[kCandUnroll];
       float pk[kCandUnroll][G];
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
-        const int q = q0 + u * P;
-        const bool ok = q < nk;
-        const int qc = ok ? q : 0;
+        const int qi = q0 + u * P;
+        const bool kok = qi < nk;
+        const int qc = kok ? qi : 0;
         load_lane<VF, HD, D>(a.v_cache + kept[qc].vb, kept[qc].row, t, a.v_data, vr[u]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) pk[u][h] = ok ? kept[qc].p[h] : 0.0f;
+        for (int h = 0; h < G; ++h) pk[u][h] = kok ? kept[qc].p[h] : 0.0f;
       }
 #pragma unroll
       for (int u = 0; u < kCandUnroll; ++u) {
         mask_raw(vr[u], q0 + u * P < nk);
         float x[D], sq;
-        v_values<VF, D>(vr[u], sm.vcen, x, sq);
+        v_values<VF, D>(vr[u], sm.vcen, x, sq, vsh);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float pw = pk[u][h] * sq;
@@ -932,9 +1029,7 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
         }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_sync();
   }
 #pragma unroll
   for (int off = T; off < kWave; off <<= 1)
@@ -942,11 +1037,12 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < D; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
+  __syncthreads();  // the reduction area overlays the kept lists
   if (r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < D; ++i) sm.red[w][h][t * D + i] = acc[h][i];
+      for (int i = 0; i < D; ++i) sm.u.red[w][h][t * D + i] = acc[h][i];
   }
   __syncthreads();
   const uint64_t pbase = (uint64_t(s) * a.num_kv_heads + g) * a.nparts;
@@ -954,7 +1050,7 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     const int h = i / HD, d = i % HD;
     float o = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) o += sm.red[ww][h][d];
+    for (int ww = 0; ww < kWaves; ++ww) o += sm.u.red[ww][h][d];
     a.vpart[(pbase + part) * G * HD + i] = o;
   }
 }

@@ -24,6 +24,21 @@
 #ifndef KVQ_SCORE_DIMS
 #define KVQ_SCORE_DIMS 0         // dims per lane in the sparse score kernel (0: as the dense kernel)
 #endif
+#ifndef KVQ_SCORE_BUFS
+#define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
+#endif
+#ifndef KVQ_DENSE_BUFS
+#define KVQ_DENSE_BUFS 2         // chunk buffers per wave in the dense split kernel
+#endif
+#ifndef KVQ_TILE_DENSE
+#define KVQ_TILE_DENSE 1         // workgroup -> (unit, kv head) map of the dense split kernel (see unit_tile)
+#endif
+#ifndef KVQ_TILE_SCORES
+#define KVQ_TILE_SCORES 1        // ... of the sparse score kernel
+#endif
+#ifndef KVQ_TILE_SPARSE_V
+#define KVQ_TILE_SPARSE_V 1      // ... of the sparse V pass
+#endif
 #ifndef KVQ_NT_LOADS
 #define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
 #endif
@@ -64,6 +79,17 @@ struct WriteArgs {
   Codebooks cb;
 };
 
+// Sparse-V candidate lists hold one segment per (split, wave of the score
+// kernel).  A wave scores every KVQ_WAVES-th chunk of 16 positions of its
+// split, so a segment never holds more than cand_segment_cap records (at
+// least 64: the V pass reads one record per lane ahead of the counts).
+__host__ __device__ constexpr uint32_t cand_segment_cap(uint32_t split_len) {
+  return ((split_len + 15u) / (16u * KVQ_WAVES) + 1u) * 16u < 64u ? 64u
+                                                                 : ((split_len + 15u) / (16u * KVQ_WAVES) + 1u) * 16u;
+}
+// Words per candidate record: page id, position, G scores, padded to 16 bytes.
+__host__ __device__ constexpr uint32_t cand_record_words(uint32_t g) { return (2u + g + 3u) / 4u * 4u; }
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint8_t* k_cache;
@@ -74,10 +100,9 @@ struct DecodeArgs {
   float* part;     // dense: [S][Hkv][nsplit][G][hd] unnormalized partial
                    // outputs of each split (relative to the split max)
   float* ml;       // [S][Hkv][nsplit][G][2] (max in log2 units, sum of exp2)
-  int32_t* cnt;    // sparse: [S][Hkv][nsplit] candidate counts
-  int32_t* cidx;   // sparse: [S][Hkv][nsplit][split_len] candidate positions
-  uint64_t* cvbase; // sparse: [S][Hkv][nsplit][split_len] byte offset of their V page
-  float* cscore;   // sparse: [S][Hkv][nsplit][split_len][G] their log2 scores
+  int32_t* cnt;    // sparse: [S][Hkv][nsplit][KVQ_WAVES] candidate counts per segment
+  uint32_t* crec;  // sparse: [S][Hkv][nsplit][KVQ_WAVES][seg_cap] candidate records
+                   // of cand_record_words(G) words: page id, position, G log2 scores
   float* vpart;    // sparse: [S][Hkv][nparts][G][hd] output partials of the V-pass parts
   uint32_t max_blocks;
   uint32_t num_seqs;
@@ -90,6 +115,7 @@ struct DecodeArgs {
   uint32_t nsplit;
   uint32_t vsplits;  // sparse: splits per V-pass part
   uint32_t nparts;   // sparse: V-pass parts per (sequence, kv head) = ceil(nsplit / vsplits)
+  uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len)
   uint64_t k_stride;
   uint64_t k_data;
   uint64_t v_stride;
