@@ -11,11 +11,16 @@ before the timed region.  Prints one JSON line.
 value      effective KV GB/s: K+V bytes of every attended (position, kv head)
            at the storage formats' sizes, per step time (sparse V skips some
            of those bytes; the roofline below counts only what must move).
-roofline   the decode call (its two kernels: score/candidate pass and V pass,
-           or split pass and merge) timed with HIP events on the stream the
-           library launches on; algorithmic bytes = K of every attended
-           position + V of every position some head keeps + q + out + the
-           page-table entries and lengths read.
+           Step and decode times are medians of per-step HIP events; between
+           steps a 1 GiB scratch read evicts L2 and the MALL (--warm: no
+           eviction), outside the timed region.
+roofline   the decode call (sparse: score pass, V pass, merge; dense: split
+           pass, merge) timed with HIP events on the stream the library
+           launches on; algorithmic bytes = K of every attended position + V
+           of every (position, kv head) some head of the group keeps (counted
+           from the stored K) + q + out + the page-table entries and lengths
+           read.  `traffic` = HBM bytes per decode call from the committed
+           rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the same sources.
 cpu_baseline  the CPU oracle timed on a sample of the same workload.
 """
 from __future__ import annotations
@@ -58,37 +63,93 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kept_rows(st, w) -> int:
+def _k_rows(st, w, kvq, j: torch.Tensor, pages: torch.Tensor) -> torch.Tensor:
+    """Stored K of positions j of one sequence as fp32 [Hkv, hd, P], read
+    back from the pool bytes with plain torch ops (turbo: in the rotated
+    basis, codes -> centroid x E4M3 group scale; fp8: E4M3 x k_scale)."""
+    Hkv, hd, bs = w.num_kv_heads, w.head_dim, w.block_size
+    lay = st.layout
+    stride, data = int(lay.k_block_stride_bytes), int(lay.k_data_section_bytes)
+    pages = pages.long()
+    rows = (j % bs)[:, None] * Hkv + torch.arange(Hkv, device="cuda")[None, :]    # [P, Hkv]
+    base = pages[:, None] * stride                                                # [P, 1]
+    pool = st.k_pool
+    if w.k_format == "bf16":
+        off = (base + rows * 2 * hd)[:, :, None] + torch.arange(0, 2 * hd, 2, device="cuda")
+        lo, hi = pool[off].int(), pool[off + 1].int()
+        k = ((lo | (hi << 8)) << 16).view(torch.float32)
+    elif w.k_format == "fp8":
+        off = (base + rows * hd)[:, :, None] + torch.arange(hd, device="cuda")
+        k = pool[off].view(torch.float8_e4m3fn).float() * st.k_scale
+    else:
+        bits = int(w.k_format[-1])
+        rb = hd * bits // 8
+        i = torch.arange(hd, device="cuda")
+        bit = i * bits
+        off = (base + rows * rb)[:, :, None] + (bit // 8)
+        word = pool[off].int() | (pool[off + 1].int() << 8)
+        code = (word >> (bit % 8)) & ((1 << bits) - 1)
+        cen = torch.as_tensor(kvq.codebook(w.k_format)["centroids"], device="cuda")
+        soff = (base + data + rows * (hd // 16))[:, :, None] + i // 16
+        sq = pool[soff].view(torch.float8_e4m3fn).float()
+        k = cen[code.long()] * sq
+    return k.permute(1, 2, 0).contiguous()
+
+
+def _hadamard(n: int) -> torch.Tensor:
+    h = torch.ones(1, 1, dtype=torch.float64)
+    while h.shape[0] < n:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    return h / math.sqrt(n)
+
+
+def kept_rows(st, w, kvq) -> int:
     """(position, kv head) pairs whose V some query head of the group keeps.
 
     Measurement bookkeeping only (plain torch on the device): scores from the
-    stored K, exact for bf16 K; for other K formats the dense count is used.
+    K actually stored in the pool, in fp32 (turbo K: the query rotated by
+    the orthonormal Hadamard matrix, which leaves the scores unchanged).
     """
     S, G, Hkv, hd = w.num_seqs, w.group, w.num_kv_heads, w.head_dim
     P = _attended(st, w)
-    if w.sparse_v_threshold <= 0.0 or w.k_format != "bf16":
+    if w.sparse_v_threshold <= 0.0:
         return int(P.sum()) * Hkv
     bs = w.block_size
-    kp = st.k_pool.view(torch.bfloat16)
-    blk_elems = bs * Hkv * hd
     total = 0
     inv = synth.inv_sqrt_d(hd)
+    rot = _hadamard(hd).float().cuda() if w.k_format.startswith("turbo") else None
     for s in range(S):
         L = int(st.lens[s])
         j0 = max(0, L - w.sliding_window) if w.sliding_window else 0
         if L <= j0:
             continue
         j = torch.arange(j0, L, device="cuda")
-        pages = st.bt_dev[s, (j // bs)].long()
-        base = pages * blk_elems + (j % bs) * Hkv * hd
-        idx = base[:, None, None] + torch.arange(Hkv, device="cuda")[None, :, None] * hd + \
-            torch.arange(hd, device="cuda")[None, None, :]
-        K = kp[idx].float().permute(1, 2, 0).contiguous()       # [Hkv, hd, P]
-        q = st.q[s].float().view(Hkv, G, hd).contiguous()
-        sc = torch.matmul(q, K) * inv                            # [Hkv, G, P]
+        K = _k_rows(st, w, kvq, j, st.bt_dev[s, (j // bs)])       # [Hkv, hd, P]
+        q = st.q[s].float().view(Hkv, G, hd)
+        if rot is not None:
+            q = torch.matmul(q, rot)
+        sc = torch.matmul(q.contiguous(), K) * inv                  # [Hkv, G, P]
         p = torch.softmax(sc, dim=-1)
         total += int((p > w.sparse_v_threshold).any(dim=1).sum())
     return total
+
+
+def stream_read_reference() -> dict:
+    """Read bandwidth of torch's own sum over 2 GiB of fp32 on this GPU (a
+    reference ceiling for a plain streaming read, not a kernel of this path)."""
+    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        x.sum()
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 10 * x.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x
+    return {"kernel": "torch.sum over 2 GiB fp32", "gbs": round(gbs, 1)}
 
 
 def _attended(st, w) -> np.ndarray:
@@ -171,6 +232,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cpu-seqs", type=int, default=24, help="sequences in the oracle sample (0: skip)")
+    ap.add_argument("--warm", action="store_true", help="no cache eviction between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -204,23 +266,39 @@ def main():
         kvq.paged_decode(st.layout, st.q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev, inv, w.sliding_window,
                          w.sparse_v_threshold, st.k_scale, st.v_scale, out=out, workspace=ws, stream=stream)
 
-    for _ in range(args.warmup):
+    # Between steps a 1 GiB scratch read evicts L2 and the MALL (outside the
+    # timed region), so every step reads the pools from HBM.  A read leaves
+    # the caches full of clean lines; a write would leave dirty ones that the
+    # next step would pay to write back.
+    scratch = None if args.warm else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def evict(i):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)
+
+    for i in range(args.warmup):
+        evict(i)
         write()
         decode()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        write()
+        evict(i)
         ev[i][0].record(stream)
-        decode()
+        write()
         ev[i][1].record(stream)
+        decode()
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    ms_step = elapsed * 1e3 / args.steps
+    dec = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    stp = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    dec_ms = float(np.median(dec))
+    ms_step = float(np.median(stp))
     assert torch.isfinite(out).all(), "non-finite decode output"
+    del scratch
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -228,15 +306,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    stream_ref = stream_read_reference()
 
     att = _attended(st, w)
     positions = int(att.sum())
     kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
     kv_dense = positions * Hkv * (kb + vb)
-    kept = kept_rows(st, w)
+    kept = kept_rows(st, w, kvq)
     alg = (positions * Hkv * kb + kept * vb + w.num_seqs * w.num_q_heads * hd * (2 + 4)
            + sum(int(math.ceil(int(L) / w.block_size)) for L in att) * 4 + w.num_seqs * 4)
     achieved = alg / (dec_ms * 1e-3) / 1e9
+    G = w.group
+    flops = positions * Hkv * G * (2 * hd + 1) + kept * G * 2 * hd   # QK + exp per position-head, PV per kept
     value = kv_dense / (ms_step * 1e-3) / 1e9
     traffic = traffic_from_profile(w.name)
     rec = {
@@ -260,11 +341,21 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
+        "decode_ms_p10_p90": [round(float(np.percentile(dec, 10)), 4), round(float(np.percentile(dec, 90)), 4)],
+        "write_ms": round(float(np.median(stp - dec)), 4),
+        "caches": "warm" if args.warm else "cold: 1 GiB scratch read between steps, outside the timed region",
+        "wall_s_timed_loop": round(elapsed, 3),
+        "stream_read_ref": stream_ref,
         "kept_v_fraction": round(kept / max(1, positions * Hkv), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 0),
-                     "kernel": "kvq_paged_decode (both kernels)", "algorithmic_bytes": alg},
+                     "kernel": ("kvq_paged_decode: scores_kernel + sparse_v_kernel + merge_kernel"
+                                if w.sparse_v_threshold > 0 else "kvq_paged_decode: split_kernel + merge_kernel"),
+                     "algorithmic_bytes": alg},
+        "roofline_alu": {"bound": "alu", "achieved": round(flops / (dec_ms * 1e-3) / 1e12, 3),
+                         "peak": 157.3, "unit": "TFLOP/s", "frac": round(flops / (dec_ms * 1e-3) / 1e12 / 157.3, 4),
+                         "algorithmic_flops": flops},
         "kernel_source_sha256": kernel_source_hash(),
     }
     if args.cpu_seqs:
