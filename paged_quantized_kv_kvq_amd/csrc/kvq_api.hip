@@ -118,8 +118,8 @@ int check_layout(const kvq_layout* l) {
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
-  uint32_t split_len, nsplit, vsplits, nparts, seg_cap;
-  uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, bytes;
+  uint32_t split_len, nsplit, seg_cap;
+  uint64_t off_part, off_ml, off_cnt, off_crec, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -142,10 +142,8 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
-  p.off_part = p.off_cnt = p.off_crec = p.off_vpart = 0;
+  p.off_part = p.off_cnt = p.off_crec = 0;
   p.seg_cap = 0;
-  p.vsplits = std::min<uint32_t>(64, std::max<uint32_t>(1, KVQ_VPART_POSITIONS / sl));  // <= kMaxStatSplits
-  p.nparts = (p.nsplit + p.vsplits - 1) / p.vsplits;
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
@@ -155,8 +153,6 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
     p.off_crec = off;
     off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
-    p.off_vpart = off;
-    off = up256(off + uint64_t(S) * nkv * p.nparts * G * hd * sizeof(float));
   }
   p.bytes = off;
   return p;
@@ -247,7 +243,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse);
   // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
   const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
-  const uint64_t nwg_v = (uint64_t(num_seqs) * p.nparts + 7) / 8 * 8 * nkv;
+  const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv;
   if (nwg >= (1ull << 31) || nwg_v >= (1ull << 31) || uint64_t(num_seqs) * num_q_heads >= (1ull << 31))
     return KVQ_ERR_UNSUPPORTED;
   if (!workspace) {
@@ -276,7 +272,6 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   } else {
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     a.crec = reinterpret_cast<uint32_t*>(ws + p.off_crec);
-    a.vpart = reinterpret_cast<float*>(ws + p.off_vpart);
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -287,8 +282,6 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
   a.window = sliding_window;
   a.split_len = p.split_len;
   a.nsplit = p.nsplit;
-  a.vsplits = p.vsplits;
-  a.nparts = p.nparts;
   a.seg_cap = p.seg_cap;
   a.k_stride = layout->k_block_stride_bytes;
   a.k_data = layout->k_data_section_bytes;
@@ -312,7 +305,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
     }
-    if (e == hipSuccess) e = launch_merge(false, layout->v_rotated != 0, int(hd), int(G), a, s);
+    if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
   } else {
     switch (kf) {
       case KVQ_BF16: e = launch_scores_bf16(int(hd), int(G), a, uint32_t(nwg), s); break;
@@ -322,7 +315,6 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);
-    if (e == hipSuccess) e = launch_merge(true, layout->v_rotated != 0, int(hd), int(G), a, s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

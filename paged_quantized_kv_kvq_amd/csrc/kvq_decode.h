@@ -13,10 +13,9 @@
 //   * split-K over positions: a workgroup handles (sequence, kv head, split of
 //     split_len positions) and ALL G = Hq/Hkv query heads of that kv head, so
 //     every K/V byte is read once, not G times;
-//   * a wave walks 16-position chunks.  When block_size >= 16 a chunk lies in
-//     one block, so its page base is a scalar and every lane address is a
-//     32-bit offset from it; the next chunk's loads are issued before the
-//     current chunk is computed (two register buffers);
+//   * a wave walks 16-position chunks (wave w: chunks w, w + 4, ...); each
+//     lane finds its position's page in an LDS copy of the split's page table;
+//     chunk loads run one chunk ahead of their use, all issued inside the loop;
 //   * inside a chunk, T = head_dim/D lanes share one position (D = 16 dims
 //     per lane, 8 for G = 8) and 64/T positions are side by side; a score is
 //     a T-lane DPP sum of bf16 dot products (v_dot2_f32_bf16 for bf16 K and
@@ -26,12 +25,13 @@
 //   * dense (threshold 0): partial (max, sum, unnormalized output) per split,
 //     combined by merge_kernel (which also applies the inverse rotation);
 //   * sparse (threshold > 0): scores_kernel keeps only candidate positions
-//     (split-local weight above thr: an upper bound on the global weight);
-//     sparse_v_kernel, one workgroup per (sequence, kv head, part of a few
-//     splits), recomputes each candidate's exact global weight, loads V only
-//     where some head of the group keeps it; merge_kernel sums the parts;
+//     (split-local weight above thr: an upper bound on the global weight),
+//     each wave in its own segment; sparse_v_kernel, one workgroup per
+//     (sequence, kv head), recomputes each candidate's exact global weight,
+//     loads V only where some head of the group keeps it, and writes the
+//     output (fp8 V scale, inverse rotation);
 //   * workgroup ids are renumbered so the kv heads of one (sequence, split)
-//     run on the same XCD and share L2 lines (the heads of a page interleave).
+//     run on the same XCD, and consecutive units rotate over the XCDs.
 #pragma once
 
 #include "kvq_device.h"
@@ -42,7 +42,6 @@ constexpr int kWaves = KVQ_WAVES;  // waves per workgroup
 constexpr int kChunk = 16;         // positions per wave iteration
 constexpr int kMaxPages = 160;     // page offsets of one split staged in LDS
 constexpr int kMaxSparseSplit = KVQ_MAX_SPARSE_SPLIT;
-constexpr int kCandUnroll = 4;   // kept V rows in flight per lane slot (sparse V)
 
 template <int F>
 struct Fmt {
@@ -613,10 +612,10 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
   __syncthreads();
 }
 
-// One workgroup per (sequence, q head).  Dense: combine the split partials
-// with log-sum-exp weights.  Sparse: sum the V-pass parts (already divided by
-// the global softmax sum).  Then the fp8 V scale and the inverse rotation.
-template <int HD, bool VROT, bool SPARSE>
+// Dense path: one workgroup per (sequence, q head) combines the split
+// partials with log-sum-exp weights, then applies the fp8 V scale and the
+// inverse rotation.
+template <int HD, bool VROT>
 __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs a, int G) {
   __shared__ float o[HD];
   const uint32_t hq = blockIdx.x % a.num_q_heads;
@@ -626,15 +625,7 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
   const int tid = threadIdx.x;
-  if constexpr (SPARSE) {
-    const int nact = ns > 0 ? (ns + int(a.vsplits) - 1) / int(a.vsplits) : 1;
-    const uint64_t pbase = (uint64_t(s) * a.num_kv_heads + g) * a.nparts;
-    for (int d = tid; d < HD; d += kWaves * kWave) {
-      float acc = 0.0f;
-      for (int p = 0; p < nact; ++p) acc += a.vpart[((pbase + p) * G + h) * HD + d];
-      o[d] = acc * a.v_scale;
-    }
-  } else {
+  {
     const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
     float M = -INFINITY;
     for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * G + h) * 2]);
@@ -837,6 +828,8 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
 }
 
 constexpr int kMaxStatSplits = 64;  // splits whose stats the V pass stages in LDS at once
+constexpr int kVWaves = KVQ_VWAVES;  // waves of a V-pass workgroup
+constexpr int kSegBatch = kWave;     // segments a V wave indexes at once (one per lane)
 
 // The V pass uses 8 dims per lane (more rows side by side, fewer registers).
 template <int HD>
@@ -859,66 +852,166 @@ __device__ __forceinline__ void load_record(const uint32_t* src, uint32_t (&rw)[
   }
 }
 
+// Staging of kept V rows in LDS: each lane reads GPL granules of CK bytes of
+// one row (LPR lanes per row), RPP rows per pass; rows sit CS bytes apart,
+// followed by their scale bytes (turbo) SB bytes apart.
+template <int VF, int HD>
+struct VStage {
+  static constexpr int RB = HD * Fmt<VF>::bits / 8;                 // code bytes per row
+  static constexpr int SB = Fmt<VF>::turbo ? HD / 16 : 0;           // scale bytes per row
+  static constexpr int CK = RB % 16 == 0 ? 16 : RB % 8 == 0 ? 8 : 4;  // load granule
+  static constexpr int NCK = RB / CK;
+  static constexpr int GPL = NCK < 4 ? NCK : 4;
+  static constexpr int LPR = (NCK + GPL - 1) / GPL;
+  static constexpr int RPP = kWave / LPR;
+  static constexpr int CS = (RB + 15) / 16 * 16;
+  static constexpr int WORDS = (RPP * CS + RPP * SB + 15) / 16 * 4 + 4;  // + slack for the 3-bit reads
+};
+
 template <int VF, int HD, int G>
 struct SparseSmem {
   float vcen[16];
   float mz[G][2];                     // global (max, 1/sum) per head
   float st[kMaxStatSplits][G][2];     // split stats being reduced
-  int pre[kWaves][kMaxStatSplits];    // per wave: inclusive prefix of its segment counts
+  int pre[kVWaves][kSegBatch];        // per wave: inclusive prefix of its batch's segment counts
   struct Kept {
     uint64_t vb;   // byte offset of the V page
     uint32_t row;  // row (offset * Hkv + kv head) in the page
     float p[G];    // kept weights (0 for heads that drop the position)
   };
   union {
-    Kept kept[kWaves][kWave];
-    float red[kWaves][G][HD];
+    struct {
+      Kept kept[kVWaves][kWave];
+      __attribute__((aligned(16))) uint32_t rows[kVWaves][VStage<VF, HD>::WORDS];
+    } live;
+    float red[kVWaves / 2][G][HD];
   } u;
 };
 
-// One workgroup per (sequence, kv head, part), a part being `vsplits`
-// consecutive splits: every candidate of those splits gets its exact global
-// weight; V is loaded only where some head of the group keeps the position.
-// Wave w of this kernel takes the records that wave w of the score kernel
-// wrote (its segments of the part's splits), so the waves share the work
-// evenly.  The wave's segment counts, a first record per lane (read ahead,
-// before the counts are known) and the split stats are all requested at once.
-// A ballot compacts the kept records of a round of 64 into LDS, and the
-// wave's lane slots then stream their V rows, kCandUnroll rows per slot in
-// flight.  Each part stores its partial output; the merge kernel sums them.
+// A lane's D dims of staged row q (LDS words `rw`), as load_lane would give them.
+template <int F, int HD, int D>
+__device__ __forceinline__ void staged_lane(const uint32_t* rw, int q, int t, Raw<F, D>& r) {
+  using VS = VStage<F, HD>;
+  constexpr int B = Raw<F, D>::bytes;
+  const int byte = q * VS::CS + t * B;
+  if constexpr (B % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < B / 4; ++i) r.w[i] = rw[byte / 4 + i];
+  } else if constexpr (B == 2) {
+    r.w[0] = (rw[byte / 4] >> ((byte & 3) * 8)) & 0xFFFFu;
+  } else {
+    // 3-bit codes: the two aligned words that cover them
+    const uint64_t v = (uint64_t(rw[byte / 4 + 1]) << 32 | rw[byte / 4]) >> ((byte & 3) * 8);
+    r.w[0] = uint32_t(v);
+    if constexpr (Raw<F, D>::words > 1) r.w[1] = uint32_t(v >> 32) & 0xFFFFu;
+  }
+  if constexpr (Fmt<F>::turbo) r.sc = rw[(VS::RPP * VS::CS + q * VS::SB + (((t * D) / 16) & ~3)) / 4];
+  else r.sc = 0;
+}
+
+// Lane `lane` copies its part of kept row (lane / LPR) of the pass into LDS.
+template <int VF, int HD, typename KeptT>
+__device__ __forceinline__ void stage_rows(const DecodeArgs& a, const KeptT* kept, int nrow, int lane, uint32_t* rw) {
+  using VS = VStage<VF, HD>;
+  const int qr = lane / VS::LPR, part = lane % VS::LPR;
+  if (qr >= nrow) return;
+  const uint8_t* blk = a.v_cache + kept[qr].vb;
+  const uint32_t row = kept[qr].row;
+  const uint8_t* src = blk + uint64_t(row) * VS::RB;
+  uint32_t g[VS::GPL][VS::CK / 4];
+  uint32_t sc[VS::SB > 0 ? VS::SB / 4 : 1];
+#pragma unroll
+  for (int j = 0; j < VS::GPL; ++j) {
+    const int c = part * VS::GPL + j;
+    if (c < VS::NCK) {
+      const uint8_t* p = src + c * VS::CK;
+      if constexpr (VS::CK == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        g[j][0] = v.x; g[j][1] = v.y; g[j][2] = v.z; g[j][3] = v.w;
+      } else if constexpr (VS::CK == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        g[j][0] = v.x; g[j][1] = v.y;
+      } else {
+        g[j][0] = *reinterpret_cast<const uint32_t*>(p);
+      }
+    }
+  }
+  if constexpr (VS::SB > 0) {
+    const uint8_t* p = blk + a.v_data + uint64_t(row) * VS::SB;
+    if (part == 0) {
+      if constexpr (VS::SB == 16) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+      } else if constexpr (VS::SB == 8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+        sc[0] = v.x; sc[1] = v.y;
+      } else {
+        sc[0] = *reinterpret_cast<const uint32_t*>(p);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < VS::GPL; ++j) {
+    const int c = part * VS::GPL + j;
+    if (c < VS::NCK) {
+      const int wo = (qr * VS::CS + c * VS::CK) / 4;
+#pragma unroll
+      for (int i = 0; i < VS::CK / 4; ++i) rw[wo + i] = g[j][i];
+    }
+  }
+  if constexpr (VS::SB > 0) {
+    if (part == 0) {
+      const int wo = (VS::RPP * VS::CS + qr * VS::SB) / 4;
+#pragma unroll
+      for (int i = 0; i < VS::SB / 4; ++i) rw[wo + i] = sc[i];
+    }
+  }
+}
+
+// One workgroup of kVWaves waves per (sequence, kv head) does the whole V side
+// of the sparse path and writes the output.  The score kernel left one record
+// segment per (split, wave); V wave v takes segments v, v + kVWaves, ...
+// (the score kernel's waves scored interleaved chunks, so the work is evenly
+// spread).  The global softmax statistics come from the split statistics;
+// each lane reads one record, keeps a position for head h when its exact
+// global weight exceeds the threshold, and a ballot compacts the kept ones
+// into LDS; the wave's lane slots then stream their V rows.  The segment
+// counts, a first record per lane (read ahead of the counts) and the split
+// statistics are all requested at once.  At the end the waves' partial sums
+// are added in LDS in a fixed order, scaled by the fp8 V scale, rotated back
+// (turbo V) and stored.
+// At most 128 registers per lane: two workgroups per CU stay resident.
 template <int VF, int HD, int G>
-__global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu(4))) void sparse_v_kernel(
+    const DecodeArgs a) {
   using GE = VGeo<HD>;
   constexpr int D = GE::D, T = GE::T, P = GE::P;
   constexpr int RS = cand_record_words(G);
+  constexpr int NT = kVWaves * kWave;
   __shared__ SparseSmem<VF, HD, G> sm;
-  const Tile tl = unit_tile<KVQ_TILE_SPARSE_V>(a, a.nparts);
-  if (!tl.valid) return;
-  const uint32_t s = tl.s, g = tl.g, part = tl.split;
+  uint32_t s, g;
+  if (!xcd_unit_tile(blockIdx.x, a.num_seqs, a.num_kv_heads, s, g)) return;
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
-  const int nact = ns > 0 ? (ns + int(a.vsplits) - 1) / int(a.vsplits) : 1;
-  if (int(part) >= nact) return;
   const uint64_t sbase = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane % T, r = lane / T;
-  const int k0 = int(part * a.vsplits);
-  const int k1 = min(ns, k0 + int(a.vsplits));
-  const int nseg = k1 - k0;  // 0 only for an empty sequence
-  // requests that do not depend on each other go out first
-  const int myc = lane < nseg ? a.cnt[(sbase + k0 + lane) * kWaves + w] : 0;
+  const int nseg_all = ns * kWaves;                                // (split, score wave) segments
+  const int nseg = nseg_all > w ? (nseg_all - w + kVWaves - 1) / kVWaves : 0;  // this wave's
+  // requests that do not depend on each other go out first: the counts of the
+  // wave's first batch of segments, a first record per lane, the statistics
+  const int myc0 = lane < nseg ? a.cnt[sbase * kWaves + w + kVWaves * lane] : 0;
   uint32_t spec[RS];
-  load_record<G>(a.crec + (((sbase + k0) * kWaves + w) * a.seg_cap + lane) * RS, spec);
+  load_record<G>(a.crec + ((sbase * kWaves + w) * a.seg_cap + lane) * RS, spec);
   if (tid < 16) {
     if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
-  // global (max, sum) per head over all splits, staged kMaxStatSplits at a time
   float runm = -INFINITY, runz = 0.0f;  // (threads < G) running stats of head tid
   for (int kb = 0; kb < ns; kb += kMaxStatSplits) {
     const int nk = min(kMaxStatSplits, ns - kb);
-    for (int i = tid; i < nk * G; i += kWaves * kWave) {
+    for (int i = tid; i < nk * G; i += NT) {
       const int k = i / G, h = i % G;
       sm.st[k][h][0] = a.ml[((sbase + kb + k) * G + h) * 2];
       sm.st[k][h][1] = a.ml[((sbase + kb + k) * G + h) * 2 + 1];
@@ -941,16 +1034,6 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     sm.mz[tid][0] = runm;
     sm.mz[tid][1] = runz > 0.0f ? 1.0f / runz : 0.0f;
   }
-  // the wave's segments: inclusive prefix of their counts
-  int pre = myc;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int v = __shfl_up(pre, off);
-    if (lane >= off) pre += v;
-  }
-  if (lane < nseg) sm.pre[w][lane] = pre;
-  const int total = nseg > 0 ? __shfl(pre, nseg - 1) : 0;
-  const int c0 = __shfl(myc, 0);
   __syncthreads();
   float M[G], iz[G];
 #pragma unroll
@@ -965,94 +1048,141 @@ __global__ __launch_bounds__(kWaves * kWave) void sparse_v_kernel(const DecodeAr
     for (int i = 0; i < D; ++i) acc[h][i] = 0.0f;
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
   const uint32_t vsh = scale_shift<D>(t);
-  auto& kept = sm.u.kept[w];
-  for (int i0 = 0; i0 < total; i0 += kWave) {
-    // 1. one record per lane -> keep decisions, compacted into the wave's LDS list
-    const int gi = i0 + lane;
-    const bool ok = gi < total;
-    uint32_t rw[RS];
+  using VS = VStage<VF, HD>;
+  auto& kept = sm.u.live.kept[w];
+  uint32_t* rows = sm.u.live.rows[w];
+  // the wave's segments, kSegBatch at a time (segment i of the wave is
+  // (split, score wave) number w + kVWaves * i of the sequence and kv head)
+  for (int sb = 0; sb < nseg; sb += kSegBatch) {
+    const int nb = min(kSegBatch, nseg - sb);
+    const int myc = sb == 0 ? myc0 : (lane < nb ? a.cnt[sbase * kWaves + w + kVWaves * (sb + lane)] : 0);
+    int pre = myc;
 #pragma unroll
-    for (int i = 0; i < RS; ++i) rw[i] = 0u;
-    if (i0 == 0 && lane < c0) {
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(pre, off);
+      if (lane >= off) pre += v;
+    }
+    wave_lds_sync();
+    if (lane < nb) sm.pre[w][lane] = pre;
+    wave_lds_sync();
+    const int total = __shfl(pre, nb - 1);
+    const int c0 = __shfl(myc, 0);
+    // record gi of the batch (segment k: the number of segments whose
+    // inclusive prefix is <= gi), or zeros past the end
+    auto fetch = [&](int gi, uint32_t (&rw)[RS]) {
+#pragma unroll
+      for (int i = 0; i < RS; ++i) rw[i] = 0u;
+      if (gi < total) {
+        int k = 0;
+#pragma unroll
+        for (int bb = kSegBatch / 2; bb > 0; bb >>= 1)
+          if (k + bb < nb && sm.pre[w][k + bb - 1] <= gi) k += bb;
+        const int off = gi - (k > 0 ? sm.pre[w][k - 1] : 0);
+        const uint64_t seg = sbase * kWaves + w + kVWaves * (sb + k);
+        load_record<G>(a.crec + (seg * a.seg_cap + off) * RS, rw);
+      }
+    };
+    // rounds of 64 records; the next round's records are requested before
+    // the current round's V rows, so the two latencies overlap
+    uint32_t rw[RS];
+    if (sb == 0 && lane < c0) {
 #pragma unroll
       for (int i = 0; i < RS; ++i) rw[i] = spec[i];
-    } else if (ok) {
-      // segment k: the number of segments whose inclusive prefix is <= gi
-      int k = 0;
-#pragma unroll
-      for (int b = kMaxStatSplits / 2; b > 0; b >>= 1)
-        if (k + b < nseg && sm.pre[w][k + b - 1] <= gi) k += b;
-      const int off = gi - (k > 0 ? sm.pre[w][k - 1] : 0);
-      load_record<G>(a.crec + (((sbase + k0 + k) * kWaves + w) * a.seg_cap + off) * RS, rw);
+    } else {
+      fetch(lane, rw);
     }
-    float p[G];
-    bool any = false;
+    for (int i0 = 0; i0 < total; i0 += kWave) {
+      // 1. one record per lane -> keep decisions, compacted into the wave's LDS list
+      const bool ok = i0 + lane < total;
+      float p[G];
+      bool any = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float pv = fast_exp2(__uint_as_float(rw[2 + h]) - M[h]) * iz[h];
-      p[h] = (ok && pv > a.thr) ? pv : 0.0f;
-      any |= p[h] > 0.0f;
-    }
-    const uint64_t bal = __ballot(any);
-    if (any) {
-      const int kk = __popcll(bal & ((1ull << lane) - 1ull));
-      kept[kk].vb = uint64_t(rw[0]) * a.v_stride;
-      kept[kk].row = (rw[1] & bmask) * a.num_kv_heads + g;
-#pragma unroll
-      for (int h = 0; h < G; ++h) kept[kk].p[h] = p[h];
-    }
-    const int nk = __popcll(bal);
-    wave_lds_sync();
-    // 2. lane slots stream the kept V rows, kCandUnroll in flight
-    for (int q0 = r; q0 < nk; q0 += P * kCandUnroll) {
-      Raw<VF, D> vr[kCandUnroll];
-      float pk[kCandUnroll][G];
-#pragma unroll
-      for (int u = 0; u < kCandUnroll; ++u) {
-        const int qi = q0 + u * P;
-        const bool kok = qi < nk;
-        const int qc = kok ? qi : 0;
-        load_lane<VF, HD, D>(a.v_cache + kept[qc].vb, kept[qc].row, t, a.v_data, vr[u]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) pk[u][h] = kok ? kept[qc].p[h] : 0.0f;
+      for (int h = 0; h < G; ++h) {
+        const float pv = fast_exp2(__uint_as_float(rw[2 + h]) - M[h]) * iz[h];
+        p[h] = (ok && pv > a.thr) ? pv : 0.0f;
+        any |= p[h] > 0.0f;
       }
+      const uint64_t bal = __ballot(any);
+      if (any) {
+        const int kk = __popcll(bal & ((1ull << lane) - 1ull));
+        kept[kk].vb = uint64_t(rw[0]) * a.v_stride;
+        kept[kk].row = (rw[1] & bmask) * a.num_kv_heads + g;
 #pragma unroll
-      for (int u = 0; u < kCandUnroll; ++u) {
-        mask_raw(vr[u], q0 + u * P < nk);
-        float x[D], sq;
-        v_values<VF, D>(vr[u], sm.vcen, x, sq, vsh);
+        for (int h = 0; h < G; ++h) kept[kk].p[h] = p[h];
+      }
+      fetch(i0 + kWave + lane, rw);
+      const int nk = __popcll(bal);
+      wave_lds_sync();
+      // 2. the kept rows' bytes go to LDS (every row of a pass requested at
+      //    once), then each lane slot reads its dims of its rows from there
+      for (int q0 = 0; q0 < nk; q0 += VS::RPP) {
+        const int nrow = min(VS::RPP, nk - q0);
+        stage_rows<VF, HD>(a, &kept[q0], nrow, lane, rows);
+        wave_lds_sync();
+        for (int q = r; q < nrow; q += P) {
+          Raw<VF, D> vr;
+          staged_lane<VF, HD, D>(rows, q, t, vr);
+          float x[D], sq;
+          v_values<VF, D>(vr, sm.vcen, x, sq, vsh);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pw = pk[u][h] * sq;
+          for (int h = 0; h < G; ++h) {
+            const float pw = kept[q0 + q].p[h] * sq;
 #pragma unroll
-          for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
+            for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
+          }
         }
+        wave_lds_sync();
       }
     }
-    wave_lds_sync();
   }
+  // lane slots of a wave hold the same dims: add them
 #pragma unroll
   for (int off = T; off < kWave; off <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < D; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
+  // waves, in a fixed order: the upper half stores, the lower half adds its own
+  constexpr int HW = kVWaves / 2;
   __syncthreads();  // the reduction area overlays the kept lists
-  if (r == 0) {
+  if (w >= HW && r == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int i = 0; i < D; ++i) sm.u.red[w][h][t * D + i] = acc[h][i];
+      for (int i = 0; i < D; ++i) sm.u.red[w - HW][h][t * D + i] = acc[h][i];
   }
   __syncthreads();
-  const uint64_t pbase = (uint64_t(s) * a.num_kv_heads + g) * a.nparts;
-  for (int i = tid; i < G * HD; i += kWaves * kWave) {
-    const int h = i / HD, d = i % HD;
-    float o = 0.0f;
+  if (w < HW && r == 0) {
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) o += sm.u.red[ww][h][d];
-    a.vpart[(pbase + part) * G * HD + i] = o;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < D; ++i) sm.u.red[w][h][t * D + i] += acc[h][i];
   }
+  __syncthreads();
+  float* o = &sm.u.red[0][0][0];  // row h of the result at o + h * HD
+  for (int i = tid; i < G * HD; i += NT) {
+    const int h = i / HD, d = i % HD;
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < HW; ++ww) v += sm.u.red[ww][h][d];
+    o[i] = v * a.v_scale;
+  }
+  __syncthreads();
+  if constexpr (Fmt<VF>::turbo) {
+    // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
+    for (int h2 = 1; h2 < HD; h2 <<= 1) {
+      for (int i = tid; i < G * HD / 2; i += NT) {
+        const int hh = i / (HD / 2), k = i % (HD / 2);
+        const int lo = hh * HD + (k / h2) * 2 * h2 + (k % h2);
+        const float x = o[lo], y = o[lo + h2];
+        o[lo] = x + y;
+        o[lo + h2] = x - y;
+      }
+      __syncthreads();
+    }
+  }
+  float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
+  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::turbo ? o[i] * a.wht_scale : o[i];
 }
 
 // ------------------------------------------------------------------ dispatch

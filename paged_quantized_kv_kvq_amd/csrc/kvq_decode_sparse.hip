@@ -1,5 +1,5 @@
-// Decode kernels that depend only on the V side: the sparse-V pass and the
-// merge (dense: log-sum-exp over splits; sparse: sum over V-pass parts; both
+// Decode kernels that depend only on the V side: the sparse-V pass (which also
+// writes the output) and the dense path's merge (log-sum-exp over splits,
 // with the inverse rotation of a rotated V side).
 #include "kvq_decode.h"
 
@@ -8,7 +8,7 @@ namespace {
 
 template <int VF, int HD>
 hipError_t sparse_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  const dim3 grid(nwg), block(kWaves * kWave);
+  const dim3 grid(nwg), block(kVWaves * kWave);
   switch (g) {
     case 1: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 1>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((sparse_v_kernel<VF, HD, 2>), grid, block, 0, st, a); break;
@@ -30,15 +30,10 @@ hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream
 }
 
 template <int HD>
-hipError_t merge_hd(bool sparse, bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_seqs * a.num_q_heads), block(kWaves * kWave);
-  if (sparse) {
-    if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true, true>), grid, block, 0, st, a, g);
-    else hipLaunchKernelGGL((merge_kernel<HD, false, true>), grid, block, 0, st, a, g);
-  } else {
-    if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true, false>), grid, block, 0, st, a, g);
-    else hipLaunchKernelGGL((merge_kernel<HD, false, false>), grid, block, 0, st, a, g);
-  }
+  if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true>), grid, block, 0, st, a, g);
+  else hipLaunchKernelGGL((merge_kernel<HD, false>), grid, block, 0, st, a, g);
   return hipGetLastError();
 }
 
@@ -55,11 +50,11 @@ hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t 
   }
 }
 
-hipError_t launch_merge(bool sparse, bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
   switch (hd) {
-    case 64: return merge_hd<64>(sparse, v_rotated, g, a, st);
-    case 128: return merge_hd<128>(sparse, v_rotated, g, a, st);
-    case 256: return merge_hd<256>(sparse, v_rotated, g, a, st);
+    case 64: return merge_hd<64>(v_rotated, g, a, st);
+    case 128: return merge_hd<128>(v_rotated, g, a, st);
+    case 256: return merge_hd<256>(v_rotated, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }

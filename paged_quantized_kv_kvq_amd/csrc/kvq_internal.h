@@ -18,8 +18,8 @@
 #ifndef KVQ_MAX_SPARSE_SPLIT
 #define KVQ_MAX_SPARSE_SPLIT 2048  // positions per split on the sparse path (scores kept in LDS)
 #endif
-#ifndef KVQ_VPART_POSITIONS
-#define KVQ_VPART_POSITIONS 2048  // positions whose candidates one sparse-V workgroup takes
+#ifndef KVQ_VWAVES
+#define KVQ_VWAVES 8             // waves of a sparse-V workgroup (one per sequence and kv head)
 #endif
 #ifndef KVQ_SCORE_DIMS
 #define KVQ_SCORE_DIMS 0         // dims per lane in the sparse score kernel (0: as the dense kernel)
@@ -103,7 +103,6 @@ struct DecodeArgs {
   int32_t* cnt;    // sparse: [S][Hkv][nsplit][KVQ_WAVES] candidate counts per segment
   uint32_t* crec;  // sparse: [S][Hkv][nsplit][KVQ_WAVES][seg_cap] candidate records
                    // of cand_record_words(G) words: page id, position, G log2 scores
-  float* vpart;    // sparse: [S][Hkv][nparts][G][hd] output partials of the V-pass parts
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
@@ -113,8 +112,6 @@ struct DecodeArgs {
   uint32_t window;
   uint32_t split_len;
   uint32_t nsplit;
-  uint32_t vsplits;  // sparse: splits per V-pass part
-  uint32_t nparts;   // sparse: V-pass parts per (sequence, kv head) = ceil(nsplit / vsplits)
   uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len)
   uint64_t k_stride;
   uint64_t k_data;
@@ -143,6 +140,6 @@ hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg
 hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_merge(bool sparse, bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq
