@@ -40,7 +40,10 @@ COMMON = [
     "-Wno-unused-command-line-argument",
 ]
 EXACT = ["-ffp-contract=off"]          # bit-exact quantization
-FAST = ["-ffp-contract=fast"]          # decode: fused multiply-adds allowed
+# decode: fused multiply-adds allowed; matrix-core accumulators kept in the
+# ordinary VGPRs (the split pass rescales them between MFMAs, and AGPR
+# accumulators would be copied out and back for every rescale)
+FAST = ["-ffp-contract=fast", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def sources():

@@ -830,6 +830,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
 constexpr int kMaxStatSplits = 64;  // splits whose stats the V pass stages in LDS at once
 constexpr int kVWaves = KVQ_VWAVES;  // waves of a V-pass workgroup
 constexpr int kSegBatch = kWave;     // segments a V wave indexes at once (one per lane)
+constexpr int kStageUnroll = 2;      // staged V rows a lane slot reads from LDS at once
 
 // The V pass uses 8 dims per lane (more rows side by side, fewer registers).
 template <int HD>
@@ -1119,16 +1120,26 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
         const int nrow = min(VS::RPP, nk - q0);
         stage_rows<VF, HD>(a, &kept[q0], nrow, lane, rows);
         wave_lds_sync();
-        for (int q = r; q < nrow; q += P) {
-          Raw<VF, D> vr;
-          staged_lane<VF, HD, D>(rows, q, t, vr);
-          float x[D], sq;
-          v_values<VF, D>(vr, sm.vcen, x, sq, vsh);
+        // kStageUnroll rows per lane slot at a time, their LDS reads issued together
+        for (int q = r; q < nrow; q += P * kStageUnroll) {
+          Raw<VF, D> vr[kStageUnroll];
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const float pw = kept[q0 + q].p[h] * sq;
+          for (int u = 0; u < kStageUnroll; ++u) {
+            const int qu = q + u * P;
+            staged_lane<VF, HD, D>(rows, qu < nrow ? qu : q, t, vr[u]);
+          }
 #pragma unroll
-            for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
+          for (int u = 0; u < kStageUnroll; ++u) {
+            const int qu = q + u * P;
+            const bool ok = qu < nrow;
+            float x[D], sq;
+            v_values<VF, D>(vr[u], sm.vcen, x, sq, vsh);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              const float pw = (ok ? kept[q0 + qu].p[h] : 0.0f) * sq;
+#pragma unroll
+              for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
+            }
           }
         }
         wave_lds_sync();
@@ -1185,19 +1196,35 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::turbo ? o[i] * a.wht_scale : o[i];
 }
 
+}  // namespace kvq
+
+#include "kvq_decode_mfma.h"
+
+namespace kvq {
+
 // ------------------------------------------------------------------ dispatch
+
+// Dense split kernel of a (K, V, head_dim, G) instance: the matrix-core one
+// where its operand sizes allow it (bf16 / fp8 K), else the VALU one.
+template <int KF, int VF, int HD, int G>
+hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
+  const dim3 grid(nwg), block(kWaves * kWave);
+  if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok)
+    hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
 
 template <int KF, int VF, int HD>
 hipError_t launch_split_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  const dim3 grid(nwg), block(kWaves * kWave);
   switch (g) {
-    case 1: hipLaunchKernelGGL((split_kernel<KF, VF, HD, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((split_kernel<KF, VF, HD, 2>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((split_kernel<KF, VF, HD, 4>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((split_kernel<KF, VF, HD, 8>), grid, block, 0, st, a); break;
+    case 1: return launch_split_one<KF, VF, HD, 1>(a, nwg, st);
+    case 2: return launch_split_one<KF, VF, HD, 2>(a, nwg, st);
+    case 4: return launch_split_one<KF, VF, HD, 4>(a, nwg, st);
+    case 8: return launch_split_one<KF, VF, HD, 8>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <int KF, int VF>

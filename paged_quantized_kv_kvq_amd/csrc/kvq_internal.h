@@ -27,6 +27,9 @@
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
+#ifndef KVQ_DENSE_MFMA
+#define KVQ_DENSE_MFMA 1         // 1: dense split pass on the matrix cores where the operands allow
+#endif
 #ifndef KVQ_DENSE_BUFS
 #define KVQ_DENSE_BUFS 2         // chunk buffers per wave in the dense split kernel
 #endif
