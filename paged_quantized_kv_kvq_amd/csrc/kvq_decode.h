@@ -1208,11 +1208,15 @@ namespace kvq {
 // where its operand sizes allow it (bf16 / fp8 K), else the VALU one.
 template <int KF, int VF, int HD, int G>
 hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  const dim3 grid(nwg), block(kWaves * kWave);
-  if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok)
-    hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), grid, block, 0, st, a);
+  if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
+    if (a.log2_bs >= 4) {  // a 16-position chunk lies in one page
+      const uint32_t nw = mfma_unit_waves(a.num_kv_heads);
+      const uint64_t n = uint64_t(a.num_seqs) * a.nsplit * (a.num_kv_heads / nw);
+      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), dim3(nwg), dim3(kWaves * kWave), 0, st, a);
   return hipGetLastError();
 }
 

@@ -2,27 +2,43 @@
 //
 // Same contract as split_kernel ("metrale_model_layers/layers/ops/
 // kv_cache_bf16k_turbov.rs", paged_decode_attn_bf16k_turbo{2,3,4}v: block
-// tables, GQA, inv_sqrt_d, sliding window; "combs_models/kv.rs", attend): one
-// workgroup per (sequence, kv head, split), four waves on interleaved
-// 16-position chunks, online softmax, and the same per-split partials for
-// merge_kernel.  What moves to the matrix cores is the arithmetic:
+// tables, GQA, inv_sqrt_d, sliding window; "combs_models/kv.rs", attend): for
+// every (sequence, kv head, split) the partial (max, sum, unnormalized output)
+// of each query head of the group, in the layout merge_kernel reads.  The
+// work is laid out for the memory system and the matrix cores:
 //
+//   * One workgroup per (sequence, split) and group of up to eight kv heads;
+//     wave w serves kv head g0 + w and walks every 16-position chunk of the
+//     split by itself.  A block row holds the kv heads of one position side
+//     by side, so the waves of a workgroup read neighbouring bytes of the
+//     same pages at about the same time and the workgroup streams whole
+//     pages.  (One workgroup per kv head reads one head's short rows at a
+//     stride; on MI355X that pattern reached about 60% of the bandwidth of
+//     the page-wide one for 128-byte K and 32-byte V rows.)
+//   * block_size >= 16, so that a chunk lies in one page: its page base is
+//     uniform (read from LDS into scalar registers once per chunk) and every
+//     lane's byte offset inside the page is fixed for the whole split.
+//     Positions of a chunk outside the split lie in the same page and are
+//     read too, then masked: their scores become -inf, their V group scales
+//     (or, for bf16 / fp8 V, their V words) zero, so that no value of an
+//     unwritten slot reaches an accumulator.
 //   * Q.K^T on v_mfma_f32_4x4x4_16b_bf16.  Block b = lane/4 takes the four
 //     positions 4(b%4).. and the quarter b/4 of head_dim; lane l supplies
 //     four dims of query head l%4 (operand A) and four dims of the K row of
-//     position l%16 (operand B).  Over the quarter's head_dim/16 steps each
-//     block accumulates partial scores; two cross-lane sums over the quarters
-//     leave every lane with the scores of position l%16 for its head group.
-//     bf16 x bf16 products are exact in fp32, and fp8 K widens exactly to
-//     bf16, so this is the same arithmetic as the VALU dot products.
+//     position l%16 (operand B).  bf16 x bf16 products are exact in fp32, and
+//     fp8 K widens exactly to bf16, so this is the arithmetic of the VALU dot
+//     products.  Two lane swaps then sum the quarters so that row k of 16
+//     lanes holds query head 4 hg + k for the chunk's 16 positions, and the
+//     softmax runs on one value per lane.
 //   * P.V on v_mfma_f32_4x4x1_16b_f32, one instruction per position and per
-//     block of 64 dims.  Lane l supplies p of head l%4 (A) and the dequantized
-//     V value of dim l*DV + v (B); register r of its accumulator is head r's
-//     output for that dim.  All operands are fp32: the products are exact.
+//     block of 64 dims.  Lane l supplies p x (group scale) of head l%4 (A)
+//     and the centroid (or value) of dim l*DV + v (B); register r of its
+//     accumulator is head r's output for that dim.  fp32 operands: the
+//     products are exact.
 //
-// The VALU keeps the K widening, the V dequantization (V rows of a chunk are
-// staged in LDS by all lanes, their E4M3 group scales decoded once), the
-// softmax and the index arithmetic.
+// The VALU keeps the K widening, the V dequantization (the chunk's V rows are
+// staged transposed in LDS by the wave, their E4M3 group scales decoded once,
+// adjacent turbo codes looked up as pairs), the softmax and the masks.
 #pragma once
 
 #include "kvq_decode.h"
@@ -32,12 +48,15 @@ namespace kvq {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
+
 template <int KF, int VF, int HD, int G>
 struct MfmaGeo {
   static constexpr int NG = (G + 3) / 4;                    // head groups of four
   static constexpr int KQ = HD / 4;                         // K dims per lane (one quarter)
   static constexpr int KSTEPS = HD / 16;                    // 4-dim steps per quarter
-  static constexpr int KQB = KQ * Fmt<KF>::bits / 8;        // K bytes per lane per chunk
+  static constexpr int RBK = HD * Fmt<KF>::bits / 8;        // K bytes per row
+  static constexpr int KQB = RBK / 4;                       // K bytes per lane per chunk
   static constexpr int DV = HD / 64;                        // V dims per lane
   static constexpr int RBC = HD * Fmt<VF>::bits / 8;        // V code bytes per row
   static constexpr int WR = RBC / 4;                        // ... in words
@@ -47,24 +66,31 @@ struct MfmaGeo {
                              (KQB % 16 == 0);
 };
 
+// One wave's staging area: the chunk's V rows transposed (word w of position
+// j at [w][j], plus one zero row of slack for 3-bit fields that cross a
+// word), their group scales decoded and transposed the same way, the chunk's
+// probabilities transposed for operand A, and the heads' rescale factors.
 template <int KF, int VF, int HD, int G>
-struct MfmaSmem {
+struct MfmaWave {
   using MG = MfmaGeo<KF, VF, HD, G>;
-  PrologueSmem<KF, HD, G> pro;
-  // the chunk's V rows, transposed (word w of position j at [w][j]; one
-  // zero row of slack for 3-bit fields that cross a word), and their group
-  // scales, decoded, transposed the same way
-  __attribute__((aligned(16))) uint32_t vcode[kWaves][MG::WR + 1][kChunk];
-  __attribute__((aligned(16))) float vscale[kWaves][Fmt<VF>::turbo ? HD / 16 : 1][kChunk];
-  __attribute__((aligned(16))) float pt[kWaves][MG::NG][4][kChunk];  // p, transposed for operand A
-  __attribute__((aligned(16))) float alpha[kWaves][MG::NG][4];        // rescale factors of a chunk
-  // turbo V: centroids of every pair of adjacent codes (index lo | hi << bits)
-  f32x2 vpair[Fmt<VF>::turbo && MG::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
-  float red[kWaves][G][HD + 2];
+  __attribute__((aligned(16))) uint32_t vcode[MG::WR + 1][kChunk];
+  __attribute__((aligned(16))) float vscale[Fmt<VF>::turbo ? HD / 16 : 1][kChunk];
+  __attribute__((aligned(16))) float pt[MG::NG][4][kChunk];
+  __attribute__((aligned(16))) float alpha[MG::NG][4];
 };
 
-// One chunk's raw data in a lane's registers: its K quarter, and its share of
-// the chunk's V rows (code words and scale words).
+template <int KF, int VF, int HD, int G>
+struct MfmaSmem {
+  uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
+  uint64_t vbase[kMaxPages];  // ... and in the V pool
+  float vcen[16];
+  // turbo V: centroids of every pair of adjacent codes (index lo | hi << bits)
+  f32x2 vpair[Fmt<VF>::turbo && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
+  MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
+};
+
+// One chunk's raw bytes in a lane's registers: its K quarter, and its share
+// of the chunk's V rows (code words, and one scale word).
 template <int KF, int VF, int HD, int G>
 struct MfmaChunk {
   using MG = MfmaGeo<KF, VF, HD, G>;
@@ -72,47 +98,6 @@ struct MfmaChunk {
   uint32_t v[MG::NSD];
   uint32_t s;
 };
-
-template <int KF, int VF, int HD, int G>
-__device__ __forceinline__ void mfma_load(const DecodeArgs& a, const PrologueSmem<KF, HD, G>& sm, int first, int c,
-                                          int pb, int pe, uint32_t g, int lane, MfmaChunk<KF, VF, HD, G>& ck) {
-  using MG = MfmaGeo<KF, VF, HD, G>;
-  const uint32_t bmask = (1u << a.log2_bs) - 1u;
-  // K: position c + lane%16, quarter lane/16 (clamped into the split; masked later)
-  {
-    const int j = min(max(c + (lane & 15), pb), pe - 1);
-    const int bi = (j >> a.log2_bs) - first;
-    const uint32_t row = (uint32_t(j) & bmask) * a.num_kv_heads + g;
-    const uint8_t* p = a.k_cache + sm.kbase[bi] + uint64_t(row) * (HD * Fmt<KF>::bits / 8) + (lane >> 4) * MG::KQB;
-#pragma unroll
-    for (int i = 0; i < MG::KQB / 16; ++i) {
-      const u32x4 x = load16(p + 16 * i);
-      ck.k[4 * i] = x.x; ck.k[4 * i + 1] = x.y; ck.k[4 * i + 2] = x.z; ck.k[4 * i + 3] = x.w;
-    }
-  }
-  // V codes: word i of the chunk's rows is word i % WR of row i / WR
-#pragma unroll
-  for (int n = 0; n < MG::NSD; ++n) {
-    const int i = lane + n * kWave;
-    const int rr = min(i / MG::WR, kChunk - 1);
-    const int j = min(max(c + rr, pb), pe - 1);
-    const int bi = (j >> a.log2_bs) - first;
-    const uint32_t row = (uint32_t(j) & bmask) * a.num_kv_heads + g;
-    const uint8_t* p = a.v_cache + sm.vbase[bi] + uint64_t(row) * MG::RBC + (i % MG::WR) * 4;
-    ck.v[n] = *reinterpret_cast<const uint32_t*>(p);
-  }
-  // V scales: word lane % SW of row lane / SW (lanes < 16 * SW)
-  if constexpr (MG::SW > 0) {
-    const int rr = min(lane / MG::SW, kChunk - 1);
-    const int j = min(max(c + rr, pb), pe - 1);
-    const int bi = (j >> a.log2_bs) - first;
-    const uint32_t row = (uint32_t(j) & bmask) * a.num_kv_heads + g;
-    const uint8_t* p = a.v_cache + sm.vbase[bi] + a.v_data + uint64_t(row) * (HD / 16) + (lane % MG::SW) * 4;
-    ck.s = *reinterpret_cast<const uint32_t*>(p);
-  } else {
-    ck.s = 0;
-  }
-}
 
 // Sum of the four head_dim quarters of a 4x4x4 score tile.  Lane l holds
 // partial scores of heads 0..3 (registers) for quarter l / 16; the result is
@@ -128,50 +113,114 @@ __device__ __forceinline__ float quarter_sum(const f32x4 d) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(x >> 32));
+  return uint64_t(hi) << 32 | lo;
+}
+
 template <int KF, int VF, int HD, int G>
-__global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const DecodeArgs a) {
   using MG = MfmaGeo<KF, VF, HD, G>;
   constexpr int NG = MG::NG, DV = MG::DV;
   __shared__ MfmaSmem<KF, VF, HD, G> sm;
-  const Tile tl = unit_tile<KVQ_TILE_DENSE>(a, a.nsplit);
-  if (!tl.valid) return;
-  const SeqSpan sp = split_span(a, tl.s, tl.split);
-  if (sp.pb >= sp.L) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // query operand A: head 4 * hg + lane % 4, dims (lane / 16) * KQ + 4 s .. + 4
+  const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);
+  const uint32_t hblocks = a.num_kv_heads / uint32_t(nw);
+  const uint32_t unit = blockIdx.x / hblocks;
+  if (unit >= a.num_seqs * a.nsplit) return;
+  const uint32_t s = unit % a.num_seqs, split = unit / a.num_seqs;
+  const uint32_t g = (blockIdx.x % hblocks) * uint32_t(nw) + uint32_t(w);
+  const SeqSpan sp = split_span(a, s, split);
+  if (sp.pb >= sp.L) return;  // uniform over the workgroup
+  const uint32_t nkv = a.num_kv_heads;
+
+  // query operand A: head 4 hg + lane % 4, dims (lane / 16) * KQ + 4 k .. + 4
   i16x4 qa[NG][MG::KSTEPS];
   {
-    const uint16_t* qg = a.q + uint64_t(tl.s) * a.q_stride + uint64_t(tl.g) * G * HD;
+    const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
       const int h = 4 * hg + (lane & 3);
 #pragma unroll
-      for (int s = 0; s < MG::KSTEPS; ++s) {
-        const int d = (lane >> 4) * MG::KQ + 4 * s;
+      for (int k = 0; k < MG::KSTEPS; ++k) {
+        const int d = (lane >> 4) * MG::KQ + 4 * k;
         if (h < G) {
           const u32x2 x = *reinterpret_cast<const u32x2*>(qg + h * HD + d);
-          qa[hg][s] = __builtin_bit_cast(i16x4, x);
+          qa[hg][k] = __builtin_bit_cast(i16x4, x);
         } else {
-          qa[hg][s] = i16x4{0, 0, 0, 0};
+          qa[hg][k] = i16x4{0, 0, 0, 0};
         }
       }
     }
   }
-  // page offsets and codebook (the QReg argument of the shared prologue is unused here)
-  {
-    QReg<KF, 16, G> unused;
-    prologue<KF, VF, HD, G, 16>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, 0, unused);
-  }
-  if constexpr (Fmt<VF>::turbo && DV >= 2) {
-    constexpr int BITS = Fmt<VF>::bits;
-    for (int e = tid; e < (1 << (2 * BITS)); e += kWaves * kWave) {
-      sm.vpair[e].x = a.cb.centroid[VF - 2][e & ((1 << BITS) - 1)];
-      sm.vpair[e].y = a.cb.centroid[VF - 2][e >> BITS];
-    }
-    __syncthreads();
-  }
+  // page offsets of the split and the V codebook, shared by the waves
   const int first = sp.pb >> a.log2_bs;
+  {
+    const int n = ((sp.pe - 1) >> a.log2_bs) - first + 1;
+    const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks + first;
+    for (int i = tid; i < n; i += int(blockDim.x)) {
+      const uint64_t page = uint64_t(uint32_t(bt[i]));
+      sm.kbase[i] = page * a.k_stride;
+      sm.vbase[i] = page * a.v_stride;
+    }
+    if constexpr (Fmt<VF>::turbo) {
+      constexpr int BITS = Fmt<VF>::bits;
+      if (tid < 16) sm.vcen[tid] = tid < (1 << BITS) ? a.cb.centroid[VF - 2][tid] : 0.0f;
+      if constexpr (DV >= 2) {
+        for (int e = tid; e < (1 << (2 * BITS)); e += int(blockDim.x)) {
+          sm.vpair[e].x = a.cb.centroid[VF - 2][e & ((1 << BITS) - 1)];
+          sm.vpair[e].y = a.cb.centroid[VF - 2][e >> BITS];
+        }
+      }
+    }
+  }
+  auto& wv = sm.wv[w];
+  if (lane < kChunk) wv.vcode[MG::WR][lane] = 0u;  // the slack row stays zero
+  // every load so far completes before the chunk loop, whose wait counts
+  // then only ever cover chunk loads
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // the lane's byte offsets inside a chunk's page, fixed for the split:
+  // K quarter lane/16 of position lane%16; code word i%WR of row i/WR for
+  // i = lane + 64 n; scale word lane%SW of row lane/SW
+  const uint32_t bmask = (1u << a.log2_bs) - 1u;
+  const uint32_t koff = ((uint32_t(lane) & 15u) * nkv + g) * MG::RBK + (uint32_t(lane) >> 4) * MG::KQB;
+  uint32_t voff[MG::NSD];
+  int vrow[MG::NSD];
+#pragma unroll
+  for (int n = 0; n < MG::NSD; ++n) {
+    const int i = lane + n * kWave;
+    vrow[n] = min(i / MG::WR, kChunk - 1);
+    voff[n] = (uint32_t(vrow[n]) * nkv + g) * MG::RBC + uint32_t(i % MG::WR) * 4u;
+  }
+  const int srow = MG::SW > 0 ? min(lane / max(MG::SW, 1), kChunk - 1) : 0;
+  const uint32_t soff = MG::SW > 0 ? a.v_data + (uint32_t(srow) * nkv + g) * (HD / 16) +
+                                         uint32_t(lane % max(MG::SW, 1)) * 4u
+                                   : 0u;
+  const int cs = sp.pb & ~(kChunk - 1);
+  const int clast = (sp.pe - 1) & ~(kChunk - 1);
+  auto load = [&](int c, MfmaChunk<KF, VF, HD, G>& ck) {
+    const int cl = min(c, clast);  // past the end: reread the last chunk (all masked)
+    const int pg = (cl >> a.log2_bs) - first;
+    const uint32_t within = uint32_t(cl) & bmask;
+    const uint64_t kb = uniform_u64(sm.kbase[pg]) + uint64_t(within) * nkv * MG::RBK;
+    const uint64_t vb = uniform_u64(sm.vbase[pg]);
+    const uint8_t* kp = a.k_cache + kb + koff;
+#pragma unroll
+    for (int i = 0; i < MG::KQB / 16; ++i) {
+      const u32x4 x = load16(kp + 16 * i);
+      ck.k[4 * i] = x.x; ck.k[4 * i + 1] = x.y; ck.k[4 * i + 2] = x.z; ck.k[4 * i + 3] = x.w;
+    }
+    const uint8_t* vp = a.v_cache + vb + uint64_t(within) * nkv * MG::RBC;
+#pragma unroll
+    for (int n = 0; n < MG::NSD; ++n) ck.v[n] = load4(vp + voff[n]);
+    if constexpr (MG::SW > 0) ck.s = load4(a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff);
+    else ck.s = 0u;
+  };
+
   const float qscale = a.qk_scale;
   // running state.  Lane l follows head 4 hg + l / 16 (its row of 16 lanes):
   // m is that head's running max (uniform in the row; finite at the start so
@@ -191,40 +240,47 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
       acc[hg][1][v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
-  auto& vcode = sm.vcode[w];
-  auto& vscale = sm.vscale[w];
-  auto& pt = sm.pt[w];
-
-  if (lane < kChunk) vcode[MG::WR][lane] = 0u;  // the slack row stays zero
+  auto& vcode = wv.vcode;
+  auto& vscale = wv.vscale;
+  auto& pt = wv.pt;
 
   auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G>& ck) {
-    // 1. stage the chunk's V rows (codes as loaded, scales decoded) in LDS
+    // 1. stage the chunk's V rows (codes as loaded, scales decoded) in LDS;
+    //    rows outside the split get zero scales (turbo) or zero values
 #pragma unroll
     for (int n = 0; n < MG::NSD; ++n) {
       const int i = lane + n * kWave;
-      if (i < kChunk * MG::WR) vcode[i % MG::WR][i / MG::WR] = ck.v[n];
+      if (i < kChunk * MG::WR) {
+        uint32_t word = ck.v[n];
+        if constexpr (!Fmt<VF>::turbo) {
+          const int j = c + vrow[n];
+          word = (j >= sp.pb && j < sp.pe) ? word : 0u;
+        }
+        vcode[i % MG::WR][vrow[n]] = word;
+      }
     }
     if constexpr (MG::SW > 0) {
       if (lane < kChunk * MG::SW) {
-        const int rr = lane / MG::SW, q4 = (lane % MG::SW) * 4;
+        const int j = c + srow, q4 = (lane % MG::SW) * 4;
+        const bool rok = j >= sp.pb && j < sp.pe;
         const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(ck.s), false);
         const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(ck.s), true);
-        vscale[q4][rr] = lo.x;
-        vscale[q4 + 1][rr] = lo.y;
-        vscale[q4 + 2][rr] = hi.x;
-        vscale[q4 + 3][rr] = hi.y;
+        vscale[q4][srow] = rok ? lo.x : 0.0f;
+        vscale[q4 + 1][srow] = rok ? lo.y : 0.0f;
+        vscale[q4 + 2][srow] = rok ? hi.x : 0.0f;
+        vscale[q4 + 3][srow] = rok ? hi.y : 0.0f;
       }
     }
     // 2. scores: position c + lane % 16, heads 4 hg + r
     i16x4 kb[MG::KSTEPS];
 #pragma unroll
-    for (int s = 0; s < MG::KSTEPS; ++s) {
+    for (int k = 0; k < MG::KSTEPS; ++k) {
       if constexpr (KF == KVQ_BF16) {
-        const u32x2 x = {ck.k[2 * s], ck.k[2 * s + 1]};
-        kb[s] = __builtin_bit_cast(i16x4, x);
+        const u32x2 x = {ck.k[2 * k], ck.k[2 * k + 1]};
+        kb[k] = __builtin_bit_cast(i16x4, x);
       } else {
-        const u32x2 x = {fp8x2_to_bf16x2<false>(ck.k[s]), fp8x2_to_bf16x2<true>(ck.k[s])};
-        kb[s] = __builtin_bit_cast(i16x4, x);
+        const u32x2 x = {fp8x2_to_bf16x2<false>(ck.k[k]), fp8x2_to_bf16x2<true>(ck.k[k])};
+        kb[k] = __builtin_bit_cast(i16x4, x);
       }
     }
     const int j = c + (lane & 15);
@@ -234,26 +290,24 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
     for (int hg = 0; hg < NG; ++hg) {
       f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int s = 0; s < MG::KSTEPS; ++s) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][s], kb[s], d, 0, 0, 0);
-      // 3. sum the four quarters so that row k of 16 lanes ends with head
-      //    4 hg + k: the half-wave swap pairs rows (0,1) with (2,3) and keeps
-      //    heads {0,1} in the low half, the row swap then pairs rows 0-1, 2-3
-      const float s = ok ? quarter_sum(d) * qscale : -INFINITY;
-      // 4. online softmax of the row's head over the chunk's 16 positions
-      const float mn = fmaxf(m[hg], group_max<16>(s));
+      for (int k = 0; k < MG::KSTEPS; ++k) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[k], d, 0, 0, 0);
+      // 3. the row's head: full score (masked positions: -inf, whatever
+      //    bytes they hold), then its online softmax over the 16 positions
+      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
+      const float mn = fmaxf(m[hg], group_max<16>(sc));
       const float al = fast_exp2(m[hg] - mn);
       grew |= mn > m[hg];
       m[hg] = mn;
-      const float p = fast_exp2(s - mn);  // 0 where masked
+      const float p = fast_exp2(sc - mn);  // 0 where masked
       lsum[hg] = fmaf(lsum[hg], al, p);
       pt[hg][lane >> 4][lane & 15] = p;
-      sm.alpha[w][hg][lane >> 4] = al;
+      wv.alpha[hg][lane >> 4] = al;
     }
     wave_lds_sync();
     if (__builtin_amdgcn_ballot_w64(grew)) {  // rare after the first chunks
 #pragma unroll
       for (int hg = 0; hg < NG; ++hg) {
-        const f32x4 al = *reinterpret_cast<const f32x4*>(&sm.alpha[w][hg][0]);
+        const f32x4 al = *reinterpret_cast<const f32x4*>(&wv.alpha[hg][0]);
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
           acc[hg][0][v] *= al;
@@ -261,7 +315,7 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
         }
       }
     }
-    // 5. P.V: the lane's operands for 8 positions at a time come from LDS in
+    // 4. P.V: the lane's operands for 8 positions at a time come from LDS in
     //    16-byte reads; even and odd positions feed two accumulator chains
 #pragma unroll
     for (int h8 = 0; h8 < kChunk; h8 += 8) {
@@ -311,7 +365,7 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
             }
         } else {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) b[q][0] = sm.pro.vcen[cw[q] & ((1u << BITS) - 1u)];
+          for (int q = 0; q < 8; ++q) b[q][0] = sm.vcen[cw[q] & ((1u << BITS) - 1u)];
         }
       } else {
         constexpr int EB = Fmt<VF>::bits / 8;
@@ -352,7 +406,10 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
     wave_lds_sync();
   };
 
-  // chunk loop: every load issued inside the loop, one chunk ahead
+  // chunk loop: chunk n sits in buffer n % NB and is loaded NB - 1 chunks
+  // ahead of its use; every load is issued inside the loop, whose rounds of
+  // NB chunks have one exit, at the bottom (the first NB - 1 uses are of
+  // zeroed buffers before the split, all masked)
   constexpr int NB = KVQ_DENSE_BUFS;
   MfmaChunk<KF, VF, HD, G> cb[NB];
 #pragma unroll
@@ -363,65 +420,49 @@ __global__ __launch_bounds__(kWaves * kWave) void split_mfma_kernel(const Decode
     for (int k = 0; k < MG::NSD; ++k) cb[i].v[k] = 0u;
     cb[i].s = 0u;
   }
-  constexpr int step = kWaves * kChunk;
-  int c = (sp.pb & ~(kChunk - 1)) + w * kChunk;  // next chunk to load; the one used trails by NB - 1
-  if (c < sp.pe) {
-    const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;
+  {
+    const int nch = (clast - cs) / kChunk + 1;
+    const int rounds = (nch + 2 * NB - 2) / NB;  // covers the chunks and the NB - 1 leading uses
+    int c = cs;  // next chunk to load
     for (int it = 0; it < rounds; ++it) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        mfma_load<KF, VF, HD, G>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, lane, cb[(i + NB - 1) % NB]);
-        consume(c - (NB - 1) * step, cb[i]);
-        c += step;
+        load(c, cb[(i + NB - 1) % NB]);
+        consume(c - (NB - 1) * kChunk, cb[i]);
+        c += kChunk;
       }
     }
   }
 
-  // the wave's state: sums over its 16 positions (lanes < 16), outputs by dim
-  const uint64_t base = (uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split;
+  // the wave's partials for its kv head: sums over the row's 16 lanes, one
+  // output dim pair per lane and head
+  const uint64_t base = (uint64_t(s) * nkv + g) * a.nsplit + split;
 #pragma unroll
   for (int hg = 0; hg < NG; ++hg) {
-    lsum[hg] = group_sum<16>(lsum[hg]);
+    const float z = group_sum<16>(lsum[hg]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * hg + r;
       if (h < G) {
+        float* dst = a.part + (base * G + h) * HD + lane * DV;
 #pragma unroll
-        for (int v = 0; v < DV; ++v) sm.red[w][h][lane * DV + v] = acc[hg][0][v][r] + acc[hg][1][v][r];
+        for (int v = 0; v < DV; ++v) dst[v] = acc[hg][0][v][r] + acc[hg][1][v][r];
       }
     }
     const int h = 4 * hg + (lane >> 4);
-    if ((lane & 15) == 0 && h < G) {  // a wave that saw no position reports -inf
-      sm.red[w][h][HD] = lsum[hg] > 0.0f ? m[hg] : -INFINITY;
-      sm.red[w][h][HD + 1] = lsum[hg];
+    if ((lane & 15) == 0 && h < G) {  // a split that saw no position reports -inf
+      a.ml[(base * G + h) * 2] = z > 0.0f ? m[hg] : -INFINITY;
+      a.ml[(base * G + h) * 2 + 1] = z;
     }
   }
-  __syncthreads();
-  for (int i = tid; i < G * HD; i += kWaves * kWave) {
-    const int h = i / HD, d = i % HD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.red[ww][h][HD]);
-    float o = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = sm.red[ww][h][HD];
-      if (mw > -INFINITY) o += fast_exp2(mw - M) * sm.red[ww][h][d];
-    }
-    a.part[(base * G + h) * HD + d] = o;
-  }
-  if (tid < G) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.red[ww][h][HD]);
-    float sum = 0.0f;
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float mw = sm.red[ww][h][HD];
-      if (mw > -INFINITY) sum += fast_exp2(mw - M) * sm.red[ww][h][HD + 1];
-    }
-    a.ml[(base * G + h) * 2] = M;
-    a.ml[(base * G + h) * 2 + 1] = sum;
-  }
+}
+
+// Workgroup shape of split_mfma_kernel: the largest divisor of the kv head
+// count up to kUnitWaves (one wave per kv head).
+inline uint32_t mfma_unit_waves(uint32_t nkv) {
+  for (uint32_t d = kUnitWaves; d > 1; --d)
+    if (nkv % d == 0) return d;
+  return 1;
 }
 
 }  // namespace kvq
