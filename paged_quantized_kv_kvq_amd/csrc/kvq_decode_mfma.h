@@ -49,6 +49,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
+constexpr int kTiles = KVQ_MFMA_TILES;  // 16-position tiles a wave takes per step
+constexpr int kStep = kTiles * kChunk;
 
 template <int KF, int VF, int HD, int G>
 struct MfmaGeo {
@@ -60,22 +62,23 @@ struct MfmaGeo {
   static constexpr int DV = HD / 64;                        // V dims per lane
   static constexpr int RBC = HD * Fmt<VF>::bits / 8;        // V code bytes per row
   static constexpr int WR = RBC / 4;                        // ... in words
-  static constexpr int SW = Fmt<VF>::turbo ? HD / 64 : 0;   // V scale words per row (4 bytes each)
+  static constexpr int NGS = Fmt<VF>::turbo ? HD / 16 : 1;  // V scale groups per row (1: no scales)
+  static constexpr int SWL = Fmt<VF>::turbo ? HD / 64 : 0;  // scale words of a row (4 groups each)
   static constexpr int NSD = (kChunk * WR + kWave - 1) / kWave;  // staged code words per lane
   static constexpr bool ok = (KF == KVQ_BF16 || KF == KVQ_FP8_E4M3) && KQB <= 64 && RBC <= 128 &&
                              (KQB % 16 == 0);
 };
 
-// One wave's staging area: the chunk's V rows transposed (word w of position
+// One wave's staging area: the step's V rows transposed (word w of position
 // j at [w][j], plus one zero row of slack for 3-bit fields that cross a
-// word), their group scales decoded and transposed the same way, the chunk's
-// probabilities transposed for operand A, and the heads' rescale factors.
+// word); operand A of P.V for every scale group (p of head r at position j
+// times the group's E4M3 scale at [group][r][j]; turbo V only, otherwise a
+// single group of plain p); and the heads' rescale factors.
 template <int KF, int VF, int HD, int G>
 struct MfmaWave {
   using MG = MfmaGeo<KF, VF, HD, G>;
-  __attribute__((aligned(16))) uint32_t vcode[MG::WR + 1][kChunk];
-  __attribute__((aligned(16))) float vscale[Fmt<VF>::turbo ? HD / 16 : 1][kChunk];
-  __attribute__((aligned(16))) float pt[MG::NG][4][kChunk];
+  __attribute__((aligned(16))) uint32_t vcode[MG::WR + 1][kStep];
+  __attribute__((aligned(16))) float pt[MG::NG][MG::NGS][4][kStep];
   __attribute__((aligned(16))) float alpha[MG::NG][4];
 };
 
@@ -89,14 +92,14 @@ struct MfmaSmem {
   MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
 };
 
-// One chunk's raw bytes in a lane's registers: its K quarter, and its share
-// of the chunk's V rows (code words, and one scale word).
+// One chunk's raw bytes in a lane's registers: its K quarter, its share of
+// the chunk's V code words, and the scale words of position lane % 16.
 template <int KF, int VF, int HD, int G>
 struct MfmaChunk {
   using MG = MfmaGeo<KF, VF, HD, G>;
   uint32_t k[MG::KQB / 4];
   uint32_t v[MG::NSD];
-  uint32_t s;
+  uint32_t s[MG::SWL > 0 ? MG::SWL : 1];
 };
 
 // Sum of the four head_dim quarters of a 4x4x4 score tile.  Lane l holds
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     }
   }
   auto& wv = sm.wv[w];
-  if (lane < kChunk) wv.vcode[MG::WR][lane] = 0u;  // the slack row stays zero
+  if (lane < kStep) wv.vcode[MG::WR][lane] = 0u;  // the slack row stays zero
   // every load so far completes before the chunk loop, whose wait counts
   // then only ever cover chunk loads
   __builtin_amdgcn_s_waitcnt(0);
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 
   // the lane's byte offsets inside a chunk's page, fixed for the split:
   // K quarter lane/16 of position lane%16; code word i%WR of row i/WR for
-  // i = lane + 64 n; scale word lane%SW of row lane/SW
+  // i = lane + 64 n; the scale words of row lane%16
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
   const uint32_t koff = ((uint32_t(lane) & 15u) * nkv + g) * MG::RBK + (uint32_t(lane) >> 4) * MG::KQB;
   uint32_t voff[MG::NSD];
@@ -196,10 +199,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     vrow[n] = min(i / MG::WR, kChunk - 1);
     voff[n] = (uint32_t(vrow[n]) * nkv + g) * MG::RBC + uint32_t(i % MG::WR) * 4u;
   }
-  const int srow = MG::SW > 0 ? min(lane / max(MG::SW, 1), kChunk - 1) : 0;
-  const uint32_t soff = MG::SW > 0 ? a.v_data + (uint32_t(srow) * nkv + g) * (HD / 16) +
-                                         uint32_t(lane % max(MG::SW, 1)) * 4u
-                                   : 0u;
+  const uint32_t soff = a.v_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16);
   const int cs = sp.pb & ~(kChunk - 1);
   const int clast = (sp.pe - 1) & ~(kChunk - 1);
   auto load = [&](int c, MfmaChunk<KF, VF, HD, G>& ck) {
@@ -217,8 +217,23 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     const uint8_t* vp = a.v_cache + vb + uint64_t(within) * nkv * MG::RBC;
 #pragma unroll
     for (int n = 0; n < MG::NSD; ++n) ck.v[n] = load4(vp + voff[n]);
-    if constexpr (MG::SW > 0) ck.s = load4(a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff);
-    else ck.s = 0u;
+    if constexpr (MG::SWL > 0) {
+      const uint8_t* sp8 = a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff;
+      if constexpr (MG::SWL == 1) {
+        ck.s[0] = load4(sp8);
+      } else if constexpr (MG::SWL == 2) {
+        const u32x2 x = load8(sp8);
+        ck.s[0] = x.x; ck.s[1] = x.y;
+      } else {
+#pragma unroll
+        for (int i = 0; i < MG::SWL / 4; ++i) {
+          const u32x4 x = load16(sp8 + 16 * i);
+          ck.s[4 * i] = x.x; ck.s[4 * i + 1] = x.y; ck.s[4 * i + 2] = x.z; ck.s[4 * i + 3] = x.w;
+        }
+      }
+    } else {
+      ck.s[0] = 0u;
+    }
   };
 
   const float qscale = a.qk_scale;
@@ -241,70 +256,96 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     }
   }
   auto& vcode = wv.vcode;
-  auto& vscale = wv.vscale;
   auto& pt = wv.pt;
 
-  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G>& ck) {
-    // 1. stage the chunk's V rows (codes as loaded, scales decoded) in LDS;
-    //    rows outside the split get zero scales (turbo) or zero values
+  // one step: tiles t = 0 .. kTiles - 1 of 16 positions, tile t starting at c + 16 t
+  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G> (&ck)[kTiles]) {
+    // 1. stage the step's V codes in LDS (bf16 / fp8 V: rows outside the
+    //    split as zeros, whatever bytes they hold)
 #pragma unroll
-    for (int n = 0; n < MG::NSD; ++n) {
-      const int i = lane + n * kWave;
-      if (i < kChunk * MG::WR) {
-        uint32_t word = ck.v[n];
-        if constexpr (!Fmt<VF>::turbo) {
-          const int j = c + vrow[n];
-          word = (j >= sp.pb && j < sp.pe) ? word : 0u;
+    for (int t = 0; t < kTiles; ++t) {
+#pragma unroll
+      for (int n = 0; n < MG::NSD; ++n) {
+        const int i = lane + n * kWave;
+        if (i < kChunk * MG::WR) {
+          uint32_t word = ck[t].v[n];
+          if constexpr (!Fmt<VF>::turbo) {
+            const int j = c + kChunk * t + vrow[n];
+            word = (j >= sp.pb && j < sp.pe) ? word : 0u;
+          }
+          vcode[i % MG::WR][kChunk * t + vrow[n]] = word;
         }
-        vcode[i % MG::WR][vrow[n]] = word;
       }
     }
-    if constexpr (MG::SW > 0) {
-      if (lane < kChunk * MG::SW) {
-        const int j = c + srow, q4 = (lane % MG::SW) * 4;
-        const bool rok = j >= sp.pb && j < sp.pe;
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(ck.s), false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(ck.s), true);
-        vscale[q4][srow] = rok ? lo.x : 0.0f;
-        vscale[q4 + 1][srow] = rok ? lo.y : 0.0f;
-        vscale[q4 + 2][srow] = rok ? hi.x : 0.0f;
-        vscale[q4 + 3][srow] = rok ? hi.y : 0.0f;
-      }
-    }
-    // 2. scores: position c + lane % 16, heads 4 hg + r
-    i16x4 kb[MG::KSTEPS];
+    // 2. scores: position c + 16 t + lane % 16, heads 4 hg + r
+    i16x4 kb[kTiles][MG::KSTEPS];
 #pragma unroll
-    for (int k = 0; k < MG::KSTEPS; ++k) {
-      if constexpr (KF == KVQ_BF16) {
-        const u32x2 x = {ck.k[2 * k], ck.k[2 * k + 1]};
-        kb[k] = __builtin_bit_cast(i16x4, x);
-      } else {
-        const u32x2 x = {fp8x2_to_bf16x2<false>(ck.k[k]), fp8x2_to_bf16x2<true>(ck.k[k])};
-        kb[k] = __builtin_bit_cast(i16x4, x);
+    for (int t = 0; t < kTiles; ++t)
+#pragma unroll
+      for (int k = 0; k < MG::KSTEPS; ++k) {
+        if constexpr (KF == KVQ_BF16) {
+          const u32x2 x = {ck[t].k[2 * k], ck[t].k[2 * k + 1]};
+          kb[t][k] = __builtin_bit_cast(i16x4, x);
+        } else {
+          const u32x2 x = {fp8x2_to_bf16x2<false>(ck[t].k[k]), fp8x2_to_bf16x2<true>(ck[t].k[k])};
+          kb[t][k] = __builtin_bit_cast(i16x4, x);
+        }
       }
-    }
-    const int j = c + (lane & 15);
-    const bool ok = j >= sp.pb && j < sp.pe;
     bool grew = false;
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
-      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 d[kTiles];
 #pragma unroll
-      for (int k = 0; k < MG::KSTEPS; ++k) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[k], d, 0, 0, 0);
-      // 3. the row's head: full score (masked positions: -inf, whatever
-      //    bytes they hold), then its online softmax over the 16 positions
-      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
-      const float mn = fmaxf(m[hg], group_max<16>(sc));
+      for (int t = 0; t < kTiles; ++t) d[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < MG::KSTEPS; ++k)
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) d[t] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[t][k], d[t], 0, 0, 0);
+      // 3. the row's head: full scores (masked positions: -inf, whatever
+      //    bytes they hold), then its online softmax over the step
+      float sc[kTiles];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const int j = c + kChunk * t + (lane & 15);
+        sc[t] = (j >= sp.pb && j < sp.pe) ? quarter_sum(d[t]) * qscale : -INFINITY;
+        mx = fmaxf(mx, sc[t]);
+      }
+      const float mn = fmaxf(m[hg], group_max<16>(mx));
       const float al = fast_exp2(m[hg] - mn);
       grew |= mn > m[hg];
       m[hg] = mn;
-      const float p = fast_exp2(sc - mn);  // 0 where masked
-      lsum[hg] = fmaf(lsum[hg], al, p);
-      pt[hg][lane >> 4][lane & 15] = p;
+      float ps = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kTiles; ++t) {
+        const float p = fast_exp2(sc[t] - mn);  // 0 where masked
+        ps += p;
+        const int col = kChunk * t + (lane & 15);
+        if constexpr (MG::SWL > 0) {
+          // operand A per scale group: p x the group's scale (outside the
+          // split the scale words are zeroed: p = 0 times a garbage NaN
+          // scale would not be 0)
+          const int j = c + col;
+          const bool rok = j >= sp.pb && j < sp.pe;
+#pragma unroll
+          for (int sw = 0; sw < MG::SWL; ++sw) {
+            const int sword = rok ? int(ck[t].s[sw]) : 0;
+            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(sword, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(sword, true);
+            pt[hg][4 * sw][lane >> 4][col] = p * lo.x;
+            pt[hg][4 * sw + 1][lane >> 4][col] = p * lo.y;
+            pt[hg][4 * sw + 2][lane >> 4][col] = p * hi.x;
+            pt[hg][4 * sw + 3][lane >> 4][col] = p * hi.y;
+          }
+        } else {
+          pt[hg][0][lane >> 4][col] = p;
+        }
+      }
+      lsum[hg] = fmaf(lsum[hg], al, ps);
       wv.alpha[hg][lane >> 4] = al;
     }
     wave_lds_sync();
-    if (__builtin_amdgcn_ballot_w64(grew)) {  // rare after the first chunks
+    if (__builtin_amdgcn_ballot_w64(grew)) {  // rare after the first steps
 #pragma unroll
       for (int hg = 0; hg < NG; ++hg) {
         const f32x4 al = *reinterpret_cast<const f32x4*>(&wv.alpha[hg][0]);
@@ -318,12 +359,14 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     // 4. P.V: the lane's operands for 8 positions at a time come from LDS in
     //    16-byte reads; even and odd positions feed two accumulator chains
 #pragma unroll
-    for (int h8 = 0; h8 < kChunk; h8 += 8) {
+    for (int h8 = 0; h8 < kStep; h8 += 8) {
+      // the lane's scale group (a block of four lanes covers 4 DV dims, all in one group)
+      const int grp = MG::SWL > 0 ? (lane * DV) / 16 : 0;
       float pa[NG][8];
 #pragma unroll
       for (int hg = 0; hg < NG; ++hg) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&pt[hg][lane & 3][h8]);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&pt[hg][lane & 3][h8 + 4]);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][h8]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][h8 + 4]);
         pa[hg][0] = x0.x; pa[hg][1] = x0.y; pa[hg][2] = x0.z; pa[hg][3] = x0.w;
         pa[hg][4] = x1.x; pa[hg][5] = x1.y; pa[hg][6] = x1.z; pa[hg][7] = x1.w;
       }
@@ -334,10 +377,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         const int wd = bit / 32, sh = bit % 32;
         const u32x4 c00 = *reinterpret_cast<const u32x4*>(&vcode[wd][h8]);
         const u32x4 c01 = *reinterpret_cast<const u32x4*>(&vcode[wd][h8 + 4]);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(&vscale[(lane * DV) / 16][h8]);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(&vscale[(lane * DV) / 16][h8 + 4]);
         uint32_t cw[8] = {c00.x, c00.y, c00.z, c00.w, c01.x, c01.y, c01.z, c01.w};
-        const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         if constexpr (32 % (DV * BITS) != 0) {  // fields may cross into the next word
           const u32x4 c10 = *reinterpret_cast<const u32x4*>(&vcode[wd + 1][h8]);
           const u32x4 c11 = *reinterpret_cast<const u32x4*>(&vcode[wd + 1][h8 + 4]);
@@ -348,12 +388,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 #pragma unroll
           for (int q = 0; q < 8; ++q) cw[q] >>= sh;
         }
-        // the group scale goes into operand A (one block = four lanes = one
-        // 16-dim group), the centroids into operand B
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-          for (int hg = 0; hg < NG; ++hg) pa[hg][q] *= ss[q];
+        // the centroids go into operand B
         if constexpr (DV >= 2) {
 #pragma unroll
           for (int q = 0; q < 8; ++q)
@@ -406,30 +441,34 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     wave_lds_sync();
   };
 
-  // chunk loop: chunk n sits in buffer n % NB and is loaded NB - 1 chunks
-  // ahead of its use; every load is issued inside the loop, whose rounds of
-  // NB chunks have one exit, at the bottom (the first NB - 1 uses are of
-  // zeroed buffers before the split, all masked)
+  // step loop: step n sits in buffer n % NB and is loaded NB - 1 steps ahead
+  // of its use; every load is issued inside the loop, whose rounds of NB
+  // steps have one exit, at the bottom (the first NB - 1 uses are of zeroed
+  // buffers before the split, all masked)
   constexpr int NB = KVQ_DENSE_BUFS;
-  MfmaChunk<KF, VF, HD, G> cb[NB];
+  MfmaChunk<KF, VF, HD, G> cb[NB][kTiles];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int k = 0; k < MG::KQB / 4; ++k) cb[i].k[k] = 0u;
+    for (int t = 0; t < kTiles; ++t) {
 #pragma unroll
-    for (int k = 0; k < MG::NSD; ++k) cb[i].v[k] = 0u;
-    cb[i].s = 0u;
-  }
+      for (int k = 0; k < MG::KQB / 4; ++k) cb[i][t].k[k] = 0u;
+#pragma unroll
+      for (int k = 0; k < MG::NSD; ++k) cb[i][t].v[k] = 0u;
+#pragma unroll
+      for (int k = 0; k < (MG::SWL > 0 ? MG::SWL : 1); ++k) cb[i][t].s[k] = 0u;
+    }
   {
-    const int nch = (clast - cs) / kChunk + 1;
-    const int rounds = (nch + 2 * NB - 2) / NB;  // covers the chunks and the NB - 1 leading uses
-    int c = cs;  // next chunk to load
+    const int nst = (clast - cs) / kStep + 1;
+    const int rounds = (nst + 2 * NB - 2) / NB;  // covers the steps and the NB - 1 leading uses
+    int c = cs;  // next step to load
     for (int it = 0; it < rounds; ++it) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        load(c, cb[(i + NB - 1) % NB]);
-        consume(c - (NB - 1) * kChunk, cb[i]);
-        c += kChunk;
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) load(c + kChunk * t, cb[(i + NB - 1) % NB][t]);
+        consume(c - (NB - 1) * kStep, cb[i]);
+        c += kStep;
       }
     }
   }

@@ -33,6 +33,9 @@
 #ifndef KVQ_DENSE_BUFS
 #define KVQ_DENSE_BUFS 2         // chunk buffers per wave in the dense split kernel
 #endif
+#ifndef KVQ_MFMA_TILES
+#define KVQ_MFMA_TILES 1         // 16-position tiles per step of a wave in the matrix-core split kernel
+#endif
 #ifndef KVQ_TILE_DENSE
 #define KVQ_TILE_DENSE 1         // workgroup -> (unit, kv head) map of the dense split kernel (see unit_tile)
 #endif
