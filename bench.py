@@ -14,8 +14,8 @@ value      effective KV GB/s: K+V bytes of every attended (position, kv head)
            Step and decode times are medians of per-step HIP events; between
            steps a 1 GiB scratch read evicts L2 and the MALL (--warm: no
            eviction), outside the timed region.
-roofline   the decode call (sparse: score pass, V pass, merge; dense: split
-           pass, merge) timed with HIP events on the stream the library
+roofline   the decode call (sparse: score pass, V pass; dense: split pass,
+           merge) timed with HIP events on the stream the library
            launches on; algorithmic bytes = K of every attended position + V
            of every (position, kv head) some head of the group keeps (counted
            from the stored K) + q + out + the page-table entries and lengths
@@ -157,6 +157,14 @@ def _attended(st, w) -> np.ndarray:
     if w.sliding_window:
         return np.minimum(L, w.sliding_window)
     return L
+
+
+def decode_kernels(w) -> str:
+    """The launches of one decode call for this workload."""
+    if w.sparse_v_threshold > 0:
+        return "kvq_paged_decode: scores_kernel + sparse_v_kernel"
+    mfma = w.k_format in ("bf16", "fp8") and w.block_size >= 16
+    return "kvq_paged_decode: " + ("split_mfma_kernel" if mfma else "split_kernel") + " + merge_kernel"
 
 
 def traffic_from_profile(workload: str):
@@ -350,8 +358,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 0),
-                     "kernel": ("kvq_paged_decode: scores_kernel + sparse_v_kernel + merge_kernel"
-                                if w.sparse_v_threshold > 0 else "kvq_paged_decode: split_kernel + merge_kernel"),
+                     "kernel": decode_kernels(w),
                      "algorithmic_bytes": alg},
         "roofline_alu": {"bound": "alu", "achieved": round(flops / (dec_ms * 1e-3) / 1e12, 3),
                          "peak": 157.3, "unit": "TFLOP/s", "frac": round(flops / (dec_ms * 1e-3) / 1e12 / 157.3, 4),
