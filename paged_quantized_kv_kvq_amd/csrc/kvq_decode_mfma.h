@@ -463,6 +463,13 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     const int rounds = (nst + 2 * NB - 2) / NB;  // covers the steps and the NB - 1 leading uses
     int c = cs;  // next step to load
     for (int it = 0; it < rounds; ++it) {
+      // every other round the waves meet (no memory fence: loads stay in
+      // flight), so that none runs more than a few chunks ahead of the
+      // others.  Their heads' V rows (32 bytes) and scale rows (8 bytes)
+      // share 128-byte lines; with the waves this close, a line is still in
+      // L2 when the last of them reads it (apart, the kernel fetched 1.11 to
+      // 1.17 times its bytes from beyond L2).
+      if ((it & 1) == 0) __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
 #pragma unroll
