@@ -163,7 +163,14 @@ def decode_kernels(w) -> str:
     """The launches of one decode call for this workload."""
     if w.sparse_v_threshold > 0:
         return "kvq_paged_decode: scores_kernel + sparse_v_kernel"
-    mfma = w.k_format in ("bf16", "fp8") and w.block_size >= 16
+    bits = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4}
+    hd = w.head_dim
+    kqb = hd * bits[w.k_format] // 32  # K bytes per lane and chunk in the matrix-core kernel
+    if w.k_format.startswith("turbo"):
+        shape_ok = kqb % 4 == 0 and kqb <= 32 and hd // 4 >= 16
+    else:
+        shape_ok = kqb <= 64 and kqb % 16 == 0
+    mfma = shape_ok and hd * bits[w.v_format] // 8 <= 128 and w.block_size >= 16
     return "kvq_paged_decode: " + ("split_mfma_kernel" if mfma else "split_kernel") + " + merge_kernel"
 
 

@@ -1,11 +1,13 @@
-// Dense split pass on the matrix cores, for bf16 and fp8 K sides.
+// Dense split pass on the matrix cores.
 //
 // Same contract as split_kernel ("metrale_model_layers/layers/ops/
 // kv_cache_bf16k_turbov.rs", paged_decode_attn_bf16k_turbo{2,3,4}v: block
-// tables, GQA, inv_sqrt_d, sliding window; "combs_models/kv.rs", attend): for
-// every (sequence, kv head, split) the partial (max, sum, unnormalized output)
-// of each query head of the group, in the layout merge_kernel reads.  The
-// work is laid out for the memory system and the matrix cores:
+// tables, GQA, inv_sqrt_d, sliding window; "combs_models/kv.rs", attend;
+// "spark_runtime/kv_cache.rs", is_wht_rotated: a rotated K side is scored
+// against the rotated query): for every (sequence, kv head, split) the partial
+// (max, sum, unnormalized output) of each query head of the group, in the
+// layout merge_kernel reads.  The work is laid out for the memory system and
+// the matrix cores:
 //
 //   * One workgroup per (sequence, split) and group of up to eight kv heads;
 //     wave w serves kv head g0 + w and walks every 16-position chunk of the
@@ -19,15 +21,21 @@
 //     uniform (read from LDS into scalar registers once per chunk) and every
 //     lane's byte offset inside the page is fixed for the whole split.
 //     Positions of a chunk outside the split lie in the same page and are
-//     read too, then masked: their scores become -inf, their V group scales
-//     (or, for bf16 / fp8 V, their V words) zero, so that no value of an
-//     unwritten slot reaches an accumulator.
-//   * Q.K^T on v_mfma_f32_4x4x4_16b_bf16.  Block b = lane/4 takes the four
-//     positions 4(b%4).. and the quarter b/4 of head_dim; lane l supplies
-//     four dims of query head l%4 (operand A) and four dims of the K row of
-//     position l%16 (operand B).  bf16 x bf16 products are exact in fp32, and
-//     fp8 K widens exactly to bf16, so this is the arithmetic of the VALU dot
-//     products.  Two lane swaps then sum the quarters so that row k of 16
+//     read too, then masked: their scores become -inf, their V words and
+//     group scales zero, so that no value of an unwritten slot reaches an
+//     accumulator.
+//   * Q.K^T, bf16 / fp8 K: v_mfma_f32_4x4x4_16b_bf16.  Block b = lane/4 takes
+//     the four positions 4(b%4).. and the quarter b/4 of head_dim; lane l
+//     supplies four dims of query head l%4 (operand A) and four dims of the K
+//     row of position l%16 (operand B).  bf16 x bf16 products are exact in
+//     fp32, and fp8 K widens exactly to bf16, so this is the arithmetic of
+//     the VALU dot products.
+//   * Q.K^T, turbo K: v_mfma_f32_4x4x1_16b_f32 over the same blocks, one dim
+//     per instruction: the rotated query (fp32) in A, the centroid of the
+//     lane's code in B (adjacent codes looked up as pairs).  One accumulator
+//     per 16-dim scale group; the lane's own position's group scales multiply
+//     the group sums afterwards.
+//   * Either way two lane swaps then sum the quarters so that row k of 16
 //     lanes holds query head 4 hg + k for the chunk's 16 positions, and the
 //     softmax runs on one value per lane.
 //   * P.V on v_mfma_f32_4x4x1_16b_f32, one instruction per position and per
@@ -36,9 +44,9 @@
 //     accumulator is head r's output for that dim.  fp32 operands: the
 //     products are exact.
 //
-// The VALU keeps the K widening, the V dequantization (the chunk's V rows are
-// staged transposed in LDS by the wave, their E4M3 group scales decoded once,
-// adjacent turbo codes looked up as pairs), the softmax and the masks.
+// The VALU keeps the K widening and lookups, the V dequantization (the
+// chunk's V rows are staged transposed in LDS by the wave, adjacent turbo
+// codes looked up as pairs), the softmax and the masks.
 #pragma once
 
 #include "kvq_decode.h"
@@ -49,36 +57,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
-constexpr int kTiles = KVQ_MFMA_TILES;  // 16-position tiles a wave takes per step
-constexpr int kStep = kTiles * kChunk;
 
 template <int KF, int VF, int HD, int G>
 struct MfmaGeo {
   static constexpr int NG = (G + 3) / 4;                    // head groups of four
+  static constexpr bool KT = Fmt<KF>::turbo;                // rotated, codebook K
   static constexpr int KQ = HD / 4;                         // K dims per lane (one quarter)
-  static constexpr int KSTEPS = HD / 16;                    // 4-dim steps per quarter
-  static constexpr int RBK = HD * Fmt<KF>::bits / 8;        // K bytes per row
+  static constexpr int KSTEPS = HD / 16;                    // 4-dim steps per quarter (bf16 / fp8 K)
+  static constexpr int RBK = HD * Fmt<KF>::bits / 8;        // K code bytes per row
   static constexpr int KQB = RBK / 4;                       // K bytes per lane per chunk
+  static constexpr int KGQ = KT ? KQ / 16 : 1;              // turbo K: scale groups per quarter
   static constexpr int DV = HD / 64;                        // V dims per lane
   static constexpr int RBC = HD * Fmt<VF>::bits / 8;        // V code bytes per row
   static constexpr int WR = RBC / 4;                        // ... in words
   static constexpr int NGS = Fmt<VF>::turbo ? HD / 16 : 1;  // V scale groups per row (1: no scales)
-  static constexpr int SWL = Fmt<VF>::turbo ? HD / 64 : 0;  // scale words of a row (4 groups each)
+  static constexpr int SWL = Fmt<VF>::turbo ? HD / 64 : 0;  // V scale words of a row (4 groups each)
   static constexpr int NSD = (kChunk * WR + kWave - 1) / kWave;  // staged code words per lane
-  static constexpr bool ok = (KF == KVQ_BF16 || KF == KVQ_FP8_E4M3) && KQB <= 64 && RBC <= 128 &&
-                             (KQB % 16 == 0);
+  static constexpr bool ok = mfma_split_ok(KF, VF, HD);
 };
 
-// One wave's staging area: the step's V rows transposed (word w of position
+// One wave's staging area: the chunk's V rows transposed (word w of position
 // j at [w][j], plus one zero row of slack for 3-bit fields that cross a
 // word); operand A of P.V for every scale group (p of head r at position j
-// times the group's E4M3 scale at [group][r][j]; turbo V only, otherwise a
-// single group of plain p); and the heads' rescale factors.
+// times the group's E4M3 scale at [group][r][j]; without scales a single
+// group of plain p); and the heads' rescale factors.
 template <int KF, int VF, int HD, int G>
 struct MfmaWave {
   using MG = MfmaGeo<KF, VF, HD, G>;
-  __attribute__((aligned(16))) uint32_t vcode[MG::WR + 1][kStep];
-  __attribute__((aligned(16))) float pt[MG::NG][MG::NGS][4][kStep];
+  __attribute__((aligned(16))) uint32_t vcode[MG::WR + 1][kChunk];
+  __attribute__((aligned(16))) float pt[MG::NG][MG::NGS][4][kChunk];
   __attribute__((aligned(16))) float alpha[MG::NG][4];
 };
 
@@ -87,22 +94,29 @@ struct MfmaSmem {
   uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
   uint64_t vbase[kMaxPages];  // ... and in the V pool
   float vcen[16];
-  // turbo V: centroids of every pair of adjacent codes (index lo | hi << bits)
+  // turbo sides: centroids of every pair of adjacent codes (index lo | hi << bits)
   f32x2 vpair[Fmt<VF>::turbo && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
-  MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
+  f32x2 kpair[Fmt<KF>::turbo ? 1 << (2 * Fmt<KF>::bits) : 1];
+  union {
+    MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
+    // turbo K, before the chunk loop: each wave's query rows, rotated in place
+    float qrot[Fmt<KF>::turbo ? kUnitWaves : 1][Fmt<KF>::turbo ? G : 1][Fmt<KF>::turbo ? HD : 1];
+  } u;
 };
 
-// One chunk's raw bytes in a lane's registers: its K quarter, its share of
-// the chunk's V code words, and the scale words of position lane % 16.
+// One chunk's raw bytes in a lane's registers: its K quarter (turbo K: and
+// the word that holds its quarter's scale bytes), its share of the chunk's V
+// code words, and the V scale words of position lane % 16.
 template <int KF, int VF, int HD, int G>
 struct MfmaChunk {
   using MG = MfmaGeo<KF, VF, HD, G>;
   uint32_t k[MG::KQB / 4];
+  uint32_t ks;
   uint32_t v[MG::NSD];
   uint32_t s[MG::SWL > 0 ? MG::SWL : 1];
 };
 
-// Sum of the four head_dim quarters of a 4x4x4 score tile.  Lane l holds
+// Sum of the four head_dim quarters of a 4x4 score tile.  Lane l holds
 // partial scores of heads 0..3 (registers) for quarter l / 16; the result is
 // the full score of head l / 16.  permlane32_swap exchanges the upper half of
 // its first operand with the lower half of its second, permlane16_swap the
@@ -122,6 +136,24 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return uint64_t(hi) << 32 | lo;
 }
 
+// `n` bytes (a multiple of 4) from p into consecutive words, in the widest
+// loads that fit.
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
+  int o = 0;
+#pragma unroll
+  for (; o + 16 <= N; o += 16) {
+    const u32x4 x = load16(p + o);
+    w[o / 4] = x.x; w[o / 4 + 1] = x.y; w[o / 4 + 2] = x.z; w[o / 4 + 3] = x.w;
+  }
+  if constexpr (N % 16 >= 8) {
+    const u32x2 x = load8(p + o);
+    w[o / 4] = x.x; w[o / 4 + 1] = x.y;
+    o += 8;
+  }
+  if constexpr (N % 8 == 4) w[o / 4] = load4(p + o);
+}
+
 template <int KF, int VF, int HD, int G>
 __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const DecodeArgs a) {
   using MG = MfmaGeo<KF, VF, HD, G>;
@@ -138,11 +170,11 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const SeqSpan sp = split_span(a, s, split);
   if (sp.pb >= sp.L) return;  // uniform over the workgroup
   const uint32_t nkv = a.num_kv_heads;
+  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
 
-  // query operand A: head 4 hg + lane % 4, dims (lane / 16) * KQ + 4 k .. + 4
-  i16x4 qa[NG][MG::KSTEPS];
-  {
-    const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
+  // bf16 / fp8 K, query operand A: head 4 hg + lane % 4, dims (lane / 16) * KQ + 4 k .. + 4
+  i16x4 qa[MG::KT ? 1 : NG][MG::KT ? 1 : MG::KSTEPS];
+  if constexpr (!MG::KT) {
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
       const int h = 4 * hg + (lane & 3);
@@ -158,7 +190,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       }
     }
   }
-  // page offsets of the split and the V codebook, shared by the waves
+  // page offsets of the split and the codebooks, shared by the waves
   const int first = sp.pb >> a.log2_bs;
   {
     const int n = ((sp.pe - 1) >> a.log2_bs) - first + 1;
@@ -178,19 +210,55 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         }
       }
     }
+    if constexpr (MG::KT) {
+      constexpr int BITS = Fmt<KF>::bits;
+      for (int e = tid; e < (1 << (2 * BITS)); e += int(blockDim.x)) {
+        sm.kpair[e].x = a.cb.centroid[KF - 2][e & ((1 << BITS) - 1)];
+        sm.kpair[e].y = a.cb.centroid[KF - 2][e >> BITS];
+      }
+    }
   }
-  auto& wv = sm.wv[w];
-  if (lane < kStep) wv.vcode[MG::WR][lane] = 0u;  // the slack row stays zero
+  // turbo K, query operand A: the rotated query (unnormalized: 1/sqrt(d)
+  // goes into the score scale), head 4 hg + lane % 4, dim (lane / 16) * KQ + k
+  float qf[MG::KT ? NG : 1][MG::KT ? MG::KQ : 1];
+  if constexpr (MG::KT) {
+    auto& qr = sm.u.qrot[w];
+    for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
+    wave_lds_sync();
+    for (int h2 = 1; h2 < HD; h2 <<= 1) {
+      for (int i = lane; i < G * HD / 2; i += kWave) {
+        const int hh = i / (HD / 2), k = i % (HD / 2);
+        const int lo = (k / h2) * 2 * h2 + (k % h2);
+        const float x = qr[hh][lo], y = qr[hh][lo + h2];
+        qr[hh][lo] = x + y;
+        qr[hh][lo + h2] = x - y;
+      }
+      wave_lds_sync();
+    }
+#pragma unroll
+    for (int hg = 0; hg < NG; ++hg) {
+      const int h = 4 * hg + (lane & 3);
+#pragma unroll
+      for (int k = 0; k < MG::KQ; ++k) qf[hg][k] = h < G ? qr[h][(lane >> 4) * MG::KQ + k] : 0.0f;
+    }
+  }
   // every load so far completes before the chunk loop, whose wait counts
-  // then only ever cover chunk loads
+  // then only ever cover chunk loads; the staging areas overlay the rotated
+  // queries, so the slack rows are cleared after the barrier
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  auto& wv = sm.u.wv[w];
+  if (lane < kChunk) wv.vcode[MG::WR][lane] = 0u;  // the slack row stays zero
 
   // the lane's byte offsets inside a chunk's page, fixed for the split:
-  // K quarter lane/16 of position lane%16; code word i%WR of row i/WR for
-  // i = lane + 64 n; the scale words of row lane%16
+  // K quarter lane/16 of position lane%16 (turbo K: and the word of that
+  // row's scale bytes that holds the quarter's groups); code word i%WR of
+  // row i/WR for i = lane + 64 n; the V scale words of row lane%16
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
   const uint32_t koff = ((uint32_t(lane) & 15u) * nkv + g) * MG::RBK + (uint32_t(lane) >> 4) * MG::KQB;
+  const uint32_t ksoff = a.k_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16) +
+                         ((uint32_t(lane) >> 4) * MG::KGQ / 4u) * 4u;
+  const int ksh = int(((uint32_t(lane) >> 4) * MG::KGQ) % 4u) * 8;  // bit offset of the first group's byte
   uint32_t voff[MG::NSD];
   int vrow[MG::NSD];
 #pragma unroll
@@ -206,37 +274,19 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     const int cl = min(c, clast);  // past the end: reread the last chunk (all masked)
     const int pg = (cl >> a.log2_bs) - first;
     const uint32_t within = uint32_t(cl) & bmask;
-    const uint64_t kb = uniform_u64(sm.kbase[pg]) + uint64_t(within) * nkv * MG::RBK;
+    const uint64_t kpage = uniform_u64(sm.kbase[pg]);
     const uint64_t vb = uniform_u64(sm.vbase[pg]);
-    const uint8_t* kp = a.k_cache + kb + koff;
-#pragma unroll
-    for (int i = 0; i < MG::KQB / 16; ++i) {
-      const u32x4 x = load16(kp + 16 * i);
-      ck.k[4 * i] = x.x; ck.k[4 * i + 1] = x.y; ck.k[4 * i + 2] = x.z; ck.k[4 * i + 3] = x.w;
-    }
+    load_words<MG::KQB>(a.k_cache + kpage + uint64_t(within) * nkv * MG::RBK + koff, ck.k);
+    if constexpr (MG::KT) ck.ks = load4(a.k_cache + kpage + uint64_t(within) * nkv * (HD / 16) + ksoff);
+    else ck.ks = 0u;
     const uint8_t* vp = a.v_cache + vb + uint64_t(within) * nkv * MG::RBC;
 #pragma unroll
     for (int n = 0; n < MG::NSD; ++n) ck.v[n] = load4(vp + voff[n]);
-    if constexpr (MG::SWL > 0) {
-      const uint8_t* sp8 = a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff;
-      if constexpr (MG::SWL == 1) {
-        ck.s[0] = load4(sp8);
-      } else if constexpr (MG::SWL == 2) {
-        const u32x2 x = load8(sp8);
-        ck.s[0] = x.x; ck.s[1] = x.y;
-      } else {
-#pragma unroll
-        for (int i = 0; i < MG::SWL / 4; ++i) {
-          const u32x4 x = load16(sp8 + 16 * i);
-          ck.s[4 * i] = x.x; ck.s[4 * i + 1] = x.y; ck.s[4 * i + 2] = x.z; ck.s[4 * i + 3] = x.w;
-        }
-      }
-    } else {
-      ck.s[0] = 0u;
-    }
+    if constexpr (MG::SWL > 0) load_words<4 * MG::SWL>(a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff, ck.s);
+    else ck.s[0] = 0u;
   };
 
-  const float qscale = a.qk_scale;
+  const float qscale = a.qk_scale * (MG::KT ? a.wht_scale : 1.0f);
   // running state.  Lane l follows head 4 hg + l / 16 (its row of 16 lanes):
   // m is that head's running max (uniform in the row; finite at the start so
   // that a chunk with every position masked rescales by exactly 1), lsum the
@@ -258,94 +308,113 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   auto& vcode = wv.vcode;
   auto& pt = wv.pt;
 
-  // one step: tiles t = 0 .. kTiles - 1 of 16 positions, tile t starting at c + 16 t
-  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G> (&ck)[kTiles]) {
-    // 1. stage the step's V codes in LDS (bf16 / fp8 V: rows outside the
-    //    split as zeros, whatever bytes they hold)
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
-#pragma unroll
-      for (int n = 0; n < MG::NSD; ++n) {
-        const int i = lane + n * kWave;
-        if (i < kChunk * MG::WR) {
-          uint32_t word = ck[t].v[n];
-          if constexpr (!Fmt<VF>::turbo) {
-            const int j = c + kChunk * t + vrow[n];
-            word = (j >= sp.pb && j < sp.pe) ? word : 0u;
-          }
-          vcode[i % MG::WR][kChunk * t + vrow[n]] = word;
-        }
-      }
-    }
-    // 2. scores: position c + 16 t + lane % 16, heads 4 hg + r
-    i16x4 kb[kTiles][MG::KSTEPS];
-#pragma unroll
-    for (int t = 0; t < kTiles; ++t)
+  // the lane's Q.K^T partial over its quarter for heads 4 hg + r (registers)
+  // at position c + lane % 16
+  auto qk = [&](const MfmaChunk<KF, VF, HD, G>& ck, int hg) -> f32x4 {
+    if constexpr (!MG::KT) {
+      i16x4 kb[MG::KSTEPS];
 #pragma unroll
       for (int k = 0; k < MG::KSTEPS; ++k) {
         if constexpr (KF == KVQ_BF16) {
-          const u32x2 x = {ck[t].k[2 * k], ck[t].k[2 * k + 1]};
-          kb[t][k] = __builtin_bit_cast(i16x4, x);
+          const u32x2 x = {ck.k[2 * k], ck.k[2 * k + 1]};
+          kb[k] = __builtin_bit_cast(i16x4, x);
         } else {
-          const u32x2 x = {fp8x2_to_bf16x2<false>(ck[t].k[k]), fp8x2_to_bf16x2<true>(ck[t].k[k])};
-          kb[t][k] = __builtin_bit_cast(i16x4, x);
+          const u32x2 x = {fp8x2_to_bf16x2<false>(ck.k[k]), fp8x2_to_bf16x2<true>(ck.k[k])};
+          kb[k] = __builtin_bit_cast(i16x4, x);
         }
       }
+      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < MG::KSTEPS; ++k) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[k], d, 0, 0, 0);
+      return d;
+    } else {
+      // code pair p (dims 2p, 2p + 1 of the quarter) sits at bits 2 BITS p of
+      // the quarter's little-endian bit stream; one accumulator per scale
+      // group, the groups interleaved for independent chains
+      constexpr int BITS = Fmt<KF>::bits, PB = 2 * BITS, PPG = 8;  // pairs per 16-dim group
+      f32x4 dg[MG::KGQ];
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) dg[gq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp)
+#pragma unroll
+        for (int gq = 0; gq < MG::KGQ; ++gq) {
+          const int p = gq * PPG + pp;
+          const int bit = p * PB, wd = bit / 32, sh = bit % 32;
+          uint32_t field;
+          if constexpr (32 % PB == 0) {
+            field = (ck.k[wd] >> sh) & ((1u << PB) - 1u);
+          } else {
+            const uint32_t hi = wd + 1 < MG::KQB / 4 ? ck.k[wd + 1] : 0u;
+            field = uint32_t((uint64_t(hi) << 32 | ck.k[wd]) >> sh) & ((1u << PB) - 1u);
+          }
+          const f32x2 cv = sm.kpair[field];
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][2 * p], cv.x, dg[gq], 0, 0, 0);
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][2 * p + 1], cv.y, dg[gq], 0, 0, 0);
+        }
+      // the groups' E4M3 scales (of this lane's position) on the group sums
+      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) {
+        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(ck.ks >> (ksh + 8 * gq)), 0);
+        d += sc * dg[gq];
+      }
+      return d;
+    }
+  };
+
+  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G>& ck) {
+    // 1. stage the chunk's V codes in LDS (bf16 / fp8 V: rows outside the
+    //    split as zeros, whatever bytes they hold)
+#pragma unroll
+    for (int n = 0; n < MG::NSD; ++n) {
+      const int i = lane + n * kWave;
+      if (i < kChunk * MG::WR) {
+        uint32_t word = ck.v[n];
+        if constexpr (!Fmt<VF>::turbo) {
+          const int j = c + vrow[n];
+          word = (j >= sp.pb && j < sp.pe) ? word : 0u;
+        }
+        vcode[i % MG::WR][vrow[n]] = word;
+      }
+    }
+    // 2. scores: position c + lane % 16, heads 4 hg + r
+    const int j = c + (lane & 15);
+    const bool ok = j >= sp.pb && j < sp.pe;
     bool grew = false;
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
-      f32x4 d[kTiles];
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) d[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int k = 0; k < MG::KSTEPS; ++k)
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) d[t] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[t][k], d[t], 0, 0, 0);
-      // 3. the row's head: full scores (masked positions: -inf, whatever
-      //    bytes they hold), then its online softmax over the step
-      float sc[kTiles];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const int j = c + kChunk * t + (lane & 15);
-        sc[t] = (j >= sp.pb && j < sp.pe) ? quarter_sum(d[t]) * qscale : -INFINITY;
-        mx = fmaxf(mx, sc[t]);
-      }
-      const float mn = fmaxf(m[hg], group_max<16>(mx));
+      const f32x4 d = qk(ck, hg);
+      // 3. the row's head: full score (masked positions: -inf, whatever
+      //    bytes they hold), then its online softmax over the chunk
+      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
+      const float mn = fmaxf(m[hg], group_max<16>(sc));
       const float al = fast_exp2(m[hg] - mn);
       grew |= mn > m[hg];
       m[hg] = mn;
-      float ps = 0.0f;
+      const float p = fast_exp2(sc - mn);  // 0 where masked
+      lsum[hg] = fmaf(lsum[hg], al, p);
+      if constexpr (MG::SWL > 0) {
+        // operand A per scale group: p x the group's scale (outside the
+        // split the scale words are zeroed: p = 0 times a garbage NaN
+        // scale would not be 0)
 #pragma unroll
-      for (int t = 0; t < kTiles; ++t) {
-        const float p = fast_exp2(sc[t] - mn);  // 0 where masked
-        ps += p;
-        const int col = kChunk * t + (lane & 15);
-        if constexpr (MG::SWL > 0) {
-          // operand A per scale group: p x the group's scale (outside the
-          // split the scale words are zeroed: p = 0 times a garbage NaN
-          // scale would not be 0)
-          const int j = c + col;
-          const bool rok = j >= sp.pb && j < sp.pe;
-#pragma unroll
-          for (int sw = 0; sw < MG::SWL; ++sw) {
-            const int sword = rok ? int(ck[t].s[sw]) : 0;
-            const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(sword, false);
-            const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(sword, true);
-            pt[hg][4 * sw][lane >> 4][col] = p * lo.x;
-            pt[hg][4 * sw + 1][lane >> 4][col] = p * lo.y;
-            pt[hg][4 * sw + 2][lane >> 4][col] = p * hi.x;
-            pt[hg][4 * sw + 3][lane >> 4][col] = p * hi.y;
-          }
-        } else {
-          pt[hg][0][lane >> 4][col] = p;
+        for (int sw = 0; sw < MG::SWL; ++sw) {
+          const int sword = ok ? int(ck.s[sw]) : 0;
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(sword, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(sword, true);
+          pt[hg][4 * sw][lane >> 4][lane & 15] = p * lo.x;
+          pt[hg][4 * sw + 1][lane >> 4][lane & 15] = p * lo.y;
+          pt[hg][4 * sw + 2][lane >> 4][lane & 15] = p * hi.x;
+          pt[hg][4 * sw + 3][lane >> 4][lane & 15] = p * hi.y;
         }
+      } else {
+        pt[hg][0][lane >> 4][lane & 15] = p;
       }
-      lsum[hg] = fmaf(lsum[hg], al, ps);
       wv.alpha[hg][lane >> 4] = al;
     }
     wave_lds_sync();
-    if (__builtin_amdgcn_ballot_w64(grew)) {  // rare after the first steps
+    if (__builtin_amdgcn_ballot_w64(grew)) {  // rare after the first chunks
 #pragma unroll
       for (int hg = 0; hg < NG; ++hg) {
         const f32x4 al = *reinterpret_cast<const f32x4*>(&wv.alpha[hg][0]);
@@ -359,7 +428,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     // 4. P.V: the lane's operands for 8 positions at a time come from LDS in
     //    16-byte reads; even and odd positions feed two accumulator chains
 #pragma unroll
-    for (int h8 = 0; h8 < kStep; h8 += 8) {
+    for (int h8 = 0; h8 < kChunk; h8 += 8) {
       // the lane's scale group (a block of four lanes covers 4 DV dims, all in one group)
       const int grp = MG::SWL > 0 ? (lane * DV) / 16 : 0;
       float pa[NG][8];
@@ -441,27 +510,26 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     wave_lds_sync();
   };
 
-  // step loop: step n sits in buffer n % NB and is loaded NB - 1 steps ahead
-  // of its use; every load is issued inside the loop, whose rounds of NB
-  // steps have one exit, at the bottom (the first NB - 1 uses are of zeroed
-  // buffers before the split, all masked)
+  // chunk loop: chunk n sits in buffer n % NB and is loaded NB - 1 chunks
+  // ahead of its use; every load is issued inside the loop, whose rounds of
+  // NB chunks have one exit, at the bottom (the first NB - 1 uses are of
+  // zeroed buffers before the split, all masked)
   constexpr int NB = KVQ_DENSE_BUFS;
-  MfmaChunk<KF, VF, HD, G> cb[NB][kTiles];
+  MfmaChunk<KF, VF, HD, G> cb[NB];
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < NB; ++i) {
 #pragma unroll
-    for (int t = 0; t < kTiles; ++t) {
+    for (int k = 0; k < MG::KQB / 4; ++k) cb[i].k[k] = 0u;
+    cb[i].ks = 0u;
 #pragma unroll
-      for (int k = 0; k < MG::KQB / 4; ++k) cb[i][t].k[k] = 0u;
+    for (int k = 0; k < MG::NSD; ++k) cb[i].v[k] = 0u;
 #pragma unroll
-      for (int k = 0; k < MG::NSD; ++k) cb[i][t].v[k] = 0u;
-#pragma unroll
-      for (int k = 0; k < (MG::SWL > 0 ? MG::SWL : 1); ++k) cb[i][t].s[k] = 0u;
-    }
+    for (int k = 0; k < (MG::SWL > 0 ? MG::SWL : 1); ++k) cb[i].s[k] = 0u;
+  }
   {
-    const int nst = (clast - cs) / kStep + 1;
-    const int rounds = (nst + 2 * NB - 2) / NB;  // covers the steps and the NB - 1 leading uses
-    int c = cs;  // next step to load
+    const int nch = (clast - cs) / kChunk + 1;
+    const int rounds = (nch + 2 * NB - 2) / NB;  // covers the chunks and the NB - 1 leading uses
+    int c = cs;  // next chunk to load
     for (int it = 0; it < rounds; ++it) {
       // every other round the waves meet (no memory fence: loads stay in
       // flight), so that none runs more than a few chunks ahead of the
@@ -472,10 +540,9 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       if ((it & 1) == 0) __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-#pragma unroll
-        for (int t = 0; t < kTiles; ++t) load(c + kChunk * t, cb[(i + NB - 1) % NB][t]);
-        consume(c - (NB - 1) * kStep, cb[i]);
-        c += kStep;
+        load(c, cb[(i + NB - 1) % NB]);
+        consume(c - (NB - 1) * kChunk, cb[i]);
+        c += kChunk;
       }
     }
   }

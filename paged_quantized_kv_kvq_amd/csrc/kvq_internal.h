@@ -33,9 +33,6 @@
 #ifndef KVQ_DENSE_BUFS
 #define KVQ_DENSE_BUFS 2         // chunk buffers per wave in the dense split kernel
 #endif
-#ifndef KVQ_MFMA_TILES
-#define KVQ_MFMA_TILES 1         // 16-position tiles per step of a wave in the matrix-core split kernel
-#endif
 #ifndef KVQ_TILE_DENSE
 #define KVQ_TILE_DENSE 1         // workgroup -> (unit, kv head) map of the dense split kernel (see unit_tile)
 #endif
@@ -50,6 +47,18 @@
 #endif
 
 namespace kvq {
+
+// Whether the dense split pass runs on the matrix cores for these formats and
+// head_dim (bf16 / fp8 K: bf16 MFMA for Q.K^T; turbo K: fp32 MFMA over the
+// rotated query; V rows of at most 128 bytes); it also needs block_size >= 16.
+__host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
+  const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf;
+  const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf;
+  const int kqb = hd * kbits / 32;  // K bytes per lane and chunk (a quarter of a row)
+  const bool kturbo = kf == KVQ_TURBO2 || kf == KVQ_TURBO3 || kf == KVQ_TURBO4;
+  return hd * vbits / 8 <= 128 &&
+         (kturbo ? (kqb % 4 == 0 && kqb <= 32 && hd / 4 >= 16) : (kqb <= 64 && kqb % 16 == 0));
+}
 
 // fp32 Lloyd-Max tables for 2/3/4-bit codes, indexed [bits - 2].
 struct Codebooks {
