@@ -83,6 +83,25 @@ def test_block_sizes(gpu_lib, bs):
     run(gpu_lib, w, tail=2, label=f"bs{bs}")
 
 
+@pytest.mark.parametrize("hkv", [3, 6, 12, 16])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo4", "turbo3")])
+def test_kv_head_counts(gpu_lib, kf, vf, hkv):
+    # the dense matrix-core kernel serves up to eight kv heads per workgroup:
+    # 3 and 6 in one workgroup, 12 as two of 6, 16 as two of 8
+    w = synth.small(4500 + hkv * 10 + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[70, 333, 16], num_q_heads=2 * hkv,
+                    num_kv_heads=hkv, head_dim=128, block_size=16, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=2, label=f"{kf}/{vf} Hkv{hkv}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+@pytest.mark.parametrize("kf,vf", [("turbo2", "fp8"), ("turbo3", "turbo2")])
+def test_block_sizes_turbo_k(gpu_lib, kf, vf, bs):
+    # chunks that start inside a page (block_size > 16) on the turbo-K matrix-core path
+    w = synth.small(4700 + bs + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[1, 95, 640, 300], num_q_heads=8,
+                    num_kv_heads=4, head_dim=128, block_size=bs, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=2, label=f"{kf}/{vf} bs{bs}")
+
+
 @pytest.mark.parametrize("thr", [1e-3, 0.05])
 @pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo3", "turbo3"), ("fp8", "fp8"), ("bf16", "bf16"),
                                    ("turbo4", "turbo2")])
