@@ -5,7 +5,9 @@ e = block_size * num_kv_heads * head_dim elements per block per side:
   bf16   2e            fp8  e
   turbo4 e/2 + e/16    turbo3 3e/8 + e/16    turbo2 e/4 + e/16
 (codes, then one FP8 scale byte per group of 16 elements), and the
-``turbo*_data_bytes`` / ``turbo*_scale_bytes`` split.
+``turbo*_data_bytes`` / ``turbo*_scale_bytes`` split.  ``KvCacheDtype::Turbo8``
+with ``turbo8_data_bytes`` / ``turbo8_scale_bytes``: one E4M3 byte per element,
+then one BF16 scale (2 bytes) per group of 16: e + 2e/16.
 "metrale_model_layers/layers/ops/kv_cache_bf16k_turbov.rs", module
 invariants: element order ``[num_blocks, block_size, num_kv_heads,
 head_dim]``; a V block is its code section followed by its scales; K and V
@@ -20,21 +22,23 @@ Readings:
     from the low bits up, turbo3 packs each 8 elements into a 24-bit
     little-endian word, element j at bits 3j.
   * The scale of group g = e' / 16 is byte g of the scale section, which
-    starts right after the code section (``data_section_bytes``).
+    starts right after the code section (``data_section_bytes``); turbo8's
+    BF16 scale of group g is the little-endian 2-byte word at 2g.
   * The block stride is the block's byte size rounded up to 16 bytes.
 """
 from __future__ import annotations
 
 import dataclasses
 
-BITS = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4}
-TURBO = ("turbo2", "turbo3", "turbo4")
+BITS = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8}
+TURBO = ("turbo2", "turbo3", "turbo4")     # Lloyd-Max codes, one E4M3 scale byte per group
+ROTATED = TURBO + ("turbo8",)              # turbo8: E4M3 values, one BF16 scale per group
 GROUP = 16
 
 
 def is_rotated(fmt: str) -> bool:
     """``is_wht_rotated``: true for the turbo sides."""
-    return fmt in TURBO
+    return fmt in ROTATED
 
 
 @dataclasses.dataclass(frozen=True)
@@ -58,7 +62,10 @@ class Side:
 
     @property
     def row_scales(self) -> int:
-        return self.head_dim // GROUP if self.fmt in TURBO else 0
+        """Scale bytes of one (position, kv head) row."""
+        if self.fmt in TURBO:
+            return self.head_dim // GROUP
+        return 2 * self.head_dim // GROUP if self.fmt == "turbo8" else 0
 
 
 def side_layout(fmt: str, block_size: int, num_kv_heads: int, head_dim: int) -> Side:
@@ -73,6 +80,8 @@ def side_layout(fmt: str, block_size: int, num_kv_heads: int, head_dim: int) -> 
         data, scales = e * 3 // 8, e // GROUP
     elif fmt == "turbo2":
         data, scales = e // 4, e // GROUP
+    elif fmt == "turbo8":
+        data, scales = e, 2 * (e // GROUP)
     else:
         raise ValueError(fmt)
     stride = (data + scales + 15) // 16 * 16

@@ -21,6 +21,14 @@ brackets, the pages are silent on them):
          k = 1..L-1 with y >= RN32(s_q * t_k) [nearest centroid, ties go
          up]; codes packed low bits first; sigma stored in the scale
          section.
+  turbo8 ("WHT + FP8 E4M3" data, "per-group BF16 scales",
+         ``KvCacheDtype::Turbo8`` and ``turbo8_scale_bytes``): y as for
+         turbo; per group of 16: a = max|y|, s = RN32(a * RN32(1/448))
+         [absmax / largest E4M3 value, the same rule with 448 for the
+         largest centroid], sigma = RNE_bf16(s), s_q = value(sigma); byte =
+         E4M3(RN32(y / s_q)) [IEEE division and the fp8 side's E4M3
+         rounding; a zero scale (an all-zero group) gives zero bytes];
+         sigma stored as a little-endian 2-byte word.
 Tokens whose slot is negative write nothing [the slot sentinel].
 """
 from __future__ import annotations
@@ -29,6 +37,8 @@ import numpy as np
 
 from . import codecs, codebook, wht
 from .layout import BITS, GROUP, TURBO, Side
+
+E4M3_INV_MAX = np.float32(1.0 / codecs.E4M3_MAX)   # RN32(1/448)
 
 _TABLES = {}
 
@@ -75,8 +85,22 @@ def turbo_quantize(x_f32: np.ndarray, fmt: str):
     return codes.reshape(N, hd), sigma
 
 
+def turbo8_quantize(x_f32: np.ndarray):
+    """Rotated rows -> (E4M3 bytes [N, hd] uint8, BF16 scale patterns [N, hd/16] uint16)."""
+    N, hd = x_f32.shape
+    y = codecs.bf16_round(wht.wht_f32(x_f32))
+    yg = y.reshape(N, hd // GROUP, GROUP)
+    a = np.max(np.abs(yg), axis=-1)
+    s = (a * E4M3_INV_MAX).astype(np.float32)
+    sigma = codecs.bf16_round_bits(s)
+    sq = codecs.bf16_bits_to_f32(sigma)
+    v = np.zeros_like(yg)
+    np.divide(yg, sq[..., None], out=v, where=sq[..., None] > 0)
+    return codecs.e4m3_encode(v.astype(np.float32)).reshape(N, hd), sigma
+
+
 def quantize_rows(x_bits: np.ndarray, fmt: str, scale: float = 1.0):
-    """bf16 rows (uint16 [N, hd]) -> (code bytes [N, row_bytes], scale bytes [N, hd/16])."""
+    """bf16 rows (uint16 [N, hd]) -> (code bytes [N, row_bytes], scale bytes [N, row_scales])."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     N, hd = x_bits.shape
     if fmt == "bf16":
@@ -88,6 +112,9 @@ def quantize_rows(x_bits: np.ndarray, fmt: str, scale: float = 1.0):
     if fmt in TURBO:
         codes, sigma = turbo_quantize(x, fmt)
         return pack_codes(codes, BITS[fmt]), sigma
+    if fmt == "turbo8":
+        data, sigma = turbo8_quantize(x)
+        return data, np.ascontiguousarray(sigma.astype("<u2")).view(np.uint8).reshape(N, -1)
     raise ValueError(fmt)
 
 

@@ -42,6 +42,10 @@ def _dequant_contig(bits, fmt, scale):
         v = codecs.bf16_bits_to_f32(data.view(np.uint16)).astype(np.float64)
     elif fmt == "fp8":
         v = codecs.e4m3_decode(data).astype(np.float64) * np.float64(np.float32(scale))
+    elif fmt == "turbo8":
+        sq = (sc[:, 0::2].astype(np.uint32) | (sc[:, 1::2].astype(np.uint32) << 8)) << 16
+        v = codecs.e4m3_decode(data).astype(np.float64) * \
+            np.repeat(sq.astype(np.uint32).view(np.float32).astype(np.float64), 16, axis=1)
     else:
         codes = W.unpack_codes(data, layout.BITS[fmt], hd)
         v = W.tables(fmt)["centroids"].astype(np.float64)[codes] * \
@@ -51,7 +55,8 @@ def _dequant_contig(bits, fmt, scale):
 
 PAIRS = [("bf16", "bf16"), ("fp8", "fp8"), ("turbo2", "turbo2"), ("turbo3", "turbo3"),
          ("turbo4", "turbo4"), ("turbo4", "turbo3"), ("bf16", "turbo4"), ("bf16", "turbo3"),
-         ("bf16", "turbo2"), ("fp8", "turbo4"), ("fp8", "turbo3"), ("fp8", "turbo2")]
+         ("bf16", "turbo2"), ("fp8", "turbo4"), ("fp8", "turbo3"), ("fp8", "turbo2"),
+         ("turbo8", "turbo8"), ("turbo4", "turbo8"), ("turbo3", "turbo8"), ("bf16", "turbo8")]
 
 
 @pytest.mark.parametrize("kf,vf", PAIRS)

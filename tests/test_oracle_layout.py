@@ -9,14 +9,15 @@ from oracle import layout
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_sizes.json")))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo2", "turbo3", "turbo4"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8"])
 @pytest.mark.parametrize("bs,nkv,hd", [(16, 8, 128), (16, 2, 64), (16, 4, 256), (32, 8, 128), (1, 1, 64)])
 def test_block_bytes_closed_form(fmt, bs, nkv, hd):
     s = layout.side_layout(fmt, bs, nkv, hd)
     e = bs * nkv * hd
     # block_bytes_dims arms, evaluated by hand
+    # (turbo8: turbo8_data_bytes = e, turbo8_scale_bytes = 2 bytes per group of 16)
     expect = {"bf16": e * 2, "fp8": e, "turbo4": e // 2 + e // 16,
-              "turbo3": e * 3 // 8 + e // 16, "turbo2": e // 4 + e // 16}[fmt]
+              "turbo3": e * 3 // 8 + e // 16, "turbo2": e // 4 + e // 16, "turbo8": e + 2 * (e // 16)}[fmt]
     assert s.data_section_bytes + s.scale_bytes == expect
     assert s.block_stride_bytes % 16 == 0 and 0 <= s.block_stride_bytes - expect < 16
 
@@ -50,5 +51,15 @@ def test_workload_strides():
 
 
 def test_rotation_flags():
-    assert [layout.is_rotated(f) for f in ("bf16", "fp8", "turbo2", "turbo3", "turbo4")] == \
-        [False, False, True, True, True]
+    assert [layout.is_rotated(f) for f in ("bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8")] == \
+        [False, False, True, True, True, True]
+
+
+def test_turbo8_sizes():
+    # 1 byte per element plus a 2-byte BF16 scale per 16: 9 bits per element,
+    # 6.25% above fp8 ("~6% extra cache memory")
+    s = layout.side_layout("turbo8", 16, 8, 128)
+    e = 16 * 8 * 128
+    assert (s.data_section_bytes, s.scale_bytes) == (e, e // 8)
+    assert 8 * (s.data_section_bytes + s.scale_bytes) / e == 9.0
+    assert s.row_bytes == 128 and s.row_scales == 16

@@ -93,6 +93,57 @@ def test_fp8_rows_match_torch():
     assert np.array_equal(data, ref) and sc.shape == (500, 0)
 
 
+def _turbo8_reference(x):
+    """The turbo8 rule through torch's own bf16 / float8_e4m3fn conversions."""
+    y = torch.from_numpy(codecs.bf16_round(wht.wht_f32(x)))
+    n, hd = y.shape
+    yg = y.reshape(n, hd // 16, 16)
+    a = yg.abs().amax(-1)
+    s = a * torch.tensor(1.0 / 448.0, dtype=torch.float32)
+    sig = s.to(torch.bfloat16)
+    sq = sig.to(torch.float32)
+    v = torch.where(sq[..., None] > 0, yg / sq.clamp_min(1e-45)[..., None], torch.zeros_like(yg))
+    codes = v.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.reshape(n, hd).numpy(), sig.view(torch.int16).numpy().view(np.uint16), y.numpy(), sq.numpy()
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+def test_turbo8_matches_torch_conversions(hd):
+    x = codecs.bf16_bits_to_f32(_rows(400, hd, 11 + hd))
+    codes, sigma = W.turbo8_quantize(x)
+    rc, rs, _, _ = _turbo8_reference(x)
+    assert np.array_equal(sigma, rs)
+    assert np.array_equal(codes, rc)
+
+
+def test_turbo8_properties():
+    x = codecs.bf16_bits_to_f32(_rows(300, 128, 21))
+    x[7] = 0.0                                   # an all-zero row: zero scales, zero bytes
+    codes, sigma = W.turbo8_quantize(x)
+    y = codecs.bf16_round(wht.wht_f32(x)).astype(np.float64)
+    sq = codecs.bf16_bits_to_f32(sigma).astype(np.float64)
+    assert np.all(sigma[7] == 0) and np.all(codes[7] == 0)
+    vals = codecs.e4m3_decode(codes).astype(np.float64).reshape(300, 8, 16)
+    yg = y.reshape(300, 8, 16)
+    # the group's largest magnitude lands on the largest E4M3 value (s_q is
+    # within 2^-9 of absmax/448, and 448 is 32 away from its neighbour 416)
+    idx = np.abs(yg).argmax(-1)
+    top = np.take_along_axis(np.abs(vals), idx[..., None], -1)[..., 0]
+    live = sq > 0
+    assert np.all(top[live] == 448.0)
+    # every element within E4M3's relative step (2^-4), or its subnormal step
+    err = np.abs(vals * sq[..., None] - yg)
+    assert np.all(err <= np.maximum(np.abs(yg) * 2.0 ** -4, sq[..., None] * 2.0 ** -9) * 1.0001)
+
+
+def test_turbo8_rows_carry_little_endian_scales():
+    x_bits = _rows(20, 128, 31)
+    data, sc = W.quantize_rows(x_bits, "turbo8")
+    codes, sigma = W.turbo8_quantize(codecs.bf16_bits_to_f32(x_bits))
+    assert np.array_equal(data, codes) and sc.shape == (20, 16)
+    assert np.array_equal(sc[:, 0::2].astype(np.uint16) | (sc[:, 1::2].astype(np.uint16) << 8), sigma)
+
+
 def test_bf16_rows_are_raw_bytes():
     x_bits = _rows(10, 64, 2)
     data, _ = W.quantize_rows(x_bits, "bf16")
@@ -100,7 +151,7 @@ def test_bf16_rows_are_raw_bytes():
 
 
 @pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo3", "turbo3"),
-                                   ("turbo4", "turbo3")])
+                                   ("turbo4", "turbo3"), ("turbo4", "turbo8"), ("turbo8", "turbo8")])
 def test_pool_placement(kf, vf):
     bs, nkv, hd, nb = 4, 2, 64, 6
     ks, vs = layout.pool_layout(kf, vf, bs, nkv, hd)
