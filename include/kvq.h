@@ -51,6 +51,12 @@ extern "C" {
  *                 every group of 16 elements is stored as 2/3/4-bit indices into
  *                 the Lloyd-Max codebook of a standard Gaussian, with one E4M3
  *                 scale byte (group absmax / largest centroid) per group.
+ *   KVQ_TURBO8    [kv_cache.rs] KvCacheDtype::Turbo8, turbo8_data_bytes /
+ *                 turbo8_scale_bytes: the row rotated and re-rounded as for
+ *                 turbo, then one OCP E4M3FN byte per element (value / group
+ *                 scale) and one BF16 scale per group of 16 (group absmax /
+ *                 448, round to nearest even), 2 bytes, little-endian, in the
+ *                 scale section.  An all-zero group stores zero bytes.
  * Rotated sides (turbo) make decode rotate the query (K side) and rotate the
  * output back (V side) -- [kv_cache.rs] is_wht_rotated. */
 typedef enum kvq_format {
@@ -58,7 +64,8 @@ typedef enum kvq_format {
   KVQ_FP8_E4M3 = 1,
   KVQ_TURBO2 = 2,
   KVQ_TURBO3 = 3,
-  KVQ_TURBO4 = 4
+  KVQ_TURBO4 = 4,
+  KVQ_TURBO8 = 8
 } kvq_format;
 
 typedef enum kvq_status {
@@ -164,7 +171,8 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
 /* Introspection (host only): the fp32 Lloyd-Max tables the turbo format uses.
  * centroids[0..L-1] ascending, thresholds[1..L-1] (midpoints; [0] = 0),
  * *inv_cmax = 1/largest centroid, *levels = L = 2^bits.  Buffers hold 16 floats.
- * Returns KVQ_ERR_INVALID_ARG for a non-turbo format or a NULL pointer. */
+ * Returns KVQ_ERR_INVALID_ARG for a format without a codebook (bf16, fp8,
+ * turbo8) or a NULL pointer. */
 int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax,
                  uint32_t* levels);
 

@@ -15,8 +15,11 @@ constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a sp
 constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 
-bool valid_format(int32_t f) { return f >= KVQ_BF16 && f <= KVQ_TURBO4; }
-bool is_turbo(int32_t f) { return f >= KVQ_TURBO2; }
+bool valid_format(int32_t f) { return (f >= KVQ_BF16 && f <= KVQ_TURBO4) || f == KVQ_TURBO8; }
+bool is_turbo(int32_t f) { return f >= KVQ_TURBO2; }  // rotated sides
+bool has_codebook(int32_t f) { return f >= KVQ_TURBO2 && f <= KVQ_TURBO4; }
+// scale bytes per group of 16 elements: E4M3 for the codebook formats, BF16 for turbo8
+uint64_t scale_bytes_per_group(int32_t f) { return has_codebook(f) ? 1u : f == KVQ_TURBO8 ? 2u : 0u; }
 uint32_t format_bits(int32_t f) { return f == KVQ_BF16 ? 16u : f == KVQ_FP8_E4M3 ? 8u : uint32_t(f); }
 bool pow2(uint64_t x) { return x && !(x & (x - 1)); }
 uint32_t log2u(uint64_t x) {
@@ -95,7 +98,7 @@ int layout_impl(int32_t kf, int32_t vf, uint32_t bs, uint32_t nkv, uint32_t hd, 
   uint64_t data[2], stride[2];
   for (int i = 0; i < 2; ++i) {
     data[i] = e * format_bits(fmts[i]) / 8;
-    const uint64_t bytes = data[i] + (is_turbo(fmts[i]) ? e / 16 : 0);
+    const uint64_t bytes = data[i] + e / 16 * scale_bytes_per_group(fmts[i]);
     stride[i] = (bytes + 15) / 16 * 16;
   }
   l.k_data_section_bytes = data[0];
@@ -303,6 +306,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO8: e = launch_split_turbo8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
@@ -312,6 +316,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_FP8_E4M3: e = launch_scores_fp8(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO2: e = launch_scores_turbo2(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO3: e = launch_scores_turbo3(int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_TURBO8: e = launch_scores_turbo8(int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);
@@ -320,7 +325,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
 }
 
 int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax, uint32_t* levels) {
-  if (!is_turbo(format) || !valid_format(format) || !centroids || !thresholds || !inv_cmax || !levels)
+  if (!has_codebook(format) || !centroids || !thresholds || !inv_cmax || !levels)
     return KVQ_ERR_INVALID_ARG;
   const Codebooks& cb = codebooks();
   const int b = format;

@@ -46,7 +46,9 @@ constexpr int kMaxSparseSplit = KVQ_MAX_SPARSE_SPLIT;
 template <int F>
 struct Fmt {
   static constexpr int bits = (F == KVQ_BF16) ? 16 : (F == KVQ_FP8_E4M3) ? 8 : F;
-  static constexpr bool turbo = F >= KVQ_TURBO2;
+  static constexpr bool turbo = F >= KVQ_TURBO2;             // rotated side
+  static constexpr bool cb = turbo && F != KVQ_TURBO8;       // Lloyd-Max codes (else E4M3 values)
+  static constexpr int sgb = cb ? 1 : (F == KVQ_TURBO8 ? 2 : 0);  // scale bytes per group of 16
 };
 
 // Lane geometry for a head size and a number of dims per lane.
@@ -135,18 +137,30 @@ __device__ __forceinline__ void load_lane(const uint8_t* __restrict__ blk, uint3
     r.w[0] = uint32_t(v);
     if constexpr (Raw<F, D>::words > 1) r.w[1] = uint32_t(v >> 32) & 0xFFFFu;
   }
-  // The scale byte is read as the aligned dword that holds it (scale_shift
-  // selects it at the use), so no byte extension sits next to the load.
-  if constexpr (Fmt<F>::turbo)
-    r.sc = *reinterpret_cast<const uint32_t*>(blk + data_bytes + uint64_t(row) * (HD / 16) + (((t * D) / 16) & ~3));
-  else
+  // The scale (an E4M3 byte, or turbo8's BF16 word) is read as the aligned
+  // dword that holds it (scale_shift selects it at the use), so no byte
+  // extension sits next to the load.
+  if constexpr (Fmt<F>::turbo) {
+    constexpr int SG = Fmt<F>::sgb;
+    r.sc = *reinterpret_cast<const uint32_t*>(blk + data_bytes + uint64_t(row) * (HD / 16 * SG) +
+                                             ((((t * D) / 16) * SG) & ~3));
+  } else {
     r.sc = 0;
+  }
 }
 
-// Bit offset of a lane's scale byte inside the dword load_lane reads.
-template <int D>
+// Bit offset of a lane's scale inside the dword load_lane reads (SG scale
+// bytes per group).
+template <int D, int SG = 1>
 __device__ __forceinline__ uint32_t scale_shift(int t) {
-  return 8u * uint32_t(((t * D) / 16) & 3);
+  return 8u * uint32_t((((t * D) / 16) * SG) & 3);
+}
+
+// The group scale a lane reads: an E4M3 byte, or turbo8's BF16 word.
+template <int F>
+__device__ __forceinline__ float group_scale(uint32_t word, uint32_t shift) {
+  if constexpr (Fmt<F>::cb) return e4m3_decode(word >> shift);
+  else return __uint_as_float((word >> shift) << 16);
 }
 
 template <int F, int D>
@@ -192,6 +206,7 @@ struct QReg {
   uint32_t qp[packed ? G : 1][packed ? D / 2 : 1];
   float qf[packed ? 1 : G][packed ? 1 : D];
   uint32_t scsh;  // scale_shift of the lane (turbo K)
+  uint32_t vsh;   // ... of the V side (turbo V)
 };
 
 // Partial score of one lane for every head (before the T-lane sum).
@@ -222,9 +237,18 @@ __device__ __forceinline__ void lane_scores(const QReg<KF, D, G>& q, const Raw<K
     }
   } else {
     float kv[D];
+    if constexpr (Fmt<KF>::cb) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) kv[i] = kcen[code_at<Fmt<KF>::bits, D>(k.w, i)];
-    const float sq = e4m3_decode(k.sc >> q.scsh);
+      for (int i = 0; i < D; ++i) kv[i] = kcen[code_at<Fmt<KF>::bits, D>(k.w, i)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(k.w[i]), false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(k.w[i]), true);
+        kv[4 * i] = lo.x; kv[4 * i + 1] = lo.y; kv[4 * i + 2] = hi.x; kv[4 * i + 3] = hi.y;
+      }
+    }
+    const float sq = group_scale<KF>(k.sc, q.scsh);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float s = 0.0f;
@@ -254,10 +278,18 @@ __device__ __forceinline__ void v_values(const Raw<VF, D>& v, const float* __res
       const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v.w[i]), true);
       x[4 * i] = lo.x; x[4 * i + 1] = lo.y; x[4 * i + 2] = hi.x; x[4 * i + 3] = hi.y;
     }
-  } else {
+  } else if constexpr (Fmt<VF>::cb) {
 #pragma unroll
     for (int i = 0; i < D; ++i) x[i] = vcen[code_at<Fmt<VF>::bits, D>(v.w, i)];
     sq = e4m3_decode(v.sc >> scsh);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(v.w[i]), false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(v.w[i]), true);
+      x[4 * i] = lo.x; x[4 * i + 1] = lo.y; x[4 * i + 2] = hi.x; x[4 * i + 3] = hi.y;
+    }
+    sq = group_scale<VF>(v.sc, scsh);
   }
 }
 
@@ -321,7 +353,8 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
                                          uint32_t g, int pb, int pe, int t, QReg<KF, D, G>& q) {
   const int tid = threadIdx.x;
   const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
-  q.scsh = scale_shift<D>(t);
+  q.scsh = scale_shift<D, Fmt<KF>::sgb == 2 ? 2 : 1>(t);
+  q.vsh = scale_shift<D, Fmt<VF>::sgb == 2 ? 2 : 1>(t);
   if constexpr (!Fmt<KF>::turbo) {
     // bf16 query pairs straight from memory (the score scale is applied
     // later); requested first so that their latency overlaps the page table's
@@ -336,8 +369,8 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
     }
   }
   if (tid < 16) {
-    if constexpr (Fmt<KF>::turbo) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
-    if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
+    if constexpr (Fmt<KF>::cb) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
+    if constexpr (Fmt<VF>::cb) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
   {
     const int first = pb >> a.log2_bs;
@@ -466,7 +499,7 @@ __device__ __forceinline__ void dense_chunk(const Raw<KF, D> (&kr)[Geo<HD, D>::U
     Raw<VF, GE::D> vm = vr[u];
     mask_raw(vm, ok[u]);  // a masked position adds 0 * (finite value)
     float x[GE::D], sq;
-    v_values<VF, GE::D>(vm, vcen, x, sq, q.scsh);  // V lanes hold the same dims as K lanes
+    v_values<VF, GE::D>(vm, vcen, x, sq, q.vsh);  // V lanes hold the same dims as K lanes
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float p = ok[u] ? fast_exp2(sc[u][h] - st.m[h]) : 0.0f;
@@ -859,7 +892,7 @@ __device__ __forceinline__ void load_record(const uint32_t* src, uint32_t (&rw)[
 template <int VF, int HD>
 struct VStage {
   static constexpr int RB = HD * Fmt<VF>::bits / 8;                 // code bytes per row
-  static constexpr int SB = Fmt<VF>::turbo ? HD / 16 : 0;           // scale bytes per row
+  static constexpr int SB = HD / 16 * Fmt<VF>::sgb;                // scale bytes per row
   static constexpr int CK = RB % 16 == 0 ? 16 : RB % 8 == 0 ? 8 : 4;  // load granule
   static constexpr int NCK = RB / CK;
   static constexpr int GPL = NCK < 4 ? NCK : 4;
@@ -906,7 +939,8 @@ __device__ __forceinline__ void staged_lane(const uint32_t* rw, int q, int t, Ra
     r.w[0] = uint32_t(v);
     if constexpr (Raw<F, D>::words > 1) r.w[1] = uint32_t(v >> 32) & 0xFFFFu;
   }
-  if constexpr (Fmt<F>::turbo) r.sc = rw[(VS::RPP * VS::CS + q * VS::SB + (((t * D) / 16) & ~3)) / 4];
+  if constexpr (Fmt<F>::turbo)
+    r.sc = rw[(VS::RPP * VS::CS + q * VS::SB + ((((t * D) / 16) * Fmt<F>::sgb) & ~3)) / 4];
   else r.sc = 0;
 }
 
@@ -940,9 +974,12 @@ __device__ __forceinline__ void stage_rows(const DecodeArgs& a, const KeptT* kep
   if constexpr (VS::SB > 0) {
     const uint8_t* p = blk + a.v_data + uint64_t(row) * VS::SB;
     if (part == 0) {
-      if constexpr (VS::SB == 16) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-        sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+      if constexpr (VS::SB % 16 == 0) {
+#pragma unroll
+        for (int i = 0; i < VS::SB / 16; ++i) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(p + 16 * i);
+          sc[4 * i] = v.x; sc[4 * i + 1] = v.y; sc[4 * i + 2] = v.z; sc[4 * i + 3] = v.w;
+        }
       } else if constexpr (VS::SB == 8) {
         const u32x2 v = *reinterpret_cast<const u32x2*>(p);
         sc[0] = v.x; sc[1] = v.y;
@@ -1007,7 +1044,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   uint32_t spec[RS];
   load_record<G>(a.crec + ((sbase * kWaves + w) * a.seg_cap + lane) * RS, spec);
   if (tid < 16) {
-    if constexpr (Fmt<VF>::turbo) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
+    if constexpr (Fmt<VF>::cb) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
   float runm = -INFINITY, runz = 0.0f;  // (threads < G) running stats of head tid
   for (int kb = 0; kb < ns; kb += kMaxStatSplits) {
@@ -1048,7 +1085,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
     for (int i = 0; i < D; ++i) acc[h][i] = 0.0f;
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
-  const uint32_t vsh = scale_shift<D>(t);
+  const uint32_t vsh = scale_shift<D, Fmt<VF>::sgb == 2 ? 2 : 1>(t);
   using VS = VStage<VF, HD>;
   auto& kept = sm.u.live.kept[w];
   uint32_t* rows = sm.u.live.rows[w];
@@ -1249,6 +1286,7 @@ hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t n
     case KVQ_TURBO2: return launch_split_hd<KF, KVQ_TURBO2>(hd, g, a, nwg, st);
     case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3>(hd, g, a, nwg, st);
     case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4>(hd, g, a, nwg, st);
+    case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

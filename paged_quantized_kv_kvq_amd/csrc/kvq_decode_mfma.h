@@ -61,17 +61,19 @@ constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
 template <int KF, int VF, int HD, int G>
 struct MfmaGeo {
   static constexpr int NG = (G + 3) / 4;                    // head groups of four
-  static constexpr bool KT = Fmt<KF>::turbo;                // rotated, codebook K
+  static constexpr bool KT = Fmt<KF>::turbo;                // rotated K (codebook codes or E4M3 values)
   static constexpr int KQ = HD / 4;                         // K dims per lane (one quarter)
   static constexpr int KSTEPS = HD / 16;                    // 4-dim steps per quarter (bf16 / fp8 K)
   static constexpr int RBK = HD * Fmt<KF>::bits / 8;        // K code bytes per row
   static constexpr int KQB = RBK / 4;                       // K bytes per lane per chunk
   static constexpr int KGQ = KT ? KQ / 16 : 1;              // turbo K: scale groups per quarter
+  static constexpr int KSG = Fmt<KF>::sgb;                  // ... bytes per group scale
+  static constexpr int KSW = KT ? (KGQ * KSG + 3) / 4 : 1;  // ... words holding the quarter's scales
   static constexpr int DV = HD / 64;                        // V dims per lane
   static constexpr int RBC = HD * Fmt<VF>::bits / 8;        // V code bytes per row
   static constexpr int WR = RBC / 4;                        // ... in words
   static constexpr int NGS = Fmt<VF>::turbo ? HD / 16 : 1;  // V scale groups per row (1: no scales)
-  static constexpr int SWL = Fmt<VF>::turbo ? HD / 64 : 0;  // V scale words of a row (4 groups each)
+  static constexpr int SWL = HD / 16 * Fmt<VF>::sgb / 4;    // V scale words of a row
   static constexpr int NSD = (kChunk * WR + kWave - 1) / kWave;  // staged code words per lane
   static constexpr bool ok = mfma_split_ok(KF, VF, HD);
 };
@@ -95,8 +97,8 @@ struct MfmaSmem {
   uint64_t vbase[kMaxPages];  // ... and in the V pool
   float vcen[16];
   // turbo sides: centroids of every pair of adjacent codes (index lo | hi << bits)
-  f32x2 vpair[Fmt<VF>::turbo && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
-  f32x2 kpair[Fmt<KF>::turbo ? 1 << (2 * Fmt<KF>::bits) : 1];
+  f32x2 vpair[Fmt<VF>::cb && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
+  f32x2 kpair[Fmt<KF>::cb ? 1 << (2 * Fmt<KF>::bits) : 1];
   union {
     MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
     // turbo K, before the chunk loop: each wave's query rows, rotated in place
@@ -105,13 +107,13 @@ struct MfmaSmem {
 };
 
 // One chunk's raw bytes in a lane's registers: its K quarter (turbo K: and
-// the word that holds its quarter's scale bytes), its share of the chunk's V
-// code words, and the V scale words of position lane % 16.
+// the words that hold its quarter's scales), its share of the chunk's V code
+// words, and the V scale words of position lane % 16.
 template <int KF, int VF, int HD, int G>
 struct MfmaChunk {
   using MG = MfmaGeo<KF, VF, HD, G>;
   uint32_t k[MG::KQB / 4];
-  uint32_t ks;
+  uint32_t ks[MG::KSW];
   uint32_t v[MG::NSD];
   uint32_t s[MG::SWL > 0 ? MG::SWL : 1];
 };
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       sm.kbase[i] = page * a.k_stride;
       sm.vbase[i] = page * a.v_stride;
     }
-    if constexpr (Fmt<VF>::turbo) {
+    if constexpr (Fmt<VF>::cb) {
       constexpr int BITS = Fmt<VF>::bits;
       if (tid < 16) sm.vcen[tid] = tid < (1 << BITS) ? a.cb.centroid[VF - 2][tid] : 0.0f;
       if constexpr (DV >= 2) {
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         }
       }
     }
-    if constexpr (MG::KT) {
+    if constexpr (Fmt<KF>::cb) {
       constexpr int BITS = Fmt<KF>::bits;
       for (int e = tid; e < (1 << (2 * BITS)); e += int(blockDim.x)) {
         sm.kpair[e].x = a.cb.centroid[KF - 2][e & ((1 << BITS) - 1)];
@@ -256,9 +258,10 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   // row i/WR for i = lane + 64 n; the V scale words of row lane%16
   const uint32_t bmask = (1u << a.log2_bs) - 1u;
   const uint32_t koff = ((uint32_t(lane) & 15u) * nkv + g) * MG::RBK + (uint32_t(lane) >> 4) * MG::KQB;
-  const uint32_t ksoff = a.k_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16) +
-                         ((uint32_t(lane) >> 4) * MG::KGQ / 4u) * 4u;
-  const int ksh = int(((uint32_t(lane) >> 4) * MG::KGQ) % 4u) * 8;  // bit offset of the first group's byte
+  // (the quarter's scales start at byte (lane/16) * KGQ * KSG of the row's scales)
+  const uint32_t ksb = (uint32_t(lane) >> 4) * MG::KGQ * MG::KSG;
+  const uint32_t ksoff = a.k_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16 * MG::KSG) + (ksb & ~3u);
+  const int ksh = int(ksb & 3u) * 8;  // bit offset of the first group's scale in ks[0]
   uint32_t voff[MG::NSD];
   int vrow[MG::NSD];
 #pragma unroll
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     vrow[n] = min(i / MG::WR, kChunk - 1);
     voff[n] = (uint32_t(vrow[n]) * nkv + g) * MG::RBC + uint32_t(i % MG::WR) * 4u;
   }
-  const uint32_t soff = a.v_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16);
+  const uint32_t soff = a.v_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16 * Fmt<VF>::sgb);
   const int cs = sp.pb & ~(kChunk - 1);
   const int clast = (sp.pe - 1) & ~(kChunk - 1);
   auto load = [&](int c, MfmaChunk<KF, VF, HD, G>& ck) {
@@ -277,12 +280,18 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     const uint64_t kpage = uniform_u64(sm.kbase[pg]);
     const uint64_t vb = uniform_u64(sm.vbase[pg]);
     load_words<MG::KQB>(a.k_cache + kpage + uint64_t(within) * nkv * MG::RBK + koff, ck.k);
-    if constexpr (MG::KT) ck.ks = load4(a.k_cache + kpage + uint64_t(within) * nkv * (HD / 16) + ksoff);
-    else ck.ks = 0u;
+    if constexpr (MG::KT) {
+#pragma unroll
+      for (int i = 0; i < MG::KSW; ++i)
+        ck.ks[i] = load4(a.k_cache + kpage + uint64_t(within) * nkv * (HD / 16 * MG::KSG) + ksoff + 4 * i);
+    } else {
+      ck.ks[0] = 0u;
+    }
     const uint8_t* vp = a.v_cache + vb + uint64_t(within) * nkv * MG::RBC;
 #pragma unroll
     for (int n = 0; n < MG::NSD; ++n) ck.v[n] = load4(vp + voff[n]);
-    if constexpr (MG::SWL > 0) load_words<4 * MG::SWL>(a.v_cache + vb + uint64_t(within) * nkv * (HD / 16) + soff, ck.s);
+    if constexpr (MG::SWL > 0)
+      load_words<4 * MG::SWL>(a.v_cache + vb + uint64_t(within) * nkv * (HD / 16 * Fmt<VF>::sgb) + soff, ck.s);
     else ck.s[0] = 0u;
   };
 
@@ -327,6 +336,32 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 #pragma unroll
       for (int k = 0; k < MG::KSTEPS; ++k) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[k], d, 0, 0, 0);
       return d;
+    } else if constexpr (!Fmt<KF>::cb) {
+      // turbo8: E4M3 values of the quarter, one accumulator per scale group
+      f32x4 dg[MG::KGQ];
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) dg[gq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // word i of each group's 16 bytes
+#pragma unroll
+        for (int gq = 0; gq < MG::KGQ; ++gq) {
+          const uint32_t wd = ck.k[gq * 4 + i];
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), true);
+          const int d0 = gq * 16 + 4 * i;
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0], lo.x, dg[gq], 0, 0, 0);
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 1], lo.y, dg[gq], 0, 0, 0);
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 2], hi.x, dg[gq], 0, 0, 0);
+          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 3], hi.y, dg[gq], 0, 0, 0);
+        }
+      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) {
+        const int bit = ksh + 16 * gq;  // BF16 scale of group gq
+        const float sc = __uint_as_float(((ck.ks[bit / 32] >> (bit % 32)) & 0xFFFFu) << 16);
+        d += sc * dg[gq];
+      }
+      return d;
     } else {
       // code pair p (dims 2p, 2p + 1 of the quarter) sits at bits 2 BITS p of
       // the quarter's little-endian bit stream; one accumulator per scale
@@ -356,7 +391,8 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int gq = 0; gq < MG::KGQ; ++gq) {
-        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(ck.ks >> (ksh + 8 * gq)), 0);
+        const int bit = ksh + 8 * gq;
+        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(ck.ks[bit / 32] >> (bit % 32)), 0);
         d += sc * dg[gq];
       }
       return d;
@@ -364,14 +400,14 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   };
 
   auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G>& ck) {
-    // 1. stage the chunk's V codes in LDS (bf16 / fp8 V: rows outside the
-    //    split as zeros, whatever bytes they hold)
+    // 1. stage the chunk's V codes in LDS (bf16 / fp8 / turbo8 V: rows
+    //    outside the split as zeros, whatever bytes they hold)
 #pragma unroll
     for (int n = 0; n < MG::NSD; ++n) {
       const int i = lane + n * kWave;
       if (i < kChunk * MG::WR) {
         uint32_t word = ck.v[n];
-        if constexpr (!Fmt<VF>::turbo) {
+        if constexpr (!Fmt<VF>::cb) {  // values (not codes) may be NaN bytes
           const int j = c + vrow[n];
           word = (j >= sp.pb && j < sp.pe) ? word : 0u;
         }
@@ -394,7 +430,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       m[hg] = mn;
       const float p = fast_exp2(sc - mn);  // 0 where masked
       lsum[hg] = fmaf(lsum[hg], al, p);
-      if constexpr (MG::SWL > 0) {
+      if constexpr (MG::SWL > 0 && Fmt<VF>::cb) {
         // operand A per scale group: p x the group's scale (outside the
         // split the scale words are zeroed: p = 0 times a garbage NaN
         // scale would not be 0)
@@ -407,6 +443,14 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
           pt[hg][4 * sw + 1][lane >> 4][lane & 15] = p * lo.y;
           pt[hg][4 * sw + 2][lane >> 4][lane & 15] = p * hi.x;
           pt[hg][4 * sw + 3][lane >> 4][lane & 15] = p * hi.y;
+        }
+      } else if constexpr (MG::SWL > 0) {
+        // turbo8: two BF16 scales per word
+#pragma unroll
+        for (int sw = 0; sw < MG::SWL; ++sw) {
+          const uint32_t sword = ok ? ck.s[sw] : 0u;
+          pt[hg][2 * sw][lane >> 4][lane & 15] = p * __uint_as_float(sword << 16);
+          pt[hg][2 * sw + 1][lane >> 4][lane & 15] = p * __uint_as_float(sword & 0xFFFF0000u);
         }
       } else {
         pt[hg][0][lane >> 4][lane & 15] = p;
@@ -440,7 +484,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         pa[hg][4] = x1.x; pa[hg][5] = x1.y; pa[hg][6] = x1.z; pa[hg][7] = x1.w;
       }
       float b[8][DV];
-      if constexpr (Fmt<VF>::turbo) {
+      if constexpr (Fmt<VF>::cb) {
         constexpr int BITS = Fmt<VF>::bits;
         const int bit = lane * DV * BITS;
         const int wd = bit / 32, sh = bit % 32;
@@ -490,7 +534,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
           const uint64_t all = (uint64_t(cw1[q]) << 32 | cw0[q]) >> ((byte % 4) * 8);
 #pragma unroll
           for (int v = 0; v < DV; ++v) {
-            if constexpr (VF == KVQ_FP8_E4M3) {
+            if constexpr (Fmt<VF>::bits == 8) {  // fp8, turbo8: E4M3 values
               const f32x2 x = __builtin_amdgcn_cvt_pk_f32_fp8(int(uint32_t(all >> (8 * (v & ~1)))), false);
               b[q][v] = (v & 1) ? x.y : x.x;
             } else {
@@ -520,7 +564,8 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
     for (int k = 0; k < MG::KQB / 4; ++k) cb[i].k[k] = 0u;
-    cb[i].ks = 0u;
+#pragma unroll
+    for (int k = 0; k < MG::KSW; ++k) cb[i].ks[k] = 0u;
 #pragma unroll
     for (int k = 0; k < MG::NSD; ++k) cb[i].v[k] = 0u;
 #pragma unroll

@@ -46,6 +46,7 @@ hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t 
     case KVQ_TURBO2: return sparse_hd<KVQ_TURBO2>(hd, g, a, nwg, st);
     case KVQ_TURBO3: return sparse_hd<KVQ_TURBO3>(hd, g, a, nwg, st);
     case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, nwg, st);
+    case KVQ_TURBO8: return sparse_hd<KVQ_TURBO8>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

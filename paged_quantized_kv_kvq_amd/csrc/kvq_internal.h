@@ -55,7 +55,7 @@ __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf;
   const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf;
   const int kqb = hd * kbits / 32;  // K bytes per lane and chunk (a quarter of a row)
-  const bool kturbo = kf == KVQ_TURBO2 || kf == KVQ_TURBO3 || kf == KVQ_TURBO4;
+  const bool kturbo = kf >= KVQ_TURBO2;  // rotated K (codebook codes or turbo8's E4M3 values)
   return hd * vbits / 8 <= 128 &&
          (kturbo ? (kqb % 4 == 0 && kqb <= 32 && hd / 4 >= 16) : (kqb <= 64 && kqb % 16 == 0));
 }
@@ -148,12 +148,14 @@ hipError_t launch_split_fp8(int vf, int hd, int g, const DecodeArgs& a, uint32_t
 hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 
 hipError_t launch_scores_bf16(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_scores_turbo8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 

@@ -4,7 +4,8 @@
 // reshape_and_cache_bf16k_turbo{2,3,4}v (slot_mapping scatter of [tokens,
 // kv_heads, head_dim] rows); "spark_runtime/kv_cache.rs", KvCacheDtype
 // (bf16 copy, fp8 E4M3 with a per-tensor scale, turbo: wht_bf16_inplace then
-// Lloyd-Max codes with one E4M3 scale per 16 elements).
+// Lloyd-Max codes with one E4M3 scale per 16 elements; Turbo8: the same
+// rotation, then E4M3 values with one BF16 scale per 16 elements).
 //
 // One wave64 writes one (token, kv head) row of one side: head_dim/64 values
 // per lane.  The rotation is done in registers: butterfly strides below the
@@ -16,6 +17,8 @@
 //   butterflies (ascending stride) -> * RN32(1/sqrt(d)) -> round to bf16 ->
 //   group absmax -> s = absmax * RN32(1/c_max) -> E4M3(s) = sigma, s_q ->
 //   code = #{k : y >= s_q * t_k} -> little-endian bit packing.
+// Turbo8 after the rounding to bf16: group absmax -> s = absmax * RN32(1/448)
+//   -> bf16(s) = sigma, s_q -> byte = E4M3(y / s_q) (0 for s_q = 0).
 #include "kvq_device.h"
 
 namespace kvq {
@@ -46,13 +49,12 @@ __device__ __forceinline__ void store_bytes(uint8_t* __restrict__ dst, int lane,
   else reinterpret_cast<uint32_t*>(dst)[lane] = v;
 }
 
-template <int HD, int BITS>
-__device__ __forceinline__ void write_turbo(const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
-                                            uint32_t row, uint64_t data_bytes, const WriteArgs& a,
-                                            int lane) {
+// The lane's E values of the row after the rotation and the rounding to
+// bf16; returns the absmax of the lane's group of 16.
+template <int HD>
+__device__ __forceinline__ float rotate_row(const uint32_t (&raw)[HD / 64], float (&y)[HD / 64],
+                                            const WriteArgs& a, int lane) {
   constexpr int E = HD / 64;
-  constexpr int L = 1 << BITS;
-  float y[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) y[e] = bf16_bits_to_float(raw[e]);
   // in-lane butterflies (stride < E)
@@ -82,7 +84,17 @@ __device__ __forceinline__ void write_turbo(const uint32_t (&raw)[HD / 64], uint
     y[e] = round_to_bf16(y[e] * a.wht_scale);
     amax = fmaxf(amax, fabsf(y[e]));
   }
-  amax = group_max<16 / E>(amax);  // one group of 16 elements = 16/E lanes
+  return group_max<16 / E>(amax);  // one group of 16 elements = 16/E lanes
+}
+
+template <int HD, int BITS>
+__device__ __forceinline__ void write_turbo(const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
+                                            uint32_t row, uint64_t data_bytes, const WriteArgs& a,
+                                            int lane) {
+  constexpr int E = HD / 64;
+  constexpr int L = 1 << BITS;
+  float y[E];
+  const float amax = rotate_row<HD>(raw, y, a, lane);
   const float s = amax * a.cb.inv_cmax[BITS - 2];
   const uint32_t sigma = e4m3_encode(s);
   const float sq = e4m3_decode(sigma);
@@ -120,6 +132,25 @@ __device__ __forceinline__ void write_turbo(const uint32_t (&raw)[HD / 64], uint
 }
 
 template <int HD>
+__device__ __forceinline__ void write_turbo8(const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
+                                             uint32_t row, uint64_t data_bytes, const WriteArgs& a, int lane) {
+  constexpr int E = HD / 64;
+  constexpr float kInvE4m3Max = 1.0f / 448.0f;  // RN32(1/448)
+  float y[E];
+  const float amax = rotate_row<HD>(raw, y, a, lane);
+  const float s = amax * kInvE4m3Max;
+  const float sq = round_to_bf16(s);
+  const uint32_t sigma = __float_as_uint(sq) >> 16;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) packed |= (sq > 0.0f ? e4m3_encode(y[e] / sq) : 0u) << (8 * e);
+  store_bytes<E>(blk + uint64_t(row) * HD, lane, packed);
+  if ((lane % (16 / E)) == 0) {
+    reinterpret_cast<uint16_t*>(blk + data_bytes + uint64_t(row) * (HD / 8))[lane / (16 / E)] = uint16_t(sigma);
+  }
+}
+
+template <int HD>
 __device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ src, uint8_t* __restrict__ blk,
                                           uint32_t row, uint64_t data_bytes, float scale,
                                           const WriteArgs& a, int lane) {
@@ -140,8 +171,10 @@ __device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ 
     write_turbo<HD, 2>(raw, blk, row, data_bytes, a, lane);
   } else if (fmt == KVQ_TURBO3) {
     write_turbo<HD, 3>(raw, blk, row, data_bytes, a, lane);
-  } else {
+  } else if (fmt == KVQ_TURBO4) {
     write_turbo<HD, 4>(raw, blk, row, data_bytes, a, lane);
+  } else {
+    write_turbo8<HD>(raw, blk, row, data_bytes, a, lane);
   }
 }
 

@@ -75,6 +75,8 @@ def test_codebook_tables_bit_equal_to_oracle(fmt, bits):
 def test_codebook_rejects_non_turbo():
     with pytest.raises(kvq.KvqError):
         kvq.codebook("bf16")
+    with pytest.raises(kvq.KvqError):
+        kvq.codebook("turbo8")  # E4M3 values, no codebook
 
 
 # ---------------------------------------------------------------- argument checks

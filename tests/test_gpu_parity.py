@@ -61,7 +61,8 @@ def test_pairs_dense(gpu_lib, kf, vf):
 
 @pytest.mark.parametrize("hd", [64, 256])
 @pytest.mark.parametrize("kf,vf", [("bf16", "bf16"), ("fp8", "turbo2"), ("turbo3", "turbo3"),
-                                   ("turbo4", "turbo3"), ("bf16", "turbo4"), ("turbo2", "fp8")])
+                                   ("turbo4", "turbo3"), ("bf16", "turbo4"), ("turbo2", "fp8"), ("turbo8", "turbo8"),
+                                   ("turbo4", "turbo8")])
 def test_head_dims(gpu_lib, kf, vf, hd):
     w = synth.small(2000 + hd + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[5, 64, 700], num_q_heads=4,
                     num_kv_heads=2, head_dim=hd, block_size=16, k_format=kf, v_format=vf)
@@ -69,7 +70,7 @@ def test_head_dims(gpu_lib, kf, vf, hd):
 
 
 @pytest.mark.parametrize("g", [1, 2, 8])
-@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3")])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3"), ("turbo3", "turbo8")])
 def test_group_sizes(gpu_lib, kf, vf, g):
     w = synth.small(3000 + g * 10 + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[33, 517, 260], num_q_heads=2 * g,
                     num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf)
@@ -93,8 +94,8 @@ def test_kv_head_counts(gpu_lib, kf, vf, hkv):
     run(gpu_lib, w, tail=2, label=f"{kf}/{vf} Hkv{hkv}")
 
 
-@pytest.mark.parametrize("bs", [32, 64])
-@pytest.mark.parametrize("kf,vf", [("turbo2", "fp8"), ("turbo3", "turbo2")])
+@pytest.mark.parametrize("bs", [2, 32, 64])
+@pytest.mark.parametrize("kf,vf", [("turbo2", "fp8"), ("turbo3", "turbo2"), ("turbo8", "turbo8")])
 def test_block_sizes_turbo_k(gpu_lib, kf, vf, bs):
     # chunks that start inside a page (block_size > 16) on the turbo-K matrix-core path
     w = synth.small(4700 + bs + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[1, 95, 640, 300], num_q_heads=8,
@@ -104,7 +105,7 @@ def test_block_sizes_turbo_k(gpu_lib, kf, vf, bs):
 
 @pytest.mark.parametrize("thr", [1e-3, 0.05])
 @pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo3", "turbo3"), ("fp8", "fp8"), ("bf16", "bf16"),
-                                   ("turbo4", "turbo2")])
+                                   ("turbo4", "turbo2"), ("turbo4", "turbo8"), ("turbo8", "turbo3")])
 def test_sparse_v(gpu_lib, kf, vf, thr):
     w = synth.small(5000 + int(thr * 1e4) + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[0, 1, 40, 1500, 2100],
                     num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf,
