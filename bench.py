@@ -46,7 +46,8 @@ from synth.gpu import stage  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 ROW_BYTES = {"bf16": lambda hd: 2 * hd, "fp8": lambda hd: hd, "turbo4": lambda hd: hd // 2 + hd // 16,
-             "turbo3": lambda hd: hd * 3 // 8 + hd // 16, "turbo2": lambda hd: hd // 4 + hd // 16}
+             "turbo3": lambda hd: hd * 3 // 8 + hd // 16, "turbo2": lambda hd: hd // 4 + hd // 16,
+             "turbo8": lambda hd: hd + hd // 8}
 METRIC = "paged-decode effective KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
 
 
@@ -66,7 +67,8 @@ def kernel_source_hash() -> str:
 def _k_rows(st, w, kvq, j: torch.Tensor, pages: torch.Tensor) -> torch.Tensor:
     """Stored K of positions j of one sequence as fp32 [Hkv, hd, P], read
     back from the pool bytes with plain torch ops (turbo: in the rotated
-    basis, codes -> centroid x E4M3 group scale; fp8: E4M3 x k_scale)."""
+    basis, codes -> centroid x E4M3 group scale, turbo8 E4M3 value x BF16
+    group scale; fp8: E4M3 x k_scale)."""
     Hkv, hd, bs = w.num_kv_heads, w.head_dim, w.block_size
     lay = st.layout
     stride, data = int(lay.k_block_stride_bytes), int(lay.k_data_section_bytes)
@@ -81,6 +83,12 @@ def _k_rows(st, w, kvq, j: torch.Tensor, pages: torch.Tensor) -> torch.Tensor:
     elif w.k_format == "fp8":
         off = (base + rows * hd)[:, :, None] + torch.arange(hd, device="cuda")
         k = pool[off].view(torch.float8_e4m3fn).float() * st.k_scale
+    elif w.k_format == "turbo8":
+        i = torch.arange(hd, device="cuda")
+        off = (base + rows * hd)[:, :, None] + i
+        soff = (base + data + rows * (hd // 8))[:, :, None] + 2 * (i // 16)
+        sc = ((pool[soff].int() | (pool[soff + 1].int() << 8)) << 16).view(torch.float32)
+        k = pool[off].view(torch.float8_e4m3fn).float() * sc
     else:
         bits = int(w.k_format[-1])
         rb = hd * bits // 8
@@ -163,7 +171,7 @@ def decode_kernels(w) -> str:
     """The launches of one decode call for this workload."""
     if w.sparse_v_threshold > 0:
         return "kvq_paged_decode: scores_kernel + sparse_v_kernel"
-    bits = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4}
+    bits = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8}
     hd = w.head_dim
     kqb = hd * bits[w.k_format] // 32  # K bytes per lane and chunk in the matrix-core kernel
     if w.k_format.startswith("turbo"):

@@ -23,6 +23,9 @@ size 16, long contexts, sliding window, sparse-V threshold 1e-3):
             Student-t(5) values
   5         turbo4 / turbo3, write 8192 tokens (last 256 of 32 seqs, shuffled),
             then decode 32 seqs, L ~ U{4096..16384}, Hq 64, Hkv 8, hd 128, bs 32
+  6         turbo4 / turbo8, 64 seqs, L ~ U{4096..16384}, Hq 32, Hkv 8, hd 128
+  7         turbo8 / turbo8, the same sequences and shapes as 6 (the symmetric pairing
+            the asymmetric one is measured against)
 """
 from __future__ import annotations
 
@@ -58,6 +61,11 @@ class Workload:
     pool_blocks: Optional[int] = None  # None: exactly the blocks the sequences need
     write_tail: int = 1               # positions per sequence written by the timed step
     fixed_lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths
+    seed_wid: Optional[int] = None    # draw every stream as this workload does (same sequences, other formats)
+
+    @property
+    def seed_id(self) -> int:
+        return self.wid if self.seed_wid is None else self.seed_wid
 
     @property
     def group(self) -> int:
@@ -77,6 +85,10 @@ WORKLOADS = {
                 dist="student_t5", sparse_v_threshold=1e-3, sliding_window=4096),
     5: Workload(5, "turbo4k-turbo3v-write", 32, 64, 8, 128, 32, "turbo4", "turbo3",
                 (4096, 16384), write_tail=256),
+    6: Workload(6, "turbo4k-turbo8v", 64, 32, 8, 128, 16, "turbo4", "turbo8", (4096, 16384),
+                outliers=True),
+    7: Workload(7, "turbo8-turbo8", 64, 32, 8, 128, 16, "turbo8", "turbo8", (4096, 16384),
+                outliers=True, seed_wid=6),
 }
 
 
@@ -96,7 +108,7 @@ def seq_lens(w: Workload) -> np.ndarray:
     lo, hi = w.seq_len
     if lo == hi:
         return np.full(w.num_seqs, lo, dtype=np.int32)
-    g = _gen(w.wid, _S_LENS, 0, "cpu")
+    g = _gen(w.seed_id, _S_LENS, 0, "cpu")
     return torch.randint(lo, hi + 1, (w.num_seqs,), generator=g).numpy().astype(np.int32)
 
 
@@ -110,7 +122,7 @@ def block_tables(w: Workload, lens: np.ndarray, max_blocks_per_seq: Optional[int
     need = [(int(L) + bs - 1) // bs for L in lens]
     total = sum(need)
     num_blocks = total if w.pool_blocks is None else max(w.pool_blocks, total)
-    g = _gen(w.wid, _S_PERM, 0, "cpu")
+    g = _gen(w.seed_id, _S_PERM, 0, "cpu")
     perm = torch.randperm(num_blocks, generator=g).numpy().astype(np.int32)
     longest = max([int(x) for x in lens] + [w.seq_len[1]])
     mb = max_blocks_per_seq or max(1, (longest + bs - 1) // bs)
@@ -124,14 +136,14 @@ def block_tables(w: Workload, lens: np.ndarray, max_blocks_per_seq: Optional[int
 
 def outlier_channels(w: Workload) -> np.ndarray:
     """4 distinct channels per kv head, fixed for the whole workload."""
-    g = _gen(w.wid, _S_OUTLIER, 0, "cpu")
+    g = _gen(w.seed_id, _S_OUTLIER, 0, "cpu")
     ch = np.stack([torch.randperm(w.head_dim, generator=g)[:4].numpy()
                    for _ in range(w.num_kv_heads)])
     return ch.astype(np.int64)
 
 
 def _draw(w: Workload, stream: int, idx: int, shape, device) -> torch.Tensor:
-    g = _gen(w.wid, stream, idx, device)
+    g = _gen(w.seed_id, stream, idx, device)
     if w.dist == "normal":
         return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
     if w.dist == "student_t5":
@@ -159,7 +171,7 @@ def kv_values(w: Workload, side: str, seq: int, length: int, device="cpu") -> to
 
 def queries(w: Workload, device="cpu") -> torch.Tensor:
     """bf16 [S, Hq, hd], N(0,1), no outliers."""
-    g = _gen(w.wid, _S_Q, 0, device)
+    g = _gen(w.seed_id, _S_Q, 0, device)
     x = torch.randn((w.num_seqs, w.num_q_heads, w.head_dim), generator=g, device=device,
                     dtype=torch.float32)
     return x.to(torch.bfloat16)
@@ -179,7 +191,7 @@ def slots_for(w: Workload, bt: np.ndarray, seq: int, positions: np.ndarray) -> n
 
 def write_order(w: Workload, n: int) -> np.ndarray:
     """Seeded shuffle of the timed write batch (scattered slot_mapping)."""
-    g = _gen(w.wid, _S_ORDER, 0, "cpu")
+    g = _gen(w.seed_id, _S_ORDER, 0, "cpu")
     return torch.randperm(n, generator=g).numpy()
 
 
