@@ -1,7 +1,8 @@
-"""bf16 and FP8 E4M3 codecs, written from the formats' definitions.
+"""bf16, FP8 E4M3 and FP4 E2M1 codecs, written from the formats' definitions.
 
 "spark_runtime/kv_cache.rs", ``KvCacheDtype::Fp8`` ("1 byte per element (FP8
-E4M3 with per-tensor scale)") and the turbo scales ("FP8 per-group scales").
+E4M3 with per-tensor scale)"), the turbo scales ("FP8 per-group scales") and
+``KvCacheDtype::Nvfp4`` (4-bit E2M1 values packed two to a byte).
 
 Readings (the pages name the format only):
   * E4M3 is the OCP "E4M3FN" variant: 1 sign, 4 exponent bits (bias 7),
@@ -10,6 +11,11 @@ Readings (the pages name the format only):
   * Encoding clamps to [-448, 448] first, then rounds to the nearest
     representable value, ties to the even mantissa.  The sign of -0 is kept.
   * bf16 rounding is round-to-nearest-even on the fp32 value.
+  * E2M1 is the OCP FP4 element type: 1 sign, 2 exponent bits (bias 1),
+    1 mantissa bit, no infinities or NaN; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4,
+    6 (codes 0..7, the sign in bit 3).  Encoding saturates to +-6, then
+    rounds to the nearest value, ties to the even mantissa; the sign of -0
+    is kept.
 """
 from __future__ import annotations
 
@@ -86,3 +92,38 @@ def e4m3_encode(v: np.ndarray) -> np.ndarray:
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
     neg = np.signbit(v)
     return (code | np.where(neg, np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+
+
+E2M1_MAX = 6.0
+
+
+def _e2m1_table() -> np.ndarray:
+    """Value of every E2M1 nibble (float64)."""
+    vals = np.empty(16, dtype=np.float64)
+    for code in range(16):
+        sign = -1.0 if code & 0x8 else 1.0
+        e = (code >> 1) & 0x3
+        m = code & 0x1
+        vals[code] = sign * (m / 2.0 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return vals
+
+
+E2M1_VALUES = _e2m1_table()
+_E2M1_POS = E2M1_VALUES[:8]   # codes 0..7 are increasing in value
+
+
+def e2m1_decode(code: np.ndarray) -> np.ndarray:
+    return E2M1_VALUES[np.asarray(code, dtype=np.uint8) & 0xF].astype(np.float32)
+
+
+def e2m1_encode(v: np.ndarray) -> np.ndarray:
+    """fp32 -> E2M1 nibble (uint8 0..15): saturate to +-6, nearest value, ties to even."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.minimum(np.abs(v.astype(np.float64)), E2M1_MAX)
+    hi = np.minimum(np.searchsorted(_E2M1_POS, a, side="left"), 7)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _E2M1_POS[lo]
+    d_hi = _E2M1_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((hi & 1) == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return (code | np.where(np.signbit(v), np.uint8(0x8), np.uint8(0))).astype(np.uint8)

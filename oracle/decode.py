@@ -52,6 +52,12 @@ def dequant_rows(pool: np.ndarray, side: Side, slots: np.ndarray, scale: float =
         sig = np.ascontiguousarray(sig.reshape(P * nkv, side.row_scales)).view("<u2")
         sq = codecs.bf16_bits_to_f32(sig).astype(np.float64)
         vals = codecs.e4m3_decode(data).astype(np.float64) * np.repeat(sq, GROUP, axis=1)
+    elif side.fmt == "nvfp4":
+        codes = unpack_codes(data, 4, hd)
+        saddr = base + side.data_section_bytes + row * side.row_scales
+        sig = pool[(saddr.reshape(-1, 1) + np.arange(side.row_scales)).ravel()]
+        sq = codecs.e4m3_decode(sig.reshape(P * nkv, side.row_scales)).astype(np.float64)
+        vals = codecs.E2M1_VALUES[codes] * np.repeat(sq, GROUP, axis=1)
     else:
         t = tables(side.fmt)
         codes = unpack_codes(data, BITS[side.fmt], hd)

@@ -7,7 +7,9 @@ e = block_size * num_kv_heads * head_dim elements per block per side:
 (codes, then one FP8 scale byte per group of 16 elements), and the
 ``turbo*_data_bytes`` / ``turbo*_scale_bytes`` split.  ``KvCacheDtype::Turbo8``
 with ``turbo8_data_bytes`` / ``turbo8_scale_bytes``: one E4M3 byte per element,
-then one BF16 scale (2 bytes) per group of 16: e + 2e/16.
+then one BF16 scale (2 bytes) per group of 16: e + 2e/16.  ``KvCacheDtype::Nvfp4``
+with ``nvfp4_data_bytes`` / ``nvfp4_scale_bytes``: turbo4's byte layout (E2M1
+nibbles, then one FP8 scale byte per group of 16), e/2 + e/16.
 "metrale_model_layers/layers/ops/kv_cache_bf16k_turbov.rs", module
 invariants: element order ``[num_blocks, block_size, num_kv_heads,
 head_dim]``; a V block is its code section followed by its scales; K and V
@@ -24,15 +26,18 @@ Readings:
   * The scale of group g = e' / 16 is byte g of the scale section, which
     starts right after the code section (``data_section_bytes``); turbo8's
     BF16 scale of group g is the little-endian 2-byte word at 2g.
+  * NVFP4 nibbles pack as turbo4's codes do (element 2k in the low nibble of
+    byte k); ``is_wht_rotated`` leaves NVFP4 out, so it is not rotated.
   * The block stride is the block's byte size rounded up to 16 bytes.
 """
 from __future__ import annotations
 
 import dataclasses
 
-BITS = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8}
+BITS = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8, "nvfp4": 4}
 TURBO = ("turbo2", "turbo3", "turbo4")     # Lloyd-Max codes, one E4M3 scale byte per group
 ROTATED = TURBO + ("turbo8",)              # turbo8: E4M3 values, one BF16 scale per group
+BYTE_SCALED = TURBO + ("nvfp4",)           # one E4M3 scale byte per group (nvfp4: E2M1 values)
 GROUP = 16
 
 
@@ -63,7 +68,7 @@ class Side:
     @property
     def row_scales(self) -> int:
         """Scale bytes of one (position, kv head) row."""
-        if self.fmt in TURBO:
+        if self.fmt in BYTE_SCALED:
             return self.head_dim // GROUP
         return 2 * self.head_dim // GROUP if self.fmt == "turbo8" else 0
 
@@ -74,7 +79,7 @@ def side_layout(fmt: str, block_size: int, num_kv_heads: int, head_dim: int) -> 
         data, scales = 2 * e, 0
     elif fmt == "fp8":
         data, scales = e, 0
-    elif fmt == "turbo4":
+    elif fmt in ("turbo4", "nvfp4"):
         data, scales = e // 2, e // GROUP
     elif fmt == "turbo3":
         data, scales = e * 3 // 8, e // GROUP

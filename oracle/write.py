@@ -29,6 +29,14 @@ brackets, the pages are silent on them):
          E4M3(RN32(y / s_q)) [IEEE division and the fp8 side's E4M3
          rounding; a zero scale (an all-zero group) gives zero bytes];
          sigma stored as a little-endian 2-byte word.
+  nvfp4  ("E2M1 packed nibbles" with "per-group FP8 scale", turbo4's byte
+         layout, not rotated): per group of 16 of x itself: a = max|x|,
+         s = RN32(a * RN32(1/6)) [absmax / largest E2M1 value, the turbo
+         rule with 6 for the largest centroid], sigma = E4M3(s), s_q =
+         value(sigma); nibble = E2M1(RN32(x / s_q)) [IEEE division as for
+         fp8; saturate to +-6, nearest, ties to the even mantissa, sign
+         kept; a zero scale gives zero nibbles]; nibbles packed as turbo4's
+         codes, sigma stored in the scale section.
 Tokens whose slot is negative write nothing [the slot sentinel].
 """
 from __future__ import annotations
@@ -39,6 +47,7 @@ from . import codecs, codebook, wht
 from .layout import BITS, GROUP, TURBO, Side
 
 E4M3_INV_MAX = np.float32(1.0 / codecs.E4M3_MAX)   # RN32(1/448)
+E2M1_INV_MAX = np.float32(1.0 / codecs.E2M1_MAX)   # RN32(1/6)
 
 _TABLES = {}
 
@@ -99,6 +108,19 @@ def turbo8_quantize(x_f32: np.ndarray):
     return codecs.e4m3_encode(v.astype(np.float32)).reshape(N, hd), sigma
 
 
+def nvfp4_quantize(x_f32: np.ndarray):
+    """Unrotated rows -> (E2M1 nibbles [N, hd] uint8, E4M3 scale bytes [N, hd/16] uint8)."""
+    N, hd = x_f32.shape
+    xg = x_f32.reshape(N, hd // GROUP, GROUP)
+    a = np.max(np.abs(xg), axis=-1)
+    s = (a * E2M1_INV_MAX).astype(np.float32)
+    sigma = codecs.e4m3_encode(s)
+    sq = codecs.e4m3_decode(sigma)
+    v = np.zeros_like(xg)
+    np.divide(xg, sq[..., None], out=v, where=sq[..., None] > 0)
+    return codecs.e2m1_encode(v.astype(np.float32)).reshape(N, hd), sigma
+
+
 def quantize_rows(x_bits: np.ndarray, fmt: str, scale: float = 1.0):
     """bf16 rows (uint16 [N, hd]) -> (code bytes [N, row_bytes], scale bytes [N, row_scales])."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
@@ -112,6 +134,9 @@ def quantize_rows(x_bits: np.ndarray, fmt: str, scale: float = 1.0):
     if fmt in TURBO:
         codes, sigma = turbo_quantize(x, fmt)
         return pack_codes(codes, BITS[fmt]), sigma
+    if fmt == "nvfp4":
+        codes, sigma = nvfp4_quantize(x)
+        return pack_codes(codes, 4), sigma
     if fmt == "turbo8":
         data, sigma = turbo8_quantize(x)
         return data, np.ascontiguousarray(sigma.astype("<u2")).view(np.uint8).reshape(N, -1)

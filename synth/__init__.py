@@ -36,7 +36,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-FORMATS = ("bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8")
+FORMATS = ("bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8", "nvfp4")
 
 # stream ids
 _S_LENS, _S_PERM, _S_OUTLIER, _S_Q, _S_K, _S_V, _S_ORDER = range(7)

@@ -71,3 +71,41 @@ def test_e4m3_encode_examples(v, code):
     # OCP E4M3FN: 17 is halfway between 16 (0x58) and 18 (0x59): ties to even -> 16;
     # 19 is halfway between 18 and 20 (0x5A): ties to even -> 20
     assert codecs.e4m3_encode(np.float32([v]))[0] == code
+
+
+# ---- E2M1 (the NVFP4 element type)
+
+def test_e2m1_values_follow_the_format_definition():
+    # 1 sign, 2 exponent bits with bias 1, 1 mantissa bit: exponent field 0 is
+    # subnormal (m/2), otherwise (1 + m/2) * 2^(e - 1)
+    assert list(codecs.E2M1_VALUES[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(codecs.E2M1_VALUES[8:]) == [-0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    assert np.signbit(codecs.E2M1_VALUES[8])
+
+
+def _e2m1_by_rint(v):
+    """Independent rounding: per binade, scale to its integer grid and let
+    np.rint (round half to even) pick; an even grid index is an even mantissa."""
+    a = np.minimum(np.abs(v.astype(np.float64)), 6.0)
+    step = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    q = np.minimum(np.rint(a / step) * step, 6.0)
+    mag = {0.0: 0, 0.5: 1, 1.0: 2, 1.5: 3, 2.0: 4, 3.0: 5, 4.0: 6, 6.0: 7}
+    code = np.array([mag[float(x)] for x in q], dtype=np.uint8)
+    return code | np.where(np.signbit(v), np.uint8(8), np.uint8(0))
+
+
+def test_e2m1_encode_matches_rint_rounding():
+    rng = np.random.default_rng(3)
+    grid = np.arange(0, 8.0 + 1e-9, 1 / 64, dtype=np.float64)       # every tie, binade edge, saturation
+    v = np.concatenate([grid, -grid, rng.uniform(-9, 9, 20000),
+                        np.nextafter(np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]), np.float32(0)),
+                        np.nextafter(np.float32([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]), np.float32(9))])
+    v = v.astype(np.float32)
+    assert np.array_equal(codecs.e2m1_encode(v), _e2m1_by_rint(v))
+
+
+@pytest.mark.parametrize("v,code", [(0.25, 0x0), (0.75, 0x2), (1.25, 0x2), (1.75, 0x4), (2.5, 0x4),
+                                    (3.5, 0x6), (5.0, 0x6), (5.01, 0x7), (100.0, 0x7), (-0.1, 0x8),
+                                    (-0.0, 0x8), (-6.0, 0xF), (0.26, 0x1)])
+def test_e2m1_encode_examples(v, code):
+    assert int(codecs.e2m1_encode(np.float32([v]))[0]) == code

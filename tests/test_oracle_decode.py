@@ -46,6 +46,9 @@ def _dequant_contig(bits, fmt, scale):
         sq = (sc[:, 0::2].astype(np.uint32) | (sc[:, 1::2].astype(np.uint32) << 8)) << 16
         v = codecs.e4m3_decode(data).astype(np.float64) * \
             np.repeat(sq.astype(np.uint32).view(np.float32).astype(np.float64), 16, axis=1)
+    elif fmt == "nvfp4":
+        nib = np.stack([data & 0xF, data >> 4], axis=-1).reshape(data.shape[0], hd)
+        v = codecs.E2M1_VALUES[nib] * np.repeat(codecs.e4m3_decode(sc).astype(np.float64), 16, axis=1)
     else:
         codes = W.unpack_codes(data, layout.BITS[fmt], hd)
         v = W.tables(fmt)["centroids"].astype(np.float64)[codes] * \
@@ -56,7 +59,8 @@ def _dequant_contig(bits, fmt, scale):
 PAIRS = [("bf16", "bf16"), ("fp8", "fp8"), ("turbo2", "turbo2"), ("turbo3", "turbo3"),
          ("turbo4", "turbo4"), ("turbo4", "turbo3"), ("bf16", "turbo4"), ("bf16", "turbo3"),
          ("bf16", "turbo2"), ("fp8", "turbo4"), ("fp8", "turbo3"), ("fp8", "turbo2"),
-         ("turbo8", "turbo8"), ("turbo4", "turbo8"), ("turbo3", "turbo8"), ("bf16", "turbo8")]
+         ("turbo8", "turbo8"), ("turbo4", "turbo8"), ("turbo3", "turbo8"), ("bf16", "turbo8"),
+         ("nvfp4", "nvfp4"), ("bf16", "nvfp4"), ("nvfp4", "turbo3"), ("turbo4", "nvfp4")]
 
 
 @pytest.mark.parametrize("kf,vf", PAIRS)

@@ -9,14 +9,15 @@ from oracle import layout
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_sizes.json")))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8", "nvfp4"])
 @pytest.mark.parametrize("bs,nkv,hd", [(16, 8, 128), (16, 2, 64), (16, 4, 256), (32, 8, 128), (1, 1, 64)])
 def test_block_bytes_closed_form(fmt, bs, nkv, hd):
     s = layout.side_layout(fmt, bs, nkv, hd)
     e = bs * nkv * hd
     # block_bytes_dims arms, evaluated by hand
-    # (turbo8: turbo8_data_bytes = e, turbo8_scale_bytes = 2 bytes per group of 16)
-    expect = {"bf16": e * 2, "fp8": e, "turbo4": e // 2 + e // 16,
+    # (turbo8: turbo8_data_bytes = e, turbo8_scale_bytes = 2 bytes per group of 16;
+    # nvfp4 shares the turbo4 arm: nibbles plus one scale byte per group of 16)
+    expect = {"bf16": e * 2, "fp8": e, "turbo4": e // 2 + e // 16, "nvfp4": e // 2 + e // 16,
               "turbo3": e * 3 // 8 + e // 16, "turbo2": e // 4 + e // 16, "turbo8": e + 2 * (e // 16)}[fmt]
     assert s.data_section_bytes + s.scale_bytes == expect
     assert s.block_stride_bytes % 16 == 0 and 0 <= s.block_stride_bytes - expect < 16
@@ -51,8 +52,16 @@ def test_workload_strides():
 
 
 def test_rotation_flags():
-    assert [layout.is_rotated(f) for f in ("bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8")] == \
-        [False, False, True, True, True, True]
+    assert [layout.is_rotated(f) for f in ("bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8", "nvfp4")] == \
+        [False, False, True, True, True, True, False]
+
+
+def test_nvfp4_shares_turbo4_layout():
+    # "same byte layout, different codebook": every size and offset agrees
+    for bs, nkv, hd in [(16, 8, 128), (1, 1, 64), (32, 4, 256)]:
+        a, b = layout.side_layout("nvfp4", bs, nkv, hd), layout.side_layout("turbo4", bs, nkv, hd)
+        assert (a.data_section_bytes, a.scale_bytes, a.block_stride_bytes, a.row_bytes, a.row_scales) == \
+            (b.data_section_bytes, b.scale_bytes, b.block_stride_bytes, b.row_bytes, b.row_scales)
 
 
 def test_turbo8_sizes():

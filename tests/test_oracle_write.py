@@ -179,3 +179,52 @@ def test_pool_placement(kf, vf):
                     assert np.array_equal(pool[b:b + side.row_scales], scl[h])
                     touched[b:b + side.row_scales] = True
         assert np.all(pool[~touched] == 0xAA)
+
+
+# ---- NVFP4
+
+def test_nvfp4_nibbles_are_a_nearest_grid_point():
+    rng = np.random.default_rng(11)
+    x = codecs.bf16_round(rng.standard_normal((256, 128)).astype(np.float32) * 3)
+    x[:, 5] *= 40
+    nib, sigma = W.nvfp4_quantize(x)
+    sq = codecs.e4m3_decode(sigma).astype(np.float64)                       # [256, 8]
+    assert np.array_equal(sigma, codecs.e4m3_encode(
+        (np.abs(x).reshape(256, 8, 16).max(-1) * np.float32(1 / 6)).astype(np.float32)))
+    grid = codecs.E2M1_VALUES[None, None, None, :] * sq[..., None, None]   # [256, 8, 1, 16]
+    xg = x.reshape(256, 8, 16).astype(np.float64)
+    deq = codecs.E2M1_VALUES[nib].reshape(256, 8, 16) * sq[..., None]
+    best = np.abs(grid - xg[..., None]).min(-1)
+    # nearest up to the one rounding of x / s_q in fp32
+    assert np.all(np.abs(deq - xg) <= best + np.abs(xg) * 2.0 ** -22)
+
+
+def test_nvfp4_zero_and_tiny_groups():
+    x = np.zeros((2, 64), np.float32)
+    x[1, 16:32] = -1e-30                                      # absmax / 6 far below E4M3's smallest step
+    nib, sigma = W.nvfp4_quantize(x)
+    assert not nib.any() and not sigma.any()
+
+
+def test_nvfp4_rows_pack_like_turbo4():
+    x_bits = codecs.bf16_round_bits(np.linspace(-5, 5, 2 * 64, dtype=np.float32).reshape(2, 64))
+    data, sc = W.quantize_rows(x_bits, "nvfp4")
+    nib, sigma = W.nvfp4_quantize(codecs.bf16_bits_to_f32(x_bits))
+    assert np.array_equal(data[:, 0] & 0xF, nib[:, 0]) and np.array_equal(data[:, 0] >> 4, nib[:, 1])
+    assert np.array_equal(sc, sigma) and data.shape == (2, 32)
+
+
+def test_turbo4_beats_nvfp4_mse_on_gaussian_rows():
+    # the Turbo4 doc comment credits rotation + the Lloyd-Max book with about
+    # half the NVFP4 error at the same bits; on N(0,1) rows the oracle gives
+    # 1.54x (with x20 outlier channels 1.44x), i.e. clearly lower, not 2x
+    rng = np.random.default_rng(0)
+    x = codecs.bf16_round(rng.standard_normal((4096, 128)).astype(np.float32))
+    codes, sig = W.turbo_quantize(x, "turbo4")
+    y = codecs.bf16_round(wht.wht_f32(x))
+    deq_t = W.tables("turbo4")["centroids"].astype(np.float64)[codes] * \
+        np.repeat(codecs.e4m3_decode(sig).astype(np.float64), 16, axis=1)
+    nib, s2 = W.nvfp4_quantize(x)
+    deq_n = codecs.E2M1_VALUES[nib] * np.repeat(codecs.e4m3_decode(s2).astype(np.float64), 16, axis=1)
+    ratio = np.mean((deq_n - x) ** 2) / np.mean((deq_t - y) ** 2)
+    assert 1.4 < ratio < 1.7
