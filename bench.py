@@ -47,7 +47,7 @@ from synth.gpu import stage  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 ROW_BYTES = {"bf16": lambda hd: 2 * hd, "fp8": lambda hd: hd, "turbo4": lambda hd: hd // 2 + hd // 16,
              "turbo3": lambda hd: hd * 3 // 8 + hd // 16, "turbo2": lambda hd: hd // 4 + hd // 16,
-             "turbo8": lambda hd: hd + hd // 8}
+             "turbo8": lambda hd: hd + hd // 8, "nvfp4": lambda hd: hd // 2 + hd // 16}
 METRIC = "paged-decode effective KV GB/s (% of HBM peak) + decode tokens/s, 1 GPU"
 
 
@@ -68,7 +68,8 @@ def _k_rows(st, w, kvq, j: torch.Tensor, pages: torch.Tensor) -> torch.Tensor:
     """Stored K of positions j of one sequence as fp32 [Hkv, hd, P], read
     back from the pool bytes with plain torch ops (turbo: in the rotated
     basis, codes -> centroid x E4M3 group scale, turbo8 E4M3 value x BF16
-    group scale; fp8: E4M3 x k_scale)."""
+    group scale; nvfp4, not rotated: E2M1 value x E4M3 group scale; fp8:
+    E4M3 x k_scale)."""
     Hkv, hd, bs = w.num_kv_heads, w.head_dim, w.block_size
     lay = st.layout
     stride, data = int(lay.k_block_stride_bytes), int(lay.k_data_section_bytes)
@@ -97,7 +98,10 @@ def _k_rows(st, w, kvq, j: torch.Tensor, pages: torch.Tensor) -> torch.Tensor:
         off = (base + rows * rb)[:, :, None] + (bit // 8)
         word = pool[off].int() | (pool[off + 1].int() << 8)
         code = (word >> (bit % 8)) & ((1 << bits) - 1)
-        cen = torch.as_tensor(kvq.codebook(w.k_format)["centroids"], device="cuda")
+        if w.k_format == "nvfp4":  # E2M1 value of each nibble
+            cen = torch.tensor([0, .5, 1, 1.5, 2, 3, 4, 6, -0., -.5, -1, -1.5, -2, -3, -4, -6], device="cuda")
+        else:
+            cen = torch.as_tensor(kvq.codebook(w.k_format)["centroids"], device="cuda")
         soff = (base + data + rows * (hd // 16))[:, :, None] + i // 16
         sq = pool[soff].view(torch.float8_e4m3fn).float()
         k = cen[code.long()] * sq
@@ -171,10 +175,10 @@ def decode_kernels(w) -> str:
     """The launches of one decode call for this workload."""
     if w.sparse_v_threshold > 0:
         return "kvq_paged_decode: scores_kernel + sparse_v_kernel"
-    bits = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8}
+    bits = {"bf16": 16, "fp8": 8, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8, "nvfp4": 4}
     hd = w.head_dim
     kqb = hd * bits[w.k_format] // 32  # K bytes per lane and chunk in the matrix-core kernel
-    if w.k_format.startswith("turbo"):
+    if w.k_format.startswith("turbo") or w.k_format == "nvfp4":  # per-16 group scales
         shape_ok = kqb % 4 == 0 and kqb <= 32 and hd // 4 >= 16
     else:
         shape_ok = kqb <= 64 and kqb % 16 == 0

@@ -57,14 +57,22 @@ extern "C" {
  *                 scale) and one BF16 scale per group of 16 (group absmax /
  *                 448, round to nearest even), 2 bytes, little-endian, in the
  *                 scale section.  An all-zero group stores zero bytes.
- * Rotated sides (turbo) make decode rotate the query (K side) and rotate the
- * output back (V side) -- [kv_cache.rs] is_wht_rotated. */
+ *   KVQ_NVFP4     [kv_cache.rs] KvCacheDtype::Nvfp4, nvfp4_data_bytes /
+ *                 nvfp4_scale_bytes (turbo4's byte layout): not rotated; per
+ *                 group of 16 one E4M3 scale byte (group absmax / 6) and one
+ *                 OCP E2M1 nibble per element (value / scale, saturated to +-6,
+ *                 round to nearest even, sign kept; element 2k in the low
+ *                 nibble of byte k).  A group whose scale encodes to 0 stores
+ *                 zero nibbles.
+ * Rotated sides (turbo2/3/4/8) make decode rotate the query (K side) and
+ * rotate the output back (V side) -- [kv_cache.rs] is_wht_rotated. */
 typedef enum kvq_format {
   KVQ_BF16 = 0,
   KVQ_FP8_E4M3 = 1,
   KVQ_TURBO2 = 2,
   KVQ_TURBO3 = 3,
   KVQ_TURBO4 = 4,
+  KVQ_NVFP4 = 5,
   KVQ_TURBO8 = 8
 } kvq_format;
 
@@ -171,8 +179,8 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
 /* Introspection (host only): the fp32 Lloyd-Max tables the turbo format uses.
  * centroids[0..L-1] ascending, thresholds[1..L-1] (midpoints; [0] = 0),
  * *inv_cmax = 1/largest centroid, *levels = L = 2^bits.  Buffers hold 16 floats.
- * Returns KVQ_ERR_INVALID_ARG for a format without a codebook (bf16, fp8,
- * turbo8) or a NULL pointer. */
+ * Returns KVQ_ERR_INVALID_ARG for a format without a Lloyd-Max codebook (bf16,
+ * fp8, turbo8, nvfp4) or a NULL pointer. */
 int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax,
                  uint32_t* levels);
 

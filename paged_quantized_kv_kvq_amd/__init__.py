@@ -24,7 +24,7 @@ __all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
            "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
            "library_path"]
 
-FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "turbo8": 8}
+FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "nvfp4": 5, "turbo8": 8}
 _NAMES = {v: k for k, v in FORMATS.items()}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvq.so")

@@ -15,12 +15,16 @@ constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a sp
 constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 
-bool valid_format(int32_t f) { return (f >= KVQ_BF16 && f <= KVQ_TURBO4) || f == KVQ_TURBO8; }
-bool is_turbo(int32_t f) { return f >= KVQ_TURBO2; }  // rotated sides
-bool has_codebook(int32_t f) { return f >= KVQ_TURBO2 && f <= KVQ_TURBO4; }
-// scale bytes per group of 16 elements: E4M3 for the codebook formats, BF16 for turbo8
-uint64_t scale_bytes_per_group(int32_t f) { return has_codebook(f) ? 1u : f == KVQ_TURBO8 ? 2u : 0u; }
-uint32_t format_bits(int32_t f) { return f == KVQ_BF16 ? 16u : f == KVQ_FP8_E4M3 ? 8u : uint32_t(f); }
+bool valid_format(int32_t f) { return (f >= KVQ_BF16 && f <= KVQ_NVFP4) || f == KVQ_TURBO8; }
+bool is_rotated(int32_t f) { return f >= KVQ_TURBO2 && f != KVQ_NVFP4; }  // is_wht_rotated
+bool has_codebook(int32_t f) { return f >= KVQ_TURBO2 && f <= KVQ_TURBO4; }  // Lloyd-Max books
+// scale bytes per group of 16 elements: E4M3 for the 2/3/4-bit formats, BF16 for turbo8
+uint64_t scale_bytes_per_group(int32_t f) {
+  return (has_codebook(f) || f == KVQ_NVFP4) ? 1u : f == KVQ_TURBO8 ? 2u : 0u;
+}
+uint32_t format_bits(int32_t f) {
+  return f == KVQ_BF16 ? 16u : f == KVQ_FP8_E4M3 ? 8u : f == KVQ_NVFP4 ? 4u : uint32_t(f);
+}
 bool pow2(uint64_t x) { return x && !(x & (x - 1)); }
 uint32_t log2u(uint64_t x) {
   uint32_t r = 0;
@@ -77,6 +81,13 @@ Codebooks build_codebooks() {
     for (int k = 1; k < L; ++k) cb.threshold[bits - 2][k] = float(0.5 * (c[k - 1] + c[k]));
     cb.inv_cmax[bits - 2] = float(1.0 / c[L - 1]);
   }
+  // NVFP4's table: the value of every E2M1 nibble (sign in bit 3, two
+  // exponent bits with bias 1, one mantissa bit; exponent 0 is subnormal)
+  for (int code = 0; code < 16; ++code) {
+    const int e = (code >> 1) & 3, m = code & 1;
+    const float mag = e == 0 ? 0.5f * float(m) : (1.0f + 0.5f * float(m)) * float(1 << e) * 0.5f;
+    cb.centroid[KVQ_NVFP4 - 2][code] = (code & 8) ? -mag : mag;
+  }
   return cb;
 }
 
@@ -92,8 +103,8 @@ int layout_impl(int32_t kf, int32_t vf, uint32_t bs, uint32_t nkv, uint32_t hd, 
   l.block_size = bs;
   l.num_kv_heads = nkv;
   l.head_dim = hd;
-  l.k_rotated = is_turbo(kf) ? 1u : 0u;
-  l.v_rotated = is_turbo(vf) ? 1u : 0u;
+  l.k_rotated = is_rotated(kf) ? 1u : 0u;
+  l.v_rotated = is_rotated(vf) ? 1u : 0u;
   const int32_t fmts[2] = {kf, vf};
   uint64_t data[2], stride[2];
   for (int i = 0; i < 2; ++i) {
@@ -307,6 +318,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO8: e = launch_split_turbo8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_NVFP4: e = launch_split_nvfp4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
@@ -317,6 +329,7 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
       case KVQ_TURBO2: e = launch_scores_turbo2(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO3: e = launch_scores_turbo3(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO8: e = launch_scores_turbo8(int(hd), int(G), a, uint32_t(nwg), s); break;
+      case KVQ_NVFP4: e = launch_scores_nvfp4(int(hd), int(G), a, uint32_t(nwg), s); break;
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);

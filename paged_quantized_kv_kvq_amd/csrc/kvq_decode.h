@@ -45,9 +45,10 @@ constexpr int kMaxSparseSplit = KVQ_MAX_SPARSE_SPLIT;
 
 template <int F>
 struct Fmt {
-  static constexpr int bits = (F == KVQ_BF16) ? 16 : (F == KVQ_FP8_E4M3) ? 8 : F;
-  static constexpr bool turbo = F >= KVQ_TURBO2;             // rotated side
-  static constexpr bool cb = turbo && F != KVQ_TURBO8;       // Lloyd-Max codes (else E4M3 values)
+  static constexpr int bits = (F == KVQ_BF16) ? 16 : (F == KVQ_FP8_E4M3) ? 8 : (F == KVQ_NVFP4) ? 4 : F;
+  static constexpr bool turbo = F >= KVQ_TURBO2;             // per-16 group scales (turbo sides, NVFP4)
+  static constexpr bool rot = turbo && F != KVQ_NVFP4;       // rotated side (is_wht_rotated)
+  static constexpr bool cb = turbo && F != KVQ_TURBO8;       // 4-bit or smaller codes through a table
   static constexpr int sgb = cb ? 1 : (F == KVQ_TURBO8 ? 2 : 0);  // scale bytes per group of 16
 };
 
@@ -392,16 +393,19 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
   } else {
     for (int i = tid; i < G * HD; i += kWaves * kWave) sm.q[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
     __syncthreads();
-    // unnormalized WHT of every q row (1/sqrt(d) goes into the score scale)
-    for (int h2 = 1; h2 < HD; h2 <<= 1) {
-      for (int i = tid; i < G * HD / 2; i += kWaves * kWave) {
-        const int hh = i / (HD / 2), k = i % (HD / 2);
-        const int lo = (k / h2) * 2 * h2 + (k % h2);
-        const float x = sm.q[hh][lo], y = sm.q[hh][lo + h2];
-        sm.q[hh][lo] = x + y;
-        sm.q[hh][lo + h2] = x - y;
+    // unnormalized WHT of every q row (1/sqrt(d) goes into the score scale);
+    // an NVFP4 K side is scored against the query as it is
+    if constexpr (Fmt<KF>::rot) {
+      for (int h2 = 1; h2 < HD; h2 <<= 1) {
+        for (int i = tid; i < G * HD / 2; i += kWaves * kWave) {
+          const int hh = i / (HD / 2), k = i % (HD / 2);
+          const int lo = (k / h2) * 2 * h2 + (k % h2);
+          const float x = sm.q[hh][lo], y = sm.q[hh][lo + h2];
+          sm.q[hh][lo] = x + y;
+          sm.q[hh][lo + h2] = x - y;
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
   const int t = lane % T, r = lane / T;
   QReg<KF, D, G> q;
   prologue<KF, VF, HD, G, D>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
-  const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
+  const float qscale = a.qk_scale * (Fmt<KF>::rot ? a.wht_scale : 1.0f);
   const int first = sp.pb >> a.log2_bs;
 
   DenseState<G, D> st;
@@ -724,7 +728,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   const int t = lane % T, r = lane / T;
   QReg<KF, D, G> q;
   prologue<KF, KVQ_BF16, HD, G, D>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
-  const float qscale = a.qk_scale * (Fmt<KF>::turbo ? a.wht_scale : 1.0f);
+  const float qscale = a.qk_scale * (Fmt<KF>::rot ? a.wht_scale : 1.0f);
   const int first = sp.pb >> a.log2_bs;
 
   float mloc[G];
@@ -1216,7 +1220,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
     o[i] = v * a.v_scale;
   }
   __syncthreads();
-  if constexpr (Fmt<VF>::turbo) {
+  if constexpr (Fmt<VF>::rot) {
     // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
     for (int h2 = 1; h2 < HD; h2 <<= 1) {
       for (int i = tid; i < G * HD / 2; i += NT) {
@@ -1230,7 +1234,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
     }
   }
   float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
-  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::turbo ? o[i] * a.wht_scale : o[i];
+  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::rot ? o[i] * a.wht_scale : o[i];
 }
 
 }  // namespace kvq
@@ -1287,6 +1291,7 @@ hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t n
     case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3>(hd, g, a, nwg, st);
     case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4>(hd, g, a, nwg, st);
     case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8>(hd, g, a, nwg, st);
+    case KVQ_NVFP4: return launch_split_hd<KF, KVQ_NVFP4>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

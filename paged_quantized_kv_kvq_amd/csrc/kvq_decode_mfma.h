@@ -30,11 +30,13 @@
 //     row of position l%16 (operand B).  bf16 x bf16 products are exact in
 //     fp32, and fp8 K widens exactly to bf16, so this is the arithmetic of
 //     the VALU dot products.
-//   * Q.K^T, turbo K: v_mfma_f32_4x4x1_16b_f32 over the same blocks, one dim
-//     per instruction: the rotated query (fp32) in A, the centroid of the
-//     lane's code in B (adjacent codes looked up as pairs).  One accumulator
-//     per 16-dim scale group; the lane's own position's group scales multiply
-//     the group sums afterwards.
+//   * Q.K^T, K with per-16 group scales (turbo, NVFP4):
+//     v_mfma_f32_4x4x1_16b_f32 over the same blocks, one dim per instruction:
+//     the query in fp32 (rotated for a turbo side) in A, the table value of
+//     the lane's code (Lloyd-Max centroid or E2M1 value; adjacent codes looked
+//     up as pairs) or turbo8's E4M3 value in B.  One accumulator per 16-dim
+//     scale group; the lane's own position's group scales multiply the group
+//     sums afterwards.
 //   * Either way two lane swaps then sum the quarters so that row k of 16
 //     lanes holds query head 4 hg + k for the chunk's 16 positions, and the
 //     softmax runs on one value per lane.
@@ -227,15 +229,17 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     auto& qr = sm.u.qrot[w];
     for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
     wave_lds_sync();
-    for (int h2 = 1; h2 < HD; h2 <<= 1) {
-      for (int i = lane; i < G * HD / 2; i += kWave) {
-        const int hh = i / (HD / 2), k = i % (HD / 2);
-        const int lo = (k / h2) * 2 * h2 + (k % h2);
-        const float x = qr[hh][lo], y = qr[hh][lo + h2];
-        qr[hh][lo] = x + y;
-        qr[hh][lo + h2] = x - y;
+    if constexpr (Fmt<KF>::rot) {  // NVFP4 K: the query as it is
+      for (int h2 = 1; h2 < HD; h2 <<= 1) {
+        for (int i = lane; i < G * HD / 2; i += kWave) {
+          const int hh = i / (HD / 2), k = i % (HD / 2);
+          const int lo = (k / h2) * 2 * h2 + (k % h2);
+          const float x = qr[hh][lo], y = qr[hh][lo + h2];
+          qr[hh][lo] = x + y;
+          qr[hh][lo + h2] = x - y;
+        }
+        wave_lds_sync();
       }
-      wave_lds_sync();
     }
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     else ck.s[0] = 0u;
   };
 
-  const float qscale = a.qk_scale * (MG::KT ? a.wht_scale : 1.0f);
+  const float qscale = a.qk_scale * (Fmt<KF>::rot ? a.wht_scale : 1.0f);
   // running state.  Lane l follows head 4 hg + l / 16 (its row of 16 lanes):
   // m is that head's running max (uniform in the row; finite at the start so
   // that a chunk with every position masked rescales by exactly 1), lsum the

@@ -47,6 +47,7 @@ hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t 
     case KVQ_TURBO3: return sparse_hd<KVQ_TURBO3>(hd, g, a, nwg, st);
     case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, nwg, st);
     case KVQ_TURBO8: return sparse_hd<KVQ_TURBO8>(hd, g, a, nwg, st);
+    case KVQ_NVFP4: return sparse_hd<KVQ_NVFP4>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -48,6 +48,22 @@ __device__ __forceinline__ uint32_t e4m3_encode(float v) {
   return code | sign;
 }
 
+// fp32 -> OCP E2M1 nibble (NVFP4's element): saturate to +-6, round to
+// nearest, ties to even, sign of -0 kept.  Each binade of the grid is an
+// evenly spaced set (steps 0.5 below 2, 1 in [2, 4), 2 in [4, 6]); scaled to
+// integers there (exactly), rintf rounds half to even, and an even grid
+// index is an even mantissa.  Index q of a binade maps to nibble q, q + 2,
+// q + 4.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fminf(fabsf(v), 6.0f);
+  uint32_t mag;
+  if (a < 2.0f) mag = uint32_t(rintf(a * 2.0f));
+  else if (a < 4.0f) mag = uint32_t(rintf(a)) + 2u;
+  else mag = uint32_t(rintf(a * 0.5f)) + 4u;
+  return mag | sign;
+}
+
 // E4M3FN byte -> fp32 value (NaN codes are never produced by the encoder).
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;

@@ -55,14 +55,16 @@ __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf;
   const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf;
   const int kqb = hd * kbits / 32;  // K bytes per lane and chunk (a quarter of a row)
-  const bool kturbo = kf >= KVQ_TURBO2;  // rotated K (codebook codes or turbo8's E4M3 values)
+  const bool kturbo = kf >= KVQ_TURBO2;  // grouped-scale K (codes through a table or turbo8's E4M3 values)
   return hd * vbits / 8 <= 128 &&
          (kturbo ? (kqb % 4 == 0 && kqb <= 32 && hd / 4 >= 16) : (kqb <= 64 && kqb % 16 == 0));
 }
 
-// fp32 Lloyd-Max tables for 2/3/4-bit codes, indexed [bits - 2].
+// fp32 Lloyd-Max tables for 2/3/4-bit codes, indexed [bits - 2], and NVFP4's
+// E2M1 values (row KVQ_NVFP4 - 2, in nibble order); a 4-bit-or-smaller format
+// F reads its table at row F - 2.
 struct Codebooks {
-  float centroid[3][16];   // ascending
+  float centroid[4][16];   // Lloyd-Max rows ascending
   float threshold[3][16];  // [k] = midpoint of centroids k-1 and k; [0] unused
   float inv_cmax[3];       // 1 / largest centroid
 };
@@ -149,6 +151,7 @@ hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint3
 hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_nvfp4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 
 hipError_t launch_scores_bf16(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
@@ -156,6 +159,7 @@ hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg
 hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_scores_nvfp4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 

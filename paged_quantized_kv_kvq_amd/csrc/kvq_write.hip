@@ -5,7 +5,9 @@
 // kv_heads, head_dim] rows); "spark_runtime/kv_cache.rs", KvCacheDtype
 // (bf16 copy, fp8 E4M3 with a per-tensor scale, turbo: wht_bf16_inplace then
 // Lloyd-Max codes with one E4M3 scale per 16 elements; Turbo8: the same
-// rotation, then E4M3 values with one BF16 scale per 16 elements).
+// rotation, then E4M3 values with one BF16 scale per 16 elements; Nvfp4:
+// no rotation, E2M1 nibbles with one E4M3 scale per 16 elements, in turbo4's
+// byte layout).
 //
 // One wave64 writes one (token, kv head) row of one side: head_dim/64 values
 // per lane.  The rotation is done in registers: butterfly strides below the
@@ -150,6 +152,37 @@ __device__ __forceinline__ void write_turbo8(const uint32_t (&raw)[HD / 64], uin
   }
 }
 
+// NVFP4: no rotation; per group of 16 of the row itself, the E4M3 scale of
+// absmax / 6, then the E2M1 nibble of x / scale (IEEE division; a zero
+// scale stores zero nibbles), packed as turbo4's codes.
+template <int HD>
+__device__ __forceinline__ void write_nvfp4(const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
+                                            uint32_t row, uint64_t data_bytes, int lane) {
+  constexpr int E = HD / 64;
+  constexpr float kInvE2m1Max = 1.0f / 6.0f;  // RN32(1/6)
+  constexpr int LU = 8 / E;                    // lanes per 32-bit word of nibbles
+  float x[E];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = bf16_bits_to_float(raw[e]);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+  amax = group_max<16 / E>(amax);
+  const uint32_t sigma = e4m3_encode(amax * kInvE2m1Max);
+  const float sq = e4m3_decode(sigma);
+  uint32_t part = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t c = sq > 0.0f ? e2m1_encode(x[e] / sq) : 0u;
+    part |= c << (4 * ((lane * E + e) % 8));
+  }
+#pragma unroll
+  for (int m = 1; m < LU; m <<= 1) part |= uint32_t(__shfl_xor(int(part), m));
+  if ((lane % LU) == 0) reinterpret_cast<uint32_t*>(blk + uint64_t(row) * (HD / 2))[lane / LU] = part;
+  if ((lane % (16 / E)) == 0) blk[data_bytes + uint64_t(row) * (HD / 16) + lane / (16 / E)] = uint8_t(sigma);
+}
+
 template <int HD>
 __device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ src, uint8_t* __restrict__ blk,
                                           uint32_t row, uint64_t data_bytes, float scale,
@@ -173,6 +206,8 @@ __device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ 
     write_turbo<HD, 3>(raw, blk, row, data_bytes, a, lane);
   } else if (fmt == KVQ_TURBO4) {
     write_turbo<HD, 4>(raw, blk, row, data_bytes, a, lane);
+  } else if (fmt == KVQ_NVFP4) {
+    write_nvfp4<HD>(raw, blk, row, data_bytes, lane);
   } else {
     write_turbo8<HD>(raw, blk, row, data_bytes, a, lane);
   }

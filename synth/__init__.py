@@ -26,6 +26,7 @@ size 16, long contexts, sliding window, sparse-V threshold 1e-3):
   6         turbo4 / turbo8, 64 seqs, L ~ U{4096..16384}, Hq 32, Hkv 8, hd 128
   7         turbo8 / turbo8, the same sequences and shapes as 6 (the symmetric pairing
             the asymmetric one is measured against)
+  8         nvfp4 / nvfp4, the same sequences and shapes as 6
 """
 from __future__ import annotations
 
@@ -88,6 +89,8 @@ WORKLOADS = {
     6: Workload(6, "turbo4k-turbo8v", 64, 32, 8, 128, 16, "turbo4", "turbo8", (4096, 16384),
                 outliers=True),
     7: Workload(7, "turbo8-turbo8", 64, 32, 8, 128, 16, "turbo8", "turbo8", (4096, 16384),
+                outliers=True, seed_wid=6),
+    8: Workload(8, "nvfp4-nvfp4", 64, 32, 8, 128, 16, "nvfp4", "nvfp4", (4096, 16384),
                 outliers=True, seed_wid=6),
 }
 

@@ -52,7 +52,8 @@ def test_layout_matches_oracle(kf, vf):
 
 def test_layout_rejects(lib):
     lay = kvq.Layout()
-    assert lib.kvq_pool_layout(5, 0, 16, 8, 128, ctypes.byref(lay)) == INVALID
+    assert lib.kvq_pool_layout(6, 0, 16, 8, 128, ctypes.byref(lay)) == INVALID   # no format 6 or 7
+    assert lib.kvq_pool_layout(0, 7, 16, 8, 128, ctypes.byref(lay)) == INVALID
     assert lib.kvq_pool_layout(0, -1, 16, 8, 128, ctypes.byref(lay)) == INVALID
     assert lib.kvq_pool_layout(0, 0, 0, 8, 128, ctypes.byref(lay)) == INVALID
     assert lib.kvq_pool_layout(0, 0, 16, 8, 128, None) == INVALID
@@ -77,6 +78,8 @@ def test_codebook_rejects_non_turbo():
         kvq.codebook("bf16")
     with pytest.raises(kvq.KvqError):
         kvq.codebook("turbo8")  # E4M3 values, no codebook
+    with pytest.raises(kvq.KvqError):
+        kvq.codebook("nvfp4")   # E2M1 values, no Lloyd-Max book
 
 
 # ---------------------------------------------------------------- argument checks

@@ -62,7 +62,7 @@ def test_pairs_dense(gpu_lib, kf, vf):
 @pytest.mark.parametrize("hd", [64, 256])
 @pytest.mark.parametrize("kf,vf", [("bf16", "bf16"), ("fp8", "turbo2"), ("turbo3", "turbo3"),
                                    ("turbo4", "turbo3"), ("bf16", "turbo4"), ("turbo2", "fp8"), ("turbo8", "turbo8"),
-                                   ("turbo4", "turbo8")])
+                                   ("turbo4", "turbo8"), ("nvfp4", "nvfp4")])
 def test_head_dims(gpu_lib, kf, vf, hd):
     w = synth.small(2000 + hd + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[5, 64, 700], num_q_heads=4,
                     num_kv_heads=2, head_dim=hd, block_size=16, k_format=kf, v_format=vf)
@@ -70,7 +70,8 @@ def test_head_dims(gpu_lib, kf, vf, hd):
 
 
 @pytest.mark.parametrize("g", [1, 2, 8])
-@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3"), ("turbo3", "turbo8")])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3"), ("turbo3", "turbo8"),
+                                   ("nvfp4", "turbo4")])
 def test_group_sizes(gpu_lib, kf, vf, g):
     w = synth.small(3000 + g * 10 + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[33, 517, 260], num_q_heads=2 * g,
                     num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf)
@@ -95,7 +96,7 @@ def test_kv_head_counts(gpu_lib, kf, vf, hkv):
 
 
 @pytest.mark.parametrize("bs", [2, 32, 64])
-@pytest.mark.parametrize("kf,vf", [("turbo2", "fp8"), ("turbo3", "turbo2"), ("turbo8", "turbo8")])
+@pytest.mark.parametrize("kf,vf", [("turbo2", "fp8"), ("turbo3", "turbo2"), ("turbo8", "turbo8"), ("nvfp4", "turbo3")])
 def test_block_sizes_turbo_k(gpu_lib, kf, vf, bs):
     # chunks that start inside a page (block_size > 16) on the turbo-K matrix-core path
     w = synth.small(4700 + bs + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[1, 95, 640, 300], num_q_heads=8,
@@ -105,7 +106,8 @@ def test_block_sizes_turbo_k(gpu_lib, kf, vf, bs):
 
 @pytest.mark.parametrize("thr", [1e-3, 0.05])
 @pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo3", "turbo3"), ("fp8", "fp8"), ("bf16", "bf16"),
-                                   ("turbo4", "turbo2"), ("turbo4", "turbo8"), ("turbo8", "turbo3")])
+                                   ("turbo4", "turbo2"), ("turbo4", "turbo8"), ("turbo8", "turbo3"), ("nvfp4", "nvfp4"),
+                                   ("bf16", "nvfp4")])
 def test_sparse_v(gpu_lib, kf, vf, thr):
     w = synth.small(5000 + int(thr * 1e4) + FMTS.index(kf) * 5 + FMTS.index(vf), lens=[0, 1, 40, 1500, 2100],
                     num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16, k_format=kf, v_format=vf,
@@ -142,3 +144,38 @@ def test_decode_is_deterministic(gpu_lib):
     b = _decode(gpu_lib, st)
     torch.cuda.synchronize()
     assert torch.isfinite(a).all() and torch.equal(a, b)
+
+
+def test_nvfp4_write_ties_and_saturation(gpu_lib):
+    # crafted rows: E2M1 ties at every binade (group absmax 6 * 2^k gives the
+    # exact scale 2^k), saturation (absmax whose E4M3 scale rounds down),
+    # zero and tiny groups, signed zeros; bytes must equal the oracle's
+    from oracle import codecs as ocodecs
+    from oracle import layout as olayout
+    from oracle import write as owrite
+    hd, nkv, bs, nb = 128, 2, 16, 4
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5,
+                     -5.0, -0.0], np.float32)
+    rng = np.random.default_rng(5)
+    x = np.zeros((4, nkv, hd), np.float32)
+    for h in range(nkv):
+        for gi in range(hd // 16):
+            x[0, h, gi * 16:(gi + 1) * 16] = rng.permutation(ties) * np.float32(2.0 ** (gi - 3 + 2 * h))
+    x[1] = rng.standard_normal((nkv, hd)) * 2
+    x[1, :, ::16] = 7.0                       # scale E4M3(7/6) = 1.125: 7 / 1.125 saturates to 6
+    x[2, 0, :16] = -1e-30                     # scale underflows to 0: zero nibbles
+    x[2, 1] = -0.0
+    x[3] = rng.standard_normal((nkv, hd)) * 3
+    bits = ocodecs.bf16_round_bits(x)
+    lay = gpu_lib.pool_layout("nvfp4", "nvfp4", bs, nkv, hd)
+    ks, vs = olayout.pool_layout("nvfp4", "nvfp4", bs, nkv, hd)
+    slots = np.array([5, 17, 33, 62], np.int64)
+    kp = gpu_lib.alloc_pool(lay, "k", nb, fill=0x7F)
+    vp = gpu_lib.alloc_pool(lay, "v", nb, fill=0x7F)
+    key = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    gpu_lib.reshape_and_cache(lay, key, key.clone(), kp, vp, torch.from_numpy(slots).cuda(), 1.0, 1.0)
+    torch.cuda.synchronize()
+    ok_ = np.full(nb * ks.block_stride_bytes, 0x7F, np.uint8)
+    ov_ = np.full(nb * vs.block_stride_bytes, 0x7F, np.uint8)
+    owrite.reshape_and_cache(ks, vs, bits, bits, ok_, ov_, slots)
+    assert np.array_equal(kp.cpu().numpy(), ok_) and np.array_equal(vp.cpu().numpy(), ov_)
