@@ -200,6 +200,39 @@ def traffic_from_profile(workload: str):
     return float(m_b.group(1))
 
 
+def host_block_manager(kvq, w, lens: np.ndarray, steps: int = 200) -> dict:
+    """Host cost of the library's block manager for this workload's decode
+    step: one position appended to every sequence (one batched call), then the
+    block tables exported; the C calls alone, on buffers made once."""
+    import ctypes
+    S, bs = len(lens), w.block_size
+    nb = int(sum((int(L) + steps + bs - 1) // bs for L in lens)) + S
+    bm = kvq.BlockManager(nb, bs)
+    ids = np.array([bm.seq_new() for _ in range(S)], np.uint32)
+    bm.append_many(ids, np.maximum(lens.astype(np.int64) - 1, 0))
+    mb = int((int(lens.max()) + steps + bs - 1) // bs)
+    lib = kvq.load()
+    ones = np.ones(S, np.uint32)
+    slots, cow = np.zeros(S, np.int64), np.zeros((S, 2), np.int32)
+    bt, ln = np.zeros((S, mb), np.int32), np.zeros(S, np.int32)
+    PU, PI = ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(ctypes.c_int32)
+    pid, pone = ids.ctypes.data_as(PU), ones.ctypes.data_as(PU)
+    pslot, pcow = slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cow.ctypes.data_as(PI)
+    pbt, pln = bt.ctypes.data_as(PI), ln.ctypes.data_as(PI)
+    ta = tt = 0.0
+    for _ in range(steps):
+        t0 = time.perf_counter()
+        rc = lib.kvq_blocks_append_many(bm._h, pid, pone, S, pslot, pcow)
+        t1 = time.perf_counter()
+        rc |= lib.kvq_blocks_table(bm._h, pid, S, mb, pbt, pln)
+        t2 = time.perf_counter()
+        assert rc == 0
+        ta += t1 - t0
+        tt += t2 - t1
+    return {"append_us_per_step": round(ta / steps * 1e6, 2), "table_us_per_step": round(tt / steps * 1e6, 2),
+            "sequences": S, "max_blocks_per_seq": mb, "steps": steps}
+
+
 def cpu_baseline(st, w, n_seqs: int):
     """Oracle (plain numpy, fp64 attention) on the first n_seqs sequences."""
     from oracle import decode as odecode
@@ -383,6 +416,7 @@ def main():
                          "peak": 157.3, "unit": "TFLOP/s", "frac": round(flops / (dec_ms * 1e-3) / 1e12 / 157.3, 4),
                          "algorithmic_flops": flops},
         "kernel_source_sha256": kernel_source_hash(),
+        "host_block_manager": host_block_manager(kvq, w, st.lens),
     }
     if args.cpu_seqs:
         log("timing the CPU oracle ...")

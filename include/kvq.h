@@ -2,7 +2,7 @@
  * kvq.h -- paged quantized KV cache for AMD Instinct MI355X (gfx950).
  *
  * Two steps of LLM decoding over a paged KV cache whose K and V sides are each
- * stored in one of five formats (any K/V pairing):
+ * stored in one of seven formats (any K/V pairing):
  *   1. kvq_reshape_and_cache: write new K/V rows into the paged pools;
  *   2. kvq_paged_decode:      one query token per sequence attends to its pages.
  * kvq_pool_layout gives the byte layout the caller allocates the pools with.
@@ -82,7 +82,8 @@ typedef enum kvq_status {
   KVQ_ERR_UNSUPPORTED = -2,  /* valid, but outside what the kernels handle  */
   KVQ_ERR_ALIGNMENT = -3,    /* a pointer or stride is not 16-byte aligned  */
   KVQ_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required  */
-  KVQ_ERR_LAUNCH = -5        /* the HIP runtime rejected a kernel launch    */
+  KVQ_ERR_LAUNCH = -5,       /* the HIP runtime rejected a kernel launch    */
+  KVQ_ERR_EXHAUSTED = -6     /* the block manager has too few free blocks   */
 } kvq_status;
 
 /* Byte layout of the two pools of one attention layer.

@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
            "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
-           "library_path"]
+           "library_path", "BlockManager"]
 
 FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "nvfp4": 5, "turbo8": 8}
 _NAMES = {v: k for k, v in FORMATS.items()}
@@ -85,6 +85,26 @@ def load():
     lib.kvq_status_string.restype = ctypes.c_char_p
     for f in ("kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode", "kvq_codebook"):
         getattr(lib, f).restype = ctypes.c_int
+    PU32, PI32, PI64 = ctypes.POINTER(U32), ctypes.POINTER(I32), ctypes.POINTER(ctypes.c_int64)
+    block_fns = {
+        "kvq_blocks_create": [U32, U32, ctypes.POINTER(P)],
+        "kvq_blocks_reset": [P],
+        "kvq_blocks_num_free": [P, PU32],
+        "kvq_blocks_ref_count": [P, U32, PU32],
+        "kvq_blocks_seq_new": [P, PU32],
+        "kvq_blocks_seq_fork": [P, U32, PU32],
+        "kvq_blocks_seq_free": [P, U32],
+        "kvq_blocks_seq_len": [P, U32, PU32, PU32],
+        "kvq_blocks_append": [P, U32, U32, PI64, PI32, PI32],
+        "kvq_blocks_popn": [P, U32, U32, PU32],
+        "kvq_blocks_append_many": [P, PU32, PU32, U32, PI64, PI32],
+        "kvq_blocks_table": [P, PU32, U32, U32, PI32, PI32],
+    }
+    for f, args in block_fns.items():
+        getattr(lib, f).argtypes = args
+        getattr(lib, f).restype = ctypes.c_int
+    lib.kvq_blocks_destroy.argtypes = [P]
+    lib.kvq_blocks_destroy.restype = None
     _lib = lib
     return lib
 
@@ -203,3 +223,87 @@ def codebook(fmt) -> dict:
     import numpy as np
     return {"levels": n, "centroids": np.array(c[:n], dtype=np.float32),
             "thresholds": np.array(t[:n], dtype=np.float32), "inv_cmax": np.float32(inv.value)}
+
+
+class BlockManager:
+    """The library's host block manager (include/kvq_blocks.h), argument
+    marshalling only.  Block ids index every pool built for the same
+    num_blocks (all layers, K and V)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check(self._lib.kvq_blocks_create(num_blocks, block_size, ctypes.byref(h)), "kvq_blocks_create")
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None:
+            self._lib.kvq_blocks_destroy(self._h)
+            self._h = None
+
+    def _u32(self, fn, *args) -> int:
+        out = ctypes.c_uint32()
+        _check(getattr(self._lib, fn)(self._h, *args, ctypes.byref(out)), fn)
+        return out.value
+
+    def reset(self) -> None:
+        _check(self._lib.kvq_blocks_reset(self._h), "kvq_blocks_reset")
+
+    def num_free(self) -> int:
+        return self._u32("kvq_blocks_num_free")
+
+    def ref_count(self, block: int) -> int:
+        return self._u32("kvq_blocks_ref_count", block)
+
+    def seq_new(self) -> int:
+        return self._u32("kvq_blocks_seq_new")
+
+    def seq_fork(self, parent: int) -> int:
+        return self._u32("kvq_blocks_seq_fork", parent)
+
+    def seq_free(self, seq: int) -> None:
+        _check(self._lib.kvq_blocks_seq_free(self._h, seq), "kvq_blocks_seq_free")
+
+    def seq_len(self, seq: int):
+        n, b = ctypes.c_uint32(), ctypes.c_uint32()
+        _check(self._lib.kvq_blocks_seq_len(self._h, seq, ctypes.byref(n), ctypes.byref(b)), "kvq_blocks_seq_len")
+        return n.value, b.value
+
+    def append(self, seq: int, n: int):
+        """(slots int64 numpy [n], (cow_src, cow_dst))."""
+        import numpy as np
+        slots = np.zeros(max(n, 1), dtype=np.int64)
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        _check(self._lib.kvq_blocks_append(self._h, seq, n, slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                           ctypes.byref(src), ctypes.byref(dst)), "kvq_blocks_append")
+        return slots[:n], (src.value, dst.value)
+
+    def append_many(self, seqs, counts):
+        """(slots int64 numpy [sum(counts)], cow int32 numpy [len(seqs), 2])."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.uint32)
+        cnt = np.ascontiguousarray(counts, dtype=np.uint32)
+        slots = np.zeros(max(int(cnt.sum()), 1), dtype=np.int64)
+        cow = np.zeros((max(len(ids), 1), 2), dtype=np.int32)
+        PU = ctypes.POINTER(ctypes.c_uint32)
+        _check(self._lib.kvq_blocks_append_many(self._h, ids.ctypes.data_as(PU), cnt.ctypes.data_as(PU), len(ids),
+                                                slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                                cow.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))),
+               "kvq_blocks_append_many")
+        return slots[:int(cnt.sum())], cow[:len(ids)]
+
+    def popn(self, seq: int, n: int) -> int:
+        return self._u32("kvq_blocks_popn", seq, n)
+
+    def table(self, seqs, max_blocks: int):
+        """(block_tables int32 numpy [len(seqs), max_blocks], seq_lens int32 numpy)."""
+        import numpy as np
+        ids = np.ascontiguousarray(seqs, dtype=np.uint32)
+        bt = np.zeros((len(ids), max_blocks), dtype=np.int32)
+        lens = np.zeros(len(ids), dtype=np.int32)
+        P32 = ctypes.POINTER(ctypes.c_int32)
+        _check(self._lib.kvq_blocks_table(self._h, ids.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), len(ids),
+                                          max_blocks, bt.ctypes.data_as(P32), lens.ctypes.data_as(P32)),
+               "kvq_blocks_table")
+        return bt, lens

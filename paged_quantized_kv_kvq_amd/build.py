@@ -3,7 +3,8 @@
     python -m paged_quantized_kv_kvq_amd.build [--jobs N] [--verbose]
 
 Every .hip file under csrc/ is compiled to an object in csrc/../_build/, in
-parallel, and linked into paged_quantized_kv_kvq_amd/libkvq.so.  The cache
+parallel, and linked into paged_quantized_kv_kvq_amd/libkvq.so; plain host
+C++ (.cpp, the block manager) is compiled by the host compiler.  The cache
 write is compiled with -ffp-contract=off: its codes must match a plain fp32
 reference bit for bit, so no multiply-add may be fused.
 """
@@ -47,14 +48,25 @@ FAST = ["-ffp-contract=fast", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def sources():
-    return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def host_cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no host C++ compiler found")
 
 
 def compile_one(src: str, verbose: bool, out_dir: str = OUT_DIR, defines=()) -> tuple:
-    obj = os.path.join(out_dir, src.replace(".hip", ".o"))
-    flags = EXACT if src in ("kvq_write.hip", "kvq_api.hip") else FAST
-    cmd = [hipcc()] + COMMON + flags + [f"-I{INCLUDE}"] + [f"-D{d}" for d in defines] + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [host_cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", "-c", os.path.join(CSRC, src),
+               "-o", obj]
+    else:
+        flags = EXACT if src in ("kvq_write.hip", "kvq_api.hip") else FAST
+        cmd = [hipcc()] + COMMON + flags + [f"-I{INCLUDE}"] + [f"-D{d}" for d in defines] + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
     t0 = time.time()
     r = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or r.returncode:

@@ -360,6 +360,7 @@ const char* kvq_status_string(int status) {
     case KVQ_ERR_ALIGNMENT: return "misaligned pointer or stride";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    case KVQ_ERR_EXHAUSTED: return "no free block left";
     default: return "unknown status";
   }
 }

@@ -1,4 +1,4 @@
-"""The C-ABI library on the host: it loads, exports what include/kvq.h
+"""The C-ABI library on the host: it loads, exports what include/*.h
 declares, and its host-only parts (layout, tables, argument checks, workspace
 size query) behave as documented.  No kernel is launched here."""
 import ctypes
@@ -13,7 +13,8 @@ from oracle import codebook as ocb
 from oracle import layout as olayout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvq.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE = 0, -1, -2, -3, -4
 
@@ -24,14 +25,15 @@ def lib():
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    src = "\n".join(open(h).read() for h in HEADERS)
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq_\w+)\s*\(", src, re.M)))
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert set(names) >= {"kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode"}
+    assert set(names) >= {"kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode", "kvq_blocks_append",
+                          "kvq_blocks_table"}
     for n in names:
         assert hasattr(lib, n), n
     out = os.popen(f"nm -D --defined-only {kvq.library_path()}").read()
