@@ -285,6 +285,140 @@ def _cpu_baseline(st, w, n_seqs, odecode, olayout, owrite):
                       f"new token + fp64 decode of all {w.num_q_heads} q heads, one thread, {dt:.1f} s"}
 
 
+def prefill_main(args, kvq, w):
+    """Chunked prefill step: write the chunks' K/V (the held-back last
+    write_tail positions of every sequence), then their queries attend."""
+    keep = range(min(args.cpu_seqs, w.num_seqs)) if args.cpu_seqs else ()
+    st = stage(w, kvq, "cuda", keep_host=keep, log=log)
+    S, Hq, Hkv, hd, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    C = np.minimum(w.write_tail, st.lens).astype(np.int64)
+    qs = np.concatenate([[0], np.cumsum(C)]).astype(np.int32)
+    T, mq = int(qs[-1]), int(C.max())
+    q = synth.prefill_queries(w, T, "cuda")
+    qs_dev = torch.from_numpy(qs).cuda()
+    inv = synth.inv_sqrt_d(hd)
+    mb = st.bt.shape[1]
+    ws = torch.empty(max(16, kvq.prefill_workspace_bytes(st.layout, S, Hq, mb, mq, w.sliding_window)),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, Hq, hd), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    scratch = None if args.warm else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)
+        if ev:
+            ev[0].record(stream)
+        kvq.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool, st.tail_slots,
+                              st.k_scale, st.v_scale, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        kvq.paged_prefill(st.layout, q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev, qs_dev, mq, inv,
+                          w.sliding_window, st.k_scale, st.v_scale, out=out, workspace=ws, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    att = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    stp = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    att_ms, ms_step = float(np.median(att)), float(np.median(stp))
+    assert torch.isfinite(out).all(), "non-finite prefill output"
+    del scratch
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    # algorithmic work: query i of a chunk of C at the end of L positions
+    # attends L - C + i + 1 keys (or the window); Q.K and P.V are 2 hd flops
+    # each per (query head, key).  Bytes: every sequence's attended K and V
+    # rows once (a lower bound), and what tiles of qt queries read by design.
+    kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
+    keys = 0
+    tile_keys = 0
+    qt = max(1, 8 // (Hq // Hkv))
+    for L, c in zip(st.lens.astype(np.int64), C):
+        p = L - c + np.arange(c)
+        lo = np.maximum(0, p + 1 - w.sliding_window) if w.sliding_window else np.zeros_like(p)
+        keys += int((p + 1 - lo).sum())
+        for t0_ in range(0, int(c), qt):
+            hi = int(p[min(t0_ + qt, c) - 1]) + 1
+            tile_keys += hi - int(lo[t0_])
+    flops = 4 * keys * Hq * hd
+    min_bytes = int(sum(int(L) for L in st.lens)) * Hkv * (kb + vb)
+    tile_bytes = tile_keys * Hkv * (kb + vb)
+    tflops = flops / (att_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "chunked-prefill query tokens/s over the quantized paged cache, 1 GPU",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "k_format": w.k_format, "v_format": w.v_format, "num_seqs": S,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": hd, "block_size": bs,
+                   "seq_lens": list(w.seq_len), "chunk": w.write_tail, "query_rows": T, "parallelism": "1 GPU"},
+        "prefill_ms": round(att_ms, 4),
+        "write_ms": round(float(np.median(stp - att)), 4),
+        "wall_s_timed_loop": round(elapsed, 3),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "kernel": "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel",
+                     "algorithmic_flops": flops},
+        "kv_bytes": {"once_per_sequence": min_bytes, "read_by_tiles": tile_bytes, "queries_per_tile": qt,
+                     "gbs_once_per_sequence": round(min_bytes / (att_ms * 1e-3) / 1e9, 1),
+                     "gbs_read_by_tiles": round(tile_bytes / (att_ms * 1e-3) / 1e9, 1)},
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    if args.cpu_seqs:
+        log("timing the CPU oracle ...")
+        rec["cpu_baseline"] = prefill_cpu_baseline(st, w, q, qs, min(args.cpu_seqs, 1), inv)  # ~10-20 s each
+    print(json.dumps(rec), flush=True)
+
+
+def prefill_cpu_baseline(st, w, q, qs, n_seqs: int, inv: float):
+    """Oracle prefill (fp64) of the first n_seqs sequences' chunks, one thread."""
+    from oracle import layout as olayout
+    from oracle import prefill as oprefill
+    from oracle import write as owrite
+    from threadpoolctl import threadpool_limits
+    seqs = list(range(n_seqs))
+    ks, vs = olayout.pool_layout(w.k_format, w.v_format, w.block_size, w.num_kv_heads, w.head_dim)
+    bs = w.block_size
+    remap = {}
+    for s in seqs:
+        for b in st.bt[s, :(int(st.lens[s]) + bs - 1) // bs]:
+            remap.setdefault(int(b), len(remap))
+    n = len(remap) + 1
+    kp = np.zeros(n * ks.block_stride_bytes, np.uint8)
+    vp = np.zeros(n * vs.block_stride_bytes, np.uint8)
+    bt = np.full_like(st.bt, -1)
+    for s in seqs:
+        nb = (int(st.lens[s]) + bs - 1) // bs
+        bt[s, :nb] = [remap[int(b)] for b in st.bt[s, :nb]]
+        K, V = st.host_kv[s]
+        pos = np.arange(int(st.lens[s]))
+        owrite.reshape_and_cache(ks, vs, K[pos], V[pos], kp, vp, bt[s, pos // bs].astype(np.int64) * bs + pos % bs,
+                                 st.k_scale, st.v_scale)
+    qb = q.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oprefill.paged_prefill(ks, vs, qb, qs, kp, vp, bt, st.lens, inv, w.sliding_window, st.k_scale, st.v_scale,
+                               seqs=seqs)
+        dt = time.perf_counter() - t0
+    rows = int(qs[n_seqs] - qs[0])
+    return {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_seqs} of {w.num_seqs} sequences ({rows} query rows): fp64 prefill attention of all "
+                      f"{w.num_q_heads} q heads, one thread, {dt:.1f} s (the chunk's write is not in the sample)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +438,8 @@ def main():
     kvq.load()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if w.prefill:
+        return prefill_main(args, kvq, w)
     keep = range(min(args.cpu_seqs, w.num_seqs)) if args.cpu_seqs else ()
     t0 = time.time()
     st = stage(w, kvq, "cuda", keep_host=keep, log=log)

@@ -177,6 +177,32 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
                      uint32_t sliding_window, float sparse_v_threshold, float k_scale,
                      float v_scale, void* workspace, size_t* workspace_bytes, void* stream);
 
+/* Chunked prefill attention over the same pools -- [kv.rs] attend with its
+ * bottom-right causal mask (query at position p sees keys 0 .. p), after the
+ * chunk's own K/V were written with kvq_reshape_and_cache; [kv_cache.rs]
+ * names chunked prefill among the kernels every format covers.
+ *   q            device, bf16 [T][num_q_heads][head_dim] with row stride
+ *                q_stride elements: the queries of sequence s are rows
+ *                query_start[s] .. query_start[s + 1] - 1, for positions
+ *                seq_lens[s] - C_s .. seq_lens[s] - 1 (C_s = its row count,
+ *                C_s <= seq_lens[s]; rows of positions below 0 are not written).
+ *   out          device, fp32 [T][num_q_heads][head_dim], one row per query.
+ *   query_start  device, int32 [num_seqs + 1], non-decreasing, query_start[0] = 0.
+ *   max_query_len  host: the largest C_s (sizes the grid; larger chunks are a
+ *                caller error: their later queries are not computed).
+ *   block_tables, seq_lens, max_blocks_per_seq, inv_sqrt_d, sliding_window
+ *                (per query: keys p - W < j <= p), k_scale, v_scale, workspace,
+ *                workspace_bytes, stream: as for kvq_paged_decode.  No sparse-V
+ *                threshold: the skip is a decode feature.
+ * Matrix-core kernel only: returns KVQ_ERR_UNSUPPORTED where kvq_paged_decode
+ * would use its VALU split kernel (block_size < 16; V rows over 128 bytes,
+ * e.g. bf16 V at head_dim 128; turbo3 K at head_dim 64). */
+int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
+                      const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+                      uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
+                      float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Introspection (host only): the fp32 Lloyd-Max tables the turbo format uses.
  * centroids[0..L-1] ascending, thresholds[1..L-1] (midpoints; [0] = 0),
  * *inv_cmax = 1/largest centroid, *levels = L = 2^bits.  Buffers hold 16 floats.

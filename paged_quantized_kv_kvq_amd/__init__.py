@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
            "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
-           "library_path", "BlockManager"]
+           "library_path", "BlockManager", "paged_prefill", "prefill_workspace_bytes"]
 
 FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "nvfp4": 5, "turbo8": 8}
 _NAMES = {v: k for k, v in FORMATS.items()}
@@ -79,6 +79,9 @@ def load():
     lib.kvq_reshape_and_cache.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, U32, U32, U32, F32, F32, P]
     lib.kvq_paged_decode.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, U32, U32, U32, F32, U32, U32,
                                      F32, F32, F32, P, ctypes.POINTER(SZ), P]
+    lib.kvq_paged_prefill.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, P, U32, U32, U32, U32, F32, U32,
+                                      U32, F32, F32, P, ctypes.POINTER(SZ), P]
+    lib.kvq_paged_prefill.restype = ctypes.c_int
     lib.kvq_codebook.argtypes = [I32, ctypes.POINTER(F32), ctypes.POINTER(F32), ctypes.POINTER(F32),
                                  ctypes.POINTER(U32)]
     lib.kvq_status_string.argtypes = [ctypes.c_int]
@@ -208,6 +211,52 @@ def paged_decode(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache
         _dev(block_tables, torch.int32, "block_tables"), _dev(seq_lens, torch.int32, "seq_lens"),
         mb, S, Hq, inv_sqrt_d, q.stride(0), sliding_window, sparse_v_threshold, k_scale, v_scale,
         _dev(workspace, torch.uint8, "workspace"), ctypes.byref(n), _stream(stream)), "kvq_paged_decode")
+    return out
+
+
+def prefill_workspace_bytes(layout: Layout, num_seqs: int, num_q_heads: int, max_blocks_per_seq: int,
+                            max_query_len: int, sliding_window: int = 0) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    _check(lib.kvq_paged_prefill(ctypes.byref(layout), None, None, None, None, None, None, None,
+                                 max_blocks_per_seq, num_seqs, num_q_heads, max_query_len, 1.0,
+                                 num_q_heads * layout.head_dim, sliding_window, 1.0, 1.0, None, ctypes.byref(n),
+                                 None), "kvq_paged_prefill (size)")
+    return n.value
+
+
+def paged_prefill(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
+                  inv_sqrt_d: float, sliding_window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """fp32 [T, Hq, hd] chunked-prefill attention output for bf16 q [T, Hq, hd]
+    (sequence s's queries are rows query_start[s] .. query_start[s + 1] - 1)."""
+    lib = load()
+    T, Hq, hd = q.shape
+    S = seq_lens.numel()
+    if q.stride(2) != 1 or q.stride(1) != hd:
+        raise ValueError("q must be [T, Hq, head_dim] with contiguous heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
+    if query_start.numel() != S + 1:
+        raise ValueError("query_start must hold num_seqs + 1 entries")
+    mb = block_tables.shape[1]
+    if out is None:
+        out = torch.empty((T, Hq, hd), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (T, Hq, hd):
+        raise ValueError("out must be contiguous fp32 [T, Hq, head_dim]")
+    need = prefill_workspace_bytes(layout, S, Hq, mb, max_query_len, sliding_window)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    _check(lib.kvq_paged_prefill(
+        ctypes.byref(layout), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.uint8, "k_cache"),
+        _dev(v_cache, torch.uint8, "v_cache"), _dev(out, torch.float32, "out"),
+        _dev(block_tables, torch.int32, "block_tables"), _dev(seq_lens, torch.int32, "seq_lens"),
+        _dev(query_start, torch.int32, "query_start"), mb, S, Hq, max_query_len, inv_sqrt_d, q.stride(0),
+        sliding_window, k_scale, v_scale, _dev(workspace, torch.uint8, "workspace"), ctypes.byref(n),
+        _stream(stream)), "kvq_paged_prefill")
     return out
 
 

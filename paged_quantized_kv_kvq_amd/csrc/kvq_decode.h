@@ -307,6 +307,31 @@ __device__ __forceinline__ SeqSpan split_span(const DecodeArgs& a, uint32_t s, u
   return r;
 }
 
+// Chunked prefill: tile `tile` of sequence s holds queries qrow0 .. qrow0 +
+// nq - 1 (rows of q and out), at positions p0 .. p0 + nq - 1, and attends the
+// key range [lo, hi); split k of the tile covers [lo + k split_len,
+// min(hi, lo + (k + 1) split_len)).  A chunk longer than its sequence (the
+// caller's contract excludes it) leaves its leading tiles empty.
+struct PrefillTile {
+  int qrow0, nq, p0, lo, hi;
+};
+
+__device__ __forceinline__ PrefillTile prefill_tile(const DecodeArgs& a, uint32_t s, uint32_t tile) {
+  PrefillTile t;
+  const int q0 = a.query_start[s], q1 = a.query_start[s + 1];
+  t.qrow0 = q0 + int(tile * a.qt);
+  t.nq = min(int(a.qt), q1 - t.qrow0);
+  t.p0 = a.seq_lens[s] - (q1 - q0) + int(tile * a.qt);
+  if (t.nq <= 0 || t.p0 < 0) {
+    t.nq = 0;
+    t.lo = t.hi = 0;
+    return t;
+  }
+  t.hi = t.p0 + t.nq;
+  t.lo = a.window != 0u ? max(0, t.p0 + 1 - int(a.window)) : 0;
+  return t;
+}
+
 struct Tile {
   uint32_t s, g, split;
   bool valid;
@@ -685,6 +710,47 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
   float* dst = a.out + (uint64_t(s) * a.num_q_heads + hq) * HD;
   for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
+}
+
+// Chunked prefill: one workgroup per (sequence, tile, q head) combines each
+// of the tile's queries' split partials as merge_kernel does, and writes the
+// query's output row.
+template <int HD, bool VROT>
+__global__ __launch_bounds__(kWaves * kWave) void prefill_merge_kernel(const DecodeArgs a, int G) {
+  __shared__ float o[HD];
+  const uint32_t hq = blockIdx.x % a.num_q_heads;
+  const uint32_t unit = blockIdx.x / a.num_q_heads;
+  const uint32_t s = unit % a.num_seqs, tile = unit / a.num_seqs;
+  const uint32_t g = hq / G, h = hq % G;
+  const PrefillTile pt = prefill_tile(a, s, tile);
+  const int R = G * int(a.qt);
+  const int ns = pt.hi > pt.lo ? (pt.hi - pt.lo + int(a.split_len) - 1) / int(a.split_len) : 0;
+  const uint64_t base = ((uint64_t(s) * a.ntiles + tile) * a.num_kv_heads + g) * a.nsplit;
+  const int tid = threadIdx.x;
+  for (int t = 0; t < pt.nq; ++t) {
+    const int r = t * G + int(h);
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * R + r) * 2]);
+    float sum = 0.0f;
+    for (int k = 0; k < ns; ++k) {
+      const float mk = a.ml[((base + k) * R + r) * 2];
+      if (mk > -INFINITY) sum += fast_exp2(mk - M) * a.ml[((base + k) * R + r) * 2 + 1];
+    }
+    const float inv = sum > 0.0f ? a.v_scale / sum : 0.0f;
+    for (int d = tid; d < HD; d += kWaves * kWave) {
+      float acc = 0.0f;
+      for (int k = 0; k < ns; ++k) {
+        const float mk = a.ml[((base + k) * R + r) * 2];
+        if (mk > -INFINITY) acc += fast_exp2(mk - M) * a.part[((base + k) * R + r) * HD + d];
+      }
+      o[d] = acc * inv;
+    }
+    __syncthreads();
+    if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
+    float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + hq) * HD;
+    for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------ sparse V
@@ -1246,52 +1312,65 @@ namespace kvq {
 // ------------------------------------------------------------------ dispatch
 
 // Dense split kernel of a (K, V, head_dim, G) instance: the matrix-core one
-// where its operand sizes allow it (bf16 / fp8 K), else the VALU one.
-template <int KF, int VF, int HD, int G>
+// where its operand sizes allow it (bf16 / fp8 K), else the VALU one.  PF:
+// the chunked-prefill form of the matrix-core kernel (tiles of prefill_qt(G)
+// queries; the host only asks for it where that kernel applies).
+template <int KF, int VF, int HD, int G, bool PF>
 hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
-    if (a.log2_bs >= 4) {  // a 16-position chunk lies in one page
+  if constexpr (PF) {
+    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G * prefill_qt(G)>::ok) {
       const uint32_t nw = mfma_unit_waves(a.num_kv_heads);
-      const uint64_t n = uint64_t(a.num_seqs) * a.nsplit * (a.num_kv_heads / nw);
-      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
+      const uint64_t n = uint64_t(a.num_seqs) * a.ntiles * a.nsplit * (a.num_kv_heads / nw);
+      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G, prefill_qt(G)>), dim3(uint32_t(n)), dim3(nw * kWave), 0,
+                         st, a);
       return hipGetLastError();
     }
+    return hipErrorInvalidValue;
+  } else {
+    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
+      if (a.log2_bs >= 4) {  // a 16-position chunk lies in one page
+        const uint32_t nw = mfma_unit_waves(a.num_kv_heads);
+        const uint64_t n = uint64_t(a.num_seqs) * a.nsplit * (a.num_kv_heads / nw);
+        hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), dim3(nwg), dim3(kWaves * kWave), 0, st, a);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), dim3(nwg), dim3(kWaves * kWave), 0, st, a);
-  return hipGetLastError();
 }
 
-template <int KF, int VF, int HD>
+template <int KF, int VF, int HD, bool PF>
 hipError_t launch_split_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (g) {
-    case 1: return launch_split_one<KF, VF, HD, 1>(a, nwg, st);
-    case 2: return launch_split_one<KF, VF, HD, 2>(a, nwg, st);
-    case 4: return launch_split_one<KF, VF, HD, 4>(a, nwg, st);
-    case 8: return launch_split_one<KF, VF, HD, 8>(a, nwg, st);
+    case 1: return launch_split_one<KF, VF, HD, 1, PF>(a, nwg, st);
+    case 2: return launch_split_one<KF, VF, HD, 2, PF>(a, nwg, st);
+    case 4: return launch_split_one<KF, VF, HD, 4, PF>(a, nwg, st);
+    case 8: return launch_split_one<KF, VF, HD, 8, PF>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int KF, int VF>
+template <int KF, int VF, bool PF>
 hipError_t launch_split_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_split_g<KF, VF, 64>(g, a, nwg, st);
-    case 128: return launch_split_g<KF, VF, 128>(g, a, nwg, st);
-    case 256: return launch_split_g<KF, VF, 256>(g, a, nwg, st);
+    case 64: return launch_split_g<KF, VF, 64, PF>(g, a, nwg, st);
+    case 128: return launch_split_g<KF, VF, 128, PF>(g, a, nwg, st);
+    case 256: return launch_split_g<KF, VF, 256, PF>(g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int KF>
+template <int KF, bool PF = false>
 hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (vf) {
-    case KVQ_BF16: return launch_split_hd<KF, KVQ_BF16>(hd, g, a, nwg, st);
-    case KVQ_FP8_E4M3: return launch_split_hd<KF, KVQ_FP8_E4M3>(hd, g, a, nwg, st);
-    case KVQ_TURBO2: return launch_split_hd<KF, KVQ_TURBO2>(hd, g, a, nwg, st);
-    case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3>(hd, g, a, nwg, st);
-    case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4>(hd, g, a, nwg, st);
-    case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8>(hd, g, a, nwg, st);
-    case KVQ_NVFP4: return launch_split_hd<KF, KVQ_NVFP4>(hd, g, a, nwg, st);
+    case KVQ_BF16: return launch_split_hd<KF, KVQ_BF16, PF>(hd, g, a, nwg, st);
+    case KVQ_FP8_E4M3: return launch_split_hd<KF, KVQ_FP8_E4M3, PF>(hd, g, a, nwg, st);
+    case KVQ_TURBO2: return launch_split_hd<KF, KVQ_TURBO2, PF>(hd, g, a, nwg, st);
+    case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3, PF>(hd, g, a, nwg, st);
+    case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4, PF>(hd, g, a, nwg, st);
+    case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8, PF>(hd, g, a, nwg, st);
+    case KVQ_NVFP4: return launch_split_hd<KF, KVQ_NVFP4, PF>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

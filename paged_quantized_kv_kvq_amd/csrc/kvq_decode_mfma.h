@@ -158,23 +158,52 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
   if constexpr (N % 8 == 4) w[o / 4] = load4(p + o);
 }
 
-template <int KF, int VF, int HD, int G>
+// QT = 0: decode, one query per sequence, rows = the G query heads.
+// QT > 0: chunked prefill.  A unit is (sequence, tile of QT queries, split of
+// the tile's key range); its rows are the QT x G (query, head) pairs, row
+// r = t G + h, and each row masks the positions after its own query (and,
+// with a window, those W or more before it).
+template <int KF, int VF, int HD, int G, int QT = 0>
 __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const DecodeArgs a) {
-  using MG = MfmaGeo<KF, VF, HD, G>;
+  constexpr int R = G * (QT > 0 ? QT : 1);  // rows: (query, head) pairs
+  using MG = MfmaGeo<KF, VF, HD, R>;
   constexpr int NG = MG::NG, DV = MG::DV;
-  __shared__ MfmaSmem<KF, VF, HD, G> sm;
+  __shared__ MfmaSmem<KF, VF, HD, R> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);
   const uint32_t hblocks = a.num_kv_heads / uint32_t(nw);
   const uint32_t unit = blockIdx.x / hblocks;
-  if (unit >= a.num_seqs * a.nsplit) return;
-  const uint32_t s = unit % a.num_seqs, split = unit / a.num_seqs;
   const uint32_t g = (blockIdx.x % hblocks) * uint32_t(nw) + uint32_t(w);
-  const SeqSpan sp = split_span(a, s, split);
-  if (sp.pb >= sp.L) return;  // uniform over the workgroup
   const uint32_t nkv = a.num_kv_heads;
-  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
+  uint32_t s, split, tile = 0;
+  SeqSpan sp;
+  PrefillTile pt0;  // prefill: the tile's queries and key range
+  if constexpr (QT == 0) {
+    if (unit >= a.num_seqs * a.nsplit) return;
+    s = unit % a.num_seqs;
+    split = unit / a.num_seqs;
+    sp = split_span(a, s, split);
+    if (sp.pb >= sp.L) return;  // uniform over the workgroup
+  } else {
+    if (unit >= a.num_seqs * a.ntiles * a.nsplit) return;
+    s = unit % a.num_seqs;
+    tile = (unit / a.num_seqs) % a.ntiles;
+    split = unit / (a.num_seqs * a.ntiles);
+    pt0 = prefill_tile(a, s, tile);
+    sp.L = pt0.hi;
+    sp.j0 = pt0.lo;
+    sp.pb = pt0.lo + int(split * a.split_len);
+    sp.pe = min(pt0.hi, sp.pb + int(a.split_len));
+    if (sp.pb >= sp.pe) return;  // uniform over the workgroup
+  }
+  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;  // decode: the group's rows
+  // prefill: query row of a tile row (nullptr: no query)
+  auto qrow = [&](int r) -> const uint16_t* {
+    const int t = r / G;
+    return (r < R && t < pt0.nq) ? a.q + uint64_t(pt0.qrow0 + t) * a.q_stride + (uint64_t(g) * G + r % G) * HD
+                                 : nullptr;
+  };
 
   // bf16 / fp8 K, query operand A: head 4 hg + lane % 4, dims (lane / 16) * KQ + 4 k .. + 4
   i16x4 qa[MG::KT ? 1 : NG][MG::KT ? 1 : MG::KSTEPS];
@@ -182,11 +211,12 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
       const int h = 4 * hg + (lane & 3);
+      const uint16_t* qr = QT == 0 ? (h < G ? qg + h * HD : nullptr) : qrow(h);
 #pragma unroll
       for (int k = 0; k < MG::KSTEPS; ++k) {
         const int d = (lane >> 4) * MG::KQ + 4 * k;
-        if (h < G) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(qg + h * HD + d);
+        if (QT == 0 ? h < G : qr != nullptr) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(qr + d);
           qa[hg][k] = __builtin_bit_cast(i16x4, x);
         } else {
           qa[hg][k] = i16x4{0, 0, 0, 0};
@@ -227,11 +257,18 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   float qf[MG::KT ? NG : 1][MG::KT ? MG::KQ : 1];
   if constexpr (MG::KT) {
     auto& qr = sm.u.qrot[w];
-    for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
+    if constexpr (QT == 0) {
+      for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
+    } else {
+      for (int i = lane; i < R * HD; i += kWave) {
+        const uint16_t* src = qrow(i / HD);
+        qr[i / HD][i % HD] = src ? bf16_bits_to_float(src[i % HD]) : 0.0f;
+      }
+    }
     wave_lds_sync();
     if constexpr (Fmt<KF>::rot) {  // NVFP4 K: the query as it is
       for (int h2 = 1; h2 < HD; h2 <<= 1) {
-        for (int i = lane; i < G * HD / 2; i += kWave) {
+        for (int i = lane; i < R * HD / 2; i += kWave) {
           const int hh = i / (HD / 2), k = i % (HD / 2);
           const int lo = (k / h2) * 2 * h2 + (k % h2);
           const float x = qr[hh][lo], y = qr[hh][lo + h2];
@@ -245,7 +282,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     for (int hg = 0; hg < NG; ++hg) {
       const int h = 4 * hg + (lane & 3);
 #pragma unroll
-      for (int k = 0; k < MG::KQ; ++k) qf[hg][k] = h < G ? qr[h][(lane >> 4) * MG::KQ + k] : 0.0f;
+      for (int k = 0; k < MG::KQ; ++k) qf[hg][k] = h < R ? qr[h][(lane >> 4) * MG::KQ + k] : 0.0f;
     }
   }
   // every load so far completes before the chunk loop, whose wait counts
@@ -277,7 +314,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const uint32_t soff = a.v_data + ((uint32_t(lane) & 15u) * nkv + g) * (HD / 16 * Fmt<VF>::sgb);
   const int cs = sp.pb & ~(kChunk - 1);
   const int clast = (sp.pe - 1) & ~(kChunk - 1);
-  auto load = [&](int c, MfmaChunk<KF, VF, HD, G>& ck) {
+  auto load = [&](int c, MfmaChunk<KF, VF, HD, R>& ck) {
     const int cl = min(c, clast);  // past the end: reread the last chunk (all masked)
     const int pg = (cl >> a.log2_bs) - first;
     const uint32_t within = uint32_t(cl) & bmask;
@@ -323,7 +360,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 
   // the lane's Q.K^T partial over its quarter for heads 4 hg + r (registers)
   // at position c + lane % 16
-  auto qk = [&](const MfmaChunk<KF, VF, HD, G>& ck, int hg) -> f32x4 {
+  auto qk = [&](const MfmaChunk<KF, VF, HD, R>& ck, int hg) -> f32x4 {
     if constexpr (!MG::KT) {
       i16x4 kb[MG::KSTEPS];
 #pragma unroll
@@ -403,7 +440,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     }
   };
 
-  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, G>& ck) {
+  auto consume = [&](int c, const MfmaChunk<KF, VF, HD, R>& ck) {
     // 1. stage the chunk's V codes in LDS (bf16 / fp8 / turbo8 V: rows
     //    outside the split as zeros, whatever bytes they hold)
 #pragma unroll
@@ -420,14 +457,28 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     }
     // 2. scores: position c + lane % 16, heads 4 hg + r
     const int j = c + (lane & 15);
-    const bool ok = j >= sp.pb && j < sp.pe;
+    const bool in_split = j >= sp.pb && j < sp.pe;
     bool grew = false;
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
+      bool ok = in_split;
+      if constexpr (QT > 0) {  // the row's own causal (and window) limits
+        const int r = 4 * hg + (lane >> 4), t = r / G, p = pt0.p0 + t;
+        ok = ok && r < R && t < pt0.nq && j <= p && (a.window == 0u || j > p - int(a.window));
+      }
       const f32x4 d = qk(ck, hg);
       // 3. the row's head: full score (masked positions: -inf, whatever
-      //    bytes they hold), then its online softmax over the chunk
-      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
+      //    bytes they hold), then its online softmax over the chunk.  The
+      //    lane swaps exchange values between the rows of one position; in
+      //    decode those rows share the mask, in prefill they do not, so there
+      //    the swaps run on every lane (a swap must not read an inactive lane).
+      float sc;
+      if constexpr (QT == 0) {
+        sc = ok ? quarter_sum(d) * qscale : -INFINITY;
+      } else {
+        const float full = quarter_sum(d) * qscale;
+        sc = ok ? full : -INFINITY;
+      }
       const float mn = fmaxf(m[hg], group_max<16>(sc));
       const float al = fast_exp2(m[hg] - mn);
       grew |= mn > m[hg];
@@ -563,7 +614,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   // NB chunks have one exit, at the bottom (the first NB - 1 uses are of
   // zeroed buffers before the split, all masked)
   constexpr int NB = KVQ_DENSE_BUFS;
-  MfmaChunk<KF, VF, HD, G> cb[NB];
+  MfmaChunk<KF, VF, HD, R> cb[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
 #pragma unroll
@@ -598,23 +649,23 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 
   // the wave's partials for its kv head: sums over the row's 16 lanes, one
   // output dim pair per lane and head
-  const uint64_t base = (uint64_t(s) * nkv + g) * a.nsplit + split;
+  const uint64_t base = ((QT == 0 ? uint64_t(s) : uint64_t(s) * a.ntiles + tile) * nkv + g) * a.nsplit + split;
 #pragma unroll
   for (int hg = 0; hg < NG; ++hg) {
     const float z = group_sum<16>(lsum[hg]);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * hg + r;
-      if (h < G) {
-        float* dst = a.part + (base * G + h) * HD + lane * DV;
+      if (h < R) {
+        float* dst = a.part + (base * R + h) * HD + lane * DV;
 #pragma unroll
         for (int v = 0; v < DV; ++v) dst[v] = acc[hg][0][v][r] + acc[hg][1][v][r];
       }
     }
     const int h = 4 * hg + (lane >> 4);
-    if ((lane & 15) == 0 && h < G) {  // a split that saw no position reports -inf
-      a.ml[(base * G + h) * 2] = z > 0.0f ? m[hg] : -INFINITY;
-      a.ml[(base * G + h) * 2 + 1] = z;
+    if ((lane & 15) == 0 && h < R) {  // a split that saw no position reports -inf
+      a.ml[(base * R + h) * 2] = z > 0.0f ? m[hg] : -INFINITY;
+      a.ml[(base * R + h) * 2 + 1] = z;
     }
   }
 }

@@ -51,9 +51,13 @@ namespace kvq {
 // Whether the dense split pass runs on the matrix cores for these formats and
 // head_dim (bf16 / fp8 K: bf16 MFMA for Q.K^T; turbo K: fp32 MFMA over the
 // rotated query; V rows of at most 128 bytes); it also needs block_size >= 16.
+// Chunked prefill: queries per tile of the matrix-core split kernel, so that
+// a tile holds 8 (query, head) rows for the group sizes 1, 2, 4, 8.
+__host__ __device__ constexpr int prefill_qt(int g) { return g >= 8 ? 1 : 8 / g; }
+
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
-  const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf;
-  const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf;
+  const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf == KVQ_NVFP4 ? 4 : kf;
+  const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf == KVQ_NVFP4 ? 4 : vf;
   const int kqb = hd * kbits / 32;  // K bytes per lane and chunk (a quarter of a row)
   const bool kturbo = kf >= KVQ_TURBO2;  // grouped-scale K (codes through a table or turbo8's E4M3 values)
   return hd * vbits / 8 <= 128 &&
@@ -138,6 +142,9 @@ struct DecodeArgs {
   float v_scale;    // fp8 V side's scale, else 1
   float thr;        // sparse-V threshold (0: dense)
   float wht_scale;  // RN32(1/sqrt(head_dim))
+  const int32_t* query_start;  // chunked prefill: [S + 1] first query row of each sequence
+  uint32_t ntiles;             // ... tiles of qt queries per sequence (of the longest chunk)
+  uint32_t qt;                 // ... queries per tile
   Codebooks cb;
 };
 
@@ -145,13 +152,20 @@ struct DecodeArgs {
 // translation unit per K format (split / score kernels) and per V format.
 hipError_t launch_write(int head_dim, const WriteArgs& a, hipStream_t st);
 
-hipError_t launch_split_bf16(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_fp8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
-hipError_t launch_split_nvfp4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_bf16(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_fp8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
+hipError_t launch_split_nvfp4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
+                                bool prefill = false);
 
 hipError_t launch_scores_bf16(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
@@ -162,5 +176,6 @@ hipError_t launch_scores_turbo8(int hd, int g, const DecodeArgs& a, uint32_t nwg
 hipError_t launch_scores_nvfp4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
+hipError_t launch_prefill_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq

@@ -27,6 +27,8 @@ size 16, long contexts, sliding window, sparse-V threshold 1e-3):
   7         turbo8 / turbo8, the same sequences and shapes as 6 (the symmetric pairing
             the asymmetric one is measured against)
   8         nvfp4 / nvfp4, the same sequences and shapes as 6
+  9         chunked prefill, bf16 / turbo4: 16 seqs, L ~ U{2048..8192}, the last 512 positions of
+            each written by the step and attended by 512 queries, Hq 32, Hkv 8, hd 128
 """
 from __future__ import annotations
 
@@ -63,6 +65,7 @@ class Workload:
     write_tail: int = 1               # positions per sequence written by the timed step
     fixed_lens: Optional[Tuple[int, ...]] = None  # explicit per-sequence lengths
     seed_wid: Optional[int] = None    # draw every stream as this workload does (same sequences, other formats)
+    prefill: bool = False             # the step is a chunked prefill of the write_tail positions
 
     @property
     def seed_id(self) -> int:
@@ -92,6 +95,8 @@ WORKLOADS = {
                 outliers=True, seed_wid=6),
     8: Workload(8, "nvfp4-nvfp4", 64, 32, 8, 128, 16, "nvfp4", "nvfp4", (4096, 16384),
                 outliers=True, seed_wid=6),
+    9: Workload(9, "prefill-bf16k-turbo4v", 16, 32, 8, 128, 16, "bf16", "turbo4", (2048, 8192),
+                outliers=True, write_tail=512, prefill=True),
 }
 
 
@@ -177,6 +182,13 @@ def queries(w: Workload, device="cpu") -> torch.Tensor:
     g = _gen(w.seed_id, _S_Q, 0, device)
     x = torch.randn((w.num_seqs, w.num_q_heads, w.head_dim), generator=g, device=device,
                     dtype=torch.float32)
+    return x.to(torch.bfloat16)
+
+
+def prefill_queries(w: Workload, num_rows: int, device="cpu") -> torch.Tensor:
+    """bf16 [num_rows, Hq, hd], N(0,1): the query rows of a chunked prefill."""
+    g = _gen(w.seed_id, _S_Q, 1, device)
+    x = torch.randn((num_rows, w.num_q_heads, w.head_dim), generator=g, device=device, dtype=torch.float32)
     return x.to(torch.bfloat16)
 
 

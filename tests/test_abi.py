@@ -163,3 +163,21 @@ def test_decode_workspace_query(lib):
 def test_status_strings(lib):
     for code in (OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, -5, 99):
         assert lib.kvq_status_string(code)
+
+
+def test_prefill_host_checks(lib):
+    # sizes are computed on the host; unsupported shapes are refused before anything is launched
+    lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
+    n = kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100)
+    assert n > 0 and n % 256 == 0
+    assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100, sliding_window=128) <= n
+    for args in [(("bf16", "bf16", 16, 8, 128), 32),     # bf16 V rows of 256 bytes: VALU-only shape
+                 (("fp8", "turbo2", 8, 8, 128), 32),     # block_size < 16
+                 (("turbo3", "turbo3", 16, 8, 64), 32),  # turbo3 K at head_dim 64
+                 (("fp8", "turbo2", 16, 8, 128), 24)]:   # G = 3
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.prefill_workspace_bytes(kvq.pool_layout(*args[0]), 4, args[1], 64, 100)
+        assert e.value.status in (UNSUPPORTED, INVALID)
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.prefill_workspace_bytes(lay, 4, 32, 64, 0)       # max_query_len 0
+    assert e.value.status == INVALID

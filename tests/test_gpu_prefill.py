@@ -1,0 +1,87 @@
+"""GPU parity of chunked prefill (kvq_paged_prefill, through the C ABI) against
+the oracle's bottom-right causal attention, on pools written by the library.
+Bars as for decode: max-abs <= 2e-3 and rel-L2 <= 1e-3 against fp64."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.gpu import stage
+from kvq_testlib import MAX_ABS, REL_L2, OracleCache, say
+from oracle import codecs as ocodecs
+from oracle import prefill as oprefill
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(kvq, w, chunks, window=0, seed=0, label=""):
+    say(f"case prefill {label}: {w} chunks {chunks}")
+    seqs = list(range(w.num_seqs))
+    st = stage(w, kvq, "cuda", keep_host=seqs, write_tail=0)
+    C = np.minimum(np.asarray(chunks), st.lens)
+    qs = np.concatenate([[0], np.cumsum(C)]).astype(np.int32)
+    T = int(qs[-1])
+    rng = np.random.default_rng(seed)
+    q = ocodecs.bf16_round_bits(rng.standard_normal((T, w.num_q_heads, w.head_dim)).astype(np.float32))
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    mq = max(1, int(C.max()))
+    need = kvq.prefill_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, st.bt.shape[1], mq, window)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")    # NaN bytes
+    out = torch.full((T, w.num_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
+    inv = synth.inv_sqrt_d(w.head_dim)
+    kvq.paged_prefill(st.layout, qd, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev, torch.from_numpy(qs).cuda(), mq,
+                      inv, window, st.k_scale, st.v_scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().astype(np.float64)
+    ora = OracleCache(st, seqs)
+    _, o64 = oprefill.paged_prefill(ora.ks, ora.vs, q, qs, ora.kp, ora.vp, ora.bt, st.lens, inv, window,
+                                    st.k_scale, st.v_scale, seqs=seqs)
+    assert np.all(np.isfinite(g)), f"{label}: non-finite output"
+    err = np.abs(g - o64)
+    rel = np.sqrt(((g - o64) ** 2).sum() / max((o64 ** 2).sum(), 1e-300))
+    assert err.max() <= MAX_ABS, f"{label}: max-abs {err.max():.3e}"
+    assert rel <= REL_L2, f"{label}: rel-L2 {rel:.3e}"
+    say(f"  ok prefill {label}: {T} queries, max-abs {err.max():.2e} rel-L2 {rel:.2e}")
+
+
+LENS = [1, 17, 300, 1100, 2500]
+CHUNKS = [1, 17, 37, 128, 600]   # the 17-long sequence is a whole prompt
+
+
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("fp8", "turbo2"), ("turbo4", "turbo3"), ("turbo8", "turbo8"),
+                                   ("nvfp4", "nvfp4"), ("turbo3", "turbo8"), ("fp8", "fp8"), ("bf16", "nvfp4"),
+                                   ("turbo2", "turbo4")])
+def test_prefill_pairs(gpu_lib, kf, vf):
+    w = synth.small(9000 + len(kf) * 7 + len(vf), lens=LENS, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    block_size=16, k_format=kf, v_format=vf)
+    run_prefill(gpu_lib, w, CHUNKS, seed=1, label=f"{kf}/{vf}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 8])
+@pytest.mark.parametrize("kf,vf", [("bf16", "turbo4"), ("turbo4", "turbo3")])
+def test_prefill_group_sizes(gpu_lib, kf, vf, g):
+    w = synth.small(9100 + g * 10 + len(kf), lens=[40, 700, 333], num_q_heads=2 * g, num_kv_heads=2, head_dim=128,
+                    block_size=16, k_format=kf, v_format=vf)
+    run_prefill(gpu_lib, w, [40, 150, 9], seed=g, label=f"{kf}/{vf} G{g}")
+
+
+@pytest.mark.parametrize("hd", [64, 256])
+@pytest.mark.parametrize("kf,vf", [("fp8", "turbo2"), ("turbo4", "turbo4"), ("nvfp4", "turbo3")])
+def test_prefill_head_dims(gpu_lib, kf, vf, hd):
+    w = synth.small(9200 + hd + len(kf), lens=[90, 517], num_q_heads=8, num_kv_heads=2, head_dim=hd, block_size=16,
+                    k_format=kf, v_format=vf)
+    run_prefill(gpu_lib, w, [90, 64], seed=hd, label=f"{kf}/{vf} hd{hd}")
+
+
+@pytest.mark.parametrize("win", [1, 100, 700])
+def test_prefill_window(gpu_lib, win):
+    w = synth.small(9300 + win, lens=[50, 333, 1600], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                    k_format="turbo3", v_format="turbo4", sliding_window=win)
+    run_prefill(gpu_lib, w, [50, 200, 900], window=win, seed=win, label=f"window {win}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_prefill_block_sizes(gpu_lib, bs):
+    w = synth.small(9400 + bs, lens=[77, 600, 1000], num_q_heads=8, num_kv_heads=4, head_dim=128, block_size=bs,
+                    k_format="fp8", v_format="turbo4")
+    run_prefill(gpu_lib, w, [77, 33, 250], seed=bs, label=f"bs{bs}")

@@ -44,7 +44,7 @@ def _decode(kvq, st):
 
 
 # sequences the oracle rebuilds per workload (its cost grows with their length)
-EXTRA = {1: 0, 2: 1, 3: 0, 4: 1, 5: 1, 6: 0, 7: 0, 8: 0}
+EXTRA = {1: 0, 2: 1, 3: 0, 4: 1, 5: 1, 6: 0, 7: 0, 8: 0, 9: 0}
 
 
 @pytest.mark.timeout(900)
@@ -56,6 +56,8 @@ def test_workload_full_size(gpu_lib, wid):
     say(f"workload {wid} ({w.name}): {w.num_seqs} seqs, lens {lens.min()}..{lens.max()}, oracle seqs {seqs}")
     with timed(f"stage workload {wid}"):
         st = stage(w, gpu_lib, "cuda", keep_host=seqs)
+    if w.prefill:
+        return _prefill_full_size(gpu_lib, w, st, seqs)
     with timed(f"write {st.tail_slots.numel()} tokens + decode"):
         if st.tail_slots.numel():
             gpu_lib.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool,
@@ -79,3 +81,41 @@ def test_workload_full_size(gpu_lib, wid):
         ref = ora.decode(st, synth.inv_sqrt_d(w.head_dim))
     e, rel, namb = check_decode(out_np, ref, seqs, f"workload {wid}")
     say(f"  ok workload {wid}: max-abs {e:.2e} rel-L2 {rel:.2e} ambiguous {namb}")
+
+
+def _prefill_full_size(kvq, w, st, seqs):
+    """The bench's prefill step (write the chunks, then their queries attend),
+    checked on the sampled sequences' query rows against the oracle prefill."""
+    from kvq_testlib import MAX_ABS, REL_L2
+    from oracle import prefill as oprefill
+    C = np.minimum(w.write_tail, st.lens).astype(np.int64)
+    qs = np.concatenate([[0], np.cumsum(C)]).astype(np.int32)
+    T, mq = int(qs[-1]), int(C.max())
+    q = synth.prefill_queries(w, T, "cuda")
+    inv = synth.inv_sqrt_d(w.head_dim)
+    need = kvq.prefill_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, st.bt.shape[1], mq, w.sliding_window)
+    ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")
+    with timed(f"write {st.tail_slots.numel()} tokens + prefill of {T} queries"):
+        kvq.reshape_and_cache(st.layout, st.tail_key, st.tail_value, st.k_pool, st.v_pool, st.tail_slots,
+                              st.k_scale, st.v_scale)
+        out = kvq.paged_prefill(st.layout, q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev,
+                                torch.from_numpy(qs).cuda(), mq, inv, w.sliding_window, st.k_scale, st.v_scale,
+                                workspace=ws).clone()
+        again = kvq.paged_prefill(st.layout, q, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev,
+                                  torch.from_numpy(qs).cuda(), mq, inv, w.sliding_window, st.k_scale, st.v_scale,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.equal(out, again)
+    with timed(f"oracle prefill for {len(seqs)} sequences"):
+        ora = OracleCache(st, seqs)
+        ora.compare_pools(st)
+        qb = q.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        _, o64 = oprefill.paged_prefill(ora.ks, ora.vs, qb, qs, ora.kp, ora.vp, ora.bt, st.lens, inv,
+                                        w.sliding_window, st.k_scale, st.v_scale, seqs=seqs)
+    rows = np.concatenate([np.arange(qs[s], qs[s + 1]) for s in seqs])
+    g = out.cpu().numpy()[rows].astype(np.float64)
+    r = o64[rows]
+    err = np.abs(g - r).max()
+    rel = np.sqrt(((g - r) ** 2).sum() / (r ** 2).sum())
+    assert err <= MAX_ABS and rel <= REL_L2, f"prefill workload: max-abs {err:.2e} rel-L2 {rel:.2e}"
+    say(f"  ok workload {w.wid} (prefill): {len(rows)} query rows, max-abs {err:.2e} rel-L2 {rel:.2e}")
