@@ -344,7 +344,8 @@ def prefill_main(args, kvq, w):
     kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
     keys = 0
     tile_keys = 0
-    qt = max(1, 8 // (Hq // Hkv))
+    rows = 16 if w.k_format in ("bf16", "fp8") and hd <= 128 else 8   # rows of a prefill tile
+    qt = max(1, rows // (Hq // Hkv))
     for L, c in zip(st.lens.astype(np.int64), C):
         p = L - c + np.arange(c)
         lo = np.maximum(0, p + 1 - w.sliding_window) if w.sliding_window else np.zeros_like(p)

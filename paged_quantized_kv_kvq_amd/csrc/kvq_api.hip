@@ -359,7 +359,7 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   if (uint64_t(max_blocks_per_seq) * bs >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   // tiles of qt queries; the key range of a tile spans at most the longest
   // sequence (or the window plus the tile)
-  const uint32_t qt = uint32_t(prefill_qt(int(G)));
+  const uint32_t qt = uint32_t(prefill_qt(layout->k_format, int(hd), int(G)));
   const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
   uint64_t span = uint64_t(max_blocks_per_seq) * bs;
   if (sliding_window && sliding_window + qt - 1 < span) span = sliding_window + qt - 1;

@@ -1313,15 +1313,16 @@ namespace kvq {
 
 // Dense split kernel of a (K, V, head_dim, G) instance: the matrix-core one
 // where its operand sizes allow it (bf16 / fp8 K), else the VALU one.  PF:
-// the chunked-prefill form of the matrix-core kernel (tiles of prefill_qt(G)
+// the chunked-prefill form of the matrix-core kernel (tiles of prefill_qt
 // queries; the host only asks for it where that kernel applies).
 template <int KF, int VF, int HD, int G, bool PF>
 hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   if constexpr (PF) {
-    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G * prefill_qt(G)>::ok) {
+    constexpr int QT = prefill_qt(KF, HD, G);
+    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G * QT>::ok) {
       const uint32_t nw = mfma_unit_waves(a.num_kv_heads);
       const uint64_t n = uint64_t(a.num_seqs) * a.ntiles * a.nsplit * (a.num_kv_heads / nw);
-      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G, prefill_qt(G)>), dim3(uint32_t(n)), dim3(nw * kWave), 0,
+      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G, QT>), dim3(uint32_t(n)), dim3(nw * kWave), 0,
                          st, a);
       return hipGetLastError();
     }

@@ -344,15 +344,18 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   // are in the MFMA layout: register r holds head 4 hg + r.
   constexpr float kNoMax = -3.0e38f;
   float m[NG], lsum[NG];
-  f32x4 acc[NG][2][DV];  // two chains: even and odd positions
+  // two chains (even and odd positions), or one where four or more row
+  // groups already give independent chains (prefill tiles of 16 rows)
+  constexpr int NCH = NG >= 4 ? 1 : 2;
+  f32x4 acc[NG][NCH][DV];
 #pragma unroll
   for (int hg = 0; hg < NG; ++hg) {
     m[hg] = kNoMax;
     lsum[hg] = 0.0f;
 #pragma unroll
     for (int v = 0; v < DV; ++v) {
-      acc[hg][0][v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      acc[hg][1][v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) acc[hg][ch][v] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
   }
   auto& vcode = wv.vcode;
@@ -519,8 +522,8 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         const f32x4 al = *reinterpret_cast<const f32x4*>(&wv.alpha[hg][0]);
 #pragma unroll
         for (int v = 0; v < DV; ++v) {
-          acc[hg][0][v] *= al;
-          acc[hg][1][v] *= al;
+#pragma unroll
+          for (int ch = 0; ch < NCH; ++ch) acc[hg][ch][v] *= al;
         }
       }
     }
@@ -604,7 +607,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
         for (int hg = 0; hg < NG; ++hg)
 #pragma unroll
           for (int v = 0; v < DV; ++v)
-            acc[hg][q & 1][v] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hg][q], b[q][v], acc[hg][q & 1][v], 0, 0, 0);
+            acc[hg][q % NCH][v] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[hg][q], b[q][v], acc[hg][q % NCH][v], 0, 0, 0);
     }
     wave_lds_sync();
   };
@@ -659,7 +662,12 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       if (h < R) {
         float* dst = a.part + (base * R + h) * HD + lane * DV;
 #pragma unroll
-        for (int v = 0; v < DV; ++v) dst[v] = acc[hg][0][v][r] + acc[hg][1][v][r];
+        for (int v = 0; v < DV; ++v) {
+          float o = acc[hg][0][v][r];
+#pragma unroll
+          for (int ch = 1; ch < NCH; ++ch) o += acc[hg][ch][v][r];
+          dst[v] = o;
+        }
       }
     }
     const int h = 4 * hg + (lane >> 4);

@@ -51,9 +51,16 @@ namespace kvq {
 // Whether the dense split pass runs on the matrix cores for these formats and
 // head_dim (bf16 / fp8 K: bf16 MFMA for Q.K^T; turbo K: fp32 MFMA over the
 // rotated query; V rows of at most 128 bytes); it also needs block_size >= 16.
-// Chunked prefill: queries per tile of the matrix-core split kernel, so that
-// a tile holds 8 (query, head) rows for the group sizes 1, 2, 4, 8.
-__host__ __device__ constexpr int prefill_qt(int g) { return g >= 8 ? 1 : 8 / g; }
+// Chunked prefill: queries per tile of the matrix-core split kernel.  A tile
+// holds 16 (query, head) rows for bf16 / fp8 K up to head_dim 128 (their
+// query operands are packed bf16), else 8 (fp32 rotated-query operands, or
+// head_dim 256): fewer tiles re-read the key range, as far as the registers go.
+__host__ __device__ constexpr int prefill_rows(int kf, int hd) {
+  return (kf == KVQ_BF16 || kf == KVQ_FP8_E4M3) && hd <= 128 ? 16 : 8;
+}
+__host__ __device__ constexpr int prefill_qt(int kf, int hd, int g) {
+  return prefill_rows(kf, hd) > g ? prefill_rows(kf, hd) / g : 1;
+}
 
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf == KVQ_NVFP4 ? 4 : kf;
