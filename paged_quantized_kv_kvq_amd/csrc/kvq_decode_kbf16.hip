@@ -6,7 +6,8 @@ namespace kvq {
 
 hipError_t launch_split_bf16(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
                                 bool prefill) {
-  return prefill ? launch_split_k<KVQ_BF16, true>(vf, hd, g, a, nwg, st) : launch_split_k<KVQ_BF16, false>(vf, hd, g, a, nwg, st);
+  return prefill ? launch_split_k<KVQ_BF16, true>(vf, hd, g, a, nwg, st)
+                 : launch_split_k<KVQ_BF16, false>(vf, hd, g, a, nwg, st);
 }
 
 hipError_t launch_scores_bf16(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {

@@ -60,6 +60,17 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
 
+// Waves (kv heads) per workgroup of one instance.  Decode with a grouped-scale
+// K side and G <= 4 is bound by its arithmetic and latency chain at 144
+// VGPRs, three waves per SIMD: workgroups of four kv heads let three of them
+// share a CU where one of eight fits (turbo8 / turbo8 and turbo4 / turbo8,
+// G = 4: 0.51 -> 0.46 ms and 0.57 -> 0.54 ms).  Everything else keeps whole
+// pages to one workgroup.
+template <int KF, int G, int QT>
+constexpr int mfma_waves_cap() {
+  return (QT == 0 && Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves;
+}
+
 template <int KF, int VF, int HD, int G>
 struct MfmaGeo {
   static constexpr int NG = (G + 3) / 4;                    // head groups of four
@@ -93,7 +104,7 @@ struct MfmaWave {
   __attribute__((aligned(16))) float alpha[MG::NG][4];
 };
 
-template <int KF, int VF, int HD, int G>
+template <int KF, int VF, int HD, int G, int NW = kUnitWaves>
 struct MfmaSmem {
   uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
   uint64_t vbase[kMaxPages];  // ... and in the V pool
@@ -102,9 +113,9 @@ struct MfmaSmem {
   f32x2 vpair[Fmt<VF>::cb && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
   f32x2 kpair[Fmt<KF>::cb ? 1 << (2 * Fmt<KF>::bits) : 1];
   union {
-    MfmaWave<KF, VF, HD, G> wv[kUnitWaves];
+    MfmaWave<KF, VF, HD, G> wv[NW];
     // turbo K, before the chunk loop: each wave's query rows, rotated in place
-    float qrot[Fmt<KF>::turbo ? kUnitWaves : 1][Fmt<KF>::turbo ? G : 1][Fmt<KF>::turbo ? HD : 1];
+    float qrot[Fmt<KF>::turbo ? NW : 1][Fmt<KF>::turbo ? G : 1][Fmt<KF>::turbo ? HD : 1];
   } u;
 };
 
@@ -168,7 +179,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   constexpr int R = G * (QT > 0 ? QT : 1);  // rows: (query, head) pairs
   using MG = MfmaGeo<KF, VF, HD, R>;
   constexpr int NG = MG::NG, DV = MG::DV;
-  __shared__ MfmaSmem<KF, VF, HD, R> sm;
+  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G, QT>()> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);
@@ -679,9 +690,9 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 }
 
 // Workgroup shape of split_mfma_kernel: the largest divisor of the kv head
-// count up to kUnitWaves (one wave per kv head).
-inline uint32_t mfma_unit_waves(uint32_t nkv) {
-  for (uint32_t d = kUnitWaves; d > 1; --d)
+// count up to `cap` (one wave per kv head).
+inline uint32_t mfma_unit_waves(uint32_t nkv, uint32_t cap = kUnitWaves) {
+  for (uint32_t d = cap; d > 1; --d)
     if (nkv % d == 0) return d;
   return 1;
 }
