@@ -14,7 +14,7 @@ from oracle import prefill as oprefill
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill(kvq, w, chunks, window=0, seed=0, label=""):
+def run_prefill(kvq, w, chunks, window=0, seed=0, label="", q_pad=0):
     say(f"case prefill {label}: {w} chunks {chunks}")
     seqs = list(range(w.num_seqs))
     st = stage(w, kvq, "cuda", keep_host=seqs, write_tail=0)
@@ -24,6 +24,10 @@ def run_prefill(kvq, w, chunks, window=0, seed=0, label=""):
     rng = np.random.default_rng(seed)
     q = ocodecs.bf16_round_bits(rng.standard_normal((T, w.num_q_heads, w.head_dim)).astype(np.float32))
     qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    if q_pad:  # rows with a larger stride: the same values inside a wider buffer
+        wide = torch.zeros((T, w.num_q_heads + q_pad, w.head_dim), dtype=torch.bfloat16, device="cuda")
+        wide[:, :w.num_q_heads] = qd
+        qd = wide[:, :w.num_q_heads]
     mq = max(1, int(C.max()))
     need = kvq.prefill_workspace_bytes(st.layout, w.num_seqs, w.num_q_heads, st.bt.shape[1], mq, window)
     ws = torch.full((max(need, 16),), 0xFF, dtype=torch.uint8, device="cuda")    # NaN bytes
@@ -85,3 +89,11 @@ def test_prefill_block_sizes(gpu_lib, bs):
     w = synth.small(9400 + bs, lens=[77, 600, 1000], num_q_heads=8, num_kv_heads=4, head_dim=128, block_size=bs,
                     k_format="fp8", v_format="turbo4")
     run_prefill(gpu_lib, w, [77, 33, 250], seed=bs, label=f"bs{bs}")
+
+
+def test_prefill_empty_chunks_and_strided_q(gpu_lib):
+    # an empty sequence, sequences without new queries between others, and q rows
+    # whose stride is wider than Hq x hd
+    w = synth.small(9500, lens=[300, 0, 64, 129, 17], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                    k_format="turbo4", v_format="turbo8")
+    run_prefill(gpu_lib, w, [33, 0, 0, 129, 5], seed=3, label="empty chunks, strided q", q_pad=3)
