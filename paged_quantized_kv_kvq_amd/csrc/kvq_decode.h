@@ -1321,7 +1321,7 @@ hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
     constexpr int QT = prefill_qt(KF, HD, G);
     if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G * QT>::ok) {
       const uint32_t nw = mfma_unit_waves(a.num_kv_heads, mfma_waves_cap<KF, G, QT>());
-      const uint64_t n = uint64_t(a.num_seqs) * a.ntiles * a.nsplit * (a.num_kv_heads / nw);
+      const uint64_t n = mfma_grid(uint64_t(a.num_seqs) * a.ntiles * a.nsplit, a.num_kv_heads / nw);
       hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G, QT>), dim3(uint32_t(n)), dim3(nw * kWave), 0,
                          st, a);
       return hipGetLastError();
@@ -1331,7 +1331,7 @@ hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
     if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
       if (a.log2_bs >= 4) {  // a 16-position chunk lies in one page
         const uint32_t nw = mfma_unit_waves(a.num_kv_heads, mfma_waves_cap<KF, G, 0>());
-        const uint64_t n = uint64_t(a.num_seqs) * a.nsplit * (a.num_kv_heads / nw);
+        const uint64_t n = mfma_grid(uint64_t(a.num_seqs) * a.nsplit, a.num_kv_heads / nw);
         hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
         return hipGetLastError();
       }

@@ -183,9 +183,19 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);
+  // workgroup -> (unit, group of kv heads).  Workgroups are dealt to the 8
+  // XCDs in turn; when a unit spans several workgroups (hblocks > 1) they are
+  // the consecutive workgroups k, k + 1, ... of one XCD (k = blockIdx / 8), so
+  // the 128-byte lines that hold several heads' scale rows of a position are
+  // fetched into one L2.  The grid is padded to whole rounds of 8 units.
   const uint32_t hblocks = a.num_kv_heads / uint32_t(nw);
-  const uint32_t unit = blockIdx.x / hblocks;
-  const uint32_t g = (blockIdx.x % hblocks) * uint32_t(nw) + uint32_t(w);
+  uint32_t unit = blockIdx.x, hb = 0;
+  if (hblocks > 1) {
+    const uint32_t k = blockIdx.x / 8u;
+    unit = (k / hblocks) * 8u + blockIdx.x % 8u;
+    hb = k % hblocks;
+  }
+  const uint32_t g = hb * uint32_t(nw) + uint32_t(w);
   const uint32_t nkv = a.num_kv_heads;
   uint32_t s, split, tile = 0;
   SeqSpan sp;
@@ -687,6 +697,13 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       a.ml[(base * R + h) * 2 + 1] = z;
     }
   }
+}
+
+// Workgroups of split_mfma_kernel for `units` units of `hblocks` workgroups
+// each (whole rounds of 8 units when a unit spans several workgroups; see the
+// mapping in the kernel).
+inline uint64_t mfma_grid(uint64_t units, uint32_t hblocks) {
+  return hblocks > 1 ? (units + 7) / 8 * 8 * hblocks : units;
 }
 
 // Workgroup shape of split_mfma_kernel: the largest divisor of the kv head
