@@ -4,7 +4,8 @@
  * Two steps of LLM decoding over a paged KV cache whose K and V sides are each
  * stored in one of seven formats (any K/V pairing):
  *   1. kvq_reshape_and_cache: write new K/V rows into the paged pools;
- *   2. kvq_paged_decode:      one query token per sequence attends to its pages.
+ *   2. kvq_paged_decode:      one query token per sequence attends to its pages
+ *      (kvq_paged_prefill:    a chunk of query tokens per sequence, causally).
  * kvq_pool_layout gives the byte layout the caller allocates the pools with.
  *
  * Sources (web pages, cited by title and item):
@@ -19,10 +20,12 @@
  *
  * Conventions for every entry point:
  *   - Pointers marked "device" are HIP device pointers; "host" ones are host
- *     memory read before the call returns.  The library allocates nothing,
- *     keeps no state between calls (apart from constant tables built once per
- *     process) and never synchronizes the host: work is queued on `stream`
- *     (a hipStream_t, NULL = the default stream) in call order.
+ *     memory read before the call returns.  The entry points of this header
+ *     allocate nothing, keep no state between calls (apart from constant
+ *     tables built once per process) and never synchronize the host: work is
+ *     queued on `stream` (a hipStream_t, NULL = the default stream) in call
+ *     order.  (The host block manager of kvq_blocks.h keeps host bookkeeping
+ *     of its own.)
  *   - Every argument is checked on the host before anything is launched; a
  *     failed check returns a negative kvq_status and launches nothing.  The
  *     checks cannot see device memory: slot ids, block ids and sequence
