@@ -186,15 +186,16 @@ def decode_kernels(w) -> str:
     return "kvq_paged_decode: " + ("split_mfma_kernel" if mfma else "split_kernel") + " + merge_kernel"
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per decode call from the committed rocprofv3 counter summary,
-    or None when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+def traffic_from_profile(workload: str, step: str = "decode"):
+    """HBM bytes per decode (or prefill) call from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{step}_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
-    m_b = re.search(r"hbm_bytes_per_decode:\s*([0-9.eE+]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_(?:decode|call):\s*([0-9.eE+]+)", txt)
     if not m_hash or not m_b or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_b.group(1))
@@ -370,7 +371,7 @@ def prefill_main(args, kvq, w):
         "write_ms": round(float(np.median(stp - att)), 4),
         "wall_s_timed_loop": round(elapsed, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "frac": round(tflops / 157.3, 4), "traffic": traffic_from_profile(w.name, "prefill"),
                      "kernel": "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel",
                      "algorithmic_flops": flops},
         "kv_bytes": {"once_per_sequence": min_bytes, "read_by_tiles": tile_bytes, "queries_per_tile": qt,
