@@ -363,9 +363,11 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
   uint64_t span = uint64_t(max_blocks_per_seq) * bs;
   if (sliding_window && sliding_window + qt - 1 < span) span = sliding_window + qt - 1;
-  uint32_t sl = kMaxSplitLen;
+  // splits as long as the staged page offsets allow (fewer partials to
+  // write and merge), shorter only while the grid is small
+  uint32_t sl = 8192;
   while (sl > 256 && uint64_t(num_seqs) * ntiles * ((span + sl - 1) / sl) * nkv < kTargetWorkgroups) sl >>= 1;
-  while (sl > 16 && sl / bs + 2 > kPagesPerSplit) sl >>= 1;
+  while (sl > 16 && sl / bs + 2 > KVQ_PREFILL_MAX_PAGES) sl >>= 1;
   const uint64_t nsplit = (span + sl - 1) / sl;
   const uint64_t units = uint64_t(num_seqs) * ntiles * nkv * nsplit;
   const uint64_t rows = uint64_t(G) * qt;

@@ -59,6 +59,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
+// page offsets of one split staged in LDS by the prefill form: a prefill
+// split is long (a tile's whole key range, up to 8192 positions at block
+// size 16), so that its partials stay few; the grid is large without splits
+constexpr int kPrefillMaxPages = KVQ_PREFILL_MAX_PAGES;
 
 // Waves (kv heads) per workgroup of one instance.  Decode with a grouped-scale
 // K side and G <= 4 is bound by its arithmetic and latency chain at 144
@@ -104,10 +108,10 @@ struct MfmaWave {
   __attribute__((aligned(16))) float alpha[MG::NG][4];
 };
 
-template <int KF, int VF, int HD, int G, int NW = kUnitWaves>
+template <int KF, int VF, int HD, int G, int NW = kUnitWaves, int NP = kMaxPages>
 struct MfmaSmem {
-  uint64_t kbase[kMaxPages];  // byte offset of each page of the split in the K pool
-  uint64_t vbase[kMaxPages];  // ... and in the V pool
+  uint64_t kbase[NP];  // byte offset of each page of the split in the K pool
+  uint64_t vbase[NP];  // ... and in the V pool
   float vcen[16];
   // turbo sides: centroids of every pair of adjacent codes (index lo | hi << bits)
   f32x2 vpair[Fmt<VF>::cb && MfmaGeo<KF, VF, HD, G>::DV >= 2 ? 1 << (2 * Fmt<VF>::bits) : 1];
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   constexpr int R = G * (QT > 0 ? QT : 1);  // rows: (query, head) pairs
   using MG = MfmaGeo<KF, VF, HD, R>;
   constexpr int NG = MG::NG, DV = MG::DV;
-  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G, QT>()> sm;
+  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G, QT>(), (QT > 0 ? kPrefillMaxPages : kMaxPages)> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);

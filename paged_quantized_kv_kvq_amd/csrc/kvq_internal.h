@@ -12,6 +12,9 @@
 #ifndef KVQ_WAVES
 #define KVQ_WAVES 4              // waves per decode workgroup
 #endif
+#ifndef KVQ_PREFILL_MAX_PAGES
+#define KVQ_PREFILL_MAX_PAGES 520   // page offsets of one prefill split staged in LDS (8192 positions at bs 16)
+#endif
 #ifndef KVQ_TARGET_WORKGROUPS
 #define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many
 #endif
