@@ -34,8 +34,9 @@ from .layout import Side, is_rotated
 def paged_prefill(k_side: Side, v_side: Side, q_bits: np.ndarray, query_start: np.ndarray,
                   k_pool: np.ndarray, v_pool: np.ndarray, block_tables: np.ndarray, seq_lens: np.ndarray,
                   inv_sqrt_d: float, sliding_window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
-                  seqs=None):
-    """(out fp32 [T, Hq, hd], out fp64 [T, Hq, hd]); rows of sequences not in `seqs` stay zero."""
+                  seqs=None, rows=None):
+    """(out fp32 [T, Hq, hd], out fp64 [T, Hq, hd]); rows of sequences not in `seqs`, and rows not
+    in `rows` when it is given (a set of query row indices), stay zero."""
     T, Hq, hd = q_bits.shape
     nkv, bs = k_side.num_kv_heads, k_side.block_size
     G = Hq // nkv
@@ -56,6 +57,8 @@ def paged_prefill(k_side: Side, v_side: Side, q_bits: np.ndarray, query_start: n
         K = dequant_rows(k_pool, k_side, slots, k_scale)          # [L, Hkv, hd]
         V = dequant_rows(v_pool, v_side, slots, v_scale)
         for i in range(C):
+            if rows is not None and q0 + i not in rows:
+                continue
             p = L - C + i
             j0 = max(0, p + 1 - sliding_window) if sliding_window > 0 else 0
             for h in range(Hq):

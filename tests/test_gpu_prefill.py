@@ -97,3 +97,34 @@ def test_prefill_empty_chunks_and_strided_q(gpu_lib):
     w = synth.small(9500, lens=[300, 0, 64, 129, 17], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                     k_format="turbo4", v_format="turbo8")
     run_prefill(gpu_lib, w, [33, 0, 0, 129, 5], seed=3, label="empty chunks, strided q", q_pad=3)
+
+
+def test_prefill_long_chunk_sampled_rows(gpu_lib):
+    # a 4096-query chunk at the end of 16384 positions and a 1000-query chunk of
+    # a 9000-long sequence: 1024 tiles, tiles whose key range spans two splits
+    # of 8192; sampled query rows (chunk edges, tile and split boundaries, random)
+    w = synth.small(9600, lens=[16384, 9000], num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    k_format="bf16", v_format="turbo3")
+    say(f"case prefill long chunk: {w}")
+    st = stage(w, gpu_lib, "cuda", keep_host=[0, 1], write_tail=0)
+    C = np.array([4096, 1000])
+    qs = np.array([0, 4096, 5096], np.int32)
+    rng = np.random.default_rng(11)
+    q = ocodecs.bf16_round_bits(rng.standard_normal((5096, w.num_q_heads, w.head_dim)).astype(np.float32))
+    qd = torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda()
+    inv = synth.inv_sqrt_d(w.head_dim)
+    out = gpu_lib.paged_prefill(st.layout, qd, st.k_pool, st.v_pool, st.bt_dev, st.lens_dev, torch.from_numpy(qs).cuda(),
+                                4096, inv)
+    torch.cuda.synchronize()
+    rows = sorted(set([0, 1, 3, 4, 5, 4095, 4094, 4096, 4097, 5095, 2047, 2048, 3807, 3808]) |
+                  set(int(x) for x in rng.choice(5096, 24, replace=False)))
+    ora = OracleCache(st, [0, 1])
+    _, o64 = oprefill.paged_prefill(ora.ks, ora.vs, q, qs, ora.kp, ora.vp, ora.bt, st.lens, inv, 0,
+                                    st.k_scale, st.v_scale, rows=set(rows))
+    g = out.cpu().numpy()[rows].astype(np.float64)
+    r = o64[rows]
+    err = np.abs(g - r).max()
+    rel = np.sqrt(((g - r) ** 2).sum() / (r ** 2).sum())
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert err <= MAX_ABS and rel <= REL_L2, f"long chunk: max-abs {err:.2e} rel-L2 {rel:.2e}"
+    say(f"  ok prefill long chunk: {len(rows)} sampled rows, max-abs {err:.2e} rel-L2 {rel:.2e}")
