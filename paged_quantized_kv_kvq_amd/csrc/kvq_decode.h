@@ -1112,7 +1112,12 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   // wave's first batch of segments, a first record per lane, the statistics
   const int myc0 = lane < nseg ? a.cnt[sbase * kWaves + w + kVWaves * lane] : 0;
   uint32_t spec[RS];
-  load_record<G>(a.crec + ((sbase * kWaves + w) * a.seg_cap + lane) * RS, spec);
+  if (w < nseg_all) {  // the wave's first segment exists (the last head's would lie past the workspace)
+    load_record<G>(a.crec + ((sbase * kWaves + w) * a.seg_cap + lane) * RS, spec);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RS; ++i) spec[i] = 0u;
+  }
   if (tid < 16) {
     if constexpr (Fmt<VF>::cb) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
   }
