@@ -674,6 +674,59 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
   __syncthreads();
 }
 
+// Log-sum-exp merge of the ns split partials of one output row: split k has
+// its (max, sum) pair at ml + k * mls and its unnormalized row at
+// part + k * ps.  M = max m_k, Z = sum_k 2^(m_k - M) l_k, and
+// o[d] = scale / Z * sum_k 2^(m_k - M) part_k[d]; splits with m_k = -inf
+// (nothing attended) add nothing.  Each loop takes B splits at a time and
+// issues all of their loads before using any, so a row waits for about
+// 3 ns / B memory round trips instead of 3 ns; the additions keep the split
+// order, so the result does not depend on B.  Decode rows have up to tens of
+// splits (B = 8); a prefill row has one or two, where wider batches only add
+// masked slots (B = 1 measured faster there).
+template <int HD, int B>
+__device__ __forceinline__ void merge_row(const float* ml, uint32_t mls, const float* part, uint32_t ps, int ns,
+                                          float scale, float* o) {
+  float M = -INFINITY;
+  for (int k0 = 0; k0 < ns; k0 += B) {
+    float m[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) m[u] = k0 + u < ns ? ml[uint64_t(k0 + u) * mls] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < B; ++u) M = fmaxf(M, m[u]);
+  }
+  float sum = 0.0f;
+  for (int k0 = 0; k0 < ns; k0 += B) {
+    float m[B], l[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bool in = k0 + u < ns;
+      m[u] = in ? ml[uint64_t(k0 + u) * mls] : -INFINITY;
+      l[u] = in ? ml[uint64_t(k0 + u) * mls + 1] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (m[u] > -INFINITY) sum += fast_exp2(m[u] - M) * l[u];
+  }
+  const float inv = sum > 0.0f ? scale / sum : 0.0f;
+  for (int d = threadIdx.x; d < HD; d += kWaves * kWave) {
+    float acc = 0.0f;
+    for (int k0 = 0; k0 < ns; k0 += B) {
+      float m[B], v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const bool in = k0 + u < ns;
+        m[u] = in ? ml[uint64_t(k0 + u) * mls] : -INFINITY;
+        v[u] = in ? part[uint64_t(k0 + u) * ps + d] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (m[u] > -INFINITY) acc += fast_exp2(m[u] - M) * v[u];
+    }
+    o[d] = acc * inv;
+  }
+}
+
 // Dense path: one workgroup per (sequence, q head) combines the split
 // partials with log-sum-exp weights, then applies the fp8 V scale and the
 // inverse rotation.
@@ -687,25 +740,8 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
   const int tid = threadIdx.x;
-  {
-    const uint64_t base = (uint64_t(s) * a.num_kv_heads + g) * a.nsplit;
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * G + h) * 2]);
-    float sum = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const float mk = a.ml[((base + k) * G + h) * 2];
-      if (mk > -INFINITY) sum += fast_exp2(mk - M) * a.ml[((base + k) * G + h) * 2 + 1];
-    }
-    const float inv = sum > 0.0f ? a.v_scale / sum : 0.0f;
-    for (int d = tid; d < HD; d += kWaves * kWave) {
-      float acc = 0.0f;
-      for (int k = 0; k < ns; ++k) {
-        const float mk = a.ml[((base + k) * G + h) * 2];
-        if (mk > -INFINITY) acc += fast_exp2(mk - M) * a.part[((base + k) * G + h) * HD + d];
-      }
-      o[d] = acc * inv;
-    }
-  }
+  const uint64_t row = ((uint64_t(s) * a.num_kv_heads + g) * a.nsplit) * G + h;  // split 0's row
+  merge_row<HD, 8>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD, uint32_t(G) * HD, ns, a.v_scale, o);
   __syncthreads();
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
   float* dst = a.out + (uint64_t(s) * a.num_q_heads + hq) * HD;
@@ -728,23 +764,8 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_merge_kernel(const Dec
   const uint64_t base = ((uint64_t(s) * a.ntiles + tile) * a.num_kv_heads + g) * a.nsplit;
   const int tid = threadIdx.x;
   for (int t = 0; t < pt.nq; ++t) {
-    const int r = t * G + int(h);
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[((base + k) * R + r) * 2]);
-    float sum = 0.0f;
-    for (int k = 0; k < ns; ++k) {
-      const float mk = a.ml[((base + k) * R + r) * 2];
-      if (mk > -INFINITY) sum += fast_exp2(mk - M) * a.ml[((base + k) * R + r) * 2 + 1];
-    }
-    const float inv = sum > 0.0f ? a.v_scale / sum : 0.0f;
-    for (int d = tid; d < HD; d += kWaves * kWave) {
-      float acc = 0.0f;
-      for (int k = 0; k < ns; ++k) {
-        const float mk = a.ml[((base + k) * R + r) * 2];
-        if (mk > -INFINITY) acc += fast_exp2(mk - M) * a.part[((base + k) * R + r) * HD + d];
-      }
-      o[d] = acc * inv;
-    }
+    const uint64_t row = base * R + uint64_t(t * G + int(h));  // split 0's row of this query and head
+    merge_row<HD, 1>(a.ml + row * 2, uint32_t(R) * 2, a.part + row * HD, uint32_t(R) * HD, ns, a.v_scale, o);
     __syncthreads();
     if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
     float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + hq) * HD;
