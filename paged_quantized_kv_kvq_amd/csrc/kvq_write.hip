@@ -9,8 +9,10 @@
 // no rotation, E2M1 nibbles with one E4M3 scale per 16 elements, in turbo4's
 // byte layout).
 //
-// One wave64 writes one (token, kv head) row of one side: head_dim/64 values
-// per lane.  The rotation is done in registers: butterfly strides below the
+// One wave64 writes the K and the V row of one (token, kv head): head_dim/64
+// values per lane and side.  Both source rows and the slot are requested
+// together (the rows do not depend on the slot), so a wave waits for one
+// memory round trip before it computes.  The rotation is done in registers: butterfly strides below the
 // per-lane count stay in the lane, the rest are lane-xor exchanges.  Group
 // absmax and code packing are lane reductions; nothing touches LDS.
 //
@@ -184,12 +186,10 @@ __device__ __forceinline__ void write_nvfp4(const uint32_t (&raw)[HD / 64], uint
 }
 
 template <int HD>
-__device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ src, uint8_t* __restrict__ blk,
+__device__ __forceinline__ void write_row(int fmt, const uint32_t (&raw)[HD / 64], uint8_t* __restrict__ blk,
                                           uint32_t row, uint64_t data_bytes, float scale,
                                           const WriteArgs& a, int lane) {
   constexpr int E = HD / 64;
-  uint32_t raw[E];
-  load_bf16<E>(src, lane, raw);
   if (fmt == KVQ_BF16) {
     uint8_t* dst = blk + uint64_t(row) * HD * 2;
     if constexpr (E == 1) reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(raw[0]);
@@ -213,39 +213,67 @@ __device__ __forceinline__ void write_row(int fmt, const uint16_t* __restrict__ 
   }
 }
 
-// Work item w = (token, kv head, side) with side fastest; one wave per item.
-template <int HD>
+// Work item w = (token, kv head) and, with SIDES, w = (token, kv head, side)
+// with the side fastest; one wave per item writes its row of each side.  A
+// wave that writes both sides waits for one round trip for two rows, which
+// pays on large writes; a small write (every wave resident at once) finishes
+// sooner with one side per wave, two shorter chains in parallel.
+template <int HD, bool SIDES>
 __global__ __launch_bounds__(256) void write_kernel(const WriteArgs a) {
+  constexpr int E = HD / 64;
+  constexpr uint32_t per_item = SIDES ? 2u : 1u;
   const uint32_t item = blockIdx.x * 4u + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const uint32_t per_token = a.num_kv_heads * 2u;
-  if (item >= a.num_tokens * per_token) return;
-  const uint32_t t = item / per_token;
-  const uint32_t rem = item - t * per_token;
-  const uint32_t h = rem >> 1;
+  if (item >= a.num_tokens * a.num_kv_heads * per_item) return;
+  const uint32_t th = item / per_item;  // (token, kv head)
+  const uint32_t t = th / a.num_kv_heads;
+  const uint32_t h = th - t * a.num_kv_heads;
+  const uint16_t* ksrc = a.key + uint64_t(t) * a.key_stride + h * HD;
+  const uint16_t* vsrc = a.value + uint64_t(t) * a.value_stride + h * HD;
   const int64_t slot = a.slots[t];
-  if (slot < 0) return;
-  const uint64_t blk = uint64_t(slot) >> a.log2_bs;
-  const uint32_t off = uint32_t(slot) & ((1u << a.log2_bs) - 1u);
-  const uint32_t row = off * a.num_kv_heads + h;
-  if ((rem & 1u) == 0) {
-    write_row<HD>(a.k_format, a.key + uint64_t(t) * a.key_stride + h * HD, a.k_cache + blk * a.k_stride,
-                  row, a.k_data, a.k_scale, a, lane);
+  // The empty asm statements read the loaded values: the compiler must issue
+  // the loads before them, and does not move the row loads below the branch
+  // on the slot.
+  if constexpr (SIDES) {
+    const bool vside = (item & 1u) != 0;
+    uint32_t raw[E];
+    load_bf16<E>(vside ? vsrc : ksrc, lane, raw);
+    asm volatile("" ::"v"(raw[0]), "v"(uint32_t(slot)));
+    if (slot < 0) return;
+    const uint64_t blk = uint64_t(slot) >> a.log2_bs;
+    const uint32_t row = (uint32_t(slot) & ((1u << a.log2_bs) - 1u)) * a.num_kv_heads + h;
+    if (!vside) write_row<HD>(a.k_format, raw, a.k_cache + blk * a.k_stride, row, a.k_data, a.k_scale, a, lane);
+    else write_row<HD>(a.v_format, raw, a.v_cache + blk * a.v_stride, row, a.v_data, a.v_scale, a, lane);
   } else {
-    write_row<HD>(a.v_format, a.value + uint64_t(t) * a.value_stride + h * HD, a.v_cache + blk * a.v_stride,
-                  row, a.v_data, a.v_scale, a, lane);
+    uint32_t kraw[E], vraw[E];
+    load_bf16<E>(ksrc, lane, kraw);
+    load_bf16<E>(vsrc, lane, vraw);
+    asm volatile("" ::"v"(kraw[0]), "v"(vraw[0]), "v"(uint32_t(slot)));
+    if (slot < 0) return;
+    const uint64_t blk = uint64_t(slot) >> a.log2_bs;
+    const uint32_t row = (uint32_t(slot) & ((1u << a.log2_bs) - 1u)) * a.num_kv_heads + h;
+    write_row<HD>(a.k_format, kraw, a.k_cache + blk * a.k_stride, row, a.k_data, a.k_scale, a, lane);
+    write_row<HD>(a.v_format, vraw, a.v_cache + blk * a.v_stride, row, a.v_data, a.v_scale, a, lane);
   }
 }
+
+// Writes of at most this many (token, kv head) rows take one wave per side.
+constexpr uint64_t kSplitSidesRows = 2048;
 
 }  // namespace
 
 hipError_t launch_write(int head_dim, const WriteArgs& a, hipStream_t st) {
-  const uint64_t items = uint64_t(a.num_tokens) * a.num_kv_heads * 2u;
+  const uint64_t rows = uint64_t(a.num_tokens) * a.num_kv_heads;
+  const bool sides = rows <= kSplitSidesRows;
+  const uint64_t items = rows * (sides ? 2u : 1u);
   const dim3 grid(uint32_t((items + 3) / 4)), block(256);
-  switch (head_dim) {
-    case 64: hipLaunchKernelGGL(write_kernel<64>, grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL(write_kernel<128>, grid, block, 0, st, a); break;
-    case 256: hipLaunchKernelGGL(write_kernel<256>, grid, block, 0, st, a); break;
+  switch (head_dim * 2 + (sides ? 1 : 0)) {
+    case 128: hipLaunchKernelGGL((write_kernel<64, false>), grid, block, 0, st, a); break;
+    case 129: hipLaunchKernelGGL((write_kernel<64, true>), grid, block, 0, st, a); break;
+    case 256: hipLaunchKernelGGL((write_kernel<128, false>), grid, block, 0, st, a); break;
+    case 257: hipLaunchKernelGGL((write_kernel<128, true>), grid, block, 0, st, a); break;
+    case 512: hipLaunchKernelGGL((write_kernel<256, false>), grid, block, 0, st, a); break;
+    case 513: hipLaunchKernelGGL((write_kernel<256, true>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
