@@ -179,3 +179,39 @@ def test_nvfp4_write_ties_and_saturation(gpu_lib):
     ov_ = np.full(nb * vs.block_stride_bytes, 0x7F, np.uint8)
     owrite.reshape_and_cache(ks, vs, bits, bits, ok_, ov_, slots)
     assert np.array_equal(kp.cpu().numpy(), ok_) and np.array_equal(vp.cpu().numpy(), ov_)
+
+
+@pytest.mark.parametrize("T", [1024, 1025])
+@pytest.mark.parametrize("kf,vf", [("turbo4", "turbo3"), ("bf16", "fp8"), ("nvfp4", "turbo8"), ("turbo2", "bf16")])
+def test_write_row_count_switch(gpu_lib, kf, vf, T):
+    # the write takes one wave per side up to 2048 (token, kv head) rows and
+    # one wave for both sides above: 1024 tokens x 2 kv heads is the last
+    # count of the first form, 1025 the first of the second; scattered slots
+    # with about one in eight skipped (-1); pool bytes must equal the oracle's
+    from oracle import layout as olayout
+    from oracle import write as owrite
+    hd, nkv, bs = 128, 2, 16
+    nb = (T + bs - 1) // bs + 3
+    say(f"case write {kf}/{vf} T={T}")
+    rng = np.random.default_rng([7100, T, FMTS.index(kf), FMTS.index(vf)])
+    kx = rng.standard_normal((T, nkv, hd)).astype(np.float32)
+    vx = rng.standard_normal((T, nkv, hd)).astype(np.float32)
+    kx[:, :, 5] *= 20.0
+    kb = torch.from_numpy(kx).to(torch.bfloat16)
+    vb = torch.from_numpy(vx).to(torch.bfloat16)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int64)
+    slots[rng.random(T) < 0.125] = -1
+    k_scale = float(np.float32(kb.float().abs().max().item() / 448.0))
+    v_scale = float(np.float32(vb.float().abs().max().item() / 448.0))
+    lay = gpu_lib.pool_layout(kf, vf, bs, nkv, hd)
+    ks, vs = olayout.pool_layout(kf, vf, bs, nkv, hd)
+    kp = gpu_lib.alloc_pool(lay, "k", nb, fill=0x7F)
+    vp = gpu_lib.alloc_pool(lay, "v", nb, fill=0x7F)
+    gpu_lib.reshape_and_cache(lay, kb.cuda(), vb.cuda(), kp, vp, torch.from_numpy(slots).cuda(), k_scale, v_scale)
+    torch.cuda.synchronize()
+    ok_ = np.full(nb * ks.block_stride_bytes, 0x7F, np.uint8)
+    ov_ = np.full(nb * vs.block_stride_bytes, 0x7F, np.uint8)
+    owrite.reshape_and_cache(ks, vs, kb.view(torch.int16).numpy().view(np.uint16),
+                             vb.view(torch.int16).numpy().view(np.uint16), ok_, ov_, slots, k_scale, v_scale)
+    assert np.array_equal(kp.cpu().numpy(), ok_), "K pool differs from the oracle"
+    assert np.array_equal(vp.cpu().numpy(), ov_), "V pool differs from the oracle"
