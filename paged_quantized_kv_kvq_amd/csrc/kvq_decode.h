@@ -678,15 +678,41 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
 // its (max, sum) pair at ml + k * mls and its unnormalized row at
 // part + k * ps.  M = max m_k, Z = sum_k 2^(m_k - M) l_k, and
 // o[d] = scale / Z * sum_k 2^(m_k - M) part_k[d]; splits with m_k = -inf
-// (nothing attended) add nothing.  Each loop takes B splits at a time and
-// issues all of their loads before using any, so a row waits for about
-// 3 ns / B memory round trips instead of 3 ns; the additions keep the split
-// order, so the result does not depend on B.  Decode rows have up to tens of
-// splits (B = 8); a prefill row has one or two, where wider batches only add
-// masked slots (B = 1 measured faster there).
+// (nothing attended) add nothing.  A row of at most B splits is read in one
+// batch (one wait); a longer row walks its splits B at a time in three
+// loops, each batch's loads issued before any is used.  The additions keep
+// the split order, so the result does not depend on B or on the path.
+// Decode rows take B = 16, prefill rows (one or two splits) B = 2.
 template <int HD, int B>
 __device__ __forceinline__ void merge_row(const float* ml, uint32_t mls, const float* part, uint32_t ps, int ns,
                                           float scale, float* o) {
+  static_assert(HD <= kWaves * kWave, "one output element per thread");
+  if (ns <= B) {
+    // every split of the row in one batch: the thread requests all maxima,
+    // sums and its element of every row at once and waits once
+    const int d = threadIdx.x;
+    float m[B], l[B], v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const bool in = u < ns;
+      m[u] = in ? ml[uint64_t(u) * mls] : -INFINITY;
+      l[u] = in ? ml[uint64_t(u) * mls + 1] : 0.0f;
+      v[u] = in && d < HD ? part[uint64_t(u) * ps + d] : 0.0f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < B; ++u) M = fmaxf(M, m[u]);
+    float sum = 0.0f, acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (m[u] > -INFINITY) {
+        const float wgt = fast_exp2(m[u] - M);
+        sum += wgt * l[u];
+        acc += wgt * v[u];
+      }
+    if (d < HD) o[d] = acc * (sum > 0.0f ? scale / sum : 0.0f);
+    return;
+  }
   float M = -INFINITY;
   for (int k0 = 0; k0 < ns; k0 += B) {
     float m[B];
@@ -741,7 +767,7 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
   const int tid = threadIdx.x;
   const uint64_t row = ((uint64_t(s) * a.num_kv_heads + g) * a.nsplit) * G + h;  // split 0's row
-  merge_row<HD, 8>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD, uint32_t(G) * HD, ns, a.v_scale, o);
+  merge_row<HD, 16>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD, uint32_t(G) * HD, ns, a.v_scale, o);
   __syncthreads();
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
   float* dst = a.out + (uint64_t(s) * a.num_q_heads + hq) * HD;
@@ -765,7 +791,7 @@ __global__ __launch_bounds__(kWaves * kWave) void prefill_merge_kernel(const Dec
   const int tid = threadIdx.x;
   for (int t = 0; t < pt.nq; ++t) {
     const uint64_t row = base * R + uint64_t(t * G + int(h));  // split 0's row of this query and head
-    merge_row<HD, 1>(a.ml + row * 2, uint32_t(R) * 2, a.part + row * HD, uint32_t(R) * HD, ns, a.v_scale, o);
+    merge_row<HD, 2>(a.ml + row * 2, uint32_t(R) * 2, a.part + row * HD, uint32_t(R) * HD, ns, a.v_scale, o);
     __syncthreads();
     if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
     float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + hq) * HD;
