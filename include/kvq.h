@@ -30,7 +30,8 @@
  *     failed check returns a negative kvq_status and launches nothing.  The
  *     checks cannot see device memory: slot ids, block ids and sequence
  *     lengths must lie in range (caller contract; an out-of-range id is a
- *     memory fault).
+ *     memory fault).  kvq_check_slots / kvq_check_tables validate host
+ *     copies of those arrays for a debug mode.
  *   - Functions are thread-safe.  Concurrent calls that write the same pool
  *     slots or the same workspace race.
  */
@@ -205,6 +206,33 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
                       uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
                       float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/* Debug validation of index arrays (host only; nothing is launched).  The
+ * entry points above cannot see device memory, so an out-of-range slot or
+ * page id there is a memory fault.  A caller in a debug mode copies its index
+ * arrays to the host and calls these first; each returns KVQ_OK, or
+ * KVQ_ERR_INVALID_ARG with the first offending token / sequence in
+ * *first_bad (host, may be NULL).  num_blocks is the number of blocks the
+ * pools hold.  Sources as for the calls they guard: [bf16k_turbov] slot =
+ * block*block_size + offset, block_tables / seq_lens; [kv.rs] the paged
+ * gather (position j in page table[j / block_size]).
+ *
+ * kvq_check_slots: every slot_mapping[t] (host int64 [num_tokens]) is
+ *   negative (skipped) or < num_blocks*block_size, and the non-negative ones
+ *   are distinct (two writes of one slot in one call race). */
+int kvq_check_slots(const kvq_layout* layout, const int64_t* slot_mapping, uint32_t num_tokens,
+                    uint64_t num_blocks, uint32_t* first_bad);
+
+/* kvq_check_tables: for every sequence s, 0 <= seq_lens[s] <=
+ *   max_blocks_per_seq*block_size, and every block_tables[s][i] (host int32
+ *   [num_seqs][max_blocks_per_seq]) that a decode (query_start == NULL) or a
+ *   chunked prefill (query_start: host int32 [num_seqs + 1]) reads lies in
+ *   [0, num_blocks): the pages of positions [j0, L) with the window start j0
+ *   of the call.  For prefill also query_start[0] == 0, non-decreasing, and
+ *   query_start[s + 1] - query_start[s] <= seq_lens[s]. */
+int kvq_check_tables(const kvq_layout* layout, const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                     uint32_t sliding_window, uint64_t num_blocks, uint32_t* first_bad);
 
 /* Introspection (host only): the fp32 Lloyd-Max tables the turbo format uses.
  * centroids[0..L-1] ascending, thresholds[1..L-1] (midpoints; [0] = 0),

@@ -14,7 +14,7 @@
  *                  the free list when it drops to 0), per-layer dtypes and
  *                  (num_kv_heads, head_dim) in KvCacheConfig; release clears
  *                  the bookkeeping with the pools.
- *   [lib.rs]       "memra_kv/lib.rs" -- PageAllocator (a stack of free page
+ *   [kv.rs]        "combs_models/kv.rs" -- PageAllocator (a stack of free page
  *                  ids, filled so that page 0 is handed out first), the paged
  *                  cache's ensure_pages (pages appended until the table covers
  *                  the length; an exhausted allocator is an error), popn (drop

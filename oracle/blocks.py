@@ -6,7 +6,7 @@ checked against.
 "spark_runtime/kv_cache.rs", ``PagedKvCache``: ``free_blocks`` and
 ``block_ref_counts`` (one count per block, so that blocks can be shared, e.g.
 by a common prefix; a block handed out counts 1 and goes back to the free
-list when its count reaches 0).  "memra_kv/lib.rs": ``PageAllocator`` (a
+list when its count reaches 0).  "combs_models/kv.rs": ``PageAllocator`` (a
 stack of free page ids, filled in reverse so that page 0 comes out first),
 ``ensure_pages`` (append pages until the table covers the length; running
 out is an error), ``popn`` (drop the last n tokens, at most the length, and

@@ -22,7 +22,8 @@ import torch
 
 __all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
            "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
-           "library_path", "BlockManager", "paged_prefill", "prefill_workspace_bytes"]
+           "library_path", "BlockManager", "paged_prefill", "prefill_workspace_bytes", "check_slots",
+           "check_tables"]
 
 FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "nvfp4": 5, "turbo8": 8}
 _NAMES = {v: k for k, v in FORMATS.items()}
@@ -84,6 +85,11 @@ def load():
     lib.kvq_paged_prefill.restype = ctypes.c_int
     lib.kvq_codebook.argtypes = [I32, ctypes.POINTER(F32), ctypes.POINTER(F32), ctypes.POINTER(F32),
                                  ctypes.POINTER(U32)]
+    U64 = ctypes.c_uint64
+    lib.kvq_check_slots.argtypes = [ctypes.POINTER(Layout), P, U32, U64, ctypes.POINTER(U32)]
+    lib.kvq_check_tables.argtypes = [ctypes.POINTER(Layout), P, P, P, U32, U32, U32, U64, ctypes.POINTER(U32)]
+    lib.kvq_check_slots.restype = ctypes.c_int
+    lib.kvq_check_tables.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     for f in ("kvq_pool_layout", "kvq_reshape_and_cache", "kvq_paged_decode", "kvq_codebook"):
@@ -151,6 +157,60 @@ def _dev(t: torch.Tensor, dtype, name: str) -> int:
     return t.data_ptr()
 
 
+def _same_device(*named) -> None:
+    devs = {t.device for _, t in named}
+    if len(devs) > 1:
+        raise ValueError("tensors on different devices: " + ", ".join(f"{n} {t.device}" for n, t in named))
+
+
+def _rows_of(t: torch.Tensor, name: str, heads: int, head_dim: int) -> None:
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != head_dim:
+        raise ValueError(f"{name} must be [rows, {heads}, {head_dim}] for this layout, got {tuple(t.shape)}")
+
+
+def _debug_checks(validate) -> bool:
+    """Debug mode: validate index arrays on the host before a launch
+    (validate=True, or KVQ_VALIDATE=1 in the environment when None)."""
+    if validate is None:
+        return os.environ.get("KVQ_VALIDATE", "0") not in ("", "0")
+    return bool(validate)
+
+
+def _pool_blocks(layout: Layout, k_cache: torch.Tensor, v_cache: torch.Tensor) -> int:
+    return min(k_cache.numel() // layout.k_block_stride_bytes, v_cache.numel() // layout.v_block_stride_bytes)
+
+
+def _host(t: torch.Tensor, dtype):
+    import numpy as np
+    return np.ascontiguousarray(t.detach().to("cpu").numpy(), dtype=dtype)
+
+
+def check_slots(layout: Layout, slot_mapping: torch.Tensor, num_blocks: int) -> None:
+    """kvq_check_slots on a host copy of slot_mapping (raises KvqError naming the token)."""
+    import numpy as np
+    lib = load()
+    sl = _host(slot_mapping, np.int64)
+    bad = ctypes.c_uint32(0)
+    st = lib.kvq_check_slots(ctypes.byref(layout), sl.ctypes.data, sl.size, num_blocks, ctypes.byref(bad))
+    _check(st, f"kvq_check_slots (token {bad.value})")
+
+
+def check_tables(layout: Layout, block_tables: torch.Tensor, seq_lens: torch.Tensor, num_blocks: int,
+                 sliding_window: int = 0, query_start: Optional[torch.Tensor] = None) -> None:
+    """kvq_check_tables on host copies (raises KvqError naming the sequence)."""
+    import numpy as np
+    lib = load()
+    bt, ln = _host(block_tables, np.int32), _host(seq_lens, np.int32)
+    qs = None if query_start is None else _host(query_start, np.int32)
+    if qs is not None and qs.size != ln.size + 1:
+        raise ValueError("query_start must hold num_seqs + 1 entries")
+    bad = ctypes.c_uint32(0)
+    st = lib.kvq_check_tables(ctypes.byref(layout), bt.ctypes.data, ln.ctypes.data,
+                              None if qs is None else qs.ctypes.data, bt.shape[1] if bt.ndim == 2 else 0,
+                              ln.size, sliding_window, num_blocks, ctypes.byref(bad))
+    _check(st, f"kvq_check_tables (sequence {bad.value})")
+
+
 def _row_stride(t: torch.Tensor, name: str) -> int:
     """Elements between rows of [rows, heads, head_dim] with contiguous heads."""
     if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
@@ -160,12 +220,19 @@ def _row_stride(t: torch.Tensor, name: str) -> int:
 
 def reshape_and_cache(layout: Layout, key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor,
                       v_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float = 1.0,
-                      v_scale: float = 1.0, stream=None) -> None:
-    """Write key/value rows ([T, Hkv, hd] bf16) into the pools at slot_mapping (int64 [T])."""
+                      v_scale: float = 1.0, stream=None, validate=None) -> None:
+    """Write key/value rows ([T, Hkv, hd] bf16) into the pools at slot_mapping (int64 [T]).
+    validate (or KVQ_VALIDATE=1): check the slots on the host first (synchronizes)."""
     lib = load()
     T = key.shape[0]
     if value.shape[0] != T or slot_mapping.numel() != T:
         raise ValueError("key, value and slot_mapping disagree on the number of tokens")
+    _rows_of(key, "key", layout.num_kv_heads, layout.head_dim)
+    _rows_of(value, "value", layout.num_kv_heads, layout.head_dim)
+    _same_device(("key", key), ("value", value), ("k_cache", k_cache), ("v_cache", v_cache),
+                 ("slot_mapping", slot_mapping))
+    if _debug_checks(validate):
+        check_slots(layout, slot_mapping, _pool_blocks(layout, k_cache, v_cache))
     _check(lib.kvq_reshape_and_cache(
         ctypes.byref(layout), _dev(key, torch.bfloat16, "key"), _dev(value, torch.bfloat16, "value"),
         _dev(k_cache, torch.uint8, "k_cache"), _dev(v_cache, torch.uint8, "v_cache"),
@@ -188,15 +255,25 @@ def paged_decode(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache
                  block_tables: torch.Tensor, seq_lens: torch.Tensor, inv_sqrt_d: float,
                  sliding_window: int = 0, sparse_v_threshold: float = 0.0, k_scale: float = 1.0,
                  v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """fp32 [S, Hq, hd] attention output for bf16 q [S, Hq, hd]."""
+                 workspace: Optional[torch.Tensor] = None, stream=None, validate=None) -> torch.Tensor:
+    """fp32 [S, Hq, hd] attention output for bf16 q [S, Hq, hd].
+    validate (or KVQ_VALIDATE=1): check the tables on the host first (synchronizes)."""
     lib = load()
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError(f"q must be [S, Hq, {layout.head_dim}] for this layout, got {tuple(q.shape)}")
     S, Hq, hd = q.shape
     if q.stride(2) != 1 or q.stride(1) != hd:
         raise ValueError("q must be [S, Hq, head_dim] with contiguous heads")
+    if seq_lens.numel() != S:
+        raise ValueError(f"seq_lens holds {seq_lens.numel()} entries for {S} sequences")
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+                 ("seq_lens", seq_lens), *((("out", out),) if out is not None else ()),
+                 *((("workspace", workspace),) if workspace is not None else ()))
     if block_tables.dim() != 2 or block_tables.shape[0] != S or not block_tables.is_contiguous():
         raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
     mb = block_tables.shape[1]
+    if _debug_checks(validate):
+        check_tables(layout, block_tables, seq_lens, _pool_blocks(layout, k_cache, v_cache), sliding_window)
     if out is None:
         out = torch.empty((S, Hq, hd), dtype=torch.float32, device=q.device)
     elif not out.is_contiguous() or tuple(out.shape) != (S, Hq, hd):
@@ -229,19 +306,28 @@ def paged_prefill(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cach
                   block_tables: torch.Tensor, seq_lens: torch.Tensor, query_start: torch.Tensor, max_query_len: int,
                   inv_sqrt_d: float, sliding_window: int = 0, k_scale: float = 1.0, v_scale: float = 1.0,
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
+                  stream=None, validate=None) -> torch.Tensor:
     """fp32 [T, Hq, hd] chunked-prefill attention output for bf16 q [T, Hq, hd]
     (sequence s's queries are rows query_start[s] .. query_start[s + 1] - 1)."""
     lib = load()
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError(f"q must be [T, Hq, {layout.head_dim}] for this layout, got {tuple(q.shape)}")
     T, Hq, hd = q.shape
     S = seq_lens.numel()
     if q.stride(2) != 1 or q.stride(1) != hd:
         raise ValueError("q must be [T, Hq, head_dim] with contiguous heads")
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+                 ("seq_lens", seq_lens), ("query_start", query_start),
+                 *((("out", out),) if out is not None else ()),
+                 *((("workspace", workspace),) if workspace is not None else ()))
     if block_tables.dim() != 2 or block_tables.shape[0] != S or not block_tables.is_contiguous():
         raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
     if query_start.numel() != S + 1:
         raise ValueError("query_start must hold num_seqs + 1 entries")
     mb = block_tables.shape[1]
+    if _debug_checks(validate):
+        check_tables(layout, block_tables, seq_lens, _pool_blocks(layout, k_cache, v_cache), sliding_window,
+                     query_start)
     if out is None:
         out = torch.empty((T, Hq, hd), dtype=torch.float32, device=q.device)
     elif not out.is_contiguous() or tuple(out.shape) != (T, Hq, hd):

@@ -74,15 +74,29 @@ def compile_one(src: str, verbose: bool, out_dir: str = OUT_DIR, defines=()) -> 
     return src, obj, r.returncode, time.time() - t0
 
 
-def build(jobs: int = 0, verbose: bool = False, lib: str = LIB, out_dir: str = OUT_DIR, defines=()) -> str:
+def _stale(src: str, out_dir: str) -> bool:
+    """An object older than its source or than any header it may include."""
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+                                         if f.endswith(".h")]
+    return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
+
+
+def build(jobs: int = 0, verbose: bool = False, lib: str = LIB, out_dir: str = OUT_DIR, defines=(),
+          incremental: bool = False) -> str:
     """Compile and link.  `defines` (NAME=VALUE) override the tuning constants of
-    csrc/kvq_internal.h; `lib` / `out_dir` place a variant build elsewhere."""
+    csrc/kvq_internal.h; `lib` / `out_dir` place a variant build elsewhere;
+    `incremental` recompiles only objects older than their inputs."""
     os.makedirs(out_dir, exist_ok=True)
     jobs = jobs or max(1, min(8, os.cpu_count() or 1))
     objs = []
     failed = []
+    todo = [s for s in sources() if not incremental or _stale(s, out_dir)]
+    objs = [os.path.join(out_dir, os.path.splitext(s)[0] + ".o") for s in sources() if s not in todo]
     with cf.ThreadPoolExecutor(jobs) as ex:
-        for src, obj, rc, dt in ex.map(lambda s: compile_one(s, verbose, out_dir, defines), sources()):
+        for src, obj, rc, dt in ex.map(lambda s: compile_one(s, verbose, out_dir, defines), todo):
             if verbose:
                 sys.stderr.write(f"  {src}: {dt:.1f}s\n")
             (failed if rc else objs).append(src if rc else obj)
@@ -101,9 +115,10 @@ def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--incremental", action="store_true", help="recompile only out-of-date objects")
     a = ap.parse_args()
     t0 = time.time()
-    print(build(a.jobs, a.verbose), f"({time.time() - t0:.1f}s)")
+    print(build(a.jobs, a.verbose, incremental=a.incremental), f"({time.time() - t0:.1f}s)")
 
 
 if __name__ == "__main__":

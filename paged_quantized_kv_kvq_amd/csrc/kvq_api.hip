@@ -4,6 +4,8 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "kvq_internal.h"
 
@@ -434,6 +436,63 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   }
   if (e == hipSuccess) e = launch_prefill_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+int kvq_check_slots(const kvq_layout* layout, const int64_t* slot_mapping, uint32_t num_tokens, uint64_t num_blocks,
+                    uint32_t* first_bad) {
+  const int st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (num_tokens && !slot_mapping) return KVQ_ERR_INVALID_ARG;
+  const uint64_t nslots = num_blocks * layout->block_size;
+  std::vector<std::pair<int64_t, uint32_t>> used;
+  used.reserve(num_tokens);
+  for (uint32_t t = 0; t < num_tokens; ++t) {
+    const int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    if (uint64_t(s) >= nslots) {
+      if (first_bad) *first_bad = t;
+      return KVQ_ERR_INVALID_ARG;
+    }
+    used.emplace_back(s, t);
+  }
+  std::sort(used.begin(), used.end());
+  uint32_t bad = UINT32_MAX;
+  for (size_t i = 1; i < used.size(); ++i)  // the later token of a repeated slot
+    if (used[i].first == used[i - 1].first) bad = std::min(bad, std::max(used[i].second, used[i - 1].second));
+  if (bad != UINT32_MAX) {
+    if (first_bad) *first_bad = bad;
+    return KVQ_ERR_INVALID_ARG;
+  }
+  return KVQ_OK;
+}
+
+int kvq_check_tables(const kvq_layout* layout, const int32_t* block_tables, const int32_t* seq_lens,
+                     const int32_t* query_start, uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                     uint32_t sliding_window, uint64_t num_blocks, uint32_t* first_bad) {
+  const int st = check_layout(layout);
+  if (st != KVQ_OK) return st;
+  if (num_seqs && (!block_tables || !seq_lens)) return KVQ_ERR_INVALID_ARG;
+  const int64_t bs = layout->block_size, cap = int64_t(max_blocks_per_seq) * bs, W = sliding_window;
+  auto fail = [&](uint32_t s) {
+    if (first_bad) *first_bad = s;
+    return KVQ_ERR_INVALID_ARG;
+  };
+  if (query_start && num_seqs && query_start[0] != 0) return fail(0);
+  for (uint32_t s = 0; s < num_seqs; ++s) {
+    const int64_t L = seq_lens[s];
+    if (L < 0 || L > cap) return fail(s);
+    int64_t j0 = W > 0 ? std::max<int64_t>(0, L - W) : 0;  // decode's window start
+    if (query_start) {
+      const int64_t C = int64_t(query_start[s + 1]) - query_start[s];
+      if (C < 0 || C > L) return fail(s);
+      if (C == 0) continue;                                  // no query reads the table
+      j0 = W > 0 ? std::max<int64_t>(0, L - C + 1 - W) : 0;  // the first query's window start
+    }
+    const int32_t* row = block_tables + uint64_t(s) * max_blocks_per_seq;
+    for (int64_t i = j0 / bs; i < (L + bs - 1) / bs; ++i)
+      if (row[i] < 0 || uint64_t(row[i]) >= num_blocks) return fail(s);
+  }
+  return KVQ_OK;
 }
 
 int kvq_codebook(int32_t format, float* centroids, float* thresholds, float* inv_cmax, uint32_t* levels) {

@@ -2,7 +2,7 @@
 // tables, append with copy on write, rollback.
 //
 // "spark_runtime/kv_cache.rs", PagedKvCache (free_blocks, block_ref_counts);
-// "memra_kv/lib.rs", PageAllocator (a stack of free ids, block 0 handed out
+// "combs_models/kv.rs", PageAllocator (a stack of free ids, block 0 handed out
 // first), ensure_pages, popn, reset.  Plain host C++: no HIP calls.
 #include <algorithm>
 #include <cstdint>

@@ -181,3 +181,64 @@ def test_prefill_host_checks(lib):
     with pytest.raises(kvq.KvqError) as e:
         kvq.prefill_workspace_bytes(lay, 4, 32, 64, 0)       # max_query_len 0
     assert e.value.status == INVALID
+
+
+def _u32p(lib):
+    return ctypes.c_uint32(0xFFFFFFFF)
+
+
+def test_check_slots(lib):
+    """kvq_check_slots: range and uniqueness of the non-negative slots; the
+    first offending token is reported."""
+    lay = kvq.pool_layout("bf16", "turbo4", 16, 2, 64)
+    nb = 4   # 64 slots
+
+    def run(slots):
+        a = np.asarray(slots, dtype=np.int64)
+        bad = _u32p(lib)
+        st = lib.kvq_check_slots(ctypes.byref(lay), a.ctypes.data, a.size, nb, ctypes.byref(bad))
+        return st, bad.value
+
+    assert run([0, 5, 63, -1, -7, 17])[0] == OK
+    assert run([])[0] == OK
+    assert run([0, 64, 3]) == (INVALID, 1)           # one past the pool
+    assert run([3, 9, 2, 9, 9]) == (INVALID, 3)      # the later token of the first repeated slot
+    assert run([-1, -1, 4])[0] == OK                 # skipped tokens may repeat
+    assert run([1 << 40])[0] == INVALID
+    with pytest.raises(kvq.KvqError):
+        import torch
+        kvq.check_slots(lay, torch.tensor([0, 0]), nb)
+
+
+def test_check_tables(lib):
+    """kvq_check_tables: lengths within the table, and every page a decode or
+    prefill reads inside the pool (pages before a window start are not read)."""
+    lay = kvq.pool_layout("fp8", "turbo2", 16, 2, 64)
+    nb, mb = 8, 4
+
+    def run(bt, lens, window=0, qs=None):
+        bt = np.ascontiguousarray(bt, dtype=np.int32)
+        ln = np.asarray(lens, dtype=np.int32)
+        q = None if qs is None else np.asarray(qs, dtype=np.int32)
+        bad = _u32p(lib)
+        st = lib.kvq_check_tables(ctypes.byref(lay), bt.ctypes.data, ln.ctypes.data,
+                                  None if q is None else q.ctypes.data, mb, ln.size, window, nb, ctypes.byref(bad))
+        return st, bad.value
+
+    bt = [[0, 1, -1, -1], [7, 6, 5, 4]]
+    assert run(bt, [32, 64])[0] == OK
+    assert run(bt, [33, 64]) == (INVALID, 0)          # reads page index 2 (-1)
+    assert run(bt, [0, 65]) == (INVALID, 1)           # longer than the table
+    assert run(bt, [-1, 4]) == (INVALID, 0)
+    assert run([[0, 1, 8, 2], [0, 0, 0, 0]], [64, 1]) == (INVALID, 0)   # page 8 of an 8-block pool
+    # a window of 16 over 64 positions reads pages 3 only: earlier entries are free
+    assert run([[-5, 99, -1, 3], [0, 0, 0, 0]], [64, 1], window=16)[0] == OK
+    assert run([[-5, 99, -1, 3], [0, 0, 0, 0]], [64, 1], window=17) == (INVALID, 0)
+    # prefill: query rows of s are its last C_s positions; the first query's window reaches back further
+    assert run([[-5, 99, 2, 3], [0, 0, 0, 0]], [64, 1], window=16, qs=[0, 16, 17])[0] == OK
+    assert run([[-5, 99, 2, 3], [0, 0, 0, 0]], [64, 1], window=16, qs=[0, 17, 18])[0] == OK   # query 47: keys 32..47
+    assert run([[-5, 99, 2, 3], [0, 0, 0, 0]], [64, 1], window=16, qs=[0, 18, 19]) == (INVALID, 0)   # key 31
+    assert run(bt, [32, 64], qs=[0, 33, 34]) == (INVALID, 0)   # more queries than positions
+    assert run(bt, [32, 64], qs=[1, 2, 3]) == (INVALID, 0)     # query_start[0] != 0
+    assert run(bt, [32, 64], qs=[0, 5, 4]) == (INVALID, 1)     # decreasing
+    assert run([[0, -1, -1, -1], [7, 6, 5, 4]], [32, 64], qs=[0, 0, 3])[0] == OK   # no queries: table unread

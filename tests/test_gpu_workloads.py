@@ -3,8 +3,9 @@
 Each workload is staged exactly as the benchmark stages it (whole pool, all
 sequences, the timed step's write batch in its shuffled slot order) and
 decoded through the same C-ABI call with the same arguments.  The oracle then
-rebuilds only a few sampled sequences (shortest, longest, one seeded pick;
-for the sliding-window workload only the pages inside the window) and checks
+rebuilds only a few sampled sequences (shortest, longest, last, middle,
+sequences 1, 3 and 7, seeded picks; for the sliding-window workload only the
+pages inside the window) and checks
 them element by element: written pool bytes bit-exact, decode outputs to the
 same max-abs / relative-L2 bar as the small cases.  Properties that hold at
 any size are checked on every sequence: all outputs finite, the decode
@@ -23,7 +24,11 @@ pytestmark = pytest.mark.gpu
 
 
 def _sample(lens: np.ndarray, wid: int, extra: int = 1):
-    picks = {int(np.argmin(lens)), int(np.argmax(lens))}
+    """Shortest, longest, last, middle, sequences 1, 3 and 7 (units are dealt to
+    the 8 XCDs in turn, so these cover several residues mod 8 even when every
+    length is equal), plus `extra` seeded picks."""
+    S = len(lens)
+    picks = {int(np.argmin(lens)), int(np.argmax(lens)), S - 1, S // 2} | {s for s in (1, 3, 7) if s < S}
     want = len(picks) + extra
     rng = np.random.default_rng(wid)
     for s in rng.permutation(len(lens)):
