@@ -1,19 +1,23 @@
 """Benchmark: paged quantized KV write + paged decode on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--also 3]
 
 A step is one pass of the whole hot path over one batch: every sequence's new
 token is written into the paged pools (kvq_reshape_and_cache, scattered slots)
 and then every sequence decodes one token over its pages (kvq_paged_decode).
 Inputs are seeded synthetic data of the workload's shapes, staged in HBM
-before the timed region.  Prints one JSON line.
+before the timed region.  Prints one JSON line: the headline workload
+(bf16 K / turbo4 V with the sparse-V skip) at the top level, and the second
+target workload (fp8 K / turbo2 V, dense, 128 x 32768) under
+"configs" (--also 0: none).
 
 value      effective KV GB/s: K+V bytes of every attended (position, kv head)
-           at the storage formats' sizes, per step time (sparse V skips some
-           of those bytes; the roofline below counts only what must move).
-           Step and decode times are medians of per-step HIP events; between
-           steps a 1 GiB scratch read evicts L2 and the MALL (--warm: no
-           eviction), outside the timed region.
+           at the storage formats' sizes (the dense-window bytes), per step
+           time.  The sparse path skips most V rows, so this counts bytes it
+           never reads; pct_hbm_peak and roofline.frac count only what must
+           move.  Step and decode times are medians of per-step HIP events;
+           between steps a 1 GiB scratch read evicts L2 and the MALL (--warm:
+           no eviction), outside the timed region.
 roofline   the decode call (sparse: score pass, V pass; dense: split pass,
            merge) timed with HIP events on the stream the library
            launches on; algorithmic bytes = K of every attended position + V
@@ -21,7 +25,15 @@ roofline   the decode call (sparse: score pass, V pass; dense: split pass,
            from the stored K) + q + out + the page-table entries and lengths
            read.  `traffic` = HBM bytes per decode call from the committed
            rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the same sources.
-cpu_baseline  the CPU oracle timed on a sample of the same workload.
+roofline_alu  the same call against the fp32 VALU ceiling of the build
+           (packed fp32 off: 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz
+           = 78.6 TFLOP/s).
+stream_read_ref  libkvq_probe.so's page-read kernel over the same page size,
+           pages in shuffled order, nothing computed: the practical read
+           ceiling of this GPU for the pool's access pattern.
+cpu_baseline  the CPU oracle timed on a sample of the same workload, in
+           worker processes (one per core of the process's CPU set, at most
+           16); its outputs are also checked against the GPU's (parity).
 """
 from __future__ import annotations
 
@@ -45,6 +57,9 @@ import synth  # noqa: E402
 from synth.gpu import stage  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+VALU_PEAK_TFLOPS = 78.6       # fp32 VALU without packed math: 256 x 4 x 16 x 2 x 2.4e9
+MFMA_BF16_TFLOPS = 2500.0     # dense matrix peaks of MI355X
+MFMA_F32_TFLOPS = 157.3
 ROW_BYTES = {"bf16": lambda hd: 2 * hd, "fp8": lambda hd: hd, "turbo4": lambda hd: hd // 2 + hd // 16,
              "turbo3": lambda hd: hd * 3 // 8 + hd // 16, "turbo2": lambda hd: hd // 4 + hd // 16,
              "turbo8": lambda hd: hd + hd // 8, "nvfp4": lambda hd: hd // 2 + hd // 16}
@@ -146,22 +161,31 @@ def kept_rows(st, w, kvq) -> int:
     return total
 
 
-def stream_read_reference() -> dict:
-    """Read bandwidth of torch's own sum over 2 GiB of fp32 on this GPU (a
-    reference ceiling for a plain streaming read, not a kernel of this path)."""
-    x = torch.ones(1 << 29, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        x.sum()
+def stream_read_reference(page_bytes: int, total_bytes: int = 4 << 30) -> dict:
+    """libkvq_probe.so's page-read kernel: pages of `page_bytes` (rounded down to
+    a multiple of 1 KiB) in shuffled order over `total_bytes`, read whole,
+    nothing computed (a reference ceiling, not a kernel of this path)."""
+    import ctypes
+    path = os.path.join(ROOT, "paged_quantized_kv_kvq_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return {"kernel": "page_read_kernel", "gbs": None, "note": "libkvq_probe.so not built"}
+    lib = ctypes.CDLL(path)
+    lib.kvq_probe_page_read.restype = ctypes.c_double
+    lib.kvq_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    pb = max(1024, page_bytes // 1024 * 1024)
+    n = total_bytes // pb
+    pool = torch.ones(n * pb, dtype=torch.uint8, device="cuda")
+    pages = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(torch.int32).cuda()
+    sink = torch.zeros(n, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(10):
-        x.sum()
-    b.record()
-    torch.cuda.synchronize()
-    gbs = 10 * x.numel() * 4 / (a.elapsed_time(b) * 1e-3) / 1e9
-    del x
-    return {"kernel": "torch.sum over 2 GiB fp32", "gbs": round(gbs, 1)}
+    reps = 10
+    sec = lib.kvq_probe_page_read(pool.data_ptr(), pages.data_ptr(), n, pb, 64, reps, sink.data_ptr(),
+                                  torch.cuda.current_stream().cuda_stream)
+    del pool, pages, sink
+    gbs = round(reps * n * pb / sec / 1e9, 1) if sec > 0 else None
+    return {"kernel": "page_read_kernel (libkvq_probe.so)", "page_bytes": pb, "pages": n, "gbs": gbs,
+            "frac_of_peak": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def _attended(st, w) -> np.ndarray:
@@ -234,62 +258,121 @@ def host_block_manager(kvq, w, lens: np.ndarray, steps: int = 200) -> dict:
             "sequences": S, "max_blocks_per_seq": mb, "steps": steps}
 
 
-def cpu_baseline(st, w, n_seqs: int):
-    """Oracle (plain numpy, fp64 attention) on the first n_seqs sequences."""
+def cpu_workers() -> int:
+    """Worker processes for the oracle baseline: the process's CPU set, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_worker(job):
+    """One worker of the CPU baseline (a spawned process: plain numpy, no GPU):
+    build the pools of its sequences with everything but the step's positions
+    (untimed), wait for the others, then time the step (write of the new
+    positions, fp64 decode of every q head)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
     from oracle import decode as odecode
     from oracle import layout as olayout
     from oracle import write as owrite
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):
-        return _cpu_baseline(st, w, n_seqs, odecode, olayout, owrite)
-
-
-def _cpu_baseline(st, w, n_seqs, odecode, olayout, owrite):
-    seqs = list(range(n_seqs))
-    ks, vs = olayout.pool_layout(w.k_format, w.v_format, w.block_size, w.num_kv_heads, w.head_dim)
-    bs = w.block_size
-    remap = {}
+    d, seqs, barrier = job["dir"], job["seqs"], job["barrier"]
+    ks, vs = olayout.pool_layout(job["k_format"], job["v_format"], job["bs"], job["hkv"], job["hd"])
+    bs, tail = job["bs"], job["tail"]
+    lens = np.load(os.path.join(d, "lens.npy"))
+    bt_all = np.load(os.path.join(d, "bt.npy"))
+    q = np.load(os.path.join(d, "q.npy"))
+    remap, bt = {}, np.full_like(bt_all, -1)
     for s in seqs:
-        for b in st.bt[s, :(int(st.lens[s]) + bs - 1) // bs]:
+        for b in bt_all[s, :(int(lens[s]) + bs - 1) // bs]:
             remap.setdefault(int(b), len(remap))
-    n = len(remap) + 1
-    kp = np.zeros(n * ks.block_stride_bytes, np.uint8)
-    vp = np.zeros(n * vs.block_stride_bytes, np.uint8)
-    bt = np.full_like(st.bt, -1)
     for s in seqs:
-        nb = (int(st.lens[s]) + bs - 1) // bs
-        bt[s, :nb] = [remap[int(b)] for b in st.bt[s, :nb]]
-    tail = w.write_tail
-    pre = {}
-    for s in seqs:  # cache contents before the step (untimed)
-        K, V = st.host_kv[s]
-        L = int(st.lens[s])
-        pos = np.arange(max(0, L - tail))
-        slots = bt[s, pos // bs].astype(np.int64) * bs + pos % bs
-        owrite.reshape_and_cache(ks, vs, K[pos], V[pos], kp, vp, slots, st.k_scale, st.v_scale)
-        pre[s] = L
-    q = st.q.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-    t0 = time.perf_counter()
-    for s in seqs:  # the step: write the new tokens, then decode
-        K, V = st.host_kv[s]
-        L = int(st.lens[s])
-        pos = np.arange(max(0, L - tail), L)
-        slots = bt[s, pos // bs].astype(np.int64) * bs + pos % bs
-        owrite.reshape_and_cache(ks, vs, K[pos], V[pos], kp, vp, slots, st.k_scale, st.v_scale)
-    odecode.paged_decode(ks, vs, q, kp, vp, bt, st.lens, synth.inv_sqrt_d(w.head_dim), w.sliding_window,
-                         w.sparse_v_threshold, st.k_scale, st.v_scale, seqs=seqs)
-    dt = time.perf_counter() - t0
-    att = _attended(st, w)[seqs].sum()
+        nb = (int(lens[s]) + bs - 1) // bs
+        bt[s, :nb] = [remap[int(b)] for b in bt_all[s, :nb]]
+    kp = np.zeros((len(remap) + 1) * ks.block_stride_bytes, np.uint8)
+    vp = np.zeros((len(remap) + 1) * vs.block_stride_bytes, np.uint8)
+    kv = {s: (np.load(os.path.join(d, f"k{s}.npy"), mmap_mode="r"), np.load(os.path.join(d, f"v{s}.npy"),
+                                                                          mmap_mode="r")) for s in seqs}
+    with threadpool_limits(1):
+        for s in seqs:
+            K, V = kv[s]
+            L = int(lens[s])
+            pos = np.arange(max(0, L - tail))
+            owrite.reshape_and_cache(ks, vs, np.asarray(K[pos]), np.asarray(V[pos]), kp, vp,
+                                     bt[s, pos // bs].astype(np.int64) * bs + pos % bs, job["k_scale"], job["v_scale"])
+        barrier.wait()
+        t0 = time.perf_counter()
+        for s in seqs:
+            K, V = kv[s]
+            L = int(lens[s])
+            pos = np.arange(max(0, L - tail), L)
+            owrite.reshape_and_cache(ks, vs, np.asarray(K[pos]), np.asarray(V[pos]), kp, vp,
+                                     bt[s, pos // bs].astype(np.int64) * bs + pos % bs, job["k_scale"], job["v_scale"])
+        res = odecode.paged_decode(ks, vs, q, kp, vp, bt, lens, job["inv"], job["window"], job["thr"],
+                                   job["k_scale"], job["v_scale"], seqs=seqs, detail=True)
+        dt = time.perf_counter() - t0
+    _, o64, band, n_amb = res
+    return dt, seqs, o64[seqs], band[seqs], n_amb[seqs]
+
+
+def cpu_baseline(st, w, seqs, out_gpu: np.ndarray) -> dict:
+    """The oracle on a sample of the same workload, spread over worker
+    processes; its outputs also check the GPU's on the sample (the decode
+    bars: max-abs 2e-3 plus the sparse-V band, rel-L2 1e-3)."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    nproc = min(cpu_workers(), len(seqs))
+    base = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    d = tempfile.mkdtemp(prefix="kvq_bench_", dir=base)
+    try:
+        np.save(os.path.join(d, "lens.npy"), st.lens)
+        np.save(os.path.join(d, "bt.npy"), st.bt)
+        np.save(os.path.join(d, "q.npy"), st.q.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        for s in seqs:
+            K, V = st.host_kv[s]
+            np.save(os.path.join(d, f"k{s}.npy"), K)
+            np.save(os.path.join(d, f"v{s}.npy"), V)
+        ctx = mp.get_context("spawn")
+        mgr = ctx.Manager()
+        barrier = mgr.Barrier(nproc)
+        # longest sequences first, dealt round-robin: the workers' shares stay even
+        order = sorted(seqs, key=lambda s: -int(st.lens[s]))
+        parts = [order[i::nproc] for i in range(nproc)]
+        jobs = [dict(dir=d, seqs=sorted(p), barrier=barrier, k_format=w.k_format, v_format=w.v_format,
+                     bs=w.block_size, hkv=w.num_kv_heads, hd=w.head_dim, tail=w.write_tail,
+                     inv=synth.inv_sqrt_d(w.head_dim), window=w.sliding_window, thr=w.sparse_v_threshold,
+                     k_scale=st.k_scale, v_scale=st.v_scale) for p in parts]
+        with ctx.Pool(nproc) as pool:
+            results = pool.map(_oracle_worker, jobs)
+        mgr.shutdown()
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    wall = max(r[0] for r in results)
+    att = int(_attended(st, w)[seqs].sum())
     kv_bytes = att * w.num_kv_heads * (ROW_BYTES[w.k_format](w.head_dim) + ROW_BYTES[w.v_format](w.head_dim))
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_seqs} of {w.num_seqs} sequences ({int(att)} attended positions): write of their "
-                      f"new token + fp64 decode of all {w.num_q_heads} q heads, one thread, {dt:.1f} s"}
+    # parity of the GPU output on the sample
+    emax, num, den, namb, ok = 0.0, 0.0, 0.0, 0, True
+    for _, ss, o64, band, n_amb in results:
+        g = out_gpu[ss].astype(np.float64)
+        err = np.abs(g - o64)
+        ok &= bool(np.all(err <= 2e-3 + band))
+        emax = max(emax, float(err.max()) if err.size else 0.0)
+        clean = n_amb == 0
+        num += float(((g - o64) ** 2)[clean].sum())
+        den += float((o64 ** 2)[clean].sum())
+        namb += int(n_amb.sum())
+    rel = math.sqrt(num / den) if den > 0 else 0.0
+    ok &= rel <= 1e-3
+    return {"value": round(kv_bytes / wall / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.num_seqs} sequences ({att} attended positions): write of their new "
+                      f"token(s) + fp64 decode of all {w.num_q_heads} q heads, {nproc} worker processes, "
+                      f"{wall:.2f} s wall (the slowest worker)",
+            "parity": {"sequences": len(seqs), "max_abs": emax, "rel_l2": rel, "ambiguous": namb, "ok": ok}}
 
 
 def prefill_main(args, kvq, w):
     """Chunked prefill step: write the chunks' K/V (the held-back last
     write_tail positions of every sequence), then their queries attend."""
-    keep = range(min(args.cpu_seqs, w.num_seqs)) if args.cpu_seqs else ()
+    ncpu = 1 if args.cpu_seqs is None else args.cpu_seqs
+    keep = range(min(ncpu, w.num_seqs)) if ncpu else ()
     st = stage(w, kvq, "cuda", keep_host=keep, log=log)
     S, Hq, Hkv, hd, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     C = np.minimum(w.write_tail, st.lens).astype(np.int64)
@@ -358,6 +441,11 @@ def prefill_main(args, kvq, w):
     min_bytes = int(sum(int(L) for L in st.lens)) * Hkv * (kb + vb)
     tile_bytes = tile_keys * Hkv * (kb + vb)
     tflops = flops / (att_ms * 1e-3) / 1e12
+    # the instruction mix's peak: Q.K on bf16 matrix cores for bf16 / fp8 K
+    # (fp32 ones over the rotated query otherwise), P.V on fp32 ones; half
+    # the flops each, so the peak is the harmonic combination
+    qk_peak = MFMA_BF16_TFLOPS if w.k_format in ("bf16", "fp8") else MFMA_F32_TFLOPS
+    peak = 1.0 / (0.5 / qk_peak + 0.5 / MFMA_F32_TFLOPS)
     rec = {
         "metric": "chunked-prefill query tokens/s over the quantized paged cache, 1 GPU",
         "value": round(T / (ms_step * 1e-3), 1),
@@ -370,8 +458,9 @@ def prefill_main(args, kvq, w):
         "prefill_ms": round(att_ms, 4),
         "write_ms": round(float(np.median(stp - att)), 4),
         "wall_s_timed_loop": round(elapsed, 3),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": 157.3, "unit": "TFLOP/s",
-                     "frac": round(tflops / 157.3, 4), "traffic": traffic_from_profile(w.name, "prefill"),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
+                     "peak_basis": f"half the flops at {qk_peak} (Q.K), half at {MFMA_F32_TFLOPS} (P.V, fp32)",
+                     "frac": round(tflops / peak, 4), "traffic": traffic_from_profile(w.name, "prefill"),
                      "kernel": "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel",
                      "algorithmic_flops": flops},
         "kv_bytes": {"once_per_sequence": min_bytes, "read_by_tiles": tile_bytes, "queries_per_tile": qt,
@@ -379,9 +468,9 @@ def prefill_main(args, kvq, w):
                      "gbs_read_by_tiles": round(tile_bytes / (att_ms * 1e-3) / 1e9, 1)},
         "kernel_source_sha256": kernel_source_hash(),
     }
-    if args.cpu_seqs:
+    if ncpu:
         log("timing the CPU oracle ...")
-        rec["cpu_baseline"] = prefill_cpu_baseline(st, w, q, qs, min(args.cpu_seqs, 1), inv)  # ~10-20 s each
+        rec["cpu_baseline"] = prefill_cpu_baseline(st, w, q, qs, min(ncpu, 1), inv)  # ~10-20 s each
     print(json.dumps(rec), flush=True)
 
 
@@ -421,28 +510,14 @@ def prefill_cpu_baseline(st, w, q, qs, n_seqs: int, inv: float):
                       f"{w.num_q_heads} q heads, one thread, {dt:.1f} s (the chunk's write is not in the sample)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(synth.WORKLOADS))
-    ap.add_argument("--cpu-seqs", type=int, default=24, help="sequences in the oracle sample (0: skip)")
-    ap.add_argument("--warm", action="store_true", help="no cache eviction between steps")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU: this path has no multi-GPU step (asked for {args.gpus}); "
-              "each GPU would serve its own sequences or kv heads with no exchange", file=sys.stderr)
-        sys.exit(2)
-    import paged_quantized_kv_kvq_amd as kvq
-    kvq.load()
-    torch.cuda.set_device(0)
-    w = synth.WORKLOADS[args.workload]
-    if w.prefill:
-        return prefill_main(args, kvq, w)
-    keep = range(min(args.cpu_seqs, w.num_seqs)) if args.cpu_seqs else ()
+def page_bytes(w) -> int:
+    """K + V bytes of one page of the pools (block_size positions, every kv head)."""
+    return w.block_size * w.num_kv_heads * (ROW_BYTES[w.k_format](w.head_dim) + ROW_BYTES[w.v_format](w.head_dim))
+
+
+def measure_decode(kvq, w, args, cpu_seqs) -> dict:
+    """Stage workload w, time K write + decode steps, and return its record."""
+    keep = list(cpu_seqs)
     t0 = time.time()
     st = stage(w, kvq, "cuda", keep_host=keep, log=log)
     log(f"staged {w.name} in {time.time() - t0:.1f}s: {int(st.lens.sum())} positions, "
@@ -471,19 +546,19 @@ def main():
     scratch = None if args.warm else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
 
-    def evict(i):
+    def evict():
         if scratch is not None:
             torch.sum(scratch, dim=0, out=sink)
 
-    for i in range(args.warmup):
-        evict(i)
+    for _ in range(args.warmup):
+        evict()
         write()
         decode()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        evict(i)
+        evict()
         ev[i][0].record(stream)
         write()
         ev[i][1].record(stream)
@@ -504,7 +579,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    stream_ref = stream_read_reference()
 
     att = _attended(st, w)
     positions = int(att.sum())
@@ -521,29 +595,21 @@ def main():
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
+        "value_basis": "dense-window K+V bytes / step time (write + decode)",
         "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
         "config": {"workload": w.name, "k_format": w.k_format, "v_format": w.v_format,
                    "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": Hkv, "head_dim": hd,
                    "block_size": w.block_size, "seq_lens": list(w.seq_len), "attended_positions": positions,
                    "sparse_v_threshold": w.sparse_v_threshold, "sliding_window": w.sliding_window,
                    "write_tokens_per_step": int(st.tail_slots.numel()), "parallelism": "1 GPU"},
-        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
         "decode_tokens_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "decode_ms": round(dec_ms, 4),
         "decode_ms_p10_p90": [round(float(np.percentile(dec, 10)), 4), round(float(np.percentile(dec, 90)), 4)],
         "write_ms": round(float(np.median(stp - dec)), 4),
         "caches": "warm" if args.warm else "cold: 1 GiB scratch read between steps, outside the timed region",
         "wall_s_timed_loop": round(elapsed, 3),
-        "stream_read_ref": stream_ref,
         "kept_v_fraction": round(kept / max(1, positions * Hkv), 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -551,14 +617,71 @@ def main():
                      "kernel": decode_kernels(w),
                      "algorithmic_bytes": alg},
         "roofline_alu": {"bound": "alu", "achieved": round(flops / (dec_ms * 1e-3) / 1e12, 3),
-                         "peak": 157.3, "unit": "TFLOP/s", "frac": round(flops / (dec_ms * 1e-3) / 1e12 / 157.3, 4),
+                         "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(flops / (dec_ms * 1e-3) / 1e12 / VALU_PEAK_TFLOPS, 4),
                          "algorithmic_flops": flops},
-        "kernel_source_sha256": kernel_source_hash(),
-        "host_block_manager": host_block_manager(kvq, w, st.lens),
     }
-    if args.cpu_seqs:
-        log("timing the CPU oracle ...")
-        rec["cpu_baseline"] = cpu_baseline(st, w, min(args.cpu_seqs, w.num_seqs))
+    if keep:
+        log(f"timing the CPU oracle on {len(keep)} sequences of {w.name} ...")
+        rec["cpu_baseline"] = cpu_baseline(st, w, keep, out.cpu().numpy())
+    rec["_lens"] = st.lens
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+# sequences of each workload the CPU baseline times (bounded: about 10-30 s of
+# single-core oracle work): every sequence of the headline workload, 16 of
+# the 128 x 32768 one, the first 8 elsewhere
+CPU_SAMPLE = {2: 64, 3: 16}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--also", type=int, default=None,
+                    help="a second decode workload measured in the same line (default: 3 with workload 2; 0: none)")
+    ap.add_argument("--cpu-seqs", type=int, default=None, help="sequences in the oracle sample (0: skip)")
+    ap.add_argument("--warm", action="store_true", help="no cache eviction between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU: this path has no multi-GPU step (asked for {args.gpus}); "
+              "each GPU would serve its own sequences or kv heads with no exchange", file=sys.stderr)
+        sys.exit(2)
+    import paged_quantized_kv_kvq_amd as kvq
+    kvq.load()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    if w.prefill:
+        return prefill_main(args, kvq, w)
+    also = args.also if args.also is not None else (3 if args.workload == 2 else 0)
+
+    def sample(wl):
+        n = args.cpu_seqs if args.cpu_seqs is not None else CPU_SAMPLE.get(wl.wid, 8)
+        return range(min(n, wl.num_seqs))
+
+    head = measure_decode(kvq, w, args, sample(w))
+    lens = head.pop("_lens")
+    rec = {"metric": METRIC, "value": head.pop("value"), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head.pop("ms_per_step"), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+    head.pop("metric")
+    rec.update(head)
+    rec["stream_read_ref"] = stream_read_reference(page_bytes(w))
+    rec["kernel_source_sha256"] = kernel_source_hash()
+    rec["host_block_manager"] = host_block_manager(kvq, w, lens)
+    if also:
+        w2 = synth.WORKLOADS[also]
+        sec = measure_decode(kvq, w2, args, sample(w2))
+        sec.pop("_lens")
+        sec.pop("metric")
+        sec["stream_read_ref"] = stream_read_reference(page_bytes(w2))
+        rec["configs"] = {w2.name: sec}
     print(json.dumps(rec), flush=True)
 
 

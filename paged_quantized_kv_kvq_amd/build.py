@@ -22,6 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
+PROBE_SRC = os.path.join(HERE, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")   # measurement only: the streaming-read reference
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the public C-ABI header
 ARCH = "gfx950"
 
@@ -108,7 +110,23 @@ def build(jobs: int = 0, verbose: bool = False, lib: str = LIB, out_dir: str = O
     if r.returncode:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
     os.replace(tmp, lib)
+    if lib == LIB and (not incremental or not os.path.exists(PROBE_LIB)
+                       or os.path.getmtime(PROBE_SRC) > os.path.getmtime(PROBE_LIB)):
+        build_probe(verbose)
     return lib
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libkvq_probe.so: the streaming-read reference kernel the benchmark times."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc()] + COMMON + ["-O3", "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose or r.returncode:
+        sys.stderr.write(" ".join(cmd) + "\n" + r.stdout + r.stderr)
+    if r.returncode:
+        raise RuntimeError("hipcc failed for the streaming-read probe")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def main() -> None:

@@ -181,19 +181,96 @@ def test_nvfp4_write_ties_and_saturation(gpu_lib):
     assert np.array_equal(kp.cpu().numpy(), ok_) and np.array_equal(vp.cpu().numpy(), ov_)
 
 
+def _write_and_compare(kvq, kf, vf, hd, nkv, bs, kbits, vbits, slots, nb, k_scale=1.0, v_scale=1.0):
+    """Write host bf16 bit rows [T, nkv, hd] through the library and the
+    oracle into poison-filled pools; every pool byte must be equal."""
+    from oracle import layout as olayout
+    from oracle import write as owrite
+    lay = kvq.pool_layout(kf, vf, bs, nkv, hd)
+    ks, vs = olayout.pool_layout(kf, vf, bs, nkv, hd)
+    kp = kvq.alloc_pool(lay, "k", nb, fill=0x7F)
+    vp = kvq.alloc_pool(lay, "v", nb, fill=0x7F)
+    key = torch.from_numpy(np.ascontiguousarray(kbits).view(np.int16)).view(torch.bfloat16).cuda()
+    val = torch.from_numpy(np.ascontiguousarray(vbits).view(np.int16)).view(torch.bfloat16).cuda()
+    kvq.reshape_and_cache(lay, key, val, kp, vp, torch.from_numpy(slots).cuda(), k_scale, v_scale)
+    torch.cuda.synchronize()
+    ok_ = np.full(nb * ks.block_stride_bytes, 0x7F, np.uint8)
+    ov_ = np.full(nb * vs.block_stride_bytes, 0x7F, np.uint8)
+    owrite.reshape_and_cache(ks, vs, kbits, vbits, ok_, ov_, slots, k_scale, v_scale)
+    for side, g, o in (("K", kp.cpu().numpy(), ok_), ("V", vp.cpu().numpy(), ov_)):
+        if not np.array_equal(g, o):
+            bad = np.flatnonzero(g != o)
+            raise AssertionError(f"{side} pool differs from the oracle at {bad.size} bytes, first {bad[:8].tolist()}")
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 0.37109375), (0.0123456789, 1.0)])
+def test_fp8_write_every_bf16_pattern(gpu_lib, k_scale, v_scale):
+    # every finite bf16 bit pattern (+-0, subnormals, the largest finites)
+    # through both fp8 sides, at scale 1 and at scales that are not powers of
+    # two (RN32(x / scale) then E4M3 with the clamp at 448); bytes bit-exact
+    hd, nkv, bs = 128, 2, 16
+    pat = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    pat = pat[((pat >> 7) & 0xFF) != 0xFF]                  # drop inf / NaN
+    T = (pat.size + nkv * hd - 1) // (nkv * hd)
+    kb = np.resize(pat, T * nkv * hd).reshape(T, nkv, hd)
+    vb = np.roll(kb.ravel(), 1000).reshape(T, nkv, hd)
+    nb = (T + bs - 1) // bs + 2
+    slots = np.random.default_rng(7050).permutation(nb * bs)[:T].astype(np.int64)
+    say(f"case fp8 write of {pat.size} bf16 patterns, scales {k_scale} / {v_scale}")
+    _write_and_compare(gpu_lib, "fp8", "fp8", hd, nkv, bs, kb, vb, slots, nb, k_scale, v_scale)
+
+
+def _crafted_rows(nkv, hd, seed):
+    """bf16 bit rows that reach the grouped-scale formats' edge cases."""
+    from oracle import codecs as ocodecs
+    rng = np.random.default_rng(seed)
+    rows = [
+        np.ones(hd),                                  # rotates to (sqrt d, 0, ...): all-zero groups after the first
+        np.full(hd, -0.0),                            # signed zeros everywhere
+        np.zeros(hd),
+        rng.standard_normal(hd) * 0.004,              # subnormal E4M3 group scales (< 2^-6)
+        rng.standard_normal(hd) * 3e-5,               # group scales that underflow to 0
+        rng.standard_normal(hd) * 1500.0,             # group scales clamped at 448
+        np.eye(1, hd, 3).ravel() * 4.0,               # rotates to a constant: every element at the group max
+        np.where(np.arange(hd) == 7, 3000.0, rng.standard_normal(hd) * 1e-3),   # one huge element
+        rng.standard_normal(hd) * 1e-39,              # bf16 denormals
+        np.repeat(rng.standard_normal(hd // 16) * 2.0, 16) * np.tile([1.0, -1.0], hd // 2),
+    ]
+    x = np.stack([np.stack([r if h == 0 else r[::-1] for h in range(nkv)]) for r in rows]).astype(np.float32)
+    return ocodecs.bf16_round_bits(x)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+@pytest.mark.parametrize("kf,vf", [("turbo2", "turbo3"), ("turbo4", "turbo8"), ("turbo8", "turbo2"),
+                                   ("turbo3", "turbo4")])
+def test_turbo_write_crafted_rows(gpu_lib, kf, vf, hd):
+    # all-zero groups, +-0, subnormal and underflowing E4M3 scales, scales
+    # clamped at 448, every element at its group's max, a single huge element,
+    # bf16 denormals; pool bytes (codes and scale bytes) bit-exact
+    nkv, bs = 2, 16
+    kb = _crafted_rows(nkv, hd, 7060 + hd)
+    vb = kb[::-1].copy()
+    T = kb.shape[0]
+    nb = 4
+    slots = np.random.default_rng(7061).permutation(nb * bs)[:T].astype(np.int64)
+    say(f"case crafted write {kf}/{vf} hd{hd}")
+    _write_and_compare(gpu_lib, kf, vf, hd, nkv, bs, kb, vb, slots, nb)
+
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("T", [1024, 1025])
 @pytest.mark.parametrize("kf,vf", [("turbo4", "turbo3"), ("bf16", "fp8"), ("nvfp4", "turbo8"), ("turbo2", "bf16")])
-def test_write_row_count_switch(gpu_lib, kf, vf, T):
+def test_write_row_count_switch(gpu_lib, kf, vf, T, hd):
     # the write takes one wave per side up to 2048 (token, kv head) rows and
     # one wave for both sides above: 1024 tokens x 2 kv heads is the last
     # count of the first form, 1025 the first of the second; scattered slots
     # with about one in eight skipped (-1); pool bytes must equal the oracle's
     from oracle import layout as olayout
     from oracle import write as owrite
-    hd, nkv, bs = 128, 2, 16
+    nkv, bs = 2, 16
     nb = (T + bs - 1) // bs + 3
-    say(f"case write {kf}/{vf} T={T}")
-    rng = np.random.default_rng([7100, T, FMTS.index(kf), FMTS.index(vf)])
+    say(f"case write {kf}/{vf} T={T} hd{hd}")
+    rng = np.random.default_rng([7100, T, FMTS.index(kf), FMTS.index(vf), hd])
     kx = rng.standard_normal((T, nkv, hd)).astype(np.float32)
     vx = rng.standard_normal((T, nkv, hd)).astype(np.float32)
     kx[:, :, 5] *= 20.0
