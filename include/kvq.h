@@ -181,6 +181,27 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
                      uint32_t sliding_window, float sparse_v_threshold, float k_scale,
                      float v_scale, void* workspace, size_t* workspace_bytes, void* stream);
 
+/* kvq_paged_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of kvq_paged_decode (same kernels, same plan; the outputs are bit-identical).
+ * The scratch it needs lives in a device array inside the library of at most
+ * 64 MiB per GPU, held from the first call on a GPU until the process ends;
+ * a call whose kvq_paged_decode workspace size exceeds that returns
+ * KVQ_ERR_WORKSPACE (nothing launched).  The call allocates nothing: no
+ * hipMalloc, no allocating library routine.
+ *   stream  must belong to the current device (else KVQ_ERR_INVALID_ARG); the
+ *           first call on a device looks up that device's scratch address.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (other streams, other threads) race.  Nothing in the scratch needs to
+ * start at zero; each call writes everything it reads. */
+int kvq_paged_decode_noalloc(const kvq_layout* layout, const void* q, const void* k_cache,
+                             const void* v_cache, float* out, const int32_t* block_tables,
+                             const int32_t* seq_lens, uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                             uint32_t num_q_heads, float inv_sqrt_d, uint32_t q_stride,
+                             uint32_t sliding_window, float sparse_v_threshold, float k_scale,
+                             float v_scale, void* stream);
+
 /* Chunked prefill attention over the same pools -- [kv.rs] attend with its
  * bottom-right causal mask (query at position p sees keys 0 .. p), after the
  * chunk's own K/V were written with kvq_reshape_and_cache; [kv_cache.rs]

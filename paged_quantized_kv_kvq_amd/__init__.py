@@ -23,7 +23,7 @@ import torch
 __all__ = ["FORMATS", "KvqError", "Layout", "load", "pool_layout", "alloc_pool",
            "reshape_and_cache", "paged_decode", "decode_workspace_bytes", "codebook",
            "library_path", "BlockManager", "paged_prefill", "prefill_workspace_bytes", "check_slots",
-           "check_tables"]
+           "check_tables", "paged_decode_noalloc"]
 
 FORMATS = {"bf16": 0, "fp8": 1, "turbo2": 2, "turbo3": 3, "turbo4": 4, "nvfp4": 5, "turbo8": 8}
 _NAMES = {v: k for k, v in FORMATS.items()}
@@ -80,6 +80,9 @@ def load():
     lib.kvq_reshape_and_cache.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, U32, U32, U32, F32, F32, P]
     lib.kvq_paged_decode.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, U32, U32, U32, F32, U32, U32,
                                      F32, F32, F32, P, ctypes.POINTER(SZ), P]
+    lib.kvq_paged_decode_noalloc.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, U32, U32, U32, F32, U32,
+                                             U32, F32, F32, F32, P]
+    lib.kvq_paged_decode_noalloc.restype = ctypes.c_int
     lib.kvq_paged_prefill.argtypes = [ctypes.POINTER(Layout), P, P, P, P, P, P, P, U32, U32, U32, U32, F32, U32,
                                       U32, F32, F32, P, ctypes.POINTER(SZ), P]
     lib.kvq_paged_prefill.restype = ctypes.c_int
@@ -288,6 +291,37 @@ def paged_decode(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache
         _dev(block_tables, torch.int32, "block_tables"), _dev(seq_lens, torch.int32, "seq_lens"),
         mb, S, Hq, inv_sqrt_d, q.stride(0), sliding_window, sparse_v_threshold, k_scale, v_scale,
         _dev(workspace, torch.uint8, "workspace"), ctypes.byref(n), _stream(stream)), "kvq_paged_decode")
+    return out
+
+
+def paged_decode_noalloc(layout: Layout, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, seq_lens: torch.Tensor, inv_sqrt_d: float,
+                         sliding_window: int = 0, sparse_v_threshold: float = 0.0, k_scale: float = 1.0,
+                         v_scale: float = 1.0, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """paged_decode through kvq_paged_decode_noalloc: no workspace, the library's
+    own per-GPU scratch (pass `out` to allocate nothing at all)."""
+    lib = load()
+    if q.dim() != 3 or q.shape[2] != layout.head_dim:
+        raise ValueError(f"q must be [S, Hq, {layout.head_dim}] for this layout, got {tuple(q.shape)}")
+    S, Hq, hd = q.shape
+    if q.stride(2) != 1 or q.stride(1) != hd:
+        raise ValueError("q must be [S, Hq, head_dim] with contiguous heads")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
+    if seq_lens.numel() != S:
+        raise ValueError(f"seq_lens holds {seq_lens.numel()} entries for {S} sequences")
+    if out is None:
+        out = torch.empty((S, Hq, hd), dtype=torch.float32, device=q.device)
+    elif not out.is_contiguous() or tuple(out.shape) != (S, Hq, hd):
+        raise ValueError("out must be contiguous fp32 [S, Hq, head_dim]")
+    _same_device(("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("block_tables", block_tables),
+                 ("seq_lens", seq_lens), ("out", out))
+    _check(lib.kvq_paged_decode_noalloc(
+        ctypes.byref(layout), _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.uint8, "k_cache"),
+        _dev(v_cache, torch.uint8, "v_cache"), _dev(out, torch.float32, "out"),
+        _dev(block_tables, torch.int32, "block_tables"), _dev(seq_lens, torch.int32, "seq_lens"),
+        block_tables.shape[1], S, Hq, inv_sqrt_d, q.stride(0), sliding_window, sparse_v_threshold, k_scale,
+        v_scale, _stream(stream)), "kvq_paged_decode_noalloc")
     return out
 
 

@@ -1,5 +1,7 @@
 // The exported C ABI: argument checks, pool layout, Lloyd-Max tables, decode
-// planning and kernel dispatch.  Nothing here touches device memory.
+// planning and kernel dispatch.  Device memory is only reached through the
+// kernels; the one device object defined here is the scratch array of the
+// allocation-free decode.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -235,7 +237,13 @@ int kvq_reshape_and_cache(const kvq_layout* layout, const void* key, const void*
   return launch_write(int(hd), a, static_cast<hipStream_t>(stream)) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
-int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
+}  // extern "C"
+
+namespace kvq {
+namespace {
+
+// kvq_paged_decode's checks, plan and launches, for both decode entry points.
+int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
                      float* out, const int32_t* block_tables, const int32_t* seq_lens,
                      uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, float inv_sqrt_d,
                      uint32_t q_stride, uint32_t sliding_window, float sparse_v_threshold, float k_scale,
@@ -337,6 +345,77 @@ int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cach
     if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+// The allocation-free decode's scratch: one copy per GPU, held until the
+// process ends.  In host code the array's name is only a stand-in; the
+// device address each GPU holds it at comes from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+std::mutex g_scratch_mu;
+void* g_scratch[256] = {};  // per device ordinal
+
+}  // namespace
+}  // namespace kvq
+
+static __device__ __align__(256) uint8_t scratch[kvq::kScratchBytes];
+
+namespace kvq {
+namespace {
+
+// The scratch address on the device `stream` belongs to (that device must be
+// the current one); looked up once per device.
+int scratch_for(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return KVQ_ERR_LAUNCH;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return KVQ_ERR_INVALID_ARG;
+    if (sdev != dev) return KVQ_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_LAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+int kvq_paged_decode(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
+                     float* out, const int32_t* block_tables, const int32_t* seq_lens,
+                     uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, float inv_sqrt_d,
+                     uint32_t q_stride, uint32_t sliding_window, float sparse_v_threshold, float k_scale,
+                     float v_scale, void* workspace, size_t* workspace_bytes, void* stream) {
+  return decode_impl(layout, q, k_cache, v_cache, out, block_tables, seq_lens, max_blocks_per_seq, num_seqs,
+                     num_q_heads, inv_sqrt_d, q_stride, sliding_window, sparse_v_threshold, k_scale, v_scale,
+                     workspace, workspace_bytes, stream);
+}
+
+int kvq_paged_decode_noalloc(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
+                             float* out, const int32_t* block_tables, const int32_t* seq_lens,
+                             uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, float inv_sqrt_d,
+                             uint32_t q_stride, uint32_t sliding_window, float sparse_v_threshold, float k_scale,
+                             float v_scale, void* stream) {
+  size_t need = 0;
+  int st = decode_impl(layout, q, k_cache, v_cache, out, block_tables, seq_lens, max_blocks_per_seq, num_seqs,
+                       num_q_heads, inv_sqrt_d, q_stride, sliding_window, sparse_v_threshold, k_scale, v_scale,
+                       nullptr, &need, stream);
+  if (st != KVQ_OK) return st;
+  if (need > kScratchBytes) return KVQ_ERR_WORKSPACE;
+  if (num_seqs == 0) return KVQ_OK;
+  void* ws = nullptr;
+  st = scratch_for(stream, &ws);
+  if (st != KVQ_OK) return st;
+  size_t have = kScratchBytes;
+  return decode_impl(layout, q, k_cache, v_cache, out, block_tables, seq_lens, max_blocks_per_seq, num_seqs,
+                     num_q_heads, inv_sqrt_d, q_stride, sliding_window, sparse_v_threshold, k_scale, v_scale, ws,
+                     &have, stream);
 }
 
 int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
