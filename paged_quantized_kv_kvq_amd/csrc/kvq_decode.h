@@ -1123,6 +1123,108 @@ __device__ __forceinline__ void stage_rows(const DecodeArgs& a, const KeptT* kep
   }
 }
 
+// The kept rows of a wave's list (nk of them) into acc: their bytes go to
+// LDS (every row of a pass requested at once), then each lane slot reads its
+// dims of its rows from there.
+template <int VF, int HD, int G, typename KeptT>
+__device__ __forceinline__ void accumulate_kept(const DecodeArgs& a, const float* vcen, const KeptT* kept, int nk,
+                                                uint32_t* rows, uint32_t vsh, float (&acc)[G][VGeo<HD>::D]) {
+  using GE = VGeo<HD>;
+  using VS = VStage<VF, HD>;
+  constexpr int D = GE::D, T = GE::T, P = GE::P;
+  const int lane = threadIdx.x & 63, t = lane % T, r = lane / T;
+  for (int q0 = 0; q0 < nk; q0 += VS::RPP) {
+    const int nrow = min(VS::RPP, nk - q0);
+    stage_rows<VF, HD>(a, &kept[q0], nrow, lane, rows);
+    wave_lds_sync();
+    // kStageUnroll rows per lane slot at a time, their LDS reads issued together
+    for (int q = r; q < nrow; q += P * kStageUnroll) {
+      Raw<VF, D> vr[kStageUnroll];
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int qu = q + u * P;
+        staged_lane<VF, HD, D>(rows, qu < nrow ? qu : q, t, vr[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kStageUnroll; ++u) {
+        const int qu = q + u * P;
+        const bool ok = qu < nrow;
+        float x[D], sq;
+        v_values<VF, D>(vr[u], vcen, x, sq, vsh);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pw = (ok ? kept[q0 + qu].p[h] : 0.0f) * sq;
+#pragma unroll
+          for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+}
+
+// The end of a sparse-V workgroup (sequence s, kv head g): the lane slots'
+// and the waves' partial sums added in a fixed order, scaled by the fp8 V
+// scale, rotated back (turbo V) and stored.
+template <int VF, int HD, int G, typename Smem>
+__device__ __forceinline__ void sparse_v_finish(const DecodeArgs& a, Smem& sm, float (&acc)[G][VGeo<HD>::D],
+                                                uint32_t s, uint32_t g) {
+  using GE = VGeo<HD>;
+  constexpr int D = GE::D, T = GE::T;
+  constexpr int NT = kVWaves * kWave;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = lane % T, r = lane / T;
+  // lane slots of a wave hold the same dims: add them
+#pragma unroll
+  for (int off = T; off < kWave; off <<= 1)
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
+  // waves, in a fixed order: the upper half stores, the lower half adds its own
+  constexpr int HW = kVWaves / 2;
+  __syncthreads();  // the reduction area overlays the kept lists
+  if (w >= HW && r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < D; ++i) sm.u.red[w - HW][h][t * D + i] = acc[h][i];
+  }
+  __syncthreads();
+  if (w < HW && r == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < D; ++i) sm.u.red[w][h][t * D + i] += acc[h][i];
+  }
+  __syncthreads();
+  float* o = &sm.u.red[0][0][0];  // row h of the result at o + h * HD
+  for (int i = tid; i < G * HD; i += NT) {
+    const int h = i / HD, d = i % HD;
+    float v = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < HW; ++ww) v += sm.u.red[ww][h][d];
+    o[i] = v * a.v_scale;
+  }
+  __syncthreads();
+  if constexpr (Fmt<VF>::rot) {
+    // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
+    for (int h2 = 1; h2 < HD; h2 <<= 1) {
+      for (int i = tid; i < G * HD / 2; i += NT) {
+        const int hh = i / (HD / 2), k = i % (HD / 2);
+        const int lo = hh * HD + (k / h2) * 2 * h2 + (k % h2);
+        const float x = o[lo], y = o[lo + h2];
+        o[lo] = x + y;
+        o[lo + h2] = x - y;
+      }
+      __syncthreads();
+    }
+  }
+  float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
+  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::rot ? o[i] * a.wht_scale : o[i];
+}
+
 // One workgroup of kVWaves waves per (sequence, kv head) does the whole V side
 // of the sparse path and writes the output.  The score kernel left one record
 // segment per (split, wave); V wave v takes segments v, v + kVWaves, ...
@@ -1273,86 +1375,11 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
       fetch(i0 + kWave + lane, rw);
       const int nk = __popcll(bal);
       wave_lds_sync();
-      // 2. the kept rows' bytes go to LDS (every row of a pass requested at
-      //    once), then each lane slot reads its dims of its rows from there
-      for (int q0 = 0; q0 < nk; q0 += VS::RPP) {
-        const int nrow = min(VS::RPP, nk - q0);
-        stage_rows<VF, HD>(a, &kept[q0], nrow, lane, rows);
-        wave_lds_sync();
-        // kStageUnroll rows per lane slot at a time, their LDS reads issued together
-        for (int q = r; q < nrow; q += P * kStageUnroll) {
-          Raw<VF, D> vr[kStageUnroll];
-#pragma unroll
-          for (int u = 0; u < kStageUnroll; ++u) {
-            const int qu = q + u * P;
-            staged_lane<VF, HD, D>(rows, qu < nrow ? qu : q, t, vr[u]);
-          }
-#pragma unroll
-          for (int u = 0; u < kStageUnroll; ++u) {
-            const int qu = q + u * P;
-            const bool ok = qu < nrow;
-            float x[D], sq;
-            v_values<VF, D>(vr[u], sm.vcen, x, sq, vsh);
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-              const float pw = (ok ? kept[q0 + qu].p[h] : 0.0f) * sq;
-#pragma unroll
-              for (int i = 0; i < D; ++i) acc[h][i] = fmaf(pw, x[i], acc[h][i]);
-            }
-          }
-        }
-        wave_lds_sync();
-      }
+      // 2. the kept rows' V values into acc
+      accumulate_kept<VF, HD, G>(a, sm.vcen, kept, nk, rows, vsh, acc);
     }
   }
-  // lane slots of a wave hold the same dims: add them
-#pragma unroll
-  for (int off = T; off < kWave; off <<= 1)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < D; ++i) acc[h][i] += __shfl_xor(acc[h][i], off);
-  // waves, in a fixed order: the upper half stores, the lower half adds its own
-  constexpr int HW = kVWaves / 2;
-  __syncthreads();  // the reduction area overlays the kept lists
-  if (w >= HW && r == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < D; ++i) sm.u.red[w - HW][h][t * D + i] = acc[h][i];
-  }
-  __syncthreads();
-  if (w < HW && r == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < D; ++i) sm.u.red[w][h][t * D + i] += acc[h][i];
-  }
-  __syncthreads();
-  float* o = &sm.u.red[0][0][0];  // row h of the result at o + h * HD
-  for (int i = tid; i < G * HD; i += NT) {
-    const int h = i / HD, d = i % HD;
-    float v = 0.0f;
-#pragma unroll
-    for (int ww = 0; ww < HW; ++ww) v += sm.u.red[ww][h][d];
-    o[i] = v * a.v_scale;
-  }
-  __syncthreads();
-  if constexpr (Fmt<VF>::rot) {
-    // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
-    for (int h2 = 1; h2 < HD; h2 <<= 1) {
-      for (int i = tid; i < G * HD / 2; i += NT) {
-        const int hh = i / (HD / 2), k = i % (HD / 2);
-        const int lo = hh * HD + (k / h2) * 2 * h2 + (k % h2);
-        const float x = o[lo], y = o[lo + h2];
-        o[lo] = x + y;
-        o[lo + h2] = x - y;
-      }
-      __syncthreads();
-    }
-  }
-  float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
-  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::rot ? o[i] * a.wht_scale : o[i];
+  sparse_v_finish<VF, HD, G>(a, sm, acc, s, g);
 }
 
 }  // namespace kvq

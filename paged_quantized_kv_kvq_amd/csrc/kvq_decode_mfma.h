@@ -123,6 +123,13 @@ struct MfmaSmem {
   } u;
 };
 
+// Column of position j in a wave's p x scale row of scale group grp.  The
+// 4-position blocks of the row are XOR-swizzled by the group: the rows of the
+// groups are 64 words apart, so unswizzled the 16-byte operand-A reads of
+// lanes in different groups all start on the same bank (an 8-way conflict);
+// swizzled, the blocks the lanes read spread over 16 bank offsets.
+__device__ __forceinline__ int pt_col(int grp, int j) { return j ^ ((grp & 3) << 2); }
+
 // One chunk's raw bytes in a lane's registers: its K quarter (turbo K: and
 // the words that hold its quarter's scales), its share of the chunk's V code
 // words, and the V scale words of position lane % 16.
@@ -522,21 +529,21 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
           const int sword = ok ? int(ck.s[sw]) : 0;
           const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(sword, false);
           const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(sword, true);
-          pt[hg][4 * sw][lane >> 4][lane & 15] = p * lo.x;
-          pt[hg][4 * sw + 1][lane >> 4][lane & 15] = p * lo.y;
-          pt[hg][4 * sw + 2][lane >> 4][lane & 15] = p * hi.x;
-          pt[hg][4 * sw + 3][lane >> 4][lane & 15] = p * hi.y;
+          pt[hg][4 * sw][lane >> 4][pt_col(4 * sw, lane & 15)] = p * lo.x;
+          pt[hg][4 * sw + 1][lane >> 4][pt_col(4 * sw + 1, lane & 15)] = p * lo.y;
+          pt[hg][4 * sw + 2][lane >> 4][pt_col(4 * sw + 2, lane & 15)] = p * hi.x;
+          pt[hg][4 * sw + 3][lane >> 4][pt_col(4 * sw + 3, lane & 15)] = p * hi.y;
         }
       } else if constexpr (MG::SWL > 0) {
         // turbo8: two BF16 scales per word
 #pragma unroll
         for (int sw = 0; sw < MG::SWL; ++sw) {
           const uint32_t sword = ok ? ck.s[sw] : 0u;
-          pt[hg][2 * sw][lane >> 4][lane & 15] = p * __uint_as_float(sword << 16);
-          pt[hg][2 * sw + 1][lane >> 4][lane & 15] = p * __uint_as_float(sword & 0xFFFF0000u);
+          pt[hg][2 * sw][lane >> 4][pt_col(2 * sw, lane & 15)] = p * __uint_as_float(sword << 16);
+          pt[hg][2 * sw + 1][lane >> 4][pt_col(2 * sw + 1, lane & 15)] = p * __uint_as_float(sword & 0xFFFF0000u);
         }
       } else {
-        pt[hg][0][lane >> 4][lane & 15] = p;
+        pt[hg][0][lane >> 4][pt_col(0, lane & 15)] = p;
       }
       wv.alpha[hg][lane >> 4] = al;
     }
@@ -561,8 +568,8 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
       float pa[NG][8];
 #pragma unroll
       for (int hg = 0; hg < NG; ++hg) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][h8]);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][h8 + 4]);
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][pt_col(grp, h8)]);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(&pt[hg][grp][lane & 3][pt_col(grp, h8 + 4)]);
         pa[hg][0] = x0.x; pa[hg][1] = x0.y; pa[hg][2] = x0.z; pa[hg][3] = x0.w;
         pa[hg][4] = x1.x; pa[hg][5] = x1.y; pa[hg][6] = x1.z; pa[hg][7] = x1.w;
       }

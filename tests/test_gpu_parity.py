@@ -292,3 +292,77 @@ def test_write_row_count_switch(gpu_lib, kf, vf, T, hd):
                              vb.view(torch.int16).numpy().view(np.uint16), ok_, ov_, slots, k_scale, v_scale)
     assert np.array_equal(kp.cpu().numpy(), ok_), "K pool differs from the oracle"
     assert np.array_equal(vp.cpu().numpy(), ov_), "V pool differs from the oracle"
+
+
+# eight kv heads (the dense matrix-core pass's widest workgroup): every V
+# format behind bf16 / fp8 K, at several shapes
+EIGHT_V = ["bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8", "nvfp4"]
+
+
+@pytest.mark.parametrize("vf", EIGHT_V)
+@pytest.mark.parametrize("kf", ["fp8", "bf16"])
+def test_eight_kv_heads_formats(gpu_lib, kf, vf):
+    hd = 64 if vf == "bf16" else 128    # V rows of at most 128 bytes
+    w = synth.small(9300 + FMTS.index(kf) * 7 + FMTS.index(vf), lens=[0, 1, 15, 17, 300, 2100, 4133],
+                    num_q_heads=32, num_kv_heads=8, head_dim=hd, block_size=16, k_format=kf, v_format=vf)
+    run(gpu_lib, w, tail=2, label=f"Hkv8 {kf}/{vf} hd{hd}")
+
+
+@pytest.mark.parametrize("g,hd,bs,win", [(1, 128, 16, 0), (2, 64, 32, 0), (8, 128, 16, 0), (4, 256, 16, 0),
+                                         (4, 128, 64, 0), (4, 128, 32, 333), (8, 64, 16, 1000), (2, 256, 128, 0)])
+def test_eight_kv_heads_shapes(gpu_lib, g, hd, bs, win):
+    kf = "fp8" if hd == 256 else "bf16"
+    w = synth.small(9400 + g * 100 + hd + bs + win, lens=[5, 64, 700, 1999, 3000], num_q_heads=8 * g,
+                    num_kv_heads=8, head_dim=hd, block_size=bs, k_format=kf, v_format="turbo2",
+                    sliding_window=win)
+    run(gpu_lib, w, tail=1, label=f"Hkv8 G{g} hd{hd} bs{bs} W{win}")
+
+
+# sparse-V with eight kv heads (bf16 / fp8 K rows of 64..256 bytes): several
+# splits per sequence, every group size, windows that start inside a chunk,
+# both thresholds
+@pytest.mark.parametrize("kf,vf,hd,g,bs,win,thr", [
+    ("bf16", "turbo4", 128, 4, 16, 0, 1e-3),
+    ("bf16", "turbo4", 128, 4, 16, 0, 0.05),
+    ("bf16", "bf16", 64, 1, 16, 0, 1e-3),
+    ("bf16", "nvfp4", 64, 8, 32, 0, 0.05),
+    ("fp8", "turbo2", 128, 2, 16, 333, 1e-3),
+    ("fp8", "turbo8", 256, 4, 128, 0, 1e-3),
+    ("fp8", "fp8", 64, 8, 16, 1000, 0.05),
+    ("bf16", "turbo3", 128, 8, 64, 700, 1e-3),
+    ("fp8", "turbo4", 128, 4, 32, 0, 1e-3),
+])
+def test_sparse_eight_kv_heads(gpu_lib, kf, vf, hd, g, bs, win, thr):
+    w = synth.small(9600 + FMTS.index(kf) * 7 + FMTS.index(vf) + hd + 10 * g + bs + win, num_q_heads=8 * g,
+                    lens=[0, 1, 15, 17, 511, 512, 513, 1500, 4133], num_kv_heads=8, head_dim=hd, block_size=bs,
+                    k_format=kf, v_format=vf, sliding_window=win, sparse_v_threshold=thr)
+    run(gpu_lib, w, tail=2, label=f"sparse Hkv8 {kf}/{vf} hd{hd} G{g} bs{bs} W{win} thr{thr}")
+
+
+def _lens(seed, n, hi, zeros=0.1):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, hi + 1, n)
+    lens[rng.random(n) < zeros] = 0
+    return [int(x) for x in lens]
+
+
+# sparse-V over many short sequences (and empty ones), with and without a
+# window; block tables sized far beyond the sequences; thousands of sequences
+@pytest.mark.parametrize("win", [0, 50])
+def test_sparse_many_short_sequences(gpu_lib, win):
+    w = synth.small(9700 + win, lens=_lens(9700 + win, 300, 200), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                    block_size=16, k_format="bf16", v_format="turbo4", sliding_window=win, sparse_v_threshold=1e-3)
+    run(gpu_lib, w, tail=1, label=f"sparse 300 seqs W{win}")
+
+
+def test_sparse_oversized_block_tables(gpu_lib):
+    w = synth.small(9710, lens=_lens(9710, 64, 100), num_q_heads=16, num_kv_heads=8, head_dim=64, block_size=32,
+                    k_format="fp8", v_format="turbo2", sparse_v_threshold=1e-3)
+    w = w.scaled(seq_len=(1, 32768))   # block tables sized for 32768 positions
+    run(gpu_lib, w, tail=1, label="sparse, oversized block tables")
+
+
+def test_sparse_thousands_of_sequences(gpu_lib):
+    w = synth.small(9720, lens=_lens(9720, 4200, 24), num_q_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+                    k_format="bf16", v_format="bf16", sparse_v_threshold=0.05)
+    run(gpu_lib, w, tail=0, label="sparse 4200 seqs")
