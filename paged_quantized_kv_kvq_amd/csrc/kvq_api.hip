@@ -242,6 +242,39 @@ int kvq_reshape_and_cache(const kvq_layout* layout, const void* key, const void*
 namespace kvq {
 namespace {
 
+// The dense decode path: the split kernel of the (K, V) pair, then the merge.
+hipError_t launch_dense(const kvq_layout* layout, const DecodeArgs& a, uint32_t hd, uint32_t G, uint32_t nwg,
+                        hipStream_t s) {
+  const int vf = layout->v_format;
+  hipError_t e;
+  switch (layout->k_format) {
+    case KVQ_BF16: e = launch_split_bf16(vf, int(hd), int(G), a, nwg, s); break;
+    case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, nwg, s); break;
+    case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, nwg, s); break;
+    case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, nwg, s); break;
+    case KVQ_TURBO8: e = launch_split_turbo8(vf, int(hd), int(G), a, nwg, s); break;
+    case KVQ_NVFP4: e = launch_split_nvfp4(vf, int(hd), int(G), a, nwg, s); break;
+    default: e = launch_split_turbo4(vf, int(hd), int(G), a, nwg, s); break;
+  }
+  return e == hipSuccess ? launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s) : e;
+}
+
+// The fields of a decode call's arguments that come from the layout and the
+// scales alone.
+void fill_common(DecodeArgs& a, const kvq_layout* layout, float inv_sqrt_d, float k_scale, float v_scale) {
+  a.log2_bs = log2u(layout->block_size);
+  a.num_kv_heads = layout->num_kv_heads;
+  a.k_stride = layout->k_block_stride_bytes;
+  a.k_data = layout->k_data_section_bytes;
+  a.v_stride = layout->v_block_stride_bytes;
+  a.v_data = layout->v_data_section_bytes;
+  const float log2e = 1.4426950408889634f;
+  a.qk_scale = inv_sqrt_d * log2e * (layout->k_format == KVQ_FP8_E4M3 ? k_scale : 1.0f);
+  a.v_scale = layout->v_format == KVQ_FP8_E4M3 ? v_scale : 1.0f;
+  a.wht_scale = float(1.0 / std::sqrt(double(layout->head_dim)));
+  a.cb = codebooks();
+}
+
 // kvq_paged_decode's checks, plan and launches, for both decode entry points.
 int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache,
                      float* out, const int32_t* block_tables, const int32_t* seq_lens,
@@ -322,16 +355,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   const int kf = layout->k_format, vf = layout->v_format;
   hipError_t e;
   if (!sparse) {
-    switch (kf) {
-      case KVQ_BF16: e = launch_split_bf16(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      case KVQ_TURBO8: e = launch_split_turbo8(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      case KVQ_NVFP4: e = launch_split_nvfp4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-      default: e = launch_split_turbo4(vf, int(hd), int(G), a, uint32_t(nwg), s); break;
-    }
-    if (e == hipSuccess) e = launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
+    e = launch_dense(layout, a, hd, G, uint32_t(nwg), s);
   } else {
     switch (kf) {
       case KVQ_BF16: e = launch_scores_bf16(int(hd), int(G), a, uint32_t(nwg), s); break;
@@ -418,6 +442,76 @@ int kvq_paged_decode_noalloc(const kvq_layout* layout, const void* q, const void
                      &have, stream);
 }
 
+}  // extern "C"
+
+namespace kvq {
+namespace {
+
+// Chunked prefill where the prefill tiles do not apply (block_size < 16, V
+// rows over 128 bytes, K quarters the tile kernel does not take): every query
+// runs as its own decode row -- its sequence's block table, the length of its
+// causal span (position + 1), its own query and output row -- through the
+// dense decode kernels.  Each query then reads its keys and values on its
+// own, so this path trades the tiles' reuse for coverage.  The workspace
+// holds the rows' map and lengths, then the dense decode workspace of
+// num_seqs * max_query_len rows.
+int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
+                      const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+                      uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
+                      float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
+                      void* workspace, size_t* workspace_bytes, void* stream) {
+  const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim, G = num_q_heads / nkv;
+  const uint64_t rows = uint64_t(num_seqs) * max_query_len;
+  if (rows >= (1ull << 31) || rows * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  const Plan p = make_plan(uint32_t(rows), nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, false);
+  const uint64_t nwg = (rows * p.nsplit + 7) / 8 * 8 * nkv;
+  if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  const uint64_t off_vrow = 0, off_vlen = up256(rows * 2 * sizeof(int32_t));
+  const uint64_t base = up256(off_vlen + rows * sizeof(int32_t));
+  const uint64_t bytes = base + p.bytes;
+  if (!workspace) {
+    *workspace_bytes = size_t(bytes);
+    return KVQ_OK;
+  }
+  if (*workspace_bytes < bytes) return KVQ_ERR_WORKSPACE;
+  if (num_seqs == 0) return KVQ_OK;
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !query_start) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4) || !aligned(workspace, 16))
+    return KVQ_ERR_ALIGNMENT;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int32_t* vrow = reinterpret_cast<int32_t*>(ws + off_vrow);
+  int32_t* vlen = reinterpret_cast<int32_t*>(ws + off_vlen);
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.out = out;
+  a.block_tables = block_tables;
+  a.seq_lens = vlen;
+  a.vrow = vrow;
+  a.ml = reinterpret_cast<float*>(ws + base + p.off_ml);
+  a.part = reinterpret_cast<float*>(ws + base + p.off_part);
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = uint32_t(rows);
+  a.num_q_heads = num_q_heads;
+  a.q_stride = q_stride;
+  a.window = sliding_window;
+  a.split_len = p.split_len;
+  a.nsplit = p.nsplit;
+  fill_common(a, layout, inv_sqrt_d, k_scale, v_scale);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prefill_rows(query_start, seq_lens, num_seqs, max_query_len, vrow, vlen, s);
+  if (e == hipSuccess) e = launch_dense(layout, a, hd, G, uint32_t(nwg), s);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
 int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
                       const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
                       uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
@@ -430,7 +524,6 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   if (num_q_heads == 0 || num_q_heads % nkv) return KVQ_ERR_INVALID_ARG;
   const uint32_t G = num_q_heads / nkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
-  if (!mfma_split_ok(layout->k_format, layout->v_format, int(hd)) || bs < 16) return KVQ_ERR_UNSUPPORTED;
   if (!std::isfinite(inv_sqrt_d) || inv_sqrt_d <= 0.0f) return KVQ_ERR_INVALID_ARG;
   if (layout->k_format == KVQ_FP8_E4M3 && !good_scale(k_scale)) return KVQ_ERR_INVALID_ARG;
   if (layout->v_format == KVQ_FP8_E4M3 && !good_scale(v_scale)) return KVQ_ERR_INVALID_ARG;
@@ -438,6 +531,10 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   if (q_stride < num_q_heads * hd) return KVQ_ERR_INVALID_ARG;
   if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
   if (uint64_t(max_blocks_per_seq) * bs >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  if (!mfma_split_ok(layout->k_format, layout->v_format, int(hd)) || bs < 16)
+    return prefill_as_decode(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start,
+                             max_blocks_per_seq, num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride,
+                             sliding_window, k_scale, v_scale, workspace, workspace_bytes, stream);
   // tiles of qt queries; the key range of a tile spans at most the longest
   // sequence (or the window plus the tile)
   const uint32_t qt = uint32_t(prefill_qt(layout->k_format, int(hd), int(G)));

@@ -294,6 +294,15 @@ __device__ __forceinline__ void v_values(const Raw<VF, D>& v, const float* __res
   }
 }
 
+// The query / output row and the block-table row of decode row s: both s in
+// a plain decode call; chunked prefill run as decode rows maps them.
+__device__ __forceinline__ uint32_t row_query(const DecodeArgs& a, uint32_t s) {
+  return a.vrow ? uint32_t(a.vrow[2 * s + 1]) : s;
+}
+__device__ __forceinline__ uint32_t row_table(const DecodeArgs& a, uint32_t s) {
+  return a.vrow ? uint32_t(a.vrow[2 * s]) : s;
+}
+
 struct SeqSpan {
   int L, j0, pb, pe;
 };
@@ -378,7 +387,7 @@ template <int KF, int VF, int HD, int G, int D>
 __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, HD, G>& sm, uint32_t s,
                                          uint32_t g, int pb, int pe, int t, QReg<KF, D, G>& q) {
   const int tid = threadIdx.x;
-  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;
+  const uint16_t* qg = a.q + uint64_t(row_query(a, s)) * a.q_stride + uint64_t(g) * G * HD;
   q.scsh = scale_shift<D, Fmt<KF>::sgb == 2 ? 2 : 1>(t);
   q.vsh = scale_shift<D, Fmt<VF>::sgb == 2 ? 2 : 1>(t);
   if constexpr (!Fmt<KF>::turbo) {
@@ -401,7 +410,7 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
   {
     const int first = pb >> a.log2_bs;
     const int n = ((pe - 1) >> a.log2_bs) - first + 1;
-    const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks + first;
+    const int32_t* bt = a.block_tables + uint64_t(row_table(a, s)) * a.max_blocks + first;
     for (int i = tid; i < n; i += kWaves * kWave) {
       const uint64_t page = uint64_t(uint32_t(bt[i]));
       sm.kbase[i] = page * a.k_stride;
@@ -762,6 +771,7 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   const uint32_t hq = blockIdx.x % a.num_q_heads;
   const uint32_t s = blockIdx.x / a.num_q_heads;
   const uint32_t g = hq / G, h = hq % G;
+  if (a.vrow && a.vrow[2 * s] < 0) return;  // a prefill row without a query: no output row
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
@@ -770,7 +780,7 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   merge_row<HD, 16>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD, uint32_t(G) * HD, ns, a.v_scale, o);
   __syncthreads();
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
-  float* dst = a.out + (uint64_t(s) * a.num_q_heads + hq) * HD;
+  float* dst = a.out + (uint64_t(row_query(a, s)) * a.num_q_heads + hq) * HD;
   for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
 }
 

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     sp.pe = min(pt0.hi, sp.pb + int(a.split_len));
     if (sp.pb >= sp.pe) return;  // uniform over the workgroup
   }
-  const uint16_t* qg = a.q + uint64_t(s) * a.q_stride + uint64_t(g) * G * HD;  // decode: the group's rows
+  const uint16_t* qg = a.q + uint64_t(row_query(a, s)) * a.q_stride + uint64_t(g) * G * HD;  // decode: the group's rows
   // prefill: query row of a tile row (nullptr: no query)
   auto qrow = [&](int r) -> const uint16_t* {
     const int t = r / G;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const int first = sp.pb >> a.log2_bs;
   {
     const int n = ((sp.pe - 1) >> a.log2_bs) - first + 1;
-    const int32_t* bt = a.block_tables + uint64_t(s) * a.max_blocks + first;
+    const int32_t* bt = a.block_tables + uint64_t(QT == 0 ? row_table(a, s) : s) * a.max_blocks + first;
     for (int i = tid; i < n; i += int(blockDim.x)) {
       const uint64_t page = uint64_t(uint32_t(bt[i]));
       sm.kbase[i] = page * a.k_stride;

@@ -46,7 +46,31 @@ hipError_t prefill_merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t s
   return hipGetLastError();
 }
 
+// Decode row v = s * mq + i is query i of sequence s: its query row and its
+// length (position + 1, the causal span), or no query (i past the chunk, or
+// a position below 0, which the caller's contract excludes).
+__global__ void prefill_rows_kernel(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
+                                    uint32_t mq, int32_t* vrow, int32_t* vlen) {
+  const uint64_t v = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (v >= uint64_t(num_seqs) * mq) return;
+  const uint32_t s = uint32_t(v / mq), i = uint32_t(v % mq);
+  const int q0 = query_start[s], n = query_start[s + 1] - q0;
+  const int p = seq_lens[s] - n + int(i);
+  const bool ok = int(i) < n && p >= 0;
+  vrow[2 * v] = ok ? int32_t(s) : -1;
+  vrow[2 * v + 1] = ok ? q0 + int32_t(i) : -1;
+  vlen[v] = ok ? p + 1 : 0;
+}
+
 }  // namespace
+
+hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
+                               uint32_t max_query_len, int32_t* vrow, int32_t* vlen, hipStream_t st) {
+  const uint64_t rows = uint64_t(num_seqs) * max_query_len;
+  hipLaunchKernelGGL(prefill_rows_kernel, dim3(uint32_t((rows + 255) / 256)), dim3(256), 0, st, query_start, seq_lens,
+                     num_seqs, max_query_len, vrow, vlen);
+  return hipGetLastError();
+}
 
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (vf) {

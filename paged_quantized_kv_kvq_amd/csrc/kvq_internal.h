@@ -152,6 +152,11 @@ struct DecodeArgs {
   float v_scale;    // fp8 V side's scale, else 1
   float thr;        // sparse-V threshold (0: dense)
   float wht_scale;  // RN32(1/sqrt(head_dim))
+  // chunked prefill run as decode rows (the shapes the prefill tiles do not
+  // cover): row s of the call is query row vrow[2 s + 1] of sequence
+  // vrow[2 s] (-1: no query), its length that query's position + 1; null in
+  // a plain decode call (row s is sequence s)
+  const int32_t* vrow;
   const int32_t* query_start;  // chunked prefill: [S + 1] first query row of each sequence
   uint32_t ntiles;             // ... tiles of qt queries per sequence (of the longest chunk)
   uint32_t qt;                 // ... queries per tile
@@ -184,6 +189,10 @@ hipError_t launch_scores_turbo3(int hd, int g, const DecodeArgs& a, uint32_t nwg
 hipError_t launch_scores_turbo4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_turbo8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_nvfp4(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+// Chunked prefill as decode rows: vrow / vlen of the num_seqs * max_query_len
+// rows (row s * max_query_len + i is query i of sequence s).
+hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
+                               uint32_t max_query_len, int32_t* vrow, int32_t* vlen, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);

@@ -171,13 +171,17 @@ def test_prefill_host_checks(lib):
     n = kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100)
     assert n > 0 and n % 256 == 0
     assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100, sliding_window=128) <= n
-    for args in [(("bf16", "bf16", 16, 8, 128), 32),     # bf16 V rows of 256 bytes: VALU-only shape
-                 (("fp8", "turbo2", 8, 8, 128), 32),     # block_size < 16
-                 (("turbo3", "turbo3", 16, 8, 64), 32),  # turbo3 K at head_dim 64
-                 (("fp8", "turbo2", 16, 8, 128), 24)]:   # G = 3
-        with pytest.raises(kvq.KvqError) as e:
-            kvq.prefill_workspace_bytes(kvq.pool_layout(*args[0]), 4, args[1], 64, 100)
-        assert e.value.status in (UNSUPPORTED, INVALID)
+    # shapes outside the prefill tiles run as decode rows: their workspace
+    # holds the dense decode workspace of num_seqs * max_query_len rows
+    for shape in [("bf16", "bf16", 16, 8, 128),     # bf16 V rows of 256 bytes
+                  ("fp8", "turbo2", 8, 8, 128),     # block_size < 16
+                  ("turbo3", "turbo3", 16, 8, 64)]:  # turbo3 K at head_dim 64
+        lay_s = kvq.pool_layout(*shape)
+        rows = kvq.prefill_workspace_bytes(lay_s, 4, 32, 64, 100)
+        assert rows >= kvq.decode_workspace_bytes(lay_s, 400, 32, 64) and rows % 256 == 0
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.prefill_workspace_bytes(kvq.pool_layout("fp8", "turbo2", 16, 8, 128), 4, 24, 64, 100)   # G = 3
+    assert e.value.status in (UNSUPPORTED, INVALID)
     with pytest.raises(kvq.KvqError) as e:
         kvq.prefill_workspace_bytes(lay, 4, 32, 64, 0)       # max_query_len 0
     assert e.value.status == INVALID

@@ -128,3 +128,21 @@ def test_prefill_long_chunk_sampled_rows(gpu_lib):
     assert np.all(np.isfinite(out.cpu().numpy()))
     assert err <= MAX_ABS and rel <= REL_L2, f"long chunk: max-abs {err:.2e} rel-L2 {rel:.2e}"
     say(f"  ok prefill long chunk: {len(rows)} sampled rows, max-abs {err:.2e} rel-L2 {rel:.2e}")
+
+
+# shapes the prefill tiles do not take (V rows over 128 bytes, K quarters of
+# other sizes, block_size < 16): every query runs as a decode row
+@pytest.mark.parametrize("kf,vf,hd,bs", [("bf16", "bf16", 128, 16), ("bf16", "bf16", 256, 16), ("fp8", "fp8", 256, 16),
+                                         ("turbo8", "turbo8", 256, 16), ("bf16", "turbo4", 256, 16),
+                                         ("turbo3", "turbo3", 64, 16), ("bf16", "turbo4", 128, 1),
+                                         ("fp8", "turbo2", 128, 2), ("turbo4", "turbo3", 128, 8)])
+def test_prefill_as_decode_rows(gpu_lib, kf, vf, hd, bs):
+    w = synth.small(9800 + hd + bs + len(kf) * 3 + len(vf), lens=[1, 17, 300, 700], num_q_heads=8, num_kv_heads=2,
+                    head_dim=hd, block_size=bs, k_format=kf, v_format=vf)
+    run_prefill(gpu_lib, w, [1, 17, 40, 100], seed=hd + bs, label=f"rows {kf}/{vf} hd{hd} bs{bs}")
+
+
+def test_prefill_as_decode_rows_window_and_empty(gpu_lib):
+    w = synth.small(9850, lens=[300, 0, 64, 129, 17], num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=4,
+                    k_format="bf16", v_format="bf16")
+    run_prefill(gpu_lib, w, [33, 0, 0, 129, 5], window=50, seed=5, label="rows, window 50, empty chunks", q_pad=2)
