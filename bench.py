@@ -428,7 +428,14 @@ def prefill_main(args, kvq, w):
     kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
     keys = 0
     tile_keys = 0
-    rows = 16 if w.k_format in ("bf16", "fp8") and hd <= 128 else 8   # rows of a prefill tile
+    # bf16 / fp8 K with block_size >= 4 runs on the bf16 tile kernel (128
+    # (query, head) rows per tile, 64 at head_dim 256); other K formats on
+    # the split kernel's tiles of 16 or 8 rows
+    bf16_tiles = w.k_format in ("bf16", "fp8") and bs >= 4
+    if bf16_tiles:
+        rows = 128 if hd <= 128 else 64
+    else:
+        rows = 16 if hd <= 128 else 8
     qt = max(1, rows // (Hq // Hkv))
     for L, c in zip(st.lens.astype(np.int64), C):
         p = L - c + np.arange(c)
@@ -441,11 +448,23 @@ def prefill_main(args, kvq, w):
     min_bytes = int(sum(int(L) for L in st.lens)) * Hkv * (kb + vb)
     tile_bytes = tile_keys * Hkv * (kb + vb)
     tflops = flops / (att_ms * 1e-3) / 1e12
-    # the instruction mix's peak: Q.K on bf16 matrix cores for bf16 / fp8 K
-    # (fp32 ones over the rotated query otherwise), P.V on fp32 ones; half
-    # the flops each, so the peak is the harmonic combination
-    qk_peak = MFMA_BF16_TFLOPS if w.k_format in ("bf16", "fp8") else MFMA_F32_TFLOPS
-    peak = 1.0 / (0.5 / qk_peak + 0.5 / MFMA_F32_TFLOPS)
+    if bf16_tiles:
+        # Q.K and P.V both on bf16 matrix cores; P.V takes its weights (and a
+        # V side that is not a bf16 value) as bf16 hi + lo pairs: 3 products
+        # per algorithmic one (2 when V is exact in bf16)
+        pv_products = 2 if w.v_format in ("bf16", "fp8", "nvfp4") else 3
+        peak = MFMA_BF16_TFLOPS
+        peak_basis = (f"every flop at {MFMA_BF16_TFLOPS} (bf16); P.V issues {pv_products} bf16 products per "
+                      "algorithmic product (hi/lo pairs), counted once")
+        issued = flops / 2 * (1 + pv_products)
+        kernel = "kvq_paged_prefill: prefill_tile_kernel"
+    else:
+        # Q.K on fp32 matrix cores over the rotated query (turbo / NVFP4 K),
+        # P.V on fp32 ones; half the flops each
+        peak = MFMA_F32_TFLOPS
+        peak_basis = f"every flop at {MFMA_F32_TFLOPS} (fp32 matrix cores)"
+        issued = flops
+        kernel = "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel"
     rec = {
         "metric": "chunked-prefill query tokens/s over the quantized paged cache, 1 GPU",
         "value": round(T / (ms_step * 1e-3), 1),
@@ -459,10 +478,10 @@ def prefill_main(args, kvq, w):
         "write_ms": round(float(np.median(stp - att)), 4),
         "wall_s_timed_loop": round(elapsed, 3),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": round(peak, 1), "unit": "TFLOP/s",
-                     "peak_basis": f"half the flops at {qk_peak} (Q.K), half at {MFMA_F32_TFLOPS} (P.V, fp32)",
+                     "peak_basis": peak_basis,
                      "frac": round(tflops / peak, 4), "traffic": traffic_from_profile(w.name, "prefill"),
-                     "kernel": "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel",
-                     "algorithmic_flops": flops},
+                     "kernel": kernel, "algorithmic_flops": flops, "issued_matrix_flops": int(issued),
+                     "issued_frac": round(issued / (att_ms * 1e-3) / 1e12 / peak, 4)},
         "kv_bytes": {"once_per_sequence": min_bytes, "read_by_tiles": tile_bytes, "queries_per_tile": qt,
                      "gbs_once_per_sequence": round(min_bytes / (att_ms * 1e-3) / 1e9, 1),
                      "gbs_read_by_tiles": round(tile_bytes / (att_ms * 1e-3) / 1e9, 1)},

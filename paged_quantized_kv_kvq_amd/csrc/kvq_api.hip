@@ -507,6 +507,54 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
+// Chunked prefill on the tile kernel (K sides exact in bf16, block_size >=
+// 4): a workgroup per (sequence, kv head, tile of queries) walks the tile's
+// key range and writes finished rows; nothing goes through the workspace,
+// which the call still takes (256 bytes) so that a null workspace keeps
+// meaning "report the size".
+int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
+                  const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
+                  uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
+                  float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
+                  void* workspace, size_t* workspace_bytes, void* stream) {
+  const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim, G = num_q_heads / nkv;
+  const uint32_t qt = uint32_t(prefill_tile_rows(int(hd))) / G;
+  const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
+  const uint64_t nwg = (uint64_t(num_seqs) * nkv + 7) / 8 * 8 * ntiles;
+  if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  const uint64_t bytes = 256;
+  if (!workspace) {
+    *workspace_bytes = size_t(bytes);
+    return KVQ_OK;
+  }
+  if (*workspace_bytes < bytes) return KVQ_ERR_WORKSPACE;
+  if (num_seqs == 0) return KVQ_OK;
+  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !query_start) return KVQ_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4) || !aligned(workspace, 16))
+    return KVQ_ERR_ALIGNMENT;
+  DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_cache = static_cast<const uint8_t*>(k_cache);
+  a.v_cache = static_cast<const uint8_t*>(v_cache);
+  a.out = out;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.query_start = query_start;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.q_stride = q_stride;
+  a.window = sliding_window;
+  a.ntiles = uint32_t(ntiles);
+  a.qt = qt;
+  fill_common(a, layout, inv_sqrt_d, k_scale, v_scale);
+  const hipError_t e = launch_prefill_tiles(layout->k_format, layout->v_format, int(hd), int(G), a, uint32_t(nwg),
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
 }  // namespace
 }  // namespace kvq
 
@@ -531,6 +579,10 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   if (q_stride < num_q_heads * hd) return KVQ_ERR_INVALID_ARG;
   if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
   if (uint64_t(max_blocks_per_seq) * bs >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
+  if (KVQ_PREFILL_TILES && (layout->k_format == KVQ_BF16 || layout->k_format == KVQ_FP8_E4M3) && bs >= 4)
+    return prefill_tiles(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start, max_blocks_per_seq,
+                         num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride, sliding_window, k_scale,
+                         v_scale, workspace, workspace_bytes, stream);
   if (!mfma_split_ok(layout->k_format, layout->v_format, int(hd)) || bs < 16)
     return prefill_as_decode(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start,
                              max_blocks_per_seq, num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride,

@@ -45,6 +45,9 @@
 #ifndef KVQ_TILE_SPARSE_V
 #define KVQ_TILE_SPARSE_V 1      // ... of the sparse V pass
 #endif
+#ifndef KVQ_PREFILL_TILES
+#define KVQ_PREFILL_TILES 1      // 1: chunked prefill with bf16 / fp8 K on the tile kernel (kvq_prefill.hip)
+#endif
 #ifndef KVQ_NT_LOADS
 #define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
 #endif
@@ -193,6 +196,10 @@ hipError_t launch_scores_nvfp4(int hd, int g, const DecodeArgs& a, uint32_t nwg,
 // rows (row s * max_query_len + i is query i of sequence s).
 hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
                                uint32_t max_query_len, int32_t* vrow, int32_t* vlen, hipStream_t st);
+// Chunked prefill on the tile kernel: (query, head) rows per workgroup for a
+// head_dim, and the launcher (K format bf16 or fp8; grid of nwg workgroups).
+int prefill_tile_rows(int hd);
+hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_prefill_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);

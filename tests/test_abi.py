@@ -167,24 +167,32 @@ def test_status_strings(lib):
 
 def test_prefill_host_checks(lib):
     # sizes are computed on the host; unsupported shapes are refused before anything is launched
+    # bf16 / fp8 K with block_size >= 4 runs on the tile kernel, which writes its
+    # rows directly: a nominal 256-byte workspace, whatever the sizes
     lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
-    n = kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100)
+    assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100) == 256
+    assert kvq.prefill_workspace_bytes(kvq.pool_layout("fp8", "bf16", 4, 8, 256), 400, 64, 4096, 9000) == 256
+    # turbo K runs on the split kernel's tiles: partials and statistics per split
+    lay_t = kvq.pool_layout("turbo4", "turbo3", 16, 8, 128)
+    n = kvq.prefill_workspace_bytes(lay_t, 4, 32, 64, 100)
     assert n > 0 and n % 256 == 0
-    assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100, sliding_window=128) <= n
-    # shapes outside the prefill tiles run as decode rows: their workspace
+    assert kvq.prefill_workspace_bytes(lay_t, 4, 32, 64, 100, sliding_window=128) <= n
+    # shapes outside both tile kernels run as decode rows: their workspace
     # holds the dense decode workspace of num_seqs * max_query_len rows
-    for shape in [("bf16", "bf16", 16, 8, 128),     # bf16 V rows of 256 bytes
-                  ("fp8", "turbo2", 8, 8, 128),     # block_size < 16
+    for shape in [("turbo4", "bf16", 16, 8, 128),   # bf16 V rows of 256 bytes
+                  ("turbo2", "turbo2", 8, 8, 128),  # turbo K, block_size < 16
+                  ("fp8", "turbo2", 2, 8, 128),     # block_size < 4
                   ("turbo3", "turbo3", 16, 8, 64)]:  # turbo3 K at head_dim 64
         lay_s = kvq.pool_layout(*shape)
         rows = kvq.prefill_workspace_bytes(lay_s, 4, 32, 64, 100)
         assert rows >= kvq.decode_workspace_bytes(lay_s, 400, 32, 64) and rows % 256 == 0
-    with pytest.raises(kvq.KvqError) as e:
-        kvq.prefill_workspace_bytes(kvq.pool_layout("fp8", "turbo2", 16, 8, 128), 4, 24, 64, 100)   # G = 3
-    assert e.value.status in (UNSUPPORTED, INVALID)
-    with pytest.raises(kvq.KvqError) as e:
-        kvq.prefill_workspace_bytes(lay, 4, 32, 64, 0)       # max_query_len 0
-    assert e.value.status == INVALID
+    for lay_g in (lay, lay_t):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.prefill_workspace_bytes(lay_g, 4, 24, 64, 100)   # G = 3
+        assert e.value.status in (UNSUPPORTED, INVALID)
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.prefill_workspace_bytes(lay_g, 4, 32, 64, 0)       # max_query_len 0
+        assert e.value.status == INVALID
 
 
 def _u32p(lib):
