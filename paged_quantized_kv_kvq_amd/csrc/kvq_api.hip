@@ -507,8 +507,8 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 
-// Chunked prefill on the tile kernel (K sides exact in bf16, block_size >=
-// 4): a workgroup per (sequence, kv head, tile of queries) walks the tile's
+// Chunked prefill on the tile kernel (block_size >= 4): a workgroup per
+// (sequence, kv head, tile of queries) walks the tile's
 // key range and writes finished rows; nothing goes through the workspace,
 // which the call still takes (256 bytes) so that a null workspace keeps
 // meaning "report the size".
@@ -518,7 +518,7 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
                   float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
                   void* workspace, size_t* workspace_bytes, void* stream) {
   const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim, G = num_q_heads / nkv;
-  const uint32_t qt = uint32_t(prefill_tile_rows(int(hd))) / G;
+  const uint32_t qt = uint32_t(prefill_tile_rows(layout->k_format, int(hd))) / G;
   const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
   const uint64_t nwg = (uint64_t(num_seqs) * nkv + 7) / 8 * 8 * ntiles;
   if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
@@ -579,7 +579,7 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
   if (q_stride < num_q_heads * hd) return KVQ_ERR_INVALID_ARG;
   if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
   if (uint64_t(max_blocks_per_seq) * bs >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
-  if (KVQ_PREFILL_TILES && (layout->k_format == KVQ_BF16 || layout->k_format == KVQ_FP8_E4M3) && bs >= 4)
+  if (KVQ_PREFILL_TILES && bs >= 4)
     return prefill_tiles(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start, max_blocks_per_seq,
                          num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride, sliding_window, k_scale,
                          v_scale, workspace, workspace_bytes, stream);

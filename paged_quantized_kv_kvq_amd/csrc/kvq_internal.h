@@ -197,8 +197,8 @@ hipError_t launch_scores_nvfp4(int hd, int g, const DecodeArgs& a, uint32_t nwg,
 hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
                                uint32_t max_query_len, int32_t* vrow, int32_t* vlen, hipStream_t st);
 // Chunked prefill on the tile kernel: (query, head) rows per workgroup for a
-// head_dim, and the launcher (K format bf16 or fp8; grid of nwg workgroups).
-int prefill_tile_rows(int hd);
+// K format and head_dim, and the launcher (grid of nwg workgroups).
+int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);

@@ -167,22 +167,16 @@ def test_status_strings(lib):
 
 def test_prefill_host_checks(lib):
     # sizes are computed on the host; unsupported shapes are refused before anything is launched
-    # bf16 / fp8 K with block_size >= 4 runs on the tile kernel, which writes its
-    # rows directly: a nominal 256-byte workspace, whatever the sizes
+    # block_size >= 4 runs on the tile kernel, which writes its rows
+    # directly: a nominal 256-byte workspace, whatever the sizes
     lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
-    assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100) == 256
-    assert kvq.prefill_workspace_bytes(kvq.pool_layout("fp8", "bf16", 4, 8, 256), 400, 64, 4096, 9000) == 256
-    # turbo K runs on the split kernel's tiles: partials and statistics per split
-    lay_t = kvq.pool_layout("turbo4", "turbo3", 16, 8, 128)
-    n = kvq.prefill_workspace_bytes(lay_t, 4, 32, 64, 100)
-    assert n > 0 and n % 256 == 0
-    assert kvq.prefill_workspace_bytes(lay_t, 4, 32, 64, 100, sliding_window=128) <= n
-    # shapes outside both tile kernels run as decode rows: their workspace
-    # holds the dense decode workspace of num_seqs * max_query_len rows
-    for shape in [("turbo4", "bf16", 16, 8, 128),   # bf16 V rows of 256 bytes
-                  ("turbo2", "turbo2", 8, 8, 128),  # turbo K, block_size < 16
-                  ("fp8", "turbo2", 2, 8, 128),     # block_size < 4
-                  ("turbo3", "turbo3", 16, 8, 64)]:  # turbo3 K at head_dim 64
+    lay_t = kvq.pool_layout("turbo4", "turbo3", 4, 8, 256)
+    for lay_s in (lay, lay_t, kvq.pool_layout("nvfp4", "bf16", 512, 8, 64)):
+        assert kvq.prefill_workspace_bytes(lay_s, 4, 32, 64, 100) == 256
+        assert kvq.prefill_workspace_bytes(lay_s, 400, 64, 4096, 9000, sliding_window=128) == 256
+    # block_size < 4 runs as decode rows: the workspace holds the dense decode
+    # workspace of num_seqs * max_query_len rows
+    for shape in [("turbo4", "bf16", 1, 8, 128), ("fp8", "turbo2", 2, 8, 128), ("turbo3", "turbo3", 2, 8, 64)]:
         lay_s = kvq.pool_layout(*shape)
         rows = kvq.prefill_workspace_bytes(lay_s, 4, 32, 64, 100)
         assert rows >= kvq.decode_workspace_bytes(lay_s, 400, 32, 64) and rows % 256 == 0

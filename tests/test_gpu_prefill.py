@@ -130,13 +130,11 @@ def test_prefill_long_chunk_sampled_rows(gpu_lib):
     say(f"  ok prefill long chunk: {len(rows)} sampled rows, max-abs {err:.2e} rel-L2 {rel:.2e}")
 
 
-# shapes neither tile kernel takes (turbo / NVFP4 K with V rows over 128 bytes,
-# K quarters of other sizes, or block_size < 16; any K with block_size < 4):
-# every query runs as a decode row
-@pytest.mark.parametrize("kf,vf,hd,bs", [("turbo4", "bf16", 128, 16), ("nvfp4", "fp8", 256, 16),
-                                         ("turbo8", "turbo8", 256, 16), ("turbo3", "turbo3", 64, 16),
-                                         ("bf16", "turbo4", 128, 1), ("fp8", "turbo2", 128, 2),
-                                         ("turbo4", "turbo3", 128, 8), ("turbo2", "turbo4", 128, 4)])
+# block_size < 4, which the tile kernel does not take: every query runs as a
+# decode row through the decode kernels
+@pytest.mark.parametrize("kf,vf,hd,bs", [("bf16", "turbo4", 128, 1), ("fp8", "turbo2", 128, 2),
+                                         ("turbo4", "bf16", 128, 1), ("turbo8", "turbo8", 256, 2),
+                                         ("turbo3", "turbo3", 64, 1), ("nvfp4", "fp8", 256, 2)])
 def test_prefill_as_decode_rows(gpu_lib, kf, vf, hd, bs):
     w = synth.small(9800 + hd + bs + len(kf) * 3 + len(vf), lens=[1, 17, 300, 700], num_q_heads=8, num_kv_heads=2,
                     head_dim=hd, block_size=bs, k_format=kf, v_format=vf)
@@ -144,40 +142,45 @@ def test_prefill_as_decode_rows(gpu_lib, kf, vf, hd, bs):
 
 
 def test_prefill_as_decode_rows_window_and_empty(gpu_lib):
-    w = synth.small(9850, lens=[300, 0, 64, 129, 17], num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=4,
+    w = synth.small(9850, lens=[300, 0, 64, 129, 17], num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=2,
                     k_format="turbo4", v_format="bf16")
     run_prefill(gpu_lib, w, [33, 0, 0, 129, 5], window=50, seed=5, label="rows, window 50, empty chunks", q_pad=2)
 
 
-# the bf16 tile kernel (bf16 / fp8 K, block_size >= 4): every V format, the
-# three head sizes, every group size, block sizes around its 64-key chunks,
-# windows around chunk edges
+# the tile kernel (block_size >= 4): every K and V format, the three head
+# sizes, every group size, block sizes around its key chunks, windows around
+# chunk edges
 TILE_V = ["bf16", "fp8", "turbo2", "turbo3", "turbo4", "turbo8", "nvfp4"]
 
 
-@pytest.mark.parametrize("kf", ["bf16", "fp8"])
+@pytest.mark.parametrize("kf", TILE_V)
 @pytest.mark.parametrize("vf", TILE_V)
 def test_prefill_tiles_formats(gpu_lib, kf, vf):
-    w = synth.small(9900 + TILE_V.index(vf) * 7 + len(kf), lens=[1, 17, 300, 1100, 2500], num_q_heads=16,
+    w = synth.small(9900 + TILE_V.index(vf) * 7 + TILE_V.index(kf), lens=[1, 17, 300, 1100, 2500], num_q_heads=16,
                     num_kv_heads=4, head_dim=128, block_size=16, k_format=kf, v_format=vf, outliers=True)
     run_prefill(gpu_lib, w, [1, 17, 37, 200, 600], seed=7, label=f"tiles {kf}/{vf}")
 
 
 @pytest.mark.parametrize("hd", [64, 128, 256])
 @pytest.mark.parametrize("g", [1, 2, 4, 8])
-def test_prefill_tiles_shapes(gpu_lib, hd, g):
-    kf = "bf16" if g in (1, 4) else "fp8"
+@pytest.mark.parametrize("rot", [False, True])
+def test_prefill_tiles_shapes(gpu_lib, hd, g, rot):
+    if rot:
+        kf = "turbo3" if g in (1, 4) else "turbo8"
+    else:
+        kf = "bf16" if g in (1, 4) else "fp8"
     vf = {64: "turbo3", 128: "nvfp4", 256: "turbo4"}[hd]
-    w = synth.small(9950 + hd + g, lens=[40, 700, 333], num_q_heads=2 * g, num_kv_heads=2, head_dim=hd,
+    w = synth.small(9950 + hd + g + 500 * rot, lens=[40, 700, 333], num_q_heads=2 * g, num_kv_heads=2, head_dim=hd,
                     block_size=16, k_format=kf, v_format=vf)
     run_prefill(gpu_lib, w, [40, 150, 9], seed=g + hd, label=f"tiles {kf}/{vf} hd{hd} G{g}")
 
 
 @pytest.mark.parametrize("bs", [4, 8, 128, 512])
-def test_prefill_tiles_block_sizes(gpu_lib, bs):
-    w = synth.small(9970 + bs, lens=[77, 600, 1000, 5], num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=bs,
-                    k_format="bf16", v_format="turbo4")
-    run_prefill(gpu_lib, w, [77, 33, 250, 5], seed=bs, label=f"tiles bs{bs}")
+@pytest.mark.parametrize("kf", ["bf16", "turbo4"])
+def test_prefill_tiles_block_sizes(gpu_lib, bs, kf):
+    w = synth.small(9970 + bs + len(kf), lens=[77, 600, 1000, 5], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    block_size=bs, k_format=kf, v_format="turbo4")
+    run_prefill(gpu_lib, w, [77, 33, 250, 5], seed=bs, label=f"tiles {kf} bs{bs}")
 
 
 @pytest.mark.parametrize("win", [1, 63, 64, 65, 700])
