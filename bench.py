@@ -428,14 +428,12 @@ def prefill_main(args, kvq, w):
     kb, vb = ROW_BYTES[w.k_format](hd), ROW_BYTES[w.v_format](hd)
     keys = 0
     tile_keys = 0
-    # bf16 / fp8 K with block_size >= 4 runs on the bf16 tile kernel (128
-    # (query, head) rows per tile, 64 at head_dim 256); other K formats on
-    # the split kernel's tiles of 16 or 8 rows
-    bf16_tiles = w.k_format in ("bf16", "fp8") and bs >= 4
-    if bf16_tiles:
-        rows = 128 if hd <= 128 else 64
-    else:
-        rows = 16 if hd <= 128 else 8
+    # block_size >= 4 runs on the tile kernel: 128 (query, head) rows per
+    # tile, 64 at head_dim 256 or with a rotated K side; smaller blocks run
+    # every query as a decode row
+    rot_k = w.k_format in ("turbo2", "turbo3", "turbo4", "turbo8")
+    tiles = bs >= 4
+    rows = (64 if rot_k or hd > 128 else 128) if tiles else Hq // Hkv
     qt = max(1, rows // (Hq // Hkv))
     for L, c in zip(st.lens.astype(np.int64), C):
         p = L - c + np.arange(c)
@@ -448,23 +446,26 @@ def prefill_main(args, kvq, w):
     min_bytes = int(sum(int(L) for L in st.lens)) * Hkv * (kb + vb)
     tile_bytes = tile_keys * Hkv * (kb + vb)
     tflops = flops / (att_ms * 1e-3) / 1e12
-    if bf16_tiles:
-        # Q.K and P.V both on bf16 matrix cores; P.V takes its weights (and a
-        # V side that is not a bf16 value) as bf16 hi + lo pairs: 3 products
-        # per algorithmic one (2 when V is exact in bf16)
+    if tiles:
+        # P.V on bf16 matrix cores with its weights (and a V side that is not
+        # a bf16 value) as bf16 hi + lo pairs: 3 products per algorithmic one
+        # (2 when V is exact in bf16); Q.K on bf16 ones, or on fp32 ones for a
+        # rotated K side.  Half the algorithmic flops each.
         pv_products = 2 if w.v_format in ("bf16", "fp8", "nvfp4") else 3
-        peak = MFMA_BF16_TFLOPS
-        peak_basis = (f"every flop at {MFMA_BF16_TFLOPS} (bf16); P.V issues {pv_products} bf16 products per "
-                      "algorithmic product (hi/lo pairs), counted once")
+        qk_peak = MFMA_F32_TFLOPS if rot_k else MFMA_BF16_TFLOPS
+        peak = 1.0 / (0.5 / qk_peak + 0.5 / MFMA_BF16_TFLOPS)
+        peak_basis = (f"half the flops (Q.K) at {qk_peak}, half (P.V) at {MFMA_BF16_TFLOPS}; P.V issues "
+                      f"{pv_products} bf16 products per algorithmic product (hi/lo pairs), counted once")
         issued = flops / 2 * (1 + pv_products)
+        # time the issued matrix instructions take at peak, over the kernel time
+        busy_s = (flops / 2 / qk_peak + flops / 2 * pv_products / MFMA_BF16_TFLOPS) / 1e12
         kernel = "kvq_paged_prefill: prefill_tile_kernel"
     else:
-        # Q.K on fp32 matrix cores over the rotated query (turbo / NVFP4 K),
-        # P.V on fp32 ones; half the flops each
         peak = MFMA_F32_TFLOPS
-        peak_basis = f"every flop at {MFMA_F32_TFLOPS} (fp32 matrix cores)"
+        peak_basis = f"every flop at {MFMA_F32_TFLOPS} (decode rows: fp32 matrix cores or VALU)"
         issued = flops
-        kernel = "kvq_paged_prefill: split_mfma_kernel (prefill tiles) + prefill_merge_kernel"
+        busy_s = flops / MFMA_F32_TFLOPS / 1e12
+        kernel = "kvq_paged_prefill: decode kernels over one row per query"
     rec = {
         "metric": "chunked-prefill query tokens/s over the quantized paged cache, 1 GPU",
         "value": round(T / (ms_step * 1e-3), 1),
@@ -481,7 +482,7 @@ def prefill_main(args, kvq, w):
                      "peak_basis": peak_basis,
                      "frac": round(tflops / peak, 4), "traffic": traffic_from_profile(w.name, "prefill"),
                      "kernel": kernel, "algorithmic_flops": flops, "issued_matrix_flops": int(issued),
-                     "issued_frac": round(issued / (att_ms * 1e-3) / 1e12 / peak, 4)},
+                     "issued_busy_frac": round(busy_s / (att_ms * 1e-3), 4)},
         "kv_bytes": {"once_per_sequence": min_bytes, "read_by_tiles": tile_bytes, "queries_per_tile": qt,
                      "gbs_once_per_sequence": round(min_bytes / (att_ms * 1e-3) / 1e9, 1),
                      "gbs_read_by_tiles": round(tile_bytes / (att_ms * 1e-3) / 1e9, 1)},

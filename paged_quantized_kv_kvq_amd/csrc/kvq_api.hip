@@ -447,14 +447,14 @@ int kvq_paged_decode_noalloc(const kvq_layout* layout, const void* q, const void
 namespace kvq {
 namespace {
 
-// Chunked prefill where the prefill tiles do not apply (block_size < 16, V
-// rows over 128 bytes, K quarters the tile kernel does not take): every query
-// runs as its own decode row -- its sequence's block table, the length of its
-// causal span (position + 1), its own query and output row -- through the
-// dense decode kernels.  Each query then reads its keys and values on its
-// own, so this path trades the tiles' reuse for coverage.  The workspace
-// holds the rows' map and lengths, then the dense decode workspace of
-// num_seqs * max_query_len rows.
+// Chunked prefill where the tile kernel does not apply (block_size < 4,
+// where a thread's four keys would span pages): every query runs as its own
+// decode row -- its sequence's block table, the length of its causal span
+// (position + 1), its own query and output row -- through the dense decode
+// kernels.  Each query then reads its keys and values on its own, so this
+// path trades the tiles' reuse for coverage.  The workspace holds the rows'
+// map and lengths, then the dense decode workspace of num_seqs *
+// max_query_len rows.
 int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
                       const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
                       uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
@@ -583,87 +583,9 @@ int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cac
     return prefill_tiles(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start, max_blocks_per_seq,
                          num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride, sliding_window, k_scale,
                          v_scale, workspace, workspace_bytes, stream);
-  if (!mfma_split_ok(layout->k_format, layout->v_format, int(hd)) || bs < 16)
-    return prefill_as_decode(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start,
-                             max_blocks_per_seq, num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride,
-                             sliding_window, k_scale, v_scale, workspace, workspace_bytes, stream);
-  // tiles of qt queries; the key range of a tile spans at most the longest
-  // sequence (or the window plus the tile)
-  const uint32_t qt = uint32_t(prefill_qt(layout->k_format, int(hd), int(G)));
-  const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
-  uint64_t span = uint64_t(max_blocks_per_seq) * bs;
-  if (sliding_window && sliding_window + qt - 1 < span) span = sliding_window + qt - 1;
-  // splits as long as the staged page offsets allow (fewer partials to
-  // write and merge), shorter only while the grid is small
-  uint32_t sl = 8192;
-  while (sl > 256 && uint64_t(num_seqs) * ntiles * ((span + sl - 1) / sl) * nkv < kTargetWorkgroups) sl >>= 1;
-  while (sl > 16 && sl / bs + 2 > KVQ_PREFILL_MAX_PAGES) sl >>= 1;
-  const uint64_t nsplit = (span + sl - 1) / sl;
-  const uint64_t units = uint64_t(num_seqs) * ntiles * nkv * nsplit;
-  const uint64_t rows = uint64_t(G) * qt;
-  const uint64_t off_ml = 0, off_part = up256(units * rows * 2 * sizeof(float));
-  const uint64_t bytes = up256(off_part + units * rows * hd * sizeof(float));
-  if (uint64_t(num_seqs) * ntiles * nsplit * nkv >= (1ull << 31) ||
-      uint64_t(num_seqs) * ntiles * num_q_heads >= (1ull << 31))
-    return KVQ_ERR_UNSUPPORTED;
-  if (!workspace) {
-    *workspace_bytes = size_t(bytes);
-    return KVQ_OK;
-  }
-  if (*workspace_bytes < bytes) return KVQ_ERR_WORKSPACE;
-  if (num_seqs == 0) return KVQ_OK;
-  if (!q || !k_cache || !v_cache || !out || !block_tables || !seq_lens || !query_start) return KVQ_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(block_tables, 4) || !aligned(seq_lens, 4) || !aligned(query_start, 4) || !aligned(workspace, 16))
-    return KVQ_ERR_ALIGNMENT;
-
-  DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.q = static_cast<const uint16_t*>(q);
-  a.k_cache = static_cast<const uint8_t*>(k_cache);
-  a.v_cache = static_cast<const uint8_t*>(v_cache);
-  a.out = out;
-  a.block_tables = block_tables;
-  a.seq_lens = seq_lens;
-  a.query_start = query_start;
-  a.ml = reinterpret_cast<float*>(ws + off_ml);
-  a.part = reinterpret_cast<float*>(ws + off_part);
-  a.max_blocks = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = nkv;
-  a.log2_bs = log2u(bs);
-  a.q_stride = q_stride;
-  a.window = sliding_window;
-  a.split_len = sl;
-  a.nsplit = uint32_t(nsplit);
-  a.ntiles = uint32_t(ntiles);
-  a.qt = qt;
-  a.k_stride = layout->k_block_stride_bytes;
-  a.k_data = layout->k_data_section_bytes;
-  a.v_stride = layout->v_block_stride_bytes;
-  a.v_data = layout->v_data_section_bytes;
-  const float log2e = 1.4426950408889634f;
-  a.qk_scale = inv_sqrt_d * log2e * (layout->k_format == KVQ_FP8_E4M3 ? k_scale : 1.0f);
-  a.v_scale = layout->v_format == KVQ_FP8_E4M3 ? v_scale : 1.0f;
-  a.wht_scale = float(1.0 / std::sqrt(double(hd)));
-  a.cb = codebooks();
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int vf = layout->v_format;
-  hipError_t e;
-  switch (layout->k_format) {
-    case KVQ_BF16: e = launch_split_bf16(vf, int(hd), int(G), a, 0, s, true); break;
-    case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, 0, s, true); break;
-    case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, 0, s, true); break;
-    case KVQ_TURBO3: e = launch_split_turbo3(vf, int(hd), int(G), a, 0, s, true); break;
-    case KVQ_TURBO8: e = launch_split_turbo8(vf, int(hd), int(G), a, 0, s, true); break;
-    case KVQ_NVFP4: e = launch_split_nvfp4(vf, int(hd), int(G), a, 0, s, true); break;
-    default: e = launch_split_turbo4(vf, int(hd), int(G), a, 0, s, true); break;
-  }
-  if (e == hipSuccess) e = launch_prefill_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+  return prefill_as_decode(layout, q, k_cache, v_cache, out, block_tables, seq_lens, query_start,
+                           max_blocks_per_seq, num_seqs, num_q_heads, max_query_len, inv_sqrt_d, q_stride,
+                           sliding_window, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 int kvq_check_slots(const kvq_layout* layout, const int64_t* slot_mapping, uint32_t num_tokens, uint64_t num_blocks,

@@ -691,7 +691,6 @@ __device__ __forceinline__ void lds_wht(float* x, float scale) {
 // batch (one wait); a longer row walks its splits B at a time in three
 // loops, each batch's loads issued before any is used.  The additions keep
 // the split order, so the result does not depend on B or on the path.
-// Decode rows take B = 16, prefill rows (one or two splits) B = 2.
 template <int HD, int B>
 __device__ __forceinline__ void merge_row(const float* ml, uint32_t mls, const float* part, uint32_t ps, int ns,
                                           float scale, float* o) {
@@ -782,32 +781,6 @@ __global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs 
   if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
   float* dst = a.out + (uint64_t(row_query(a, s)) * a.num_q_heads + hq) * HD;
   for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
-}
-
-// Chunked prefill: one workgroup per (sequence, tile, q head) combines each
-// of the tile's queries' split partials as merge_kernel does, and writes the
-// query's output row.
-template <int HD, bool VROT>
-__global__ __launch_bounds__(kWaves * kWave) void prefill_merge_kernel(const DecodeArgs a, int G) {
-  __shared__ float o[HD];
-  const uint32_t hq = blockIdx.x % a.num_q_heads;
-  const uint32_t unit = blockIdx.x / a.num_q_heads;
-  const uint32_t s = unit % a.num_seqs, tile = unit / a.num_seqs;
-  const uint32_t g = hq / G, h = hq % G;
-  const PrefillTile pt = prefill_tile(a, s, tile);
-  const int R = G * int(a.qt);
-  const int ns = pt.hi > pt.lo ? (pt.hi - pt.lo + int(a.split_len) - 1) / int(a.split_len) : 0;
-  const uint64_t base = ((uint64_t(s) * a.ntiles + tile) * a.num_kv_heads + g) * a.nsplit;
-  const int tid = threadIdx.x;
-  for (int t = 0; t < pt.nq; ++t) {
-    const uint64_t row = base * R + uint64_t(t * G + int(h));  // split 0's row of this query and head
-    merge_row<HD, 2>(a.ml + row * 2, uint32_t(R) * 2, a.part + row * HD, uint32_t(R) * HD, ns, a.v_scale, o);
-    __syncthreads();
-    if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
-    float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + hq) * HD;
-    for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
-    __syncthreads();
-  }
 }
 
 // ------------------------------------------------------------------ sparse V
@@ -1401,66 +1374,53 @@ namespace kvq {
 // ------------------------------------------------------------------ dispatch
 
 // Dense split kernel of a (K, V, head_dim, G) instance: the matrix-core one
-// where its operand sizes allow it (bf16 / fp8 K), else the VALU one.  PF:
-// the chunked-prefill form of the matrix-core kernel (tiles of prefill_qt
-// queries; the host only asks for it where that kernel applies).
-template <int KF, int VF, int HD, int G, bool PF>
+// where its operand sizes allow it and a 16-position chunk lies in one page,
+// else the VALU one.
+template <int KF, int VF, int HD, int G>
 hipError_t launch_split_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  if constexpr (PF) {
-    constexpr int QT = prefill_qt(KF, HD, G);
-    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G * QT>::ok) {
-      const uint32_t nw = mfma_unit_waves(a.num_kv_heads, mfma_waves_cap<KF, G, QT>());
-      const uint64_t n = mfma_grid(uint64_t(a.num_seqs) * a.ntiles * a.nsplit, a.num_kv_heads / nw);
-      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G, QT>), dim3(uint32_t(n)), dim3(nw * kWave), 0,
-                         st, a);
+  if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
+    if (a.log2_bs >= 4) {
+      const uint32_t nw = mfma_unit_waves(a.num_kv_heads, mfma_waves_cap<KF, G>());
+      const uint64_t n = mfma_grid(uint64_t(a.num_seqs) * a.nsplit, a.num_kv_heads / nw);
+      hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
       return hipGetLastError();
     }
-    return hipErrorInvalidValue;
-  } else {
-    if constexpr (KVQ_DENSE_MFMA && MfmaGeo<KF, VF, HD, G>::ok) {
-      if (a.log2_bs >= 4) {  // a 16-position chunk lies in one page
-        const uint32_t nw = mfma_unit_waves(a.num_kv_heads, mfma_waves_cap<KF, G, 0>());
-        const uint64_t n = mfma_grid(uint64_t(a.num_seqs) * a.nsplit, a.num_kv_heads / nw);
-        hipLaunchKernelGGL((split_mfma_kernel<KF, VF, HD, G>), dim3(uint32_t(n)), dim3(nw * kWave), 0, st, a);
-        return hipGetLastError();
-      }
-    }
-    hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), dim3(nwg), dim3(kWaves * kWave), 0, st, a);
-    return hipGetLastError();
   }
+  hipLaunchKernelGGL((split_kernel<KF, VF, HD, G>), dim3(nwg), dim3(kWaves * kWave), 0, st, a);
+  return hipGetLastError();
 }
 
-template <int KF, int VF, int HD, bool PF>
+template <int KF, int VF, int HD>
 hipError_t launch_split_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (g) {
-    case 1: return launch_split_one<KF, VF, HD, 1, PF>(a, nwg, st);
-    case 2: return launch_split_one<KF, VF, HD, 2, PF>(a, nwg, st);
-    case 4: return launch_split_one<KF, VF, HD, 4, PF>(a, nwg, st);
-    case 8: return launch_split_one<KF, VF, HD, 8, PF>(a, nwg, st);
+    case 1: return launch_split_one<KF, VF, HD, 1>(a, nwg, st);
+    case 2: return launch_split_one<KF, VF, HD, 2>(a, nwg, st);
+    case 4: return launch_split_one<KF, VF, HD, 4>(a, nwg, st);
+    case 8: return launch_split_one<KF, VF, HD, 8>(a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int KF, int VF, bool PF>
+template <int KF, int VF>
 hipError_t launch_split_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (hd) {
-    case 64: return launch_split_g<KF, VF, 64, PF>(g, a, nwg, st);
-    case 128: return launch_split_g<KF, VF, 128, PF>(g, a, nwg, st);
-    case 256: return launch_split_g<KF, VF, 256, PF>(g, a, nwg, st);
+    case 64: return launch_split_g<KF, VF, 64>(g, a, nwg, st);
+    case 128: return launch_split_g<KF, VF, 128>(g, a, nwg, st);
+    case 256: return launch_split_g<KF, VF, 256>(g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int KF, bool PF = false>
+template <int KF>
 hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
   switch (vf) {
-    case KVQ_BF16: return launch_split_hd<KF, KVQ_BF16, PF>(hd, g, a, nwg, st);
-    case KVQ_FP8_E4M3: return launch_split_hd<KF, KVQ_FP8_E4M3, PF>(hd, g, a, nwg, st);
-    case KVQ_TURBO2: return launch_split_hd<KF, KVQ_TURBO2, PF>(hd, g, a, nwg, st);
-    case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3, PF>(hd, g, a, nwg, st);
-    case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4, PF>(hd, g, a, nwg, st);
-    case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8, PF>(hd, g, a, nwg, st);
-    case KVQ_NVFP4: return launch_split_hd<KF, KVQ_NVFP4, PF>(hd, g, a, nwg, st);
+    case KVQ_BF16: return launch_split_hd<KF, KVQ_BF16>(hd, g, a, nwg, st);
+    case KVQ_FP8_E4M3: return launch_split_hd<KF, KVQ_FP8_E4M3>(hd, g, a, nwg, st);
+    case KVQ_TURBO2: return launch_split_hd<KF, KVQ_TURBO2>(hd, g, a, nwg, st);
+    case KVQ_TURBO3: return launch_split_hd<KF, KVQ_TURBO3>(hd, g, a, nwg, st);
+    case KVQ_TURBO4: return launch_split_hd<KF, KVQ_TURBO4>(hd, g, a, nwg, st);
+    case KVQ_TURBO8: return launch_split_hd<KF, KVQ_TURBO8>(hd, g, a, nwg, st);
+    case KVQ_NVFP4: return launch_split_hd<KF, KVQ_NVFP4>(hd, g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,13 +1,11 @@
-// Decode and chunked-prefill kernels with a turbo2 K side: the dense split kernel for every V format,
+// Decode kernels with a turbo2 K side: the dense split kernel for every V format,
 // head_dim and group size, and the score kernel of the sparse-V path.
 #include "kvq_decode.h"
 
 namespace kvq {
 
-hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill) {
-  return prefill ? launch_split_k<KVQ_TURBO2, true>(vf, hd, g, a, nwg, st)
-                 : launch_split_k<KVQ_TURBO2, false>(vf, hd, g, a, nwg, st);
+hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
+  return launch_split_k<KVQ_TURBO2>(vf, hd, g, a, nwg, st);
 }
 
 hipError_t launch_scores_turbo2(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {

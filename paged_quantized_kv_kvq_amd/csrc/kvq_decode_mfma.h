@@ -59,10 +59,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
-// page offsets of one split staged in LDS by the prefill form: a prefill
-// split is long (a tile's whole key range, up to 8192 positions at block
-// size 16), so that its partials stay few; the grid is large without splits
-constexpr int kPrefillMaxPages = KVQ_PREFILL_MAX_PAGES;
 
 // Waves (kv heads) per workgroup of one instance.  Decode with a grouped-scale
 // K side and G <= 4 is bound by its arithmetic and latency chain at 144
@@ -70,9 +66,9 @@ constexpr int kPrefillMaxPages = KVQ_PREFILL_MAX_PAGES;
 // share a CU where one of eight fits (turbo8 / turbo8 and turbo4 / turbo8,
 // G = 4: 0.51 -> 0.46 ms and 0.57 -> 0.54 ms).  Everything else keeps whole
 // pages to one workgroup.
-template <int KF, int G, int QT>
+template <int KF, int G>
 constexpr int mfma_waves_cap() {
-  return (QT == 0 && Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves;
+  return (Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves;
 }
 
 template <int KF, int VF, int HD, int G>
@@ -180,17 +176,14 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
   if constexpr (N % 8 == 4) w[o / 4] = load4(p + o);
 }
 
-// QT = 0: decode, one query per sequence, rows = the G query heads.
-// QT > 0: chunked prefill.  A unit is (sequence, tile of QT queries, split of
-// the tile's key range); its rows are the QT x G (query, head) pairs, row
-// r = t G + h, and each row masks the positions after its own query (and,
-// with a window, those W or more before it).
-template <int KF, int VF, int HD, int G, int QT = 0>
+// One query per sequence; the rows of a wave are the G query heads of its
+// kv head.
+template <int KF, int VF, int HD, int G>
 __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const DecodeArgs a) {
-  constexpr int R = G * (QT > 0 ? QT : 1);  // rows: (query, head) pairs
+  constexpr int R = G;  // rows: the query heads
   using MG = MfmaGeo<KF, VF, HD, R>;
   constexpr int NG = MG::NG, DV = MG::DV;
-  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G, QT>(), (QT > 0 ? kPrefillMaxPages : kMaxPages)> sm;
+  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G>(), kMaxPages> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);
@@ -208,34 +201,11 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   }
   const uint32_t g = hb * uint32_t(nw) + uint32_t(w);
   const uint32_t nkv = a.num_kv_heads;
-  uint32_t s, split, tile = 0;
-  SeqSpan sp;
-  PrefillTile pt0;  // prefill: the tile's queries and key range
-  if constexpr (QT == 0) {
-    if (unit >= a.num_seqs * a.nsplit) return;
-    s = unit % a.num_seqs;
-    split = unit / a.num_seqs;
-    sp = split_span(a, s, split);
-    if (sp.pb >= sp.L) return;  // uniform over the workgroup
-  } else {
-    if (unit >= a.num_seqs * a.ntiles * a.nsplit) return;
-    s = unit % a.num_seqs;
-    tile = (unit / a.num_seqs) % a.ntiles;
-    split = unit / (a.num_seqs * a.ntiles);
-    pt0 = prefill_tile(a, s, tile);
-    sp.L = pt0.hi;
-    sp.j0 = pt0.lo;
-    sp.pb = pt0.lo + int(split * a.split_len);
-    sp.pe = min(pt0.hi, sp.pb + int(a.split_len));
-    if (sp.pb >= sp.pe) return;  // uniform over the workgroup
-  }
-  const uint16_t* qg = a.q + uint64_t(row_query(a, s)) * a.q_stride + uint64_t(g) * G * HD;  // decode: the group's rows
-  // prefill: query row of a tile row (nullptr: no query)
-  auto qrow = [&](int r) -> const uint16_t* {
-    const int t = r / G;
-    return (r < R && t < pt0.nq) ? a.q + uint64_t(pt0.qrow0 + t) * a.q_stride + (uint64_t(g) * G + r % G) * HD
-                                 : nullptr;
-  };
+  if (unit >= a.num_seqs * a.nsplit) return;
+  const uint32_t s = unit % a.num_seqs, split = unit / a.num_seqs;
+  const SeqSpan sp = split_span(a, s, split);
+  if (sp.pb >= sp.L) return;  // uniform over the workgroup
+  const uint16_t* qg = a.q + uint64_t(row_query(a, s)) * a.q_stride + uint64_t(g) * G * HD;  // the group's rows
 
   // bf16 / fp8 K, query operand A: head 4 hg + lane % 4, dims (lane / 16) * KQ + 4 k .. + 4
   i16x4 qa[MG::KT ? 1 : NG][MG::KT ? 1 : MG::KSTEPS];
@@ -243,12 +213,11 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
       const int h = 4 * hg + (lane & 3);
-      const uint16_t* qr = QT == 0 ? (h < G ? qg + h * HD : nullptr) : qrow(h);
 #pragma unroll
       for (int k = 0; k < MG::KSTEPS; ++k) {
         const int d = (lane >> 4) * MG::KQ + 4 * k;
-        if (QT == 0 ? h < G : qr != nullptr) {
-          const u32x2 x = *reinterpret_cast<const u32x2*>(qr + d);
+        if (h < G) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(qg + h * HD + d);
           qa[hg][k] = __builtin_bit_cast(i16x4, x);
         } else {
           qa[hg][k] = i16x4{0, 0, 0, 0};
@@ -260,7 +229,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const int first = sp.pb >> a.log2_bs;
   {
     const int n = ((sp.pe - 1) >> a.log2_bs) - first + 1;
-    const int32_t* bt = a.block_tables + uint64_t(QT == 0 ? row_table(a, s) : s) * a.max_blocks + first;
+    const int32_t* bt = a.block_tables + uint64_t(row_table(a, s)) * a.max_blocks + first;
     for (int i = tid; i < n; i += int(blockDim.x)) {
       const uint64_t page = uint64_t(uint32_t(bt[i]));
       sm.kbase[i] = page * a.k_stride;
@@ -289,14 +258,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   float qf[MG::KT ? NG : 1][MG::KT ? MG::KQ : 1];
   if constexpr (MG::KT) {
     auto& qr = sm.u.qrot[w];
-    if constexpr (QT == 0) {
-      for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
-    } else {
-      for (int i = lane; i < R * HD; i += kWave) {
-        const uint16_t* src = qrow(i / HD);
-        qr[i / HD][i % HD] = src ? bf16_bits_to_float(src[i % HD]) : 0.0f;
-      }
-    }
+    for (int i = lane; i < G * HD; i += kWave) qr[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
     wave_lds_sync();
     if constexpr (Fmt<KF>::rot) {  // NVFP4 K: the query as it is
       for (int h2 = 1; h2 < HD; h2 <<= 1) {
@@ -377,7 +339,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   constexpr float kNoMax = -3.0e38f;
   float m[NG], lsum[NG];
   // two chains (even and odd positions), or one where four or more row
-  // groups already give independent chains (prefill tiles of 16 rows)
+  // groups already give independent chains
   constexpr int NCH = NG >= 4 ? 1 : 2;
   f32x4 acc[NG][NCH][DV];
 #pragma unroll
@@ -496,24 +458,13 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
     bool grew = false;
 #pragma unroll
     for (int hg = 0; hg < NG; ++hg) {
-      bool ok = in_split;
-      if constexpr (QT > 0) {  // the row's own causal (and window) limits
-        const int r = 4 * hg + (lane >> 4), t = r / G, p = pt0.p0 + t;
-        ok = ok && r < R && t < pt0.nq && j <= p && (a.window == 0u || j > p - int(a.window));
-      }
+      const bool ok = in_split;
       const f32x4 d = qk(ck, hg);
       // 3. the row's head: full score (masked positions: -inf, whatever
       //    bytes they hold), then its online softmax over the chunk.  The
-      //    lane swaps exchange values between the rows of one position; in
-      //    decode those rows share the mask, in prefill they do not, so there
-      //    the swaps run on every lane (a swap must not read an inactive lane).
-      float sc;
-      if constexpr (QT == 0) {
-        sc = ok ? quarter_sum(d) * qscale : -INFINITY;
-      } else {
-        const float full = quarter_sum(d) * qscale;
-        sc = ok ? full : -INFINITY;
-      }
+      //    lane swaps exchange values between the rows of one position, which
+      //    share the mask: a swap never reads an inactive lane.
+      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
       const float mn = fmaxf(m[hg], group_max<16>(sc));
       const float al = fast_exp2(m[hg] - mn);
       grew |= mn > m[hg];
@@ -684,7 +635,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 
   // the wave's partials for its kv head: sums over the row's 16 lanes, one
   // output dim pair per lane and head
-  const uint64_t base = ((QT == 0 ? uint64_t(s) : uint64_t(s) * a.ntiles + tile) * nkv + g) * a.nsplit + split;
+  const uint64_t base = (uint64_t(s) * nkv + g) * a.nsplit + split;
 #pragma unroll
   for (int hg = 0; hg < NG; ++hg) {
     const float z = group_sum<16>(lsum[hg]);

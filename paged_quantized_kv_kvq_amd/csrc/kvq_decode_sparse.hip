@@ -1,7 +1,7 @@
 // Decode kernels that depend only on the V side: the sparse-V pass (which also
 // writes the output) and the dense path's merge (log-sum-exp over splits,
-// with the inverse rotation of a rotated V side), for decode and for chunked
-// prefill.
+// with the inverse rotation of a rotated V side); and the row map of chunked
+// prefill run as decode rows.
 #include "kvq_decode.h"
 
 namespace kvq {
@@ -35,14 +35,6 @@ hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.num_seqs * a.num_q_heads), block(kWaves * kWave);
   if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true>), grid, block, 0, st, a, g);
   else hipLaunchKernelGGL((merge_kernel<HD, false>), grid, block, 0, st, a, g);
-  return hipGetLastError();
-}
-
-template <int HD>
-hipError_t prefill_merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_seqs * a.ntiles * a.num_q_heads), block(kWaves * kWave);
-  if (vrot) hipLaunchKernelGGL((prefill_merge_kernel<HD, true>), grid, block, 0, st, a, g);
-  else hipLaunchKernelGGL((prefill_merge_kernel<HD, false>), grid, block, 0, st, a, g);
   return hipGetLastError();
 }
 
@@ -90,15 +82,6 @@ hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipS
     case 64: return merge_hd<64>(v_rotated, g, a, st);
     case 128: return merge_hd<128>(v_rotated, g, a, st);
     case 256: return merge_hd<256>(v_rotated, g, a, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_prefill_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
-  switch (hd) {
-    case 64: return prefill_merge_hd<64>(v_rotated, g, a, st);
-    case 128: return prefill_merge_hd<128>(v_rotated, g, a, st);
-    case 256: return prefill_merge_hd<256>(v_rotated, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,9 +12,6 @@
 #ifndef KVQ_WAVES
 #define KVQ_WAVES 4              // waves per decode workgroup
 #endif
-#ifndef KVQ_PREFILL_MAX_PAGES
-#define KVQ_PREFILL_MAX_PAGES 520   // page offsets of one prefill split staged in LDS (8192 positions at bs 16)
-#endif
 #ifndef KVQ_TARGET_WORKGROUPS
 #define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many
 #endif
@@ -46,7 +43,7 @@
 #define KVQ_TILE_SPARSE_V 1      // ... of the sparse V pass
 #endif
 #ifndef KVQ_PREFILL_TILES
-#define KVQ_PREFILL_TILES 1      // 1: chunked prefill with bf16 / fp8 K on the tile kernel (kvq_prefill.hip)
+#define KVQ_PREFILL_TILES 1      // 1: chunked prefill on the tile kernel (kvq_prefill.h) where block_size >= 4
 #endif
 #ifndef KVQ_NT_LOADS
 #define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
@@ -57,17 +54,6 @@ namespace kvq {
 // Whether the dense split pass runs on the matrix cores for these formats and
 // head_dim (bf16 / fp8 K: bf16 MFMA for Q.K^T; turbo K: fp32 MFMA over the
 // rotated query; V rows of at most 128 bytes); it also needs block_size >= 16.
-// Chunked prefill: queries per tile of the matrix-core split kernel.  A tile
-// holds 16 (query, head) rows for bf16 / fp8 K up to head_dim 128 (their
-// query operands are packed bf16), else 8 (fp32 rotated-query operands, or
-// head_dim 256): fewer tiles re-read the key range, as far as the registers go.
-__host__ __device__ constexpr int prefill_rows(int kf, int hd) {
-  return (kf == KVQ_BF16 || kf == KVQ_FP8_E4M3) && hd <= 128 ? 16 : 8;
-}
-__host__ __device__ constexpr int prefill_qt(int kf, int hd, int g) {
-  return prefill_rows(kf, hd) > g ? prefill_rows(kf, hd) / g : 1;
-}
-
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf == KVQ_NVFP4 ? 4 : kf;
   const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf == KVQ_NVFP4 ? 4 : vf;
@@ -155,8 +141,8 @@ struct DecodeArgs {
   float v_scale;    // fp8 V side's scale, else 1
   float thr;        // sparse-V threshold (0: dense)
   float wht_scale;  // RN32(1/sqrt(head_dim))
-  // chunked prefill run as decode rows (the shapes the prefill tiles do not
-  // cover): row s of the call is query row vrow[2 s + 1] of sequence
+  // chunked prefill run as decode rows (block sizes the prefill tiles do
+  // not take): row s of the call is query row vrow[2 s + 1] of sequence
   // vrow[2 s] (-1: no query), its length that query's position + 1; null in
   // a plain decode call (row s is sequence s)
   const int32_t* vrow;
@@ -170,20 +156,13 @@ struct DecodeArgs {
 // translation unit per K format (split / score kernels) and per V format.
 hipError_t launch_write(int head_dim, const WriteArgs& a, hipStream_t st);
 
-hipError_t launch_split_bf16(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_fp8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
-hipError_t launch_split_nvfp4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st,
-                                bool prefill = false);
+hipError_t launch_split_bf16(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_fp8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_turbo2(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_turbo3(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_turbo4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_turbo8(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+hipError_t launch_split_nvfp4(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 
 hipError_t launch_scores_bf16(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_scores_fp8(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
@@ -202,6 +181,5 @@ int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
-hipError_t launch_prefill_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq
