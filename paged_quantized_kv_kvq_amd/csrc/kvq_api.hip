@@ -18,6 +18,11 @@ constexpr uint32_t kMaxSplitLen = 4096;
 constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a split live in LDS
 constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
+// chunked prefill on the tile kernel: a grid of fewer workgroups than this
+// splits the tiles' key ranges (two per CU fill the GPU), into splits of at
+// least kTileSplitChunks chunks
+constexpr uint64_t kTilePrefillWorkgroups = 512;
+constexpr uint64_t kTileSplitChunks = 16;
 
 bool valid_format(int32_t f) { return (f >= KVQ_BF16 && f <= KVQ_NVFP4) || f == KVQ_TURBO8; }
 bool is_rotated(int32_t f) { return f >= KVQ_TURBO2 && f != KVQ_NVFP4; }  // is_wht_rotated
@@ -508,21 +513,43 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
 }
 
 // Chunked prefill on the tile kernel (block_size >= 4): a workgroup per
-// (sequence, kv head, tile of queries) walks the tile's
-// key range and writes finished rows; nothing goes through the workspace,
-// which the call still takes (256 bytes) so that a null workspace keeps
-// meaning "report the size".
+// (sequence, kv head, tile of queries) walks the tile's key range and writes
+// finished rows.  A grid too small to fill the GPU (few sequences and tiles,
+// long key ranges) splits the range instead: each split writes its rows'
+// partials and a merge kernel combines them.  Without splits nothing goes
+// through the workspace, which the call still takes (256 bytes) so that a
+// null workspace keeps meaning "report the size".
 int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
                   const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
                   uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,
                   float inv_sqrt_d, uint32_t q_stride, uint32_t sliding_window, float k_scale, float v_scale,
                   void* workspace, size_t* workspace_bytes, void* stream) {
   const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim, G = num_q_heads / nkv;
-  const uint32_t qt = uint32_t(prefill_tile_rows(layout->k_format, int(hd))) / G;
+  const uint32_t rows = uint32_t(prefill_tile_rows(layout->k_format, int(hd)));
+  const uint32_t qt = rows / G, nk = 8192 / hd;  // queries per tile, keys per chunk
   const uint64_t ntiles = (uint64_t(max_query_len) + qt - 1) / qt;
-  const uint64_t nwg = (uint64_t(num_seqs) * nkv + 7) / 8 * 8 * ntiles;
-  if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
-  const uint64_t bytes = 256;
+  // chunks a tile's key range can span: the table's reach (or the window
+  // plus the tile), aligned to chunks
+  uint64_t span = uint64_t(max_blocks_per_seq) * layout->block_size;
+  if (sliding_window && sliding_window + qt - 1 < span) span = sliding_window + qt - 1;
+  const uint64_t nch = (span + nk - 1) / nk + 1;
+  const uint64_t base = uint64_t(num_seqs) * nkv * ntiles;
+  uint64_t nsplit = 1, split_len = 0;
+  if (base < kTilePrefillWorkgroups) {
+    nsplit = std::min<uint64_t>((kTilePrefillWorkgroups + base - 1) / base, nch / kTileSplitChunks);
+    if (nsplit > 1) {
+      const uint64_t cps = (nch + nsplit - 1) / nsplit;
+      split_len = cps * nk;
+      nsplit = (nch + cps - 1) / cps;
+    } else {
+      nsplit = 1;
+    }
+  }
+  const uint64_t nwg = (base * nsplit / ntiles + 7) / 8 * 8 * ntiles;
+  const uint64_t prow = base * nsplit * rows;  // partial rows
+  const uint64_t off_ml = 0, off_part = up256(prow * 2 * sizeof(float));
+  const uint64_t bytes = nsplit > 1 ? up256(off_part + prow * hd * sizeof(float)) : 256;
+  if (nwg >= (1ull << 31) || base * nsplit * rows / 4 >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   if (!workspace) {
     *workspace_bytes = size_t(bytes);
     return KVQ_OK;
@@ -535,6 +562,7 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
     return KVQ_ERR_ALIGNMENT;
   DecodeArgs a;
   std::memset(&a, 0, sizeof(a));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   a.q = static_cast<const uint16_t*>(q);
   a.k_cache = static_cast<const uint8_t*>(k_cache);
   a.v_cache = static_cast<const uint8_t*>(v_cache);
@@ -542,6 +570,8 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.query_start = query_start;
+  a.ml = reinterpret_cast<float*>(ws + off_ml);
+  a.part = reinterpret_cast<float*>(ws + off_part);
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -549,9 +579,12 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
   a.window = sliding_window;
   a.ntiles = uint32_t(ntiles);
   a.qt = qt;
+  a.nsplit = uint32_t(nsplit);
+  a.split_len = uint32_t(split_len);
   fill_common(a, layout, inv_sqrt_d, k_scale, v_scale);
-  const hipError_t e = launch_prefill_tiles(layout->k_format, layout->v_format, int(hd), int(G), a, uint32_t(nwg),
-                                            static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_prefill_tiles(layout->k_format, layout->v_format, int(hd), int(G), a, uint32_t(nwg), st);
+  if (e == hipSuccess && nsplit > 1) e = launch_prefill_tile_merge(layout->v_rotated != 0, int(hd), int(G), a, st);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 

@@ -179,6 +179,8 @@ hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_le
 // K format and head_dim, and the launcher (grid of nwg workgroups).
 int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+// ... and the merge of its key splits (a.nsplit > 1)
+hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 

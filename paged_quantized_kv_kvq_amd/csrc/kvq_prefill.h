@@ -228,24 +228,32 @@ __device__ __forceinline__ f32x4v mfma_bf16(u32x4 a, u32x4 b, f32x4v c) {
                                                   0, 0);
 }
 
-// Workgroup -> (sequence, kv head, tile).  The tiles of one (sequence, kv
-// head) read the same keys at about the same time: they go to one XCD
-// (workgroup i runs on XCD i % 8), and groups of 8 such units rotate over
-// the XCDs.
+// Workgroup -> (sequence, kv head, split of the key range, tile).  The
+// tiles of one (sequence, kv head, split) read the same keys at about the
+// same time: they go to one XCD (workgroup i runs on XCD i % 8), and groups
+// of 8 such units rotate over the XCDs.
 struct TileId {
-  uint32_t s, g, tile;
+  uint32_t s, g, split, tile;
   bool valid;
 };
 __device__ __forceinline__ TileId tile_id(const DecodeArgs& a) {
   const uint32_t i = blockIdx.x, x = i & 7u, rest = i >> 3;
-  const uint32_t tile = rest % a.ntiles;
   const uint32_t unit = (rest / a.ntiles) * 8u + x;
+  const uint32_t sg = unit / a.nsplit;
   TileId t;
-  t.tile = tile;
-  t.s = unit / a.num_kv_heads;
-  t.g = unit % a.num_kv_heads;
-  t.valid = unit < a.num_seqs * a.num_kv_heads;
+  t.tile = rest % a.ntiles;
+  t.split = unit % a.nsplit;
+  t.s = sg / a.num_kv_heads;
+  t.g = sg % a.num_kv_heads;
+  t.valid = sg < a.num_seqs * a.num_kv_heads;
   return t;
+}
+
+// Chunks of NK keys of a tile's range [lo, hi), aligned to NK; with splits
+// (small grids), split k takes chunks [k cps, (k + 1) cps) of them.
+template <int NK>
+__device__ __forceinline__ int tile_chunks(const PrefillTile& pt) {
+  return (pt.hi - (pt.lo / NK) * NK + NK - 1) / NK;
 }
 
 template <int KF, int VF, int HD>
@@ -342,11 +350,15 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
   // this thread's share of every chunk: keys 4 kq .. 4 kq + 3, dims 8 db ..
   const int kq = tid / TG::DB, db = tid % TG::DB;
   const int c_first = (pt.lo / NK) * NK;
-  const int nch = (pt.hi - c_first + NK - 1) / NK;
+  const int nch = tile_chunks<NK>(pt);
+  const int cps = int(a.split_len) / NK;                         // chunks per split
+  const int cbeg = a.nsplit > 1 ? int(id.split) * cps : 0;
+  const int cend = a.nsplit > 1 ? min(nch, cbeg + cps) : nch;
+  if (cbeg >= cend) return;  // a split past the tile's keys (uniform)
   const int32_t* table = a.block_tables + uint64_t(id.s) * a.max_blocks;
   auto page_of = [&](int c) -> uint32_t {  // page of the thread's key quad in chunk c (0: none)
     const int j = c_first + c * NK + 4 * kq;
-    return (c < nch && j < pt.hi) ? uint32_t(table[j >> a.log2_bs]) : 0u;
+    return (c < cend && j < pt.hi) ? uint32_t(table[j >> a.log2_bs]) : 0u;
   };
   uint32_t kr[4][KW], ks[4], vr[4][VW], vs[4];
   auto load_chunk = [&](int c, uint32_t pid) {
@@ -363,8 +375,8 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
     }
   };
 
-  uint32_t pid_next = page_of(1);
-  load_chunk(0, page_of(0));
+  uint32_t pid_next = page_of(cbeg + 1);
+  load_chunk(cbeg, page_of(cbeg));
 
   // running reference m (log2 units) and the lane's share of the sum of
   // 2^(score - m) for query row n16 of each block.  The reference moves only
@@ -385,7 +397,8 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
   const int lo_all = a.window ? pt.p0 + pt.nq - int(a.window) : 0;  // every row sees keys >= this
   const float qk = KROT ? a.qk_scale * a.wht_scale : a.qk_scale;
 
-  for (int c = 0; c < nch; ++c) {
+  __syncthreads();  // the code-pair tables are in LDS before any thread looks one up
+  for (int c = cbeg; c < cend; ++c) {
     const int c0 = c_first + c * NK;
     // dequantize this thread's share; keys outside [lo, hi) become zeros
     // (only chunks at the ends of the range hold such keys)
@@ -459,7 +472,7 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
       }
     }
     // the next chunk's raw bytes travel while this one is on the matrix cores
-    if (c + 1 < nch) {
+    if (c + 1 < cend) {
       const uint32_t pid = pid_next;
       pid_next = page_of(c + 2);
       load_chunk(c + 1, pid);
@@ -579,8 +592,23 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
     }
   }
 
-  // epilogue: normalize, fp8 V scale, inverse rotation, store.  Lane holds
-  // dims 16 d + 4 jg + i of query row n16 of each block.
+  // epilogue.  Lane holds dims 16 d + 4 jg + i of query row n16 of each
+  // block.  With splits: the row's reference m, its sum and unnormalized
+  // output (rotated basis) for the merge.  Else: normalize, fp8 V scale,
+  // inverse rotation, store.
+  if (a.nsplit > 1) {
+    const uint64_t unit = ((uint64_t(id.s) * a.ntiles + id.tile) * nkv + g) * a.nsplit + id.split;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = lanegroup_sum(lsum[qb]);
+      const uint64_t row = unit * TG::ROWS + uint64_t(TG::RW * wave + 16 * qb + n16);
+      float* dst = a.part + row * HD + 4 * jg;
+#pragma unroll
+      for (int d = 0; d < OD; ++d) *reinterpret_cast<f32x4v*>(dst + 16 * d) = acc[d][qb];
+      if (jg == 0) *reinterpret_cast<f32x2*>(a.ml + row * 2) = f32x2{m[qb], l};
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = lanegroup_sum(lsum[qb]);
@@ -645,6 +673,69 @@ hipError_t launch_kf(int vf, int hd, const DecodeArgs& a, int G, uint32_t nwg, h
     case KVQ_NVFP4: return launch_hd<KF, KVQ_NVFP4>(hd, a, G, nwg, st);
     default: return launch_hd<KF, KVQ_TURBO8>(hd, a, G, nwg, st);
   }
+}
+
+// Split partials of one output row per wave: row r of tile `tile` of
+// (sequence, kv head) is query r / G, head r % G.  Log-sum-exp over the
+// splits that hold keys (in split order), the fp8 V scale, the inverse
+// rotation of a rotated V side (dims lane * HD/64 + e: bits below in
+// registers, the rest across lanes), then the row.
+template <int HD, bool VROT>
+__global__ __launch_bounds__(256) void tile_merge_kernel(const DecodeArgs a, int G) {
+  constexpr int NK = 8192 / HD, DPL = HD / kWave;
+  const int lane = threadIdx.x & 63;
+  const int rows = int(a.qt) * G;
+  const uint64_t wrow = uint64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // over (s, tile, g, r)
+  const int r = int(wrow % uint64_t(rows));
+  const uint64_t stg = wrow / uint64_t(rows);
+  const uint32_t g = uint32_t(stg % a.num_kv_heads), tile = uint32_t((stg / a.num_kv_heads) % a.ntiles);
+  const uint32_t s = uint32_t(stg / (uint64_t(a.num_kv_heads) * a.ntiles));
+  if (s >= a.num_seqs) return;
+  const PrefillTile pt = prefill_tile(a, s, tile);
+  const int t = r / G, h = r % G;
+  if (t >= pt.nq) return;
+  const int ns = (tile_chunks<NK>(pt) + int(a.split_len) / NK - 1) / (int(a.split_len) / NK);
+  const uint64_t row0 = (uint64_t(stg) * a.nsplit) * uint64_t(rows) + uint64_t(r);  // split 0's row
+  const uint64_t sstride = uint64_t(rows);
+  float M = -INFINITY;
+  for (int k = 0; k < ns; ++k) M = fmaxf(M, a.ml[(row0 + k * sstride) * 2]);
+  float z = 0.0f, o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+  for (int k = 0; k < ns; ++k) {
+    const uint64_t row = row0 + k * sstride;
+    const float w = fast_exp2(a.ml[row * 2] - M);
+    z += w * a.ml[row * 2 + 1];
+    const float* src = a.part + row * HD + lane * DPL;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] += w * src[e];
+  }
+  const float inv = a.v_scale / z;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] *= inv;
+  if constexpr (VROT) {
+#pragma unroll
+    for (int hb = 1; hb < DPL; hb <<= 1)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e)
+        if ((e & hb) == 0) {
+          const float u = o[e], v = o[e + hb];
+          o[e] = u + v;
+          o[e + hb] = u - v;
+        }
+#pragma unroll
+    for (int b = 1; b < kWave; b <<= 1)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const float p = __shfl_xor(o[e], b);
+        o[e] = (lane & b) ? p - o[e] : o[e] + p;
+      }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] *= a.wht_scale;
+  }
+  float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + g * G + h) * HD + lane * DPL;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) dst[e] = o[e];
 }
 
 // The rotated K formats' instances (kvq_prefill_rot.hip).

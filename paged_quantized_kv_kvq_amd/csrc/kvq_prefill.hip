@@ -22,4 +22,24 @@ hipError_t launch_prefill_tiles(int kf, int vf, int hd, int G, const DecodeArgs&
   }
 }
 
+hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int G, const DecodeArgs& a, hipStream_t st) {
+  const uint64_t waves = uint64_t(a.num_seqs) * a.ntiles * a.num_kv_heads * a.qt * uint32_t(G);
+  const dim3 grid(uint32_t((waves + 3) / 4)), block(256);
+  switch (hd) {
+    case 64:
+      if (v_rotated) prefill::tile_merge_kernel<64, true><<<grid, block, 0, st>>>(a, G);
+      else prefill::tile_merge_kernel<64, false><<<grid, block, 0, st>>>(a, G);
+      break;
+    case 128:
+      if (v_rotated) prefill::tile_merge_kernel<128, true><<<grid, block, 0, st>>>(a, G);
+      else prefill::tile_merge_kernel<128, false><<<grid, block, 0, st>>>(a, G);
+      break;
+    default:
+      if (v_rotated) prefill::tile_merge_kernel<256, true><<<grid, block, 0, st>>>(a, G);
+      else prefill::tile_merge_kernel<256, false><<<grid, block, 0, st>>>(a, G);
+      break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace kvq

@@ -172,8 +172,15 @@ def test_prefill_host_checks(lib):
     lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
     lay_t = kvq.pool_layout("turbo4", "turbo3", 4, 8, 256)
     for lay_s in (lay, lay_t, kvq.pool_layout("nvfp4", "bf16", 512, 8, 64)):
-        assert kvq.prefill_workspace_bytes(lay_s, 4, 32, 64, 100) == 256
+        assert kvq.prefill_workspace_bytes(lay_s, 400, 32, 64, 100) == 256
         assert kvq.prefill_workspace_bytes(lay_s, 400, 64, 4096, 9000, sliding_window=128) == 256
+    # ... and so does a small grid whose key ranges are short (1024 keys)
+    assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100) == 256
+    # a grid of few tiles over long key ranges splits the ranges: partial rows
+    # (statistics + unnormalized output) of every split
+    one = kvq.prefill_workspace_bytes(lay, 1, 32, 2048, 64)   # 1 sequence, 32768 keys, 2 tiles x 8 kv heads
+    assert one > 256 and one % 256 == 0
+    assert one >= 2 * 8 * 2 * 128 * 128 * 4     # at least two splits of 128 rows x 128 dims per tile
     # block_size < 4 runs as decode rows: the workspace holds the dense decode
     # workspace of num_seqs * max_query_len rows
     for shape in [("turbo4", "bf16", 1, 8, 128), ("fp8", "turbo2", 2, 8, 128), ("turbo3", "turbo3", 2, 8, 64)]:

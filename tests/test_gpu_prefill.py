@@ -194,3 +194,20 @@ def test_prefill_tiles_empty_chunks_and_strided_q(gpu_lib):
     w = synth.small(9995, lens=[300, 0, 64, 129, 17], num_q_heads=16, num_kv_heads=2, head_dim=128, block_size=4,
                     k_format="bf16", v_format="bf16")
     run_prefill(gpu_lib, w, [33, 0, 0, 129, 5], window=50, seed=5, label="tiles, window 50, empty chunks", q_pad=2)
+
+
+# key splits: a grid of few tiles over long key ranges splits each range and
+# merges the splits' partials; many sequences fill the grid without splits
+@pytest.mark.parametrize("kf,vf,win", [("bf16", "turbo4", 0), ("turbo4", "turbo3", 0), ("fp8", "bf16", 3000),
+                                       ("nvfp4", "turbo8", 0)])
+def test_prefill_tiles_split_long(gpu_lib, kf, vf, win):
+    w = synth.small(9700 + len(kf) + len(vf) + win, lens=[12000, 33], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    block_size=16, k_format=kf, v_format=vf, sliding_window=win)
+    run_prefill(gpu_lib, w, [300, 33], window=win, seed=9, label=f"tiles split {kf}/{vf} window {win}")
+
+
+def test_prefill_tiles_many_sequences_no_split(gpu_lib):
+    lens = [int(x) for x in np.random.default_rng(77).integers(60, 400, 48)]
+    w = synth.small(9760, lens=lens, num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                    k_format="bf16", v_format="turbo4")
+    run_prefill(gpu_lib, w, [min(L, 100) for L in lens], seed=3, label="tiles, 48 sequences, no split")
