@@ -18,6 +18,7 @@ constexpr uint32_t kMaxSplitLen = 4096;
 constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a split live in LDS
 constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
+constexpr uint64_t kSparseTargetWorkgroups = KVQ_SPARSE_TARGET_WORKGROUPS;
 // chunked prefill on the tile kernel: a grid of fewer workgroups than this
 // splits the tiles' key ranges (two per CU fill the GPU), into splits of at
 // least kTileSplitChunks chunks
@@ -148,14 +149,19 @@ struct Plan {
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 
 // Split length: the smallest power of two >= 256 giving about
-// kTargetWorkgroups workgroups over the longest possible window.
+// kTargetWorkgroups (kv head, split) units over the longest possible window
+// (dense: a workgroup serves up to eight kv heads of a split), or
+// kSparseTargetWorkgroups on the sparse path, whose score kernel runs a
+// workgroup per unit: two per CU, all resident at once, instead of 2048
+// shorter ones over several rounds (workload 4: score pass 50 -> 43 us).
 Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
                uint32_t window, bool sparse) {
   uint64_t span = uint64_t(max_blocks) * bs;
   if (window && window < span) span = window;
   const uint64_t work = span * S * nkv;
   uint32_t sl = 256;
-  while (sl < kMaxSplitLen && uint64_t(sl) * kTargetWorkgroups < work) sl <<= 1;
+  const uint64_t target = sparse ? kSparseTargetWorkgroups : kTargetWorkgroups;
+  while (sl < kMaxSplitLen && uint64_t(sl) * target < work) sl <<= 1;
   if (sparse && sl > kMaxSparseSplitLen) sl = kMaxSparseSplitLen;
   while (sl > 16 && sl / bs + 2 > kPagesPerSplit) sl >>= 1;
   Plan p;

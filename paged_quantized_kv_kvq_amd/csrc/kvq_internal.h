@@ -13,7 +13,10 @@
 #define KVQ_WAVES 4              // waves per decode workgroup
 #endif
 #ifndef KVQ_TARGET_WORKGROUPS
-#define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many
+#define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many (kv head, split) units
+#endif
+#ifndef KVQ_SPARSE_TARGET_WORKGROUPS
+#define KVQ_SPARSE_TARGET_WORKGROUPS 512  // ... on the sparse path (its score kernel runs one workgroup per unit)
 #endif
 #ifndef KVQ_MAX_SPARSE_SPLIT
 #define KVQ_MAX_SPARSE_SPLIT 2048  // positions per split on the sparse path (scores kept in LDS)
