@@ -14,9 +14,9 @@
 namespace kvq {
 namespace {
 
-constexpr uint32_t kMaxSplitLen = 4096;
+constexpr uint32_t kMaxSplitLen = KVQ_MAX_SPLIT;
 constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a split live in LDS
-constexpr uint32_t kPagesPerSplit = 160;                       // page offsets of a split live in LDS
+constexpr uint32_t kPagesPerSplit = KVQ_MAX_PAGES;             // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 constexpr uint64_t kSparseTargetWorkgroups = KVQ_SPARSE_TARGET_WORKGROUPS;
 // chunked prefill on the tile kernel: a grid of fewer workgroups than this

@@ -40,7 +40,7 @@ namespace kvq {
 
 constexpr int kWaves = KVQ_WAVES;  // waves per workgroup
 constexpr int kChunk = 16;         // positions per wave iteration
-constexpr int kMaxPages = 160;     // page offsets of one split staged in LDS
+constexpr int kMaxPages = KVQ_MAX_PAGES;  // page offsets of one split staged in LDS
 constexpr int kMaxSparseSplit = KVQ_MAX_SPARSE_SPLIT;
 
 template <int F>

@@ -15,6 +15,12 @@
 #ifndef KVQ_TARGET_WORKGROUPS
 #define KVQ_TARGET_WORKGROUPS 2048  // the split length is chosen to give about this many (kv head, split) units
 #endif
+#ifndef KVQ_MAX_PAGES
+#define KVQ_MAX_PAGES 160        // page offsets of one decode split staged in LDS
+#endif
+#ifndef KVQ_MAX_SPLIT
+#define KVQ_MAX_SPLIT 4096       // longest decode split (positions)
+#endif
 #ifndef KVQ_SPARSE_TARGET_WORKGROUPS
 #define KVQ_SPARSE_TARGET_WORKGROUPS 512  // ... on the sparse path (its score kernel runs one workgroup per unit)
 #endif
