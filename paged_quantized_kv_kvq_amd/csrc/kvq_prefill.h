@@ -121,10 +121,15 @@ __device__ __forceinline__ int vt_col(int kappa) {
 }
 
 // One thread's raw bytes of one key: 8 dims of its K row and of its V row
-// (+ the word holding the V group scale).
+// (+ the word holding the V group scale).  The words stay as loaded (a 2- or
+// 3-bit piece inside its aligned words, a scale byte inside its word) and
+// are shifted into place only where they are used: a shift right after the
+// load would make the wave wait for the next chunk's bytes before working on
+// the current one.
 template <int F>
 struct PieceWords {
-  static constexpr int n = (8 * Fmt<F>::bits + 31) / 32;
+  static constexpr int n = (8 * Fmt<F>::bits + 31) / 32;     // words of the piece
+  static constexpr int raw = Fmt<F>::bits == 3 ? 2 : n;     // words as loaded
 };
 
 template <int F>
@@ -139,27 +144,52 @@ __device__ __forceinline__ void load_piece(const uint8_t* row, int b, uint32_t* 
   } else if constexpr (bits == 4) {
     w[0] = load4(row + 4 * b);
   } else if constexpr (bits == 2) {
-    w[0] = (load4(row + 4 * (b >> 1)) >> (16 * (b & 1))) & 0xFFFFu;
+    w[0] = load4(row + 4 * (b >> 1));
   } else {
     // 3 bytes at byte 3b: the two aligned words that cover them (at most 5
     // bytes past the row, still inside the block: rows, then the scales)
-    const int off = 3 * b, base = off & ~3;
-    const uint32_t w0 = load4(row + base), w1 = load4(row + base + 4);
-    w[0] = uint32_t(((uint64_t(w1) << 32) | w0) >> (8 * (off & 3))) & 0xFFFFFFu;
+    const int base = (3 * b) & ~3;
+    w[0] = load4(row + base);
+    w[1] = load4(row + base + 4);
   }
 }
 
-// The word holding the group scale of dims 8b .. 8b + 7 of row prow (scale
-// section at sbase; turbo8: a bf16 word, else an E4M3 byte) in its low bits.
+// Bit offset of the piece inside its loaded words (2- and 3-bit codes).
+template <int F>
+__device__ __forceinline__ uint32_t piece_shift(int b) {
+  constexpr int bits = Fmt<F>::bits;
+  return bits == 2 ? 16u * uint32_t(b & 1) : bits == 3 ? 8u * uint32_t((3 * b) & 3) : 0u;
+}
+
+// The piece's words from the loaded ones.
+template <int F>
+__device__ __forceinline__ void piece_words(const uint32_t* r, uint32_t sh, uint32_t* w) {
+  constexpr int bits = Fmt<F>::bits;
+  if constexpr (bits == 2) {
+    w[0] = (r[0] >> sh) & 0xFFFFu;
+  } else if constexpr (bits == 3) {
+    w[0] = uint32_t(((uint64_t(r[1]) << 32) | r[0]) >> sh) & 0xFFFFFFu;
+  } else {
+#pragma unroll
+    for (int i = 0; i < PieceWords<F>::n; ++i) w[i] = r[i];
+  }
+}
+
+// The word holding the group scale of dims 8b .. 8b + 7 of a row whose
+// scales start at srow (turbo8: a bf16 word, else an E4M3 byte), as loaded;
+// scale_shift gives the scale's bit offset in it.
 template <int F, int HD>
-__device__ __forceinline__ uint32_t load_scale(const uint8_t* sbase, uint32_t prow, int b) {
+__device__ __forceinline__ uint32_t load_scale(const uint8_t* srow, int b) {
   if constexpr (Fmt<F>::sgb == 0) {
     return 0u;
   } else {
-    constexpr int SR = (HD / 16) * Fmt<F>::sgb;  // scale bytes per row
     const int o = (b >> 1) * Fmt<F>::sgb;
-    return load4(sbase + uint64_t(prow) * SR + (o & ~3)) >> (8 * (o & 3));
+    return load4(srow + (o & ~3));
   }
+}
+template <int F>
+__device__ __forceinline__ uint32_t scale_shift(int b) {
+  return 8u * uint32_t(((b >> 1) * Fmt<F>::sgb) & 3);
 }
 
 // The 8 values of a piece in fp32 (exact: products of at most 12
@@ -257,7 +287,7 @@ __device__ __forceinline__ int tile_chunks(const PrefillTile& pt) {
 }
 
 template <int KF, int VF, int HD>
-__global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, int G) {
+__global__ __launch_bounds__(256, HD <= 128 ? 2 : 1) void prefill_tile_kernel(const DecodeArgs a, int G) {
   using TG = TGeo<KF, HD>;
   constexpr int NK = TG::NK, QB = TG::QB, KT = TG::KT, KS = TG::KS, DS = TG::DS, OD = TG::OD;
   constexpr bool KROT = TG::KROT;                   // rotated K: fp32 scores
@@ -360,18 +390,24 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
     const int j = c_first + c * NK + 4 * kq;
     return (c < cend && j < pt.hi) ? uint32_t(table[j >> a.log2_bs]) : 0u;
   };
-  uint32_t kr[4][KW], ks[4], vr[4][VW], vs[4];
+  uint32_t kr[4][PieceWords<KF>::raw], ks[4], vr[4][PieceWords<VF>::raw], vs[4];
+  const uint32_t kpsh = piece_shift<KF>(db), vpsh = piece_shift<VF>(db);
+  const uint32_t kssh = scale_shift<KF>(db), vssh = scale_shift<VF>(db);
+  // the thread's four keys are consecutive rows of one page, nkv rows
+  // apart: one 64-bit base per side and chunk, then 32-bit row steps
+  constexpr uint32_t KSR = (HD / 16) * Fmt<KF>::sgb, VSR = (HD / 16) * Fmt<VF>::sgb;  // scale bytes per row
+  const uint32_t kstep = nkv * KRB, vstep = nkv * VRB, ksstep = nkv * KSR, vsstep = nkv * VSR;
   auto load_chunk = [&](int c, uint32_t pid) {
-    const int j = c_first + c * NK + 4 * kq;
+    const uint32_t prow = (uint32_t(c_first + c * NK + 4 * kq) & (bs - 1u)) * nkv + g;
     const uint8_t* kb = a.k_cache + uint64_t(pid) * a.k_stride;
     const uint8_t* vb = a.v_cache + uint64_t(pid) * a.v_stride;
+    const uint32_t ko = prow * KRB, vo = prow * VRB, kso = prow * KSR, vso = prow * VSR;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t prow = ((uint32_t(j + t) & (bs - 1u)) * nkv + g);
-      load_piece<KF>(kb + uint64_t(prow) * KRB, db, kr[t]);
-      ks[t] = load_scale<KF, HD>(kb + a.k_data, prow, db);
-      load_piece<VF>(vb + uint64_t(prow) * VRB, db, vr[t]);
-      vs[t] = load_scale<VF, HD>(vb + a.v_data, prow, db);
+      load_piece<KF>(kb + (ko + t * kstep), db, kr[t]);
+      ks[t] = load_scale<KF, HD>(kb + a.k_data + (kso + t * ksstep), db);
+      load_piece<VF>(vb + (vo + t * vstep), db, vr[t]);
+      vs[t] = load_scale<VF, HD>(vb + a.v_data + (vso + t * vsstep), db);
     }
   };
 
@@ -400,65 +436,59 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
   __syncthreads();  // the code-pair tables are in LDS before any thread looks one up
   for (int c = cbeg; c < cend; ++c) {
     const int c0 = c_first + c * NK;
-    // dequantize this thread's share; keys outside [lo, hi) become zeros
-    // (only chunks at the ends of the range hold such keys)
+    __syncthreads();  // every wave is done with the previous chunk's LDS
+    // dequantize this thread's share straight into LDS (nothing is held
+    // across a barrier); keys outside [lo, hi) become zeros (only chunks at
+    // the ends of the range hold such keys)
     const bool ends = c0 < pt.lo || c0 + NK > pt.hi;
-    uint32_t vh[8][2], vl[VLO ? 8 : 1][2], kh[4][KROT ? 8 : 4];
-    {
-      float x[4][8];
+    uint32_t vh[8][2], vl[VLO ? 8 : 1][2];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = c0 + 4 * kq + t;
+    for (int pr = 0; pr < 2; ++pr) {  // keys 2 pr, 2 pr + 1
+      float x[2][8];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = 2 * pr + u, kappa = 4 * kq + t, j = c0 + kappa;
         const bool ok = !ends || (j >= pt.lo && j < pt.hi);
+        uint32_t kp[KW], vp[VW];
+        piece_words<KF>(kr[t], kpsh, kp);
+        piece_words<VF>(vr[t], vpsh, vp);
+        uint32_t ksw = ks[t] >> kssh, vsw = vs[t] >> vssh;
         if (ends) {
 #pragma unroll
-          for (int i = 0; i < KW; ++i) kr[t][i] = ok ? kr[t][i] : 0u;
+          for (int i = 0; i < KW; ++i) kp[i] = ok ? kp[i] : 0u;
 #pragma unroll
-          for (int i = 0; i < VW; ++i) vr[t][i] = ok ? vr[t][i] : 0u;
-          ks[t] = ok ? ks[t] : 0u;
-          vs[t] = ok ? vs[t] : 0u;
+          for (int i = 0; i < VW; ++i) vp[i] = ok ? vp[i] : 0u;
+          ksw = ok ? ksw : 0u;
+          vsw = ok ? vsw : 0u;
         }
+        // the key's K row piece, straight to LDS
         if constexpr (KF == KVQ_BF16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) kh[t][i] = kr[t][i];
+          *reinterpret_cast<u32x4*>(&sm.kt[kappa * (HD / 2) + 4 * kt_unit<HD>(kappa, db)]) =
+              u32x4{kp[0], kp[1], kp[2], kp[3]};
         } else if constexpr (KF == KVQ_FP8_E4M3) {
-          kh[t][0] = fp8x2_to_bf16x2<false>(kr[t][0]);
-          kh[t][1] = fp8x2_to_bf16x2<true>(kr[t][0]);
-          kh[t][2] = fp8x2_to_bf16x2<false>(kr[t][1]);
-          kh[t][3] = fp8x2_to_bf16x2<true>(kr[t][1]);
+          *reinterpret_cast<u32x4*>(&sm.kt[kappa * (HD / 2) + 4 * kt_unit<HD>(kappa, db)]) =
+              u32x4{fp8x2_to_bf16x2<false>(kp[0]), fp8x2_to_bf16x2<true>(kp[0]), fp8x2_to_bf16x2<false>(kp[1]),
+                    fp8x2_to_bf16x2<true>(kp[1])};
         } else {
           float y[8];
-          piece_values<KF>(kr[t], ks[t], sm.kpair, y);
+          piece_values<KF>(kp, ksw, sm.kpair, y);
+          if constexpr (KROT) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            if constexpr (KROT) kh[t][i] = __float_as_uint(y[i]);
-            else if (i < 4) kh[t][i] = pack_bf16(y[2 * i], y[2 * i + 1]);  // exact (NVFP4)
+            for (int v = 0; v < 2; ++v)
+              *reinterpret_cast<u32x4*>(&sm.kt[kappa * HD + 4 * kf_unit(kappa, 2 * db + v)]) =
+                  u32x4{__float_as_uint(y[4 * v]), __float_as_uint(y[4 * v + 1]), __float_as_uint(y[4 * v + 2]),
+                        __float_as_uint(y[4 * v + 3])};
+          } else {  // exact in bf16 (NVFP4)
+            *reinterpret_cast<u32x4*>(&sm.kt[kappa * (HD / 2) + 4 * kt_unit<HD>(kappa, db)]) =
+                u32x4{pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7])};
           }
         }
-        piece_values<VF>(vr[t], vs[t], sm.vpair, x[t]);
+        piece_values<VF>(vp, vsw, sm.vpair, x[u]);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        vh[e][0] = pack_bf16(x[0][e], x[1][e]);
-        vh[e][1] = pack_bf16(x[2][e], x[3][e]);
-        if constexpr (VLO) {
-          vl[e][0] = pack_bf16(x[0][e] - lo_half(vh[e][0]), x[1][e] - hi_half(vh[e][0]));
-          vl[e][1] = pack_bf16(x[2][e] - lo_half(vh[e][1]), x[3][e] - hi_half(vh[e][1]));
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with the previous chunk's LDS
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int kappa = 4 * kq + t;
-      if constexpr (KROT) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v)
-          *reinterpret_cast<u32x4*>(&sm.kt[kappa * HD + 4 * kf_unit(kappa, 2 * db + v)]) =
-              u32x4{kh[t][4 * v], kh[t][4 * v + 1], kh[t][4 * v + 2], kh[t][4 * v + 3]};
-      } else {
-        *reinterpret_cast<u32x4*>(&sm.kt[kappa * (HD / 2) + 4 * kt_unit<HD>(kappa, db)]) =
-            u32x4{kh[t][0], kh[t][1], kh[t][2], kh[t][3]};
+        vh[e][pr] = pack_bf16(x[0][e], x[1][e]);
+        if constexpr (VLO) vl[e][pr] = pack_bf16(x[0][e] - lo_half(vh[e][pr]), x[1][e] - hi_half(vh[e][pr]));
       }
     }
     {
@@ -473,9 +503,8 @@ __global__ __launch_bounds__(256) void prefill_tile_kernel(const DecodeArgs a, i
     }
     // the next chunk's raw bytes travel while this one is on the matrix cores
     if (c + 1 < cend) {
-      const uint32_t pid = pid_next;
-      pid_next = page_of(c + 2);
-      load_chunk(c + 1, pid);
+      load_chunk(c + 1, pid_next);
+      pid_next = page_of(c + 2);  // after the loads that read the old value: no copy, no early wait
     }
     __syncthreads();
 
