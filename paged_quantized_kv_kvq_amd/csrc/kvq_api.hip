@@ -148,6 +148,15 @@ struct Plan {
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 
+// Page offsets a split may stage for the kernel that will run: the
+// matrix-core split kernel (KVQ_DENSE_MFMA, operands it takes, block_size
+// >= 16) by its K format, everything else the common limit.
+uint32_t dense_pages(const kvq_layout* layout, bool sparse) {
+  const bool mfma = KVQ_DENSE_MFMA && !sparse && layout->block_size >= 16 &&
+                    mfma_split_ok(layout->k_format, layout->v_format, int(layout->head_dim));
+  return mfma ? uint32_t(dense_max_pages(layout->k_format)) : kPagesPerSplit;
+}
+
 // Split length: the smallest power of two >= 256 giving about
 // kTargetWorkgroups (kv head, split) units over the longest possible window
 // (dense: a workgroup serves up to eight kv heads of a split), or
@@ -155,7 +164,7 @@ uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 // workgroup per unit: two per CU, all resident at once, instead of 2048
 // shorter ones over several rounds (workload 4: score pass 50 -> 43 us).
 Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
-               uint32_t window, bool sparse) {
+               uint32_t window, bool sparse, uint32_t max_pages) {
   uint64_t span = uint64_t(max_blocks) * bs;
   if (window && window < span) span = window;
   const uint64_t work = span * S * nkv;
@@ -163,7 +172,7 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   const uint64_t target = sparse ? kSparseTargetWorkgroups : kTargetWorkgroups;
   while (sl < kMaxSplitLen && uint64_t(sl) * target < work) sl <<= 1;
   if (sparse && sl > kMaxSparseSplitLen) sl = kMaxSparseSplitLen;
-  while (sl > 16 && sl / bs + 2 > kPagesPerSplit) sl >>= 1;
+  while (sl > 16 && sl / bs + 2 > max_pages) sl >>= 1;
   Plan p;
   p.split_len = sl;
   p.nsplit = uint32_t(span == 0 ? 1 : (span + sl - 1) / sl);
@@ -308,7 +317,8 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
   if (uint64_t(max_blocks_per_seq) * layout->block_size >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const bool sparse = sparse_v_threshold > 0.0f;
-  const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse);
+  const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse,
+                           dense_pages(layout, sparse));
   // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
   const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
   const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv;
@@ -474,7 +484,8 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   const uint32_t nkv = layout->num_kv_heads, hd = layout->head_dim, G = num_q_heads / nkv;
   const uint64_t rows = uint64_t(num_seqs) * max_query_len;
   if (rows >= (1ull << 31) || rows * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
-  const Plan p = make_plan(uint32_t(rows), nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, false);
+  const Plan p = make_plan(uint32_t(rows), nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, false,
+                           dense_pages(layout, false));
   const uint64_t nwg = (rows * p.nsplit + 7) / 8 * 8 * nkv;
   if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const uint64_t off_vrow = 0, off_vlen = up256(rows * 2 * sizeof(int32_t));

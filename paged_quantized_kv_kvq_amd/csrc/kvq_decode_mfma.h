@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   constexpr int R = G;  // rows: the query heads
   using MG = MfmaGeo<KF, VF, HD, R>;
   constexpr int NG = MG::NG, DV = MG::DV;
-  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G>(), kMaxPages> sm;
+  __shared__ MfmaSmem<KF, VF, HD, R, mfma_waves_cap<KF, G>(), dense_max_pages(KF)> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nw = __builtin_amdgcn_readfirstlane(int(blockDim.x) >> 6);

@@ -18,6 +18,9 @@
 #ifndef KVQ_MAX_PAGES
 #define KVQ_MAX_PAGES 160        // page offsets of one decode split staged in LDS
 #endif
+#ifndef KVQ_MFMA_MAX_PAGES
+#define KVQ_MFMA_MAX_PAGES 260   // ... for the matrix-core split kernel with a bf16 / fp8 K side
+#endif
 #ifndef KVQ_MAX_SPLIT
 #define KVQ_MAX_SPLIT 4096       // longest decode split (positions)
 #endif
@@ -63,6 +66,15 @@ namespace kvq {
 // Whether the dense split pass runs on the matrix cores for these formats and
 // head_dim (bf16 / fp8 K: bf16 MFMA for Q.K^T; turbo K: fp32 MFMA over the
 // rotated query; V rows of at most 128 bytes); it also needs block_size >= 16.
+// Page offsets one split of the dense decode pass may stage: the matrix-core
+// kernel with a bf16 / fp8 K side takes longer splits (fewer partials to
+// write and merge; workload 3: 16 -> 8 splits per sequence, 2% faster), the
+// grouped-scale K paths keep shorter ones (longer ones measured 6% slower on
+// workloads 6 and 7).
+__host__ __device__ constexpr int dense_max_pages(int kf) {
+  return kf == KVQ_BF16 || kf == KVQ_FP8_E4M3 ? KVQ_MFMA_MAX_PAGES : KVQ_MAX_PAGES;
+}
+
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf == KVQ_NVFP4 ? 4 : kf;
   const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf == KVQ_NVFP4 ? 4 : vf;
