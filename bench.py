@@ -30,7 +30,8 @@ roofline_alu  the same call against the fp32 VALU ceiling of the build
            = 78.6 TFLOP/s).
 stream_read_ref  libkvq_probe.so's page-read kernel over the same page size,
            pages in shuffled order, nothing computed: the practical read
-           ceiling of this GPU for the pool's access pattern.
+           ceiling of this GPU for the pool's access pattern; `lds_direct`
+           is the same read with the pages loaded straight into LDS.
 cpu_baseline  the CPU oracle timed on a sample of the same workload, in
            worker processes (one per core of the process's CPU set, at most
            16); its outputs are also checked against the GPU's (parity).
@@ -182,10 +183,20 @@ def stream_read_reference(page_bytes: int, total_bytes: int = 4 << 30) -> dict:
     reps = 10
     sec = lib.kvq_probe_page_read(pool.data_ptr(), pages.data_ptr(), n, pb, 64, reps, sink.data_ptr(),
                                   torch.cuda.current_stream().cuda_stream)
-    del pool, pages, sink
     gbs = round(reps * n * pb / sec / 1e9, 1) if sec > 0 else None
-    return {"kernel": "page_read_kernel (libkvq_probe.so)", "page_bytes": pb, "pages": n, "gbs": gbs,
-            "frac_of_peak": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
+    rec = {"kernel": "page_read_kernel (libkvq_probe.so)", "page_bytes": pb, "pages": n, "gbs": gbs,
+           "frac_of_peak": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
+    # the same pages read straight into LDS through a ring of three stages
+    if hasattr(lib, "kvq_probe_page_read_lds") and pb * 3 <= 160 * 1024:
+        lib.kvq_probe_page_read_lds.restype = ctypes.c_double
+        lib.kvq_probe_page_read_lds.argtypes = lib.kvq_probe_page_read.argtypes
+        sec = lib.kvq_probe_page_read_lds(pool.data_ptr(), pages.data_ptr(), n, pb, 64, reps, sink.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+        lds = round(reps * n * pb / sec / 1e9, 1) if sec > 0 else None
+        rec["lds_direct"] = {"kernel": "page_read_lds_kernel (libkvq_probe.so)", "gbs": lds,
+                             "frac_of_peak": None if lds is None else round(lds / HBM_PEAK_GBS, 4)}
+    del pool, pages, sink
+    return rec
 
 
 def _attended(st, w) -> np.ndarray:
