@@ -19,6 +19,7 @@ constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a sp
 constexpr uint32_t kPagesPerSplit = KVQ_MAX_PAGES;             // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 constexpr uint64_t kSparseTargetWorkgroups = KVQ_SPARSE_TARGET_WORKGROUPS;
+constexpr uint64_t kVTargetWorkgroups = KVQ_V_TARGET_WORKGROUPS;
 // chunked prefill on the tile kernel: a grid of fewer workgroups than this
 // splits the tiles' key ranges (two per CU fill the GPU), into splits of at
 // least kTileSplitChunks chunks
@@ -142,8 +143,8 @@ int check_layout(const kvq_layout* l) {
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
-  uint32_t split_len, nsplit, seg_cap;
-  uint64_t off_part, off_ml, off_cnt, off_crec, bytes;
+  uint32_t split_len, nsplit, seg_cap, vparts;
+  uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -180,8 +181,9 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
-  p.off_part = p.off_cnt = p.off_crec = 0;
+  p.off_part = p.off_cnt = p.off_crec = p.off_vpart = 0;
   p.seg_cap = 0;
+  p.vparts = 1;
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
@@ -191,6 +193,16 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
     p.off_crec = off;
     off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
+    // V-pass parts: as many as keep the launch within kVTargetWorkgroups and
+    // every wave of the longest sequence with a segment of its own
+    const uint64_t pairs = uint64_t(S) * nkv;
+    while (p.vparts < kMaxVParts && pairs * p.vparts * 2 <= kVTargetWorkgroups &&
+           p.vparts * 2 * KVQ_VWAVES <= p.nsplit * KVQ_WAVES)
+      p.vparts *= 2;
+    if (p.vparts > 1) {
+      p.off_vpart = off;
+      off = up256(off + pairs * p.vparts * G * hd * sizeof(float));
+    }
   }
   p.bytes = off;
   return p;
@@ -321,7 +333,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
                            dense_pages(layout, sparse));
   // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
   const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
-  const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv;
+  const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv * p.vparts;
   if (nwg >= (1ull << 31) || nwg_v >= (1ull << 31) || uint64_t(num_seqs) * num_q_heads >= (1ull << 31))
     return KVQ_ERR_UNSUPPORTED;
   if (!workspace) {
@@ -350,6 +362,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   } else {
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     a.crec = reinterpret_cast<uint32_t*>(ws + p.off_crec);
+    if (p.vparts > 1) a.vpart = reinterpret_cast<float*>(ws + p.off_vpart);
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -361,6 +374,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   a.split_len = p.split_len;
   a.nsplit = p.nsplit;
   a.seg_cap = p.seg_cap;
+  a.vparts = p.vparts;
   a.k_stride = layout->k_block_stride_bytes;
   a.k_data = layout->k_data_section_bytes;
   a.v_stride = layout->v_block_stride_bytes;
@@ -388,6 +402,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
       default: e = launch_scores_turbo4(int(hd), int(G), a, uint32_t(nwg), s); break;
     }
     if (e == hipSuccess) e = launch_sparse_v(vf, int(hd), int(G), a, uint32_t(nwg_v), s);
+    if (e == hipSuccess && p.vparts > 1) e = launch_sparse_v_merge(layout->v_rotated != 0, int(hd), int(G), a, s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

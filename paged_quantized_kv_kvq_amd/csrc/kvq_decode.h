@@ -1146,12 +1146,35 @@ __device__ __forceinline__ void accumulate_kept(const DecodeArgs& a, const float
   }
 }
 
-// The end of a sparse-V workgroup (sequence s, kv head g): the lane slots'
-// and the waves' partial sums added in a fixed order, scaled by the fp8 V
-// scale, rotated back (turbo V) and stored.
+// The G output rows of (sequence s, kv head g) from their sums in LDS (o, G x
+// HD): x v_scale, rotated back (a rotated V side) and stored.
+template <int HD, int G, bool VROT, int NT>
+__device__ __forceinline__ void store_sparse_rows(const DecodeArgs& a, float* o, uint32_t s, uint32_t g) {
+  const int tid = threadIdx.x;
+  if constexpr (VROT) {
+    // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
+    for (int h2 = 1; h2 < HD; h2 <<= 1) {
+      for (int i = tid; i < G * HD / 2; i += NT) {
+        const int hh = i / (HD / 2), k = i % (HD / 2);
+        const int lo = hh * HD + (k / h2) * 2 * h2 + (k % h2);
+        const float x = o[lo], y = o[lo + h2];
+        o[lo] = x + y;
+        o[lo + h2] = x - y;
+      }
+      __syncthreads();
+    }
+  }
+  float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
+  for (int i = tid; i < G * HD; i += NT) dst[i] = VROT ? o[i] * a.wht_scale : o[i];
+}
+
+// The end of a sparse-V workgroup (part `part` of sequence s, kv head g): the
+// lane slots' and the waves' partial sums added in a fixed order.  With one
+// part the result is scaled by the fp8 V scale, rotated back (turbo V) and
+// stored; with several, each part stores its sum for sparse_v_merge_kernel.
 template <int VF, int HD, int G, typename Smem>
 __device__ __forceinline__ void sparse_v_finish(const DecodeArgs& a, Smem& sm, float (&acc)[G][VGeo<HD>::D],
-                                                uint32_t s, uint32_t g) {
+                                                uint32_t s, uint32_t g, uint32_t part) {
   using GE = VGeo<HD>;
   constexpr int D = GE::D, T = GE::T;
   constexpr int NT = kVWaves * kWave;
@@ -1183,6 +1206,17 @@ __device__ __forceinline__ void sparse_v_finish(const DecodeArgs& a, Smem& sm, f
   }
   __syncthreads();
   float* o = &sm.u.red[0][0][0];  // row h of the result at o + h * HD
+  if (a.vparts > 1) {
+    float* mine = a.vpart + ((uint64_t(s) * a.num_kv_heads + g) * a.vparts + part) * (G * HD);
+    for (int i = tid; i < G * HD; i += NT) {
+      const int h = i / HD, d = i % HD;
+      float v = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < HW; ++ww) v += sm.u.red[ww][h][d];
+      mine[i] = v;
+    }
+    return;
+  }
   for (int i = tid; i < G * HD; i += NT) {
     const int h = i / HD, d = i % HD;
     float v = 0.0f;
@@ -1191,28 +1225,77 @@ __device__ __forceinline__ void sparse_v_finish(const DecodeArgs& a, Smem& sm, f
     o[i] = v * a.v_scale;
   }
   __syncthreads();
-  if constexpr (Fmt<VF>::rot) {
-    // inverse rotation of every head's row (the orthonormal WHT is its own inverse)
-    for (int h2 = 1; h2 < HD; h2 <<= 1) {
-      for (int i = tid; i < G * HD / 2; i += NT) {
-        const int hh = i / (HD / 2), k = i % (HD / 2);
-        const int lo = hh * HD + (k / h2) * 2 * h2 + (k % h2);
-        const float x = o[lo], y = o[lo + h2];
-        o[lo] = x + y;
-        o[lo + h2] = x - y;
-      }
-      __syncthreads();
-    }
-  }
-  float* dst = a.out + (uint64_t(s) * a.num_q_heads + uint64_t(g) * G) * HD;
-  for (int i = tid; i < G * HD; i += NT) dst[i] = Fmt<VF>::rot ? o[i] * a.wht_scale : o[i];
+  store_sparse_rows<HD, G, Fmt<VF>::rot, NT>(a, o, s, g);
 }
 
-// One workgroup of kVWaves waves per (sequence, kv head) does the whole V side
-// of the sparse path and writes the output.  The score kernel left one record
-// segment per (split, wave); V wave v takes segments v, v + kVWaves, ...
-// (the score kernel's waves scored interleaved chunks, so the work is evenly
-// spread).  The global softmax statistics come from the split statistics;
+// The V parts' sums of one output row (sequence, q head) per wave, added in
+// part order, x v_scale, rotated back (a rotated V side: butterflies inside
+// the lane for the low index bits, then lane exchanges) and stored.  Lane l
+// holds dims l * E ... l * E + E - 1.
+template <int HD, bool VROT>
+__global__ __launch_bounds__(256) void sparse_v_merge_kernel(const DecodeArgs a, uint32_t G) {
+  constexpr int E = HD / kWave;
+  constexpr int kMaxParts = int(kMaxVParts);
+  const uint64_t row = uint64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // s * num_q_heads + q head
+  if (row >= uint64_t(a.num_seqs) * a.num_q_heads) return;
+  const int lane = threadIdx.x & 63;
+  const uint64_t pair = row / G;
+  const float* src = a.vpart + (pair * a.vparts * G + row % G) * HD + lane * E;
+  // every part's values requested at once (parts past the last re-read it)
+  float v[kMaxParts][E];
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k) {
+    const float* p = src + uint64_t(min(uint32_t(k), a.vparts - 1u)) * G * HD;
+    if constexpr (E == 4) {
+      const float4 f = *reinterpret_cast<const float4*>(p);
+      v[k][0] = f.x; v[k][1] = f.y; v[k][2] = f.z; v[k][3] = f.w;
+    } else if constexpr (E == 2) {
+      const float2 f = *reinterpret_cast<const float2*>(p);
+      v[k][0] = f.x; v[k][1] = f.y;
+    } else {
+      v[k][0] = *p;
+    }
+  }
+  float x[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    x[i] = v[0][i];
+#pragma unroll
+    for (int k = 1; k < kMaxParts; ++k)
+      if (uint32_t(k) < a.vparts) x[i] += v[k][i];
+    x[i] *= a.v_scale;
+  }
+  if constexpr (VROT) {
+#pragma unroll
+    for (int h2 = 1; h2 < E; h2 <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if (!(i & h2)) {
+          const float p = x[i], q = x[i + h2];
+          x[i] = p + q;
+          x[i + h2] = p - q;
+        }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        const float o = __shfl_xor(x[i], m);
+        x[i] = (lane & m) ? o - x[i] : x[i] + o;
+      }
+#pragma unroll
+    for (int i = 0; i < E; ++i) x[i] *= a.wht_scale;
+  }
+  float* dst = a.out + row * HD + lane * E;
+  if constexpr (E == 4) *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+  else if constexpr (E == 2) *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
+  else dst[0] = x[0];
+}
+
+// a.vparts workgroups of kVWaves waves per (sequence, kv head) do the V side
+// of the sparse path and write the output.  The score kernel left one record
+// segment per (split, wave); V wave v of part p (wave W = p * kVWaves + v of
+// the NW = vparts * kVWaves) takes segments W, W + NW, ... (the score kernel's
+// waves scored interleaved chunks, so the work is evenly spread).  The global softmax statistics come from the split statistics;
 // each lane reads one record, keeps a position for head h when its exact
 // global weight exceeds the threshold, and a ballot compacts the kept ones
 // into LDS; the wave's lane slots then stream their V rows.  The segment
@@ -1230,7 +1313,10 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   constexpr int NT = kVWaves * kWave;
   __shared__ SparseSmem<VF, HD, G> sm;
   uint32_t s, g;
-  if (!xcd_unit_tile(blockIdx.x, a.num_seqs, a.num_kv_heads, s, g)) return;
+  // the parts of a (sequence, kv head) run on one XCD
+  const uint32_t part = (blockIdx.x >> 3) % a.vparts;
+  const uint32_t tile = (blockIdx.x & 7u) | (((blockIdx.x >> 3) / a.vparts) << 3);
+  if (!xcd_unit_tile(tile, a.num_seqs, a.num_kv_heads, s, g)) return;
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
@@ -1238,14 +1324,15 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane % T, r = lane / T;
-  const int nseg_all = ns * kWaves;                                // (split, score wave) segments
-  const int nseg = nseg_all > w ? (nseg_all - w + kVWaves - 1) / kVWaves : 0;  // this wave's
+  const int nseg_all = ns * kWaves;  // (split, score wave) segments
+  const int NW = int(a.vparts) * kVWaves, W = int(part) * kVWaves + w;
+  const int nseg = nseg_all > W ? (nseg_all - W + NW - 1) / NW : 0;  // this wave's
   // requests that do not depend on each other go out first: the counts of the
   // wave's first batch of segments, a first record per lane, the statistics
-  const int myc0 = lane < nseg ? a.cnt[sbase * kWaves + w + kVWaves * lane] : 0;
+  const int myc0 = lane < nseg ? a.cnt[sbase * kWaves + W + NW * lane] : 0;
   uint32_t spec[RS];
-  if (w < nseg_all) {  // the wave's first segment exists (the last head's would lie past the workspace)
-    load_record<G>(a.crec + ((sbase * kWaves + w) * a.seg_cap + lane) * RS, spec);
+  if (W < nseg_all) {  // the wave's first segment exists (the last head's would lie past the workspace)
+    load_record<G>(a.crec + ((sbase * kWaves + W) * a.seg_cap + lane) * RS, spec);
   } else {
 #pragma unroll
     for (int i = 0; i < RS; ++i) spec[i] = 0u;
@@ -1297,10 +1384,10 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   auto& kept = sm.u.live.kept[w];
   uint32_t* rows = sm.u.live.rows[w];
   // the wave's segments, kSegBatch at a time (segment i of the wave is
-  // (split, score wave) number w + kVWaves * i of the sequence and kv head)
+  // (split, score wave) number W + NW * i of the sequence and kv head)
   for (int sb = 0; sb < nseg; sb += kSegBatch) {
     const int nb = min(kSegBatch, nseg - sb);
-    const int myc = sb == 0 ? myc0 : (lane < nb ? a.cnt[sbase * kWaves + w + kVWaves * (sb + lane)] : 0);
+    const int myc = sb == 0 ? myc0 : (lane < nb ? a.cnt[sbase * kWaves + W + NW * (sb + lane)] : 0);
     int pre = myc;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -1323,7 +1410,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
         for (int bb = kSegBatch / 2; bb > 0; bb >>= 1)
           if (k + bb < nb && sm.pre[w][k + bb - 1] <= gi) k += bb;
         const int off = gi - (k > 0 ? sm.pre[w][k - 1] : 0);
-        const uint64_t seg = sbase * kWaves + w + kVWaves * (sb + k);
+        const uint64_t seg = sbase * kWaves + W + NW * (sb + k);
         load_record<G>(a.crec + (seg * a.seg_cap + off) * RS, rw);
       }
     };
@@ -1362,7 +1449,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
       accumulate_kept<VF, HD, G>(a, sm.vcen, kept, nk, rows, vsh, acc);
     }
   }
-  sparse_v_finish<VF, HD, G>(a, sm, acc, s, g);
+  sparse_v_finish<VF, HD, G>(a, sm, acc, s, g, part);
 }
 
 }  // namespace kvq

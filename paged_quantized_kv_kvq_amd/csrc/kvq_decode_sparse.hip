@@ -1,7 +1,7 @@
-// Decode kernels that depend only on the V side: the sparse-V pass (which also
-// writes the output) and the dense path's merge (log-sum-exp over splits,
-// with the inverse rotation of a rotated V side); and the row map of chunked
-// prefill run as decode rows.
+// Decode kernels that depend only on the V side: the sparse-V pass (which
+// writes the output, or its parts' sums and then their merge) and the dense
+// path's merge (log-sum-exp over splits, with the inverse rotation of a
+// rotated V side); and the row map of chunked prefill run as decode rows.
 #include "kvq_decode.h"
 
 namespace kvq {
@@ -28,6 +28,14 @@ hipError_t sparse_hd(int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream
     case 256: return sparse_g<VF, 256>(g, a, nwg, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <int HD>
+hipError_t sparse_merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(uint32_t((uint64_t(a.num_seqs) * a.num_q_heads + 3) / 4)), block(256);
+  if (vrot) hipLaunchKernelGGL((sparse_v_merge_kernel<HD, true>), grid, block, 0, st, a, uint32_t(g));
+  else hipLaunchKernelGGL((sparse_v_merge_kernel<HD, false>), grid, block, 0, st, a, uint32_t(g));
+  return hipGetLastError();
 }
 
 template <int HD>
@@ -73,6 +81,15 @@ hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t 
     case KVQ_TURBO4: return sparse_hd<KVQ_TURBO4>(hd, g, a, nwg, st);
     case KVQ_TURBO8: return sparse_hd<KVQ_TURBO8>(hd, g, a, nwg, st);
     case KVQ_NVFP4: return sparse_hd<KVQ_NVFP4>(hd, g, a, nwg, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_sparse_v_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st) {
+  switch (hd) {
+    case 64: return sparse_merge_hd<64>(v_rotated, g, a, st);
+    case 128: return sparse_merge_hd<128>(v_rotated, g, a, st);
+    case 256: return sparse_merge_hd<256>(v_rotated, g, a, st);
     default: return hipErrorInvalidValue;
   }
 }

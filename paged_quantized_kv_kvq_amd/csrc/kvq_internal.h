@@ -31,7 +31,10 @@
 #define KVQ_MAX_SPARSE_SPLIT 2048  // positions per split on the sparse path (scores kept in LDS)
 #endif
 #ifndef KVQ_VWAVES
-#define KVQ_VWAVES 8             // waves of a sparse-V workgroup (one per sequence and kv head)
+#define KVQ_VWAVES 8             // waves of a sparse-V workgroup
+#endif
+#ifndef KVQ_V_TARGET_WORKGROUPS
+#define KVQ_V_TARGET_WORKGROUPS 512  // the sparse V pass splits each (sequence, kv head) into parts up to about this many
 #endif
 #ifndef KVQ_SCORE_DIMS
 #define KVQ_SCORE_DIMS 0         // dims per lane in the sparse score kernel (0: as the dense kernel)
@@ -131,6 +134,9 @@ __host__ __device__ constexpr uint32_t cand_segment_cap(uint32_t split_len) {
 // Words per candidate record: page id, position, G scores, padded to 16 bytes.
 __host__ __device__ constexpr uint32_t cand_record_words(uint32_t g) { return (2u + g + 3u) / 4u * 4u; }
 
+// Most workgroups the sparse V pass gives one (sequence, kv head).
+constexpr uint32_t kMaxVParts = 8;
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint8_t* k_cache;
@@ -144,6 +150,7 @@ struct DecodeArgs {
   int32_t* cnt;    // sparse: [S][Hkv][nsplit][KVQ_WAVES] candidate counts per segment
   uint32_t* crec;  // sparse: [S][Hkv][nsplit][KVQ_WAVES][seg_cap] candidate records
                    // of cand_record_words(G) words: page id, position, G log2 scores
+  float* vpart;    // sparse, vparts > 1: [S][Hkv][vparts][G][hd] the V parts' sums
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
@@ -154,6 +161,7 @@ struct DecodeArgs {
   uint32_t split_len;
   uint32_t nsplit;
   uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len)
+  uint32_t vparts;   // sparse: V-pass workgroups per (sequence, kv head)
   uint64_t k_stride;
   uint64_t k_data;
   uint64_t v_stride;
@@ -203,6 +211,8 @@ hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs&
 // ... and the merge of its key splits (a.nsplit > 1)
 hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
+// ... and the sum of its parts (a.vparts > 1), one workgroup per (sequence, kv head)
+hipError_t launch_sparse_v_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
 
 }  // namespace kvq
