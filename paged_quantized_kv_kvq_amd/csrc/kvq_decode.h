@@ -665,60 +665,71 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
 
 // ------------------------------------------------------------------ merge
 
-// Rotate an LDS row of HD values by the orthonormal WHT (brings a rotated V
-// side's output back).  All threads of the block take part.
-template <int HD>
-__device__ __forceinline__ void lds_wht(float* x, float scale) {
-  const int tid = threadIdx.x;
-  for (int h2 = 1; h2 < HD; h2 <<= 1) {
-    for (int k = tid; k < HD / 2; k += kWaves * kWave) {
-      const int lo = (k / h2) * 2 * h2 + (k % h2);
-      const float u = x[lo], v = x[lo + h2];
-      x[lo] = u + v;
-      x[lo + h2] = u - v;
+// Rotate a row of E * 64 values held by a wave (lane l holds elements l * E
+// ... l * E + E - 1) by the orthonormal WHT, which brings a rotated V side's
+// output back: butterflies inside the lane for the low index bits, then lane
+// exchanges, in the order of increasing stride; then x scale.
+template <int E>
+__device__ __forceinline__ void wave_wht(float (&x)[E], int lane, float scale) {
+#pragma unroll
+  for (int h2 = 1; h2 < E; h2 <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (!(i & h2)) {
+        const float p = x[i], q = x[i + h2];
+        x[i] = p + q;
+        x[i + h2] = p - q;
+      }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float o = __shfl_xor(x[i], m);
+      x[i] = (lane & m) ? o - x[i] : x[i] + o;
     }
-    __syncthreads();
-  }
-  for (int d = tid; d < HD; d += kWaves * kWave) x[d] *= scale;
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < E; ++i) x[i] *= scale;
 }
 
-// Log-sum-exp merge of the ns split partials of one output row: split k has
-// its (max, sum) pair at ml + k * mls and its unnormalized row at
-// part + k * ps.  M = max m_k, Z = sum_k 2^(m_k - M) l_k, and
-// o[d] = scale / Z * sum_k 2^(m_k - M) part_k[d]; splits with m_k = -inf
-// (nothing attended) add nothing.  A row of at most B splits is read in one
-// batch (one wait); a longer row walks its splits B at a time in three
-// loops, each batch's loads issued before any is used.  The additions keep
-// the split order, so the result does not depend on B or on the path.
-template <int HD, int B>
+// Log-sum-exp merge of the ns split partials of one output row, by one wave
+// (lane l: elements l * E ...): split k has its (max, sum) pair at ml + k *
+// mls and its unnormalized row at part + k * ps.  M = max m_k, Z = sum_k
+// 2^(m_k - M) l_k, and o[d] = scale / Z * sum_k 2^(m_k - M) part_k[d];
+// splits with m_k = -inf (nothing attended) add nothing.  A row of at most B
+// splits is read in one batch (one wait); a longer row walks its splits B at
+// a time in three loops, each batch's loads issued before any is used.  The
+// additions keep the split order, so the result does not depend on B or on
+// the path.
+template <int E, int B>
 __device__ __forceinline__ void merge_row(const float* ml, uint32_t mls, const float* part, uint32_t ps, int ns,
-                                          float scale, float* o) {
-  static_assert(HD <= kWaves * kWave, "one output element per thread");
+                                          float scale, float (&o)[E]) {
   if (ns <= B) {
-    // every split of the row in one batch: the thread requests all maxima,
-    // sums and its element of every row at once and waits once
-    const int d = threadIdx.x;
-    float m[B], l[B], v[B];
+    float m[B], l[B], v[B][E];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const bool in = u < ns;
       m[u] = in ? ml[uint64_t(u) * mls] : -INFINITY;
       l[u] = in ? ml[uint64_t(u) * mls + 1] : 0.0f;
-      v[u] = in && d < HD ? part[uint64_t(u) * ps + d] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[u][i] = in ? part[uint64_t(u) * ps + i] : 0.0f;
     }
     float M = -INFINITY;
 #pragma unroll
     for (int u = 0; u < B; ++u) M = fmaxf(M, m[u]);
-    float sum = 0.0f, acc = 0.0f;
+    float sum = 0.0f, acc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[i] = 0.0f;
 #pragma unroll
     for (int u = 0; u < B; ++u)
       if (m[u] > -INFINITY) {
         const float wgt = fast_exp2(m[u] - M);
         sum += wgt * l[u];
-        acc += wgt * v[u];
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] += wgt * v[u][i];
       }
-    if (d < HD) o[d] = acc * (sum > 0.0f ? scale / sum : 0.0f);
+    const float inv = sum > 0.0f ? scale / sum : 0.0f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) o[i] = acc[i] * inv;
     return;
   }
   float M = -INFINITY;
@@ -743,44 +754,53 @@ __device__ __forceinline__ void merge_row(const float* ml, uint32_t mls, const f
       if (m[u] > -INFINITY) sum += fast_exp2(m[u] - M) * l[u];
   }
   const float inv = sum > 0.0f ? scale / sum : 0.0f;
-  for (int d = threadIdx.x; d < HD; d += kWaves * kWave) {
-    float acc = 0.0f;
-    for (int k0 = 0; k0 < ns; k0 += B) {
-      float m[B], v[B];
+  float acc[E];
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const bool in = k0 + u < ns;
-        m[u] = in ? ml[uint64_t(k0 + u) * mls] : -INFINITY;
-        v[u] = in ? part[uint64_t(k0 + u) * ps + d] : 0.0f;
-      }
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
+  for (int k0 = 0; k0 < ns; k0 += B) {
+    float m[B], v[B][E];
 #pragma unroll
-      for (int u = 0; u < B; ++u)
-        if (m[u] > -INFINITY) acc += fast_exp2(m[u] - M) * v[u];
+    for (int u = 0; u < B; ++u) {
+      const bool in = k0 + u < ns;
+      m[u] = in ? ml[uint64_t(k0 + u) * mls] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[u][i] = in ? part[uint64_t(k0 + u) * ps + i] : 0.0f;
     }
-    o[d] = acc * inv;
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (m[u] > -INFINITY) {
+        const float wgt = fast_exp2(m[u] - M);
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[i] += wgt * v[u][i];
+      }
   }
+#pragma unroll
+  for (int i = 0; i < E; ++i) o[i] = acc[i] * inv;
 }
 
-// Dense path: one workgroup per (sequence, q head) combines the split
-// partials with log-sum-exp weights, then applies the fp8 V scale and the
-// inverse rotation.
+// Dense path: one wave per output row (sequence, q head), four rows per
+// workgroup, combines the split partials with log-sum-exp weights, then
+// applies the fp8 V scale and the inverse rotation.
 template <int HD, bool VROT>
-__global__ __launch_bounds__(kWaves * kWave) void merge_kernel(const DecodeArgs a, int G) {
-  __shared__ float o[HD];
-  const uint32_t hq = blockIdx.x % a.num_q_heads;
-  const uint32_t s = blockIdx.x / a.num_q_heads;
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a, int G) {
+  constexpr int E = HD / kWave;
+  const uint64_t rowq = uint64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);  // s * num_q_heads + q head
+  if (rowq >= uint64_t(a.num_seqs) * a.num_q_heads) return;
+  const uint32_t s = uint32_t(rowq / a.num_q_heads), hq = uint32_t(rowq % a.num_q_heads);
   const uint32_t g = hq / G, h = hq % G;
   if (a.vrow && a.vrow[2 * s] < 0) return;  // a prefill row without a query: no output row
   const SeqSpan sp = split_span(a, s, 0);
   const int span = sp.L - sp.j0;
   const int ns = span > 0 ? (span + int(a.split_len) - 1) / int(a.split_len) : 0;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const uint64_t row = ((uint64_t(s) * a.num_kv_heads + g) * a.nsplit) * G + h;  // split 0's row
-  merge_row<HD, 16>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD, uint32_t(G) * HD, ns, a.v_scale, o);
-  __syncthreads();
-  if constexpr (VROT) lds_wht<HD>(o, a.wht_scale);
-  float* dst = a.out + (uint64_t(row_query(a, s)) * a.num_q_heads + hq) * HD;
-  for (int d = tid; d < HD; d += kWaves * kWave) dst[d] = o[d];
+  float o[E];
+  merge_row<E, 16>(a.ml + row * 2, uint32_t(G) * 2, a.part + row * HD + lane * E, uint32_t(G) * HD, ns,
+                   a.v_scale, o);
+  if constexpr (VROT) wave_wht<E>(o, lane, a.wht_scale);
+  float* dst = a.out + (uint64_t(row_query(a, s)) * a.num_q_heads + hq) * HD + lane * E;
+#pragma unroll
+  for (int i = 0; i < E; ++i) dst[i] = o[i];
 }
 
 // ------------------------------------------------------------------ sparse V
@@ -1265,26 +1285,7 @@ __global__ __launch_bounds__(256) void sparse_v_merge_kernel(const DecodeArgs a,
       if (uint32_t(k) < a.vparts) x[i] += v[k][i];
     x[i] *= a.v_scale;
   }
-  if constexpr (VROT) {
-#pragma unroll
-    for (int h2 = 1; h2 < E; h2 <<= 1)
-#pragma unroll
-      for (int i = 0; i < E; ++i)
-        if (!(i & h2)) {
-          const float p = x[i], q = x[i + h2];
-          x[i] = p + q;
-          x[i + h2] = p - q;
-        }
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1)
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        const float o = __shfl_xor(x[i], m);
-        x[i] = (lane & m) ? o - x[i] : x[i] + o;
-      }
-#pragma unroll
-    for (int i = 0; i < E; ++i) x[i] *= a.wht_scale;
-  }
+  if constexpr (VROT) wave_wht<E>(x, lane, a.wht_scale);
   float* dst = a.out + row * HD + lane * E;
   if constexpr (E == 4) *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
   else if constexpr (E == 2) *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);

@@ -40,7 +40,7 @@ hipError_t sparse_merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st
 
 template <int HD>
 hipError_t merge_hd(bool vrot, int g, const DecodeArgs& a, hipStream_t st) {
-  const dim3 grid(a.num_seqs * a.num_q_heads), block(kWaves * kWave);
+  const dim3 grid(uint32_t((uint64_t(a.num_seqs) * a.num_q_heads + 3) / 4)), block(256);
   if (vrot) hipLaunchKernelGGL((merge_kernel<HD, true>), grid, block, 0, st, a, g);
   else hipLaunchKernelGGL((merge_kernel<HD, false>), grid, block, 0, st, a, g);
   return hipGetLastError();

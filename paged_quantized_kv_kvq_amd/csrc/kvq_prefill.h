@@ -742,26 +742,7 @@ __global__ __launch_bounds__(256) void tile_merge_kernel(const DecodeArgs a, int
   const float inv = a.v_scale / z;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] *= inv;
-  if constexpr (VROT) {
-#pragma unroll
-    for (int hb = 1; hb < DPL; hb <<= 1)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e)
-        if ((e & hb) == 0) {
-          const float u = o[e], v = o[e + hb];
-          o[e] = u + v;
-          o[e + hb] = u - v;
-        }
-#pragma unroll
-    for (int b = 1; b < kWave; b <<= 1)
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        const float p = __shfl_xor(o[e], b);
-        o[e] = (lane & b) ? p - o[e] : o[e] + p;
-      }
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] *= a.wht_scale;
-  }
+  if constexpr (VROT) wave_wht<DPL>(o, lane, a.wht_scale);
   float* dst = a.out + (uint64_t(pt.qrow0 + t) * a.num_q_heads + g * G + h) * HD + lane * DPL;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) dst[e] = o[e];
