@@ -144,7 +144,7 @@ bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
   uint32_t split_len, nsplit, seg_cap, vparts;
-  uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, bytes;
+  uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, off_order, bytes;
 };
 
 uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
@@ -181,7 +181,7 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   uint64_t off = 0;
   p.off_ml = off;
   off = up256(off + units * G * 2 * sizeof(float));
-  p.off_part = p.off_cnt = p.off_crec = p.off_vpart = 0;
+  p.off_part = p.off_cnt = p.off_crec = p.off_vpart = p.off_order = 0;
   p.seg_cap = 0;
   p.vparts = 1;
   if (!sparse) {
@@ -193,6 +193,8 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
     p.off_crec = off;
     off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
+    p.off_order = off;
+    off = up256(off + uint64_t(S) * p.nsplit * sizeof(uint32_t));
     // V-pass parts: as many as keep the launch within kVTargetWorkgroups and
     // every wave of the longest sequence with a segment of its own
     const uint64_t pairs = uint64_t(S) * nkv;
@@ -363,6 +365,11 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     a.crec = reinterpret_cast<uint32_t*>(ws + p.off_crec);
     if (p.vparts > 1) a.vpart = reinterpret_cast<float*>(ws + p.off_vpart);
+    // Longest units first (a sorting launch ahead of the score kernel) where
+    // lengths can differ: without a window.  With one, every sequence at least
+    // as long as the window has the same span, and the extra launch (about 4 us)
+    // costs more than it saves.
+    if (KVQ_SCORE_ORDER && sliding_window == 0) a.order = reinterpret_cast<uint32_t*>(ws + p.off_order);
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
@@ -392,7 +399,8 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   if (!sparse) {
     e = launch_dense(layout, a, hd, G, uint32_t(nwg), s);
   } else {
-    switch (kf) {
+    e = a.order ? launch_unit_order(a, s) : hipSuccess;
+    if (e == hipSuccess) switch (kf) {
       case KVQ_BF16: e = launch_scores_bf16(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_FP8_E4M3: e = launch_scores_fp8(int(hd), int(G), a, uint32_t(nwg), s); break;
       case KVQ_TURBO2: e = launch_scores_turbo2(int(hd), int(G), a, uint32_t(nwg), s); break;

@@ -349,7 +349,8 @@ struct Tile {
 // (sequence, split, kv head) of this workgroup; `per_seq` units per sequence.
 // Units are numbered split-major (unit = split * S + sequence): the units of
 // one split index rotate over the XCDs, and so do the (fewer) later splits
-// that only long sequences have.
+// that only long sequences have.  With a.order, the workgroups take the units
+// in its order instead (the sparse score kernel: longest first).
 //
 // MODE 1 keeps the kv heads of a unit on one XCD; MODE 0 numbers workgroups
 // unit-major (wg = unit * Hkv + head), so that with 8 kv heads each XCD takes
@@ -365,6 +366,7 @@ __device__ __forceinline__ Tile unit_tile(const DecodeArgs& a, uint32_t per_seq)
     head = blockIdx.x % a.num_kv_heads;
     t.valid = unit < a.num_seqs * per_seq;
   }
+  if (t.valid && a.order) unit = a.order[unit];
   t.g = head;
   t.s = unit % a.num_seqs;
   t.split = unit / a.num_seqs;

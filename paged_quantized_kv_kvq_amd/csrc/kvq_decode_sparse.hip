@@ -62,7 +62,57 @@ __global__ void prefill_rows_kernel(const int32_t* query_start, const int32_t* s
   vlen[v] = ok ? p + 1 : 0;
 }
 
+// The score kernel's units (split * S + sequence) in order of decreasing
+// length, bucketed by 16 positions (a counting sort in one workgroup; units
+// of one bucket in any order).  Started longest first, the units leave short
+// ones for the end of the launch, when fewer workgroups share the memory
+// bandwidth: a unit's workgroup streams its K rows at a limited rate, so a
+// long unit started late would stretch the launch.
+__global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a) {
+  constexpr int NB = kMaxSparseSplit / kChunk + 1;
+  constexpr int BPL = (NB + kWave - 1) / kWave;  // buckets per lane of the scan
+  __shared__ uint32_t cnt[BPL * kWave];
+  const uint32_t n = a.num_seqs * a.nsplit;
+  for (int b = threadIdx.x; b < BPL * kWave; b += 1024) cnt[b] = 0u;
+  __syncthreads();
+  auto bucket = [&](uint32_t u) {
+    const SeqSpan sp = split_span(a, u % a.num_seqs, u / a.num_seqs);
+    const int len = sp.pe > sp.pb ? sp.pe - sp.pb : 0;
+    return min((len + kChunk - 1) / kChunk, NB - 1);
+  };
+  for (uint32_t u = threadIdx.x; u < n; u += 1024) atomicAdd(&cnt[bucket(u)], 1u);
+  __syncthreads();
+  if (threadIdx.x < kWave) {  // first slot of each bucket, the longest bucket first: one wave's scan
+    const int lane = threadIdx.x;
+    uint32_t c[BPL], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {  // lane l takes buckets top - l * BPL - i (descending)
+      c[i] = cnt[BPL * kWave - 1 - (lane * BPL + i)];
+      sum += c[i];
+    }
+    uint32_t pre = sum;  // inclusive scan over the lanes
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t v = __shfl_up(pre, off);
+      if (lane >= off) pre += v;
+    }
+    uint32_t at = pre - sum;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      cnt[BPL * kWave - 1 - (lane * BPL + i)] = at;
+      at += c[i];
+    }
+  }
+  __syncthreads();
+  for (uint32_t u = threadIdx.x; u < n; u += 1024) a.order[atomicAdd(&cnt[bucket(u)], 1u)] = u;
+}
+
 }  // namespace
+
+hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_rows(const int32_t* query_start, const int32_t* seq_lens, uint32_t num_seqs,
                                uint32_t max_query_len, int32_t* vrow, int32_t* vlen, hipStream_t st) {

@@ -39,6 +39,9 @@
 #ifndef KVQ_SCORE_DIMS
 #define KVQ_SCORE_DIMS 0         // dims per lane in the sparse score kernel (0: as the dense kernel)
 #endif
+#ifndef KVQ_SCORE_ORDER
+#define KVQ_SCORE_ORDER 1        // 1: the sparse score kernel takes its units longest first
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
@@ -151,6 +154,7 @@ struct DecodeArgs {
   uint32_t* crec;  // sparse: [S][Hkv][nsplit][KVQ_WAVES][seg_cap] candidate records
                    // of cand_record_words(G) words: page id, position, G log2 scores
   float* vpart;    // sparse, vparts > 1: [S][Hkv][vparts][G][hd] the V parts' sums
+  uint32_t* order;  // sparse: [S * nsplit] units (split * S + sequence), longest first (null: in that order)
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
@@ -210,6 +214,8 @@ int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the merge of its key splits (a.nsplit > 1)
 hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
+// Sparse path: the order in which the score kernel takes its units (a.order)
+hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the sum of its parts (a.vparts > 1), one workgroup per (sequence, kv head)
 hipError_t launch_sparse_v_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
