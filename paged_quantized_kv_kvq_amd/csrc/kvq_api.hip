@@ -184,6 +184,8 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   p.off_part = p.off_cnt = p.off_crec = p.off_vpart = p.off_order = 0;
   p.seg_cap = 0;
   p.vparts = 1;
+  p.off_order = off;
+  off = up256(off + uint64_t(S) * p.nsplit * sizeof(uint32_t));
   if (!sparse) {
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
@@ -193,8 +195,6 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
     p.off_crec = off;
     off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
-    p.off_order = off;
-    off = up256(off + uint64_t(S) * p.nsplit * sizeof(uint32_t));
     // V-pass parts: as many as keep the launch within kVTargetWorkgroups and
     // every wave of the longest sequence with a segment of its own
     const uint64_t pairs = uint64_t(S) * nkv;
@@ -280,8 +280,8 @@ namespace {
 hipError_t launch_dense(const kvq_layout* layout, const DecodeArgs& a, uint32_t hd, uint32_t G, uint32_t nwg,
                         hipStream_t s) {
   const int vf = layout->v_format;
-  hipError_t e;
-  switch (layout->k_format) {
+  hipError_t e = a.order ? launch_unit_order(a, s) : hipSuccess;
+  if (e == hipSuccess) switch (layout->k_format) {
     case KVQ_BF16: e = launch_split_bf16(vf, int(hd), int(G), a, nwg, s); break;
     case KVQ_FP8_E4M3: e = launch_split_fp8(vf, int(hd), int(G), a, nwg, s); break;
     case KVQ_TURBO2: e = launch_split_turbo2(vf, int(hd), int(G), a, nwg, s); break;
@@ -291,6 +291,13 @@ hipError_t launch_dense(const kvq_layout* layout, const DecodeArgs& a, uint32_t 
     default: e = launch_split_turbo4(vf, int(hd), int(G), a, nwg, s); break;
   }
   return e == hipSuccess ? launch_merge(layout->v_rotated != 0, int(hd), int(G), a, s) : e;
+}
+
+// Dense-path options: a sequence's splits share its span equally, and
+// (KVQ_DENSE_ORDER) the split kernel takes its units longest first.
+void dense_options(DecodeArgs& a, uint8_t* ws, const Plan& p) {
+  a.eq_split = KVQ_EQ_SPLITS;
+  if (KVQ_DENSE_ORDER) a.order = reinterpret_cast<uint32_t*>(ws + p.off_order);
 }
 
 // The fields of a decode call's arguments that come from the layout and the
@@ -361,6 +368,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   a.ml = reinterpret_cast<float*>(ws + p.off_ml);
   if (!sparse) {
     a.part = reinterpret_cast<float*>(ws + p.off_part);
+    dense_options(a, ws, p);
   } else {
     a.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
     a.crec = reinterpret_cast<uint32_t*>(ws + p.off_crec);
@@ -538,6 +546,7 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   a.vrow = vrow;
   a.ml = reinterpret_cast<float*>(ws + base + p.off_ml);
   a.part = reinterpret_cast<float*>(ws + base + p.off_part);
+  dense_options(a, ws + base, p);
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = uint32_t(rows);
   a.num_q_heads = num_q_heads;

@@ -303,6 +303,10 @@ __device__ __forceinline__ uint32_t row_table(const DecodeArgs& a, uint32_t s) {
   return a.vrow ? uint32_t(a.vrow[2 * s]) : s;
 }
 
+// Positions [pb, pe) of a split of sequence s, whose window is [j0, L).  A
+// sequence's span takes n = ceil(span / split_len) splits: all full but the
+// last, or (a.eq_split) all of q = ceil(span / n) positions but the last,
+// where q >= n keeps the last split non-empty (otherwise the former).
 struct SeqSpan {
   int L, j0, pb, pe;
 };
@@ -311,8 +315,14 @@ __device__ __forceinline__ SeqSpan split_span(const DecodeArgs& a, uint32_t s, u
   SeqSpan r;
   r.L = a.seq_lens[s];
   r.j0 = (a.window != 0u && r.L > int(a.window)) ? r.L - int(a.window) : 0;
-  r.pb = r.j0 + int(split * a.split_len);
-  r.pe = min(r.L, r.pb + int(a.split_len));
+  int sl = int(a.split_len);
+  const int span = r.L - r.j0;
+  if (a.eq_split && span > 0) {
+    const int n = (span + sl - 1) / sl, q = (span + n - 1) / n;
+    if (q >= n) sl = q;  // n splits of q positions (q >= n: split n - 1 is not empty)
+  }
+  r.pb = r.j0 + int(split) * sl;
+  r.pe = min(r.L, r.pb + sl);
   return r;
 }
 

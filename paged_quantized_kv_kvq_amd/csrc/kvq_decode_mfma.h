@@ -202,6 +202,7 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
   const uint32_t g = hb * uint32_t(nw) + uint32_t(w);
   const uint32_t nkv = a.num_kv_heads;
   if (unit >= a.num_seqs * a.nsplit) return;
+  if (a.order) unit = a.order[unit];
   const uint32_t s = unit % a.num_seqs, split = unit / a.num_seqs;
   const SeqSpan sp = split_span(a, s, split);
   if (sp.pb >= sp.L) return;  // uniform over the workgroup

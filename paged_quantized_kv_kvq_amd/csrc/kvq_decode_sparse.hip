@@ -62,14 +62,14 @@ __global__ void prefill_rows_kernel(const int32_t* query_start, const int32_t* s
   vlen[v] = ok ? p + 1 : 0;
 }
 
-// The score kernel's units (split * S + sequence) in order of decreasing
+// A split kernel's units (split * S + sequence) in order of decreasing
 // length, bucketed by 16 positions (a counting sort in one workgroup; units
 // of one bucket in any order).  Started longest first, the units leave short
 // ones for the end of the launch, when fewer workgroups share the memory
 // bandwidth: a unit's workgroup streams its K rows at a limited rate, so a
 // long unit started late would stretch the launch.
 __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a) {
-  constexpr int NB = kMaxSparseSplit / kChunk + 1;
+  constexpr int NB = (KVQ_MAX_SPLIT > kMaxSparseSplit ? KVQ_MAX_SPLIT : kMaxSparseSplit) / kChunk + 1;
   constexpr int BPL = (NB + kWave - 1) / kWave;  // buckets per lane of the scan
   __shared__ uint32_t cnt[BPL * kWave];
   const uint32_t n = a.num_seqs * a.nsplit;

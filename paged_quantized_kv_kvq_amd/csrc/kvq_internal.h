@@ -42,6 +42,12 @@
 #ifndef KVQ_SCORE_ORDER
 #define KVQ_SCORE_ORDER 1        // 1: the sparse score kernel takes its units longest first
 #endif
+#ifndef KVQ_EQ_SPLITS
+#define KVQ_EQ_SPLITS 1          // 1: on the dense path a sequence's splits share its span equally
+#endif
+#ifndef KVQ_DENSE_ORDER
+#define KVQ_DENSE_ORDER 1        // 1: the dense split kernel takes its units longest first
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
@@ -154,7 +160,7 @@ struct DecodeArgs {
   uint32_t* crec;  // sparse: [S][Hkv][nsplit][KVQ_WAVES][seg_cap] candidate records
                    // of cand_record_words(G) words: page id, position, G log2 scores
   float* vpart;    // sparse, vparts > 1: [S][Hkv][vparts][G][hd] the V parts' sums
-  uint32_t* order;  // sparse: [S * nsplit] units (split * S + sequence), longest first (null: in that order)
+  uint32_t* order;  // [S * nsplit] units (split * S + sequence), longest first (null: in that order)
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
@@ -166,6 +172,7 @@ struct DecodeArgs {
   uint32_t nsplit;
   uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len)
   uint32_t vparts;   // sparse: V-pass workgroups per (sequence, kv head)
+  uint32_t eq_split;  // 1: a sequence's splits share its span equally (split_span)
   uint64_t k_stride;
   uint64_t k_data;
   uint64_t v_stride;
@@ -214,7 +221,7 @@ int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the merge of its key splits (a.nsplit > 1)
 hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
-// Sparse path: the order in which the score kernel takes its units (a.order)
+// The order in which a split kernel takes its units (a.order)
 hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the sum of its parts (a.vparts > 1), one workgroup per (sequence, kv head)
