@@ -19,6 +19,7 @@ constexpr uint32_t kMaxSparseSplitLen = KVQ_MAX_SPARSE_SPLIT;  // scores of a sp
 constexpr uint32_t kPagesPerSplit = KVQ_MAX_PAGES;             // page offsets of a split live in LDS
 constexpr uint64_t kTargetWorkgroups = KVQ_TARGET_WORKGROUPS;
 constexpr uint64_t kSparseTargetWorkgroups = KVQ_SPARSE_TARGET_WORKGROUPS;
+constexpr uint64_t kMinWorkgroups = KVQ_MIN_WORKGROUPS;
 constexpr uint64_t kVTargetWorkgroups = KVQ_V_TARGET_WORKGROUPS;
 // chunked prefill on the tile kernel: a grid of fewer workgroups than this
 // splits the tiles' key ranges (two per CU fill the GPU), into splits of at
@@ -152,10 +153,20 @@ uint64_t up256(uint64_t x) { return (x + 255) / 256 * 256; }
 // Page offsets a split may stage for the kernel that will run: the
 // matrix-core split kernel (KVQ_DENSE_MFMA, operands it takes, block_size
 // >= 16) by its K format, everything else the common limit.
+bool dense_on_mfma(const kvq_layout* layout, bool sparse) {
+  return KVQ_DENSE_MFMA && !sparse && layout->block_size >= 16 &&
+         mfma_split_ok(layout->k_format, layout->v_format, int(layout->head_dim));
+}
 uint32_t dense_pages(const kvq_layout* layout, bool sparse) {
-  const bool mfma = KVQ_DENSE_MFMA && !sparse && layout->block_size >= 16 &&
-                    mfma_split_ok(layout->k_format, layout->v_format, int(layout->head_dim));
-  return mfma ? uint32_t(dense_max_pages(layout->k_format)) : kPagesPerSplit;
+  return dense_on_mfma(layout, sparse) ? uint32_t(dense_max_pages(layout->k_format)) : kPagesPerSplit;
+}
+
+// Workgroups of the split kernel per (sequence, split): one per kv head, or
+// one per group of kv heads on the matrix-core kernel.
+uint32_t wg_per_unit(const kvq_layout* layout, uint32_t G, bool sparse) {
+  const uint32_t nkv = layout->num_kv_heads;
+  if (!dense_on_mfma(layout, sparse)) return nkv;
+  return nkv / mfma_unit_waves(nkv, uint32_t(mfma_waves_cap_of(layout->k_format, int(G))));
 }
 
 // Split length: the smallest power of two >= 256 giving about
@@ -164,8 +175,15 @@ uint32_t dense_pages(const kvq_layout* layout, bool sparse) {
 // kSparseTargetWorkgroups on the sparse path, whose score kernel runs a
 // workgroup per unit: two per CU, all resident at once, instead of 2048
 // shorter ones over several rounds (workload 4: score pass 50 -> 43 us).
+// On the dense path, then halved while the split kernel would get fewer than
+// kMinWorkgroups workgroups (wpu per (sequence, split)) over the longest
+// possible window (the table's reach; shorter sequences leave some empty):
+// the matrix-core kernel with eight kv heads per workgroup and 194 VGPRs
+// (turbo4 K, G = 8) holds one workgroup per CU, and 32 sequences of
+// 4096-16384 positions in splits of 2048 left CUs idle (0.348 -> 0.311 ms
+// with splits of 1024).
 Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
-               uint32_t window, bool sparse, uint32_t max_pages) {
+               uint32_t window, bool sparse, uint32_t max_pages, uint32_t wpu) {
   uint64_t span = uint64_t(max_blocks) * bs;
   if (window && window < span) span = window;
   const uint64_t work = span * S * nkv;
@@ -173,6 +191,7 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   const uint64_t target = sparse ? kSparseTargetWorkgroups : kTargetWorkgroups;
   while (sl < kMaxSplitLen && uint64_t(sl) * target < work) sl <<= 1;
   if (sparse && sl > kMaxSparseSplitLen) sl = kMaxSparseSplitLen;
+  while (!sparse && sl > 256 && uint64_t(S) * ((span + sl - 1) / sl) * wpu < kMinWorkgroups) sl >>= 1;
   while (sl > 16 && sl / bs + 2 > max_pages) sl >>= 1;
   Plan p;
   p.split_len = sl;
@@ -339,7 +358,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   if (uint64_t(max_blocks_per_seq) * layout->block_size >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const bool sparse = sparse_v_threshold > 0.0f;
   const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse,
-                           dense_pages(layout, sparse));
+                           dense_pages(layout, sparse), wg_per_unit(layout, G, sparse));
   // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
   const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
   const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv * p.vparts;
@@ -516,7 +535,7 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   const uint64_t rows = uint64_t(num_seqs) * max_query_len;
   if (rows >= (1ull << 31) || rows * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const Plan p = make_plan(uint32_t(rows), nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, false,
-                           dense_pages(layout, false));
+                           dense_pages(layout, false), wg_per_unit(layout, G, false));
   const uint64_t nwg = (rows * p.nsplit + 7) / 8 * 8 * nkv;
   if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const uint64_t off_vrow = 0, off_vlen = up256(rows * 2 * sizeof(int32_t));

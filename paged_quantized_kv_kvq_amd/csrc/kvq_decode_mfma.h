@@ -68,7 +68,8 @@ constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
 // pages to one workgroup.
 template <int KF, int G>
 constexpr int mfma_waves_cap() {
-  return (Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves;
+  static_assert(mfma_waves_cap_of(KF, G) == ((Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves), "host and device caps");
+  return mfma_waves_cap_of(KF, G);
 }
 
 template <int KF, int VF, int HD, int G>
@@ -669,12 +670,5 @@ inline uint64_t mfma_grid(uint64_t units, uint32_t hblocks) {
   return hblocks > 1 ? (units + 7) / 8 * 8 * hblocks : units;
 }
 
-// Workgroup shape of split_mfma_kernel: the largest divisor of the kv head
-// count up to `cap` (one wave per kv head).
-inline uint32_t mfma_unit_waves(uint32_t nkv, uint32_t cap = kUnitWaves) {
-  for (uint32_t d = cap; d > 1; --d)
-    if (nkv % d == 0) return d;
-  return 1;
-}
 
 }  // namespace kvq

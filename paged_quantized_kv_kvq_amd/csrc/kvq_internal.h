@@ -24,6 +24,9 @@
 #ifndef KVQ_MAX_SPLIT
 #define KVQ_MAX_SPLIT 4096       // longest decode split (positions)
 #endif
+#ifndef KVQ_MIN_WORKGROUPS
+#define KVQ_MIN_WORKGROUPS 1024  // ... and dense splits are shortened until the split kernel gets this many workgroups
+#endif
 #ifndef KVQ_SPARSE_TARGET_WORKGROUPS
 #define KVQ_SPARSE_TARGET_WORKGROUPS 512  // ... on the sparse path (its score kernel runs one workgroup per unit)
 #endif
@@ -69,6 +72,9 @@
 #ifndef KVQ_PREFILL_TILES
 #define KVQ_PREFILL_TILES 1      // 1: chunked prefill on the tile kernel (kvq_prefill.h) where block_size >= 4
 #endif
+#ifndef KVQ_PREFILL_TILE_DESC
+#define KVQ_PREFILL_TILE_DESC 1  // 1: a unit's prefill tiles start from the last (longest key range)
+#endif
 #ifndef KVQ_NT_LOADS
 #define KVQ_NT_LOADS 0           // 1: K/V chunk loads carry the non-temporal hint
 #endif
@@ -85,6 +91,16 @@ namespace kvq {
 // workloads 6 and 7).
 __host__ __device__ constexpr int dense_max_pages(int kf) {
   return kf == KVQ_BF16 || kf == KVQ_FP8_E4M3 ? KVQ_MFMA_MAX_PAGES : KVQ_MAX_PAGES;
+}
+
+// Most kv heads (waves) per workgroup of the matrix-core split kernel: four
+// with a grouped-scale K side and G <= 4, else eight; and the heads per
+// workgroup for nkv kv heads (the largest divisor of nkv up to that cap).
+__host__ __device__ constexpr int mfma_waves_cap_of(int kf, int g) { return (kf >= KVQ_TURBO2 && g <= 4) ? 4 : 8; }
+__host__ __device__ constexpr uint32_t mfma_unit_waves(uint32_t nkv, uint32_t cap) {
+  for (uint32_t d = cap; d > 1; --d)
+    if (nkv % d == 0) return d;
+  return 1;
 }
 
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {

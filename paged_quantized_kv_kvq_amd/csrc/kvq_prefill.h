@@ -271,7 +271,11 @@ __device__ __forceinline__ TileId tile_id(const DecodeArgs& a) {
   const uint32_t unit = (rest / a.ntiles) * 8u + x;
   const uint32_t sg = unit / a.nsplit;
   TileId t;
+#if KVQ_PREFILL_TILE_DESC
+  t.tile = a.ntiles - 1u - rest % a.ntiles;
+#else
   t.tile = rest % a.ntiles;
+#endif
   t.split = unit % a.nsplit;
   t.s = sg / a.num_kv_heads;
   t.g = sg % a.num_kv_heads;
