@@ -815,21 +815,30 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a, int G) {
   for (int i = 0; i < E; ++i) dst[i] = o[i];
 }
 
-// ------------------------------------------------------------------ sparse V
-
-template <int KF, int HD, int G>
-struct ScoreSmem {
-  PrologueSmem<KF, HD, G> pro;
-  float sc[kMaxSparseSplit * G];
-  float wm[kWaves][G];  // per-wave max and sum of exp2(score - max)
-  float wz[kWaves][G];
-};
-
+// LDS writes of a wave visible to its own lanes (no workgroup barrier)
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
+
+}  // namespace kvq
+
+#include "kvq_decode_mfma.h"
+
+namespace kvq {
+
+// ------------------------------------------------------------------ sparse V
+
+template <int KF, int HD, int G, bool MF>
+struct ScoreSmem {
+  PrologueSmem<KF, HD, G> pro;
+  float sc[kMaxSparseSplit * G];
+  float wm[kWaves][G];  // per-wave max and sum of exp2(score - max)
+  float wz[kWaves][G];
+  // matrix-core scores of a codebook K side: centroids of every pair of adjacent codes
+  f32x2 kpair[MF && Fmt<KF>::cb ? 1 << (2 * Fmt<KF>::bits) : 1];
+};
 
 // Scores of one split; stores the split's (max, sum) and the candidate
 // positions whose split-local weight exceeds thr * (1 - 1e-4).  The global
@@ -840,13 +849,22 @@ __device__ __forceinline__ void wave_lds_sync() {
 // reduces its own scores (max, sum), one barrier combines the waves, and each
 // wave then compacts its own candidates into its own segment of the record
 // list (no further barriers).  A record is (page id, position, G log2 scores).
-template <int KF, int HD, int G>
+//
+// MF: the K side is scored on the matrix cores as in the dense kernel (lane l
+// takes quarter l / 16 of position l % 16's row, v_mfma_f32_4x4x1_16b_f32
+// against the rotated query, a permlane reduce-scatter of the quarters), so
+// lane l ends with the score of head l / 16 at position l % 16; the rest is
+// the same.  The VALU version spent 62 instructions per (position, kv head)
+// on turbo3 K at head_dim 256 (code unpacking, lookups, four heads' FMAs,
+// 16-lane sums).
+template <int KF, int HD, int G, bool MF>
 __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs a) {
   constexpr int D = LaneDims<G>::score;
   using GE = Geo<HD, D>;
   constexpr int T = GE::T;
   constexpr int RS = cand_record_words(G);
-  __shared__ ScoreSmem<KF, HD, G> sm;
+  static_assert(!MF || (mfma_scores_ok(KF, HD, G) && kWaves * kChunk == 64), "matrix-core scores");
+  __shared__ ScoreSmem<KF, HD, G, MF> sm;
   const Tile tl = unit_tile<KVQ_TILE_SCORES>(a, a.nsplit);
   if (!tl.valid) return;
   const SeqSpan sp = split_span(a, tl.s, tl.split);
@@ -862,49 +880,125 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-  auto consume = [&](int c, const Raw<KF, D>(&kr)[GE::U], const bool(&ok)[GE::U]) {
-    float sc[GE::U][G];
-    chunk_scores<KF, HD, G, D>(q, sm.pro.kcen, qscale, kr, ok, sc);
-#pragma unroll
-    for (int u = 0; u < GE::U; ++u) {
-      const int j = c + u * GE::P + r;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        mloc[h] = fmaxf(mloc[h], sc[u][h]);
-        if (ok[u] && t == 0) sm.sc[(j - sp.pb) * G + h] = sc[u][h];
-      }
-    }
-  };
-  // The wave's chunks c, c + step, ...; chunk n sits in buffer n % NB and is
-  // loaded NB - 1 chunks ahead of its use.  Every load is issued inside the
-  // loop (the first NB - 1 uses are of empty, all-masked buffers), and the
-  // loop runs whole rounds of NB chunks with one exit at the bottom; a chunk
-  // past the end is all masked (its loads read the clamped last position, an
-  // L2 hit).  With one loop entry state and no early exit the compiler keeps
-  // NB - 1 chunks in flight across the back edge.
-  constexpr int NB = KVQ_SCORE_BUFS;
-  Raw<KF, D> kb[NB][GE::U];
-  Raw<KVQ_BF16, D> vdummy[GE::U];
-  bool ob[NB][GE::U];
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-#pragma unroll
-    for (int u = 0; u < GE::U; ++u) {
-      zero_raw(kb[i][u]);
-      ob[i][u] = false;
-    }
   constexpr int step = kWaves * kChunk;
   const int cs = sp.pb & ~(kChunk - 1);
-  int c = cs + w * kChunk;  // next chunk to load; the one used trails by NB - 1
-  if (c < sp.pe) {
-    const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;  // covers chunks + NB - 1 uses
-    for (int it = 0; it < rounds; ++it) {
+  if constexpr (MF) {
+    using MG = MfmaGeo<KF, KVQ_BF16, HD, 4>;
+    if constexpr (Fmt<KF>::cb) {
+      constexpr int BITS = Fmt<KF>::bits;
+      for (int e = tid; e < (1 << (2 * BITS)); e += kWaves * kWave) {
+        sm.kpair[e].x = a.cb.centroid[KF - 2][e & ((1 << BITS) - 1)];
+        sm.kpair[e].y = a.cb.centroid[KF - 2][e >> BITS];
+      }
+    }
+    // operand A: the rotated query of head lane % 4 over quarter lane / 16
+    float qf[MG::KQ];
+    {
+      const int h = lane & 3;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r,
-                                               kb[(i + NB - 1) % NB], vdummy, ob[(i + NB - 1) % NB]);
-        consume(c - (NB - 1) * step, kb[i], ob[i]);
-        c += step;
+      for (int k = 0; k < MG::KQ; ++k) qf[k] = h < G ? sm.pro.q[h][(lane >> 4) * MG::KQ + k] : 0.0f;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the chunk loop starts with only its own loads outstanding
+    __syncthreads();
+    const uint32_t nkv = a.num_kv_heads, bmask = (1u << a.log2_bs) - 1u;
+    const uint32_t koff = ((uint32_t(lane) & 15u) * nkv + tl.g) * MG::RBK + (uint32_t(lane) >> 4) * MG::KQB;
+    const uint32_t ksb = (uint32_t(lane) >> 4) * MG::KGQ * MG::KSG;
+    const uint32_t ksoff = a.k_data + ((uint32_t(lane) & 15u) * nkv + tl.g) * (HD / 16 * MG::KSG) + (ksb & ~3u);
+    const int ksh = int(ksb & 3u) * 8;
+    const int clast = (sp.pe - 1) & ~(kChunk - 1);
+    const int head = lane >> 4;
+    struct KChunk {
+      uint32_t k[MG::KQB / 4];
+      uint32_t ks[MG::KSW];
+    };
+    auto load = [&](int c, KChunk& ck) {
+      const int cl = min(c, clast);  // past the end: reread the last chunk (all masked)
+      const int pg = (cl >> a.log2_bs) - first;
+      const uint64_t kpage = uniform_u64(sm.pro.kbase[pg]);
+      const uint32_t within = uint32_t(cl) & bmask;
+      load_words<MG::KQB>(a.k_cache + kpage + uint64_t(within) * nkv * MG::RBK + koff, ck.k);
+#pragma unroll
+      for (int i = 0; i < MG::KSW; ++i)
+        ck.ks[i] = load4(a.k_cache + kpage + uint64_t(within) * nkv * (HD / 16 * MG::KSG) + ksoff + 4 * i);
+    };
+    auto consume = [&](int c, const KChunk& ck) {
+      const f32x4 d = mfma_qk_turbo<KF, HD>(ck.k, ck.ks, ksh, qf, sm.kpair);
+      const int j = c + (lane & 15);
+      const bool ok = j >= sp.pb && j < sp.pe;
+      // the swaps exchange values between the lanes of one position, which
+      // share the mask: a swap never reads an inactive lane
+      const float sc = ok ? quarter_sum(d) * qscale : -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (h == head) mloc[h] = fmaxf(mloc[h], sc);
+      if (ok && head < G) sm.sc[(j - sp.pb) * G + head] = sc;
+    };
+    // the wave's chunks c, c + step, ...; chunk n sits in buffer n % NB and
+    // is loaded NB - 1 chunks ahead of its use, as in the VALU loop below
+    constexpr int NB = KVQ_SCORE_BUFS;
+    KChunk kb[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+#pragma unroll
+      for (int k = 0; k < MG::KQB / 4; ++k) kb[i].k[k] = 0u;
+#pragma unroll
+      for (int k = 0; k < MG::KSW; ++k) kb[i].ks[k] = 0u;
+    }
+    int c = cs + w * kChunk;
+    if (c < sp.pe) {
+      const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;
+      for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          load(c, kb[(i + NB - 1) % NB]);
+          consume(c - (NB - 1) * step, kb[i]);
+          c += step;
+        }
+      }
+    }
+  } else {
+    auto consume = [&](int c, const Raw<KF, D>(&kr)[GE::U], const bool(&ok)[GE::U]) {
+      float sc[GE::U][G];
+      chunk_scores<KF, HD, G, D>(q, sm.pro.kcen, qscale, kr, ok, sc);
+#pragma unroll
+      for (int u = 0; u < GE::U; ++u) {
+        const int j = c + u * GE::P + r;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          mloc[h] = fmaxf(mloc[h], sc[u][h]);
+          if (ok[u] && t == 0) sm.sc[(j - sp.pb) * G + h] = sc[u][h];
+        }
+      }
+    };
+    // The wave's chunks c, c + step, ...; chunk n sits in buffer n % NB and is
+    // loaded NB - 1 chunks ahead of its use.  Every load is issued inside the
+    // loop (the first NB - 1 uses are of empty, all-masked buffers), and the
+    // loop runs whole rounds of NB chunks with one exit at the bottom; a chunk
+    // past the end is all masked (its loads read the clamped last position, an
+    // L2 hit).  With one loop entry state and no early exit the compiler keeps
+    // NB - 1 chunks in flight across the back edge.
+    constexpr int NB = KVQ_SCORE_BUFS;
+    Raw<KF, D> kb[NB][GE::U];
+    Raw<KVQ_BF16, D> vdummy[GE::U];
+    bool ob[NB][GE::U];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int u = 0; u < GE::U; ++u) {
+        zero_raw(kb[i][u]);
+        ob[i][u] = false;
+      }
+    int c = cs + w * kChunk;  // next chunk to load; the one used trails by NB - 1
+    if (c < sp.pe) {
+      const int rounds = ((sp.pe - 1 - c) / step + 2 * NB - 1) / NB;  // covers chunks + NB - 1 uses
+      for (int it = 0; it < rounds; ++it) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          load_chunk<KF, KVQ_BF16, HD, G, D, false>(a, sm.pro, first, c, sp.pb, sp.pe, tl.g, t, r,
+                                                 kb[(i + NB - 1) % NB], vdummy, ob[(i + NB - 1) % NB]);
+          consume(c - (NB - 1) * step, kb[i], ob[i]);
+          c += step;
+        }
       }
     }
   }
@@ -1465,11 +1559,6 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   sparse_v_finish<VF, HD, G>(a, sm, acc, s, g, part);
 }
 
-}  // namespace kvq
-
-#include "kvq_decode_mfma.h"
-
-namespace kvq {
 
 // ------------------------------------------------------------------ dispatch
 
@@ -1525,14 +1614,27 @@ hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t n
   }
 }
 
+// The score kernel of a (K, head_dim, G) instance: the matrix-core scores
+// where they apply (block_size >= 16), else the VALU ones.
+template <int KF, int HD, int G>
+void launch_scores_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
+  const dim3 grid(nwg), block(kWaves * kWave);
+  if constexpr (KVQ_SCORE_MFMA && mfma_scores_ok(KF, HD, G)) {
+    if (a.log2_bs >= 4) {
+      hipLaunchKernelGGL((scores_kernel<KF, HD, G, true>), grid, block, 0, st, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((scores_kernel<KF, HD, G, false>), grid, block, 0, st, a);
+}
+
 template <int KF, int HD>
 hipError_t launch_scores_g(int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  const dim3 grid(nwg), block(kWaves * kWave);
   switch (g) {
-    case 1: hipLaunchKernelGGL((scores_kernel<KF, HD, 1>), grid, block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((scores_kernel<KF, HD, 2>), grid, block, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((scores_kernel<KF, HD, 4>), grid, block, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((scores_kernel<KF, HD, 8>), grid, block, 0, st, a); break;
+    case 1: launch_scores_one<KF, HD, 1>(a, nwg, st); break;
+    case 2: launch_scores_one<KF, HD, 2>(a, nwg, st); break;
+    case 4: launch_scores_one<KF, HD, 4>(a, nwg, st); break;
+    case 8: launch_scores_one<KF, HD, 8>(a, nwg, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

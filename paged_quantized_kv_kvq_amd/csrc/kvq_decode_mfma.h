@@ -177,6 +177,77 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
   if constexpr (N % 8 == 4) w[o / 4] = load4(p + o);
 }
 
+// Q.K^T partials of a grouped-scale K side on the matrix cores: lane l holds
+// the raw bytes of its quarter (lane / 16) of position l % 16's row (k), the
+// words that hold the quarter's group scales (ks, the first group at bit
+// ksh) and operand A, the rotated query of head l % 4 over the quarter's dims
+// (qf).  Returns the four heads' partial scores of position l % 16 over the
+// quarter (the MFMA 4x4 layout).  One accumulator per scale group, the groups
+// interleaved for independent chains; each group's scale multiplies its sum
+// once.
+template <int KF, int HD>
+__device__ __forceinline__ f32x4 mfma_qk_turbo(const uint32_t* k, const uint32_t* ks, int ksh, const float* qf,
+                                               const f32x2* kpair) {
+  using MG = MfmaGeo<KF, KVQ_BF16, HD, 4>;
+  f32x4 dg[MG::KGQ];
+#pragma unroll
+  for (int gq = 0; gq < MG::KGQ; ++gq) dg[gq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if constexpr (!Fmt<KF>::cb) {
+    // turbo8: E4M3 values of the quarter
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // word i of each group's 16 bytes
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) {
+        const uint32_t wd = k[gq * 4 + i];
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), true);
+        const int d0 = gq * 16 + 4 * i;
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[d0], lo.x, dg[gq], 0, 0, 0);
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[d0 + 1], lo.y, dg[gq], 0, 0, 0);
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[d0 + 2], hi.x, dg[gq], 0, 0, 0);
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[d0 + 3], hi.y, dg[gq], 0, 0, 0);
+      }
+    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int gq = 0; gq < MG::KGQ; ++gq) {
+      const int bit = ksh + 16 * gq;  // BF16 scale of group gq
+      const float sc = __uint_as_float(((ks[bit / 32] >> (bit % 32)) & 0xFFFFu) << 16);
+      d += sc * dg[gq];
+    }
+    return d;
+  } else {
+    // code pair p (dims 2p, 2p + 1 of the quarter) sits at bits 2 BITS p of
+    // the quarter's little-endian bit stream, looked up as a pair of centroids
+    constexpr int BITS = Fmt<KF>::bits, PB = 2 * BITS, PPG = 8;  // pairs per 16-dim group
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp)
+#pragma unroll
+      for (int gq = 0; gq < MG::KGQ; ++gq) {
+        const int p = gq * PPG + pp;
+        const int bit = p * PB, wd = bit / 32, sh = bit % 32;
+        uint32_t field;
+        if constexpr (32 % PB == 0) {
+          field = (k[wd] >> sh) & ((1u << PB) - 1u);
+        } else {
+          const uint32_t hi = wd + 1 < MG::KQB / 4 ? k[wd + 1] : 0u;
+          field = uint32_t((uint64_t(hi) << 32 | k[wd]) >> sh) & ((1u << PB) - 1u);
+        }
+        const f32x2 cv = kpair[field];
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p], cv.x, dg[gq], 0, 0, 0);
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p + 1], cv.y, dg[gq], 0, 0, 0);
+      }
+    // the groups' E4M3 scales (of this lane's position) on the group sums
+    f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int gq = 0; gq < MG::KGQ; ++gq) {
+      const int bit = ksh + 8 * gq;
+      const float sc = __builtin_amdgcn_cvt_f32_fp8(int(ks[bit / 32] >> (bit % 32)), 0);
+      d += sc * dg[gq];
+    }
+    return d;
+  }
+}
+
 // One query per sequence; the rows of a wave are the G query heads of its
 // kv head.
 template <int KF, int VF, int HD, int G>
@@ -376,66 +447,8 @@ __global__ __launch_bounds__(kUnitWaves * kWave) void split_mfma_kernel(const De
 #pragma unroll
       for (int k = 0; k < MG::KSTEPS; ++k) d = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(qa[hg][k], kb[k], d, 0, 0, 0);
       return d;
-    } else if constexpr (!Fmt<KF>::cb) {
-      // turbo8: E4M3 values of the quarter, one accumulator per scale group
-      f32x4 dg[MG::KGQ];
-#pragma unroll
-      for (int gq = 0; gq < MG::KGQ; ++gq) dg[gq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)  // word i of each group's 16 bytes
-#pragma unroll
-        for (int gq = 0; gq < MG::KGQ; ++gq) {
-          const uint32_t wd = ck.k[gq * 4 + i];
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(int(wd), true);
-          const int d0 = gq * 16 + 4 * i;
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0], lo.x, dg[gq], 0, 0, 0);
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 1], lo.y, dg[gq], 0, 0, 0);
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 2], hi.x, dg[gq], 0, 0, 0);
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][d0 + 3], hi.y, dg[gq], 0, 0, 0);
-        }
-      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int gq = 0; gq < MG::KGQ; ++gq) {
-        const int bit = ksh + 16 * gq;  // BF16 scale of group gq
-        const float sc = __uint_as_float(((ck.ks[bit / 32] >> (bit % 32)) & 0xFFFFu) << 16);
-        d += sc * dg[gq];
-      }
-      return d;
     } else {
-      // code pair p (dims 2p, 2p + 1 of the quarter) sits at bits 2 BITS p of
-      // the quarter's little-endian bit stream; one accumulator per scale
-      // group, the groups interleaved for independent chains
-      constexpr int BITS = Fmt<KF>::bits, PB = 2 * BITS, PPG = 8;  // pairs per 16-dim group
-      f32x4 dg[MG::KGQ];
-#pragma unroll
-      for (int gq = 0; gq < MG::KGQ; ++gq) dg[gq] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int pp = 0; pp < PPG; ++pp)
-#pragma unroll
-        for (int gq = 0; gq < MG::KGQ; ++gq) {
-          const int p = gq * PPG + pp;
-          const int bit = p * PB, wd = bit / 32, sh = bit % 32;
-          uint32_t field;
-          if constexpr (32 % PB == 0) {
-            field = (ck.k[wd] >> sh) & ((1u << PB) - 1u);
-          } else {
-            const uint32_t hi = wd + 1 < MG::KQB / 4 ? ck.k[wd + 1] : 0u;
-            field = uint32_t((uint64_t(hi) << 32 | ck.k[wd]) >> sh) & ((1u << PB) - 1u);
-          }
-          const f32x2 cv = sm.kpair[field];
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][2 * p], cv.x, dg[gq], 0, 0, 0);
-          dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[hg][2 * p + 1], cv.y, dg[gq], 0, 0, 0);
-        }
-      // the groups' E4M3 scales (of this lane's position) on the group sums
-      f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int gq = 0; gq < MG::KGQ; ++gq) {
-        const int bit = ksh + 8 * gq;
-        const float sc = __builtin_amdgcn_cvt_f32_fp8(int(ck.ks[bit / 32] >> (bit % 32)), 0);
-        d += sc * dg[gq];
-      }
-      return d;
+      return mfma_qk_turbo<KF, HD>(ck.k, ck.ks, ksh, qf[hg], sm.kpair);
     }
   };
 

@@ -51,6 +51,9 @@
 #ifndef KVQ_DENSE_ORDER
 #define KVQ_DENSE_ORDER 1        // 1: the dense split kernel takes its units longest first
 #endif
+#ifndef KVQ_SCORE_MFMA
+#define KVQ_SCORE_MFMA 1         // 1: the sparse score kernel scores a grouped-scale K side on the matrix cores
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
@@ -101,6 +104,14 @@ __host__ __device__ constexpr uint32_t mfma_unit_waves(uint32_t nkv, uint32_t ca
   for (uint32_t d = cap; d > 1; --d)
     if (nkv % d == 0) return d;
   return 1;
+}
+
+// The sparse score kernel scores a grouped-scale K side on the matrix cores
+// (the dense kernel's turbo-K operand layout) where its quarter rows fit and
+// G <= 4, and block_size >= 16 (a 16-position chunk in one page).
+__host__ __device__ constexpr bool mfma_scores_ok(int kf, int hd, int g) {
+  const int kqb = hd * (kf == KVQ_NVFP4 ? 4 : kf) / 32;  // K bytes per lane and chunk (a quarter of a row)
+  return kf >= KVQ_TURBO2 && g <= 4 && kqb % 4 == 0 && kqb <= 32 && hd / 4 >= 16;
 }
 
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
