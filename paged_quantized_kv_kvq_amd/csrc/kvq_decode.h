@@ -199,6 +199,32 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rotate a row of E * 64 values held by a wave (lane l holds elements l * E
+// ... l * E + E - 1) by the orthonormal WHT, which brings a rotated V side's
+// output back: butterflies inside the lane for the low index bits, then lane
+// exchanges, in the order of increasing stride; then x scale.
+template <int E>
+__device__ __forceinline__ void wave_wht(float (&x)[E], int lane, float scale) {
+#pragma unroll
+  for (int h2 = 1; h2 < E; h2 <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (!(i & h2)) {
+        const float p = x[i], q = x[i + h2];
+        x[i] = p + q;
+        x[i + h2] = p - q;
+      }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const float o = __shfl_xor(x[i], m);
+      x[i] = (lane & m) ? o - x[i] : x[i] + o;
+    }
+#pragma unroll
+  for (int i = 0; i < E; ++i) x[i] *= scale;
+}
+
 // Query registers of one lane: packed bf16 pairs (bf16 / fp8 K) or the rotated
 // fp32 query (turbo K), for the lane's D dims of each of the G heads.
 template <int KF, int D, int G>
@@ -415,20 +441,47 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
       }
     }
   }
-  if (tid < 16) {
-    if constexpr (Fmt<KF>::cb) sm.kcen[tid] = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid] : 0.0f;
-    if constexpr (Fmt<VF>::cb) sm.vcen[tid] = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid] : 0.0f;
-  }
-  {
-    const int first = pb >> a.log2_bs;
-    const int n = ((pe - 1) >> a.log2_bs) - first + 1;
-    const int32_t* bt = a.block_tables + uint64_t(row_table(a, s)) * a.max_blocks + first;
-    for (int i = tid; i < n; i += kWaves * kWave) {
-      const uint64_t page = uint64_t(uint32_t(bt[i]));
-      sm.kbase[i] = page * a.k_stride;
-      sm.vbase[i] = page * a.v_stride;
-      sm.page[i] = uint32_t(page);
+  // The page ids of the split (one per thread), the turbo K query rows (in
+  // 16-byte pieces, rotated in LDS below) and the centroids are all requested
+  // before any is stored: one round trip.
+  static_assert(kMaxPages <= kWaves * kWave, "a page id per thread");
+  const int first = pb >> a.log2_bs;
+  const int n = ((pe - 1) >> a.log2_bs) - first + 1;
+  const int32_t* bt = a.block_tables + uint64_t(row_table(a, s)) * a.max_blocks + first;
+  const uint32_t page = tid < n ? uint32_t(bt[tid]) : 0u;
+  // (turbo K: query row h goes to wave h % kWaves, lane l taking elements
+  // l * QE ... l * QE + QE - 1)
+  const int lane = tid & 63, wq = tid >> 6;
+  constexpr int QE = HD / kWave, QR = Fmt<KF>::turbo ? (G + kWaves - 1) / kWaves : 1;
+  float qx[QR][QE];
+  if constexpr (Fmt<KF>::turbo) {
+#pragma unroll
+    for (int k = 0; k < QR; ++k) {
+      const int h = wq + k * kWaves;
+      const uint16_t* src = qg + (h < G ? h : 0) * HD + lane * QE;
+      if constexpr (QE == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        qx[k][0] = __uint_as_float(v.x << 16); qx[k][1] = __uint_as_float(v.x & 0xFFFF0000u);
+        qx[k][2] = __uint_as_float(v.y << 16); qx[k][3] = __uint_as_float(v.y & 0xFFFF0000u);
+      } else if constexpr (QE == 2) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(src);
+        qx[k][0] = __uint_as_float(v << 16); qx[k][1] = __uint_as_float(v & 0xFFFF0000u);
+      } else {
+        qx[k][0] = bf16_bits_to_float(*src);
+      }
     }
+  }
+  float kc = 0.0f, vc = 0.0f;
+  if constexpr (Fmt<KF>::cb) kc = tid < (1 << Fmt<KF>::bits) ? a.cb.centroid[KF - 2][tid & 15] : 0.0f;
+  if constexpr (Fmt<VF>::cb) vc = tid < (1 << Fmt<VF>::bits) ? a.cb.centroid[VF - 2][tid & 15] : 0.0f;
+  if (tid < 16) {
+    if constexpr (Fmt<KF>::cb) sm.kcen[tid] = kc;
+    if constexpr (Fmt<VF>::cb) sm.vcen[tid] = vc;
+  }
+  if (tid < n) {
+    sm.kbase[tid] = uint64_t(page) * a.k_stride;
+    sm.vbase[tid] = uint64_t(page) * a.v_stride;
+    sm.page[tid] = page;
   }
   if constexpr (!Fmt<KF>::turbo) {
     // Every load so far is complete before the chunk loop starts: the loop
@@ -437,22 +490,19 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   } else {
-    for (int i = tid; i < G * HD; i += kWaves * kWave) sm.q[i / HD][i % HD] = bf16_bits_to_float(qg[i]);
-    __syncthreads();
-    // unnormalized WHT of every q row (1/sqrt(d) goes into the score scale);
-    // an NVFP4 K side is scored against the query as it is
-    if constexpr (Fmt<KF>::rot) {
-      for (int h2 = 1; h2 < HD; h2 <<= 1) {
-        for (int i = tid; i < G * HD / 2; i += kWaves * kWave) {
-          const int hh = i / (HD / 2), k = i % (HD / 2);
-          const int lo = (k / h2) * 2 * h2 + (k % h2);
-          const float x = sm.q[hh][lo], y = sm.q[hh][lo + h2];
-          sm.q[hh][lo] = x + y;
-          sm.q[hh][lo + h2] = x - y;
-        }
-        __syncthreads();
+    // unnormalized WHT of every query row in its wave's registers (1/sqrt(d)
+    // goes into the score scale); an NVFP4 K side is scored against the query
+    // as it is
+#pragma unroll
+    for (int k = 0; k < QR; ++k) {
+      const int h = wq + k * kWaves;
+      if constexpr (Fmt<KF>::rot) wave_wht<QE>(qx[k], lane, 1.0f);
+      if (h < G) {
+#pragma unroll
+        for (int i = 0; i < QE; ++i) sm.q[h][lane * QE + i] = qx[k][i];
       }
     }
+    __syncthreads();
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -677,32 +727,6 @@ __global__ __launch_bounds__(kWaves * kWave) void split_kernel(const DecodeArgs 
 
 // ------------------------------------------------------------------ merge
 
-// Rotate a row of E * 64 values held by a wave (lane l holds elements l * E
-// ... l * E + E - 1) by the orthonormal WHT, which brings a rotated V side's
-// output back: butterflies inside the lane for the low index bits, then lane
-// exchanges, in the order of increasing stride; then x scale.
-template <int E>
-__device__ __forceinline__ void wave_wht(float (&x)[E], int lane, float scale) {
-#pragma unroll
-  for (int h2 = 1; h2 < E; h2 <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; ++i)
-      if (!(i & h2)) {
-        const float p = x[i], q = x[i + h2];
-        x[i] = p + q;
-        x[i + h2] = p - q;
-      }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1)
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const float o = __shfl_xor(x[i], m);
-      x[i] = (lane & m) ? o - x[i] : x[i] + o;
-    }
-#pragma unroll
-  for (int i = 0; i < E; ++i) x[i] *= scale;
-}
-
 // Log-sum-exp merge of the ns split partials of one output row, by one wave
 // (lane l: elements l * E ...): split k has its (max, sum) pair at ml + k *
 // mls and its unnormalized row at part + k * ps.  M = max m_k, Z = sum_k
@@ -884,11 +908,11 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   const int cs = sp.pb & ~(kChunk - 1);
   if constexpr (MF) {
     using MG = MfmaGeo<KF, KVQ_BF16, HD, 4>;
-    if constexpr (Fmt<KF>::cb) {
+    if constexpr (Fmt<KF>::cb) {  // from the centroids the prologue put in LDS
       constexpr int BITS = Fmt<KF>::bits;
       for (int e = tid; e < (1 << (2 * BITS)); e += kWaves * kWave) {
-        sm.kpair[e].x = a.cb.centroid[KF - 2][e & ((1 << BITS) - 1)];
-        sm.kpair[e].y = a.cb.centroid[KF - 2][e >> BITS];
+        sm.kpair[e].x = sm.pro.kcen[e & ((1 << BITS) - 1)];
+        sm.kpair[e].y = sm.pro.kcen[e >> BITS];
       }
     }
     // operand A: the rotated query of head lane % 4 over quarter lane / 16
@@ -935,7 +959,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
     };
     // the wave's chunks c, c + step, ...; chunk n sits in buffer n % NB and
     // is loaded NB - 1 chunks ahead of its use, as in the VALU loop below
-    constexpr int NB = KVQ_SCORE_BUFS;
+    constexpr int NB = KVQ_SCORE_MFMA_BUFS;
     KChunk kb[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {

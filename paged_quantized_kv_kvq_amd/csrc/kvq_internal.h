@@ -54,6 +54,9 @@
 #ifndef KVQ_SCORE_MFMA
 #define KVQ_SCORE_MFMA 1         // 1: the sparse score kernel scores a grouped-scale K side on the matrix cores
 #endif
+#ifndef KVQ_SCORE_MFMA_BUFS
+#define KVQ_SCORE_MFMA_BUFS 2    // ... its chunk buffers per wave
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
