@@ -946,7 +946,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
         ck.ks[i] = load4(a.k_cache + kpage + uint64_t(within) * nkv * (HD / 16 * MG::KSG) + ksoff + 4 * i);
     };
     auto consume = [&](int c, const KChunk& ck) {
-      const f32x4 d = mfma_qk_turbo<KF, HD>(ck.k, ck.ks, ksh, qf, sm.kpair);
+      const f32x4 d = mfma_qk_turbo<KF, HD, KVQ_SCORE_LOOKUPS>(ck.k, ck.ks, ksh, qf, sm.kpair);
       const int j = c + (lane & 15);
       const bool ok = j >= sp.pb && j < sp.pe;
       // the swaps exchange values between the lanes of one position, which

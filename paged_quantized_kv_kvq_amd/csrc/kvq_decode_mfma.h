@@ -185,7 +185,11 @@ __device__ __forceinline__ void load_words(const uint8_t* p, uint32_t* w) {
 // quarter (the MFMA 4x4 layout).  One accumulator per scale group, the groups
 // interleaved for independent chains; each group's scale multiplies its sum
 // once.
-template <int KF, int HD>
+//
+// Codebook K sides look their code pairs up in LDS NL at a time, each batch
+// requested before its products, so that NL lookups share one wait (the
+// additions into each group's accumulator keep the same order for any NL).
+template <int KF, int HD, int NL = MfmaGeo<KF, KVQ_BF16, HD, 4>::KGQ>
 __device__ __forceinline__ f32x4 mfma_qk_turbo(const uint32_t* k, const uint32_t* ks, int ksh, const float* qf,
                                                const f32x2* kpair) {
   using MG = MfmaGeo<KF, KVQ_BF16, HD, 4>;
@@ -219,11 +223,15 @@ __device__ __forceinline__ f32x4 mfma_qk_turbo(const uint32_t* k, const uint32_t
     // code pair p (dims 2p, 2p + 1 of the quarter) sits at bits 2 BITS p of
     // the quarter's little-endian bit stream, looked up as a pair of centroids
     constexpr int BITS = Fmt<KF>::bits, PB = 2 * BITS, PPG = 8;  // pairs per 16-dim group
+    constexpr int NP = MG::KGQ * PPG;  // pairs of the quarter, visited q = pp * KGQ + gq
+    constexpr int NB = NL < NP ? NL : NP;
+    static_assert(NP % NB == 0, "whole batches");
 #pragma unroll
-    for (int pp = 0; pp < PPG; ++pp)
+    for (int q0 = 0; q0 < NP; q0 += NB) {
+      f32x2 cv[NB];
 #pragma unroll
-      for (int gq = 0; gq < MG::KGQ; ++gq) {
-        const int p = gq * PPG + pp;
+      for (int b = 0; b < NB; ++b) {
+        const int q = q0 + b, p = (q % MG::KGQ) * PPG + q / MG::KGQ;
         const int bit = p * PB, wd = bit / 32, sh = bit % 32;
         uint32_t field;
         if constexpr (32 % PB == 0) {
@@ -232,10 +240,15 @@ __device__ __forceinline__ f32x4 mfma_qk_turbo(const uint32_t* k, const uint32_t
           const uint32_t hi = wd + 1 < MG::KQB / 4 ? k[wd + 1] : 0u;
           field = uint32_t((uint64_t(hi) << 32 | k[wd]) >> sh) & ((1u << PB) - 1u);
         }
-        const f32x2 cv = kpair[field];
-        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p], cv.x, dg[gq], 0, 0, 0);
-        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p + 1], cv.y, dg[gq], 0, 0, 0);
+        cv[b] = kpair[field];
       }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int q = q0 + b, gq = q % MG::KGQ, p = gq * PPG + q / MG::KGQ;
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p], cv[b].x, dg[gq], 0, 0, 0);
+        dg[gq] = __builtin_amdgcn_mfma_f32_4x4x1f32(qf[2 * p + 1], cv[b].y, dg[gq], 0, 0, 0);
+      }
+    }
     // the groups' E4M3 scales (of this lane's position) on the group sums
     f32x4 d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll

@@ -57,6 +57,9 @@
 #ifndef KVQ_SCORE_MFMA_BUFS
 #define KVQ_SCORE_MFMA_BUFS 2    // ... its chunk buffers per wave
 #endif
+#ifndef KVQ_SCORE_LOOKUPS
+#define KVQ_SCORE_LOOKUPS 16     // ... its code-pair lookups requested at once
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
