@@ -144,7 +144,7 @@ int check_layout(const kvq_layout* l) {
 bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
 
 struct Plan {
-  uint32_t split_len, nsplit, seg_cap, vparts;
+  uint32_t split_len, nsplit, seg_cap, segs, vparts;
   uint64_t off_part, off_ml, off_cnt, off_crec, off_vpart, off_order, bytes;
 };
 
@@ -183,7 +183,7 @@ uint32_t wg_per_unit(const kvq_layout* layout, uint32_t G, bool sparse) {
 // 4096-16384 positions in splits of 2048 left CUs idle (0.348 -> 0.311 ms
 // with splits of 1024).
 Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
-               uint32_t window, bool sparse, uint32_t max_pages, uint32_t wpu) {
+               uint32_t window, bool sparse, uint32_t max_pages, uint32_t wpu, uint32_t segs) {
   uint64_t span = uint64_t(max_blocks) * bs;
   if (window && window < span) span = window;
   const uint64_t work = span * S * nkv;
@@ -202,6 +202,7 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
   off = up256(off + units * G * 2 * sizeof(float));
   p.off_part = p.off_cnt = p.off_crec = p.off_vpart = p.off_order = 0;
   p.seg_cap = 0;
+  p.segs = segs;
   p.vparts = 1;
   p.off_order = off;
   off = up256(off + uint64_t(S) * p.nsplit * sizeof(uint32_t));
@@ -209,16 +210,16 @@ Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_b
     p.off_part = off;
     off = up256(off + units * G * hd * sizeof(float));
   } else {
-    p.seg_cap = cand_segment_cap(sl);
+    p.seg_cap = cand_segment_cap(sl, segs);
     p.off_cnt = off;
-    off = up256(off + units * KVQ_WAVES * sizeof(int32_t));
+    off = up256(off + units * segs * sizeof(int32_t));
     p.off_crec = off;
-    off = up256(off + units * KVQ_WAVES * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
+    off = up256(off + units * segs * p.seg_cap * cand_record_words(G) * sizeof(uint32_t));
     // V-pass parts: as many as keep the launch within kVTargetWorkgroups and
     // every wave of the longest sequence with a segment of its own
     const uint64_t pairs = uint64_t(S) * nkv;
     while (p.vparts < kMaxVParts && pairs * p.vparts * 2 <= kVTargetWorkgroups &&
-           p.vparts * 2 * KVQ_VWAVES <= p.nsplit * KVQ_WAVES)
+           p.vparts * 2 * KVQ_VWAVES <= p.nsplit * segs)
       p.vparts *= 2;
     if (p.vparts > 1) {
       p.off_vpart = off;
@@ -357,8 +358,9 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   if (q_stride % 8) return KVQ_ERR_ALIGNMENT;
   if (uint64_t(max_blocks_per_seq) * layout->block_size >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const bool sparse = sparse_v_threshold > 0.0f;
+  const uint32_t segs = score_waves(scores_on_mfma(layout->k_format, int(hd), int(G), layout->block_size));
   const Plan p = make_plan(num_seqs, nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, sparse,
-                           dense_pages(layout, sparse), wg_per_unit(layout, G, sparse));
+                           dense_pages(layout, sparse), wg_per_unit(layout, G, sparse), segs);
   // grids of (unit, kv head) tiles, units padded to a multiple of the 8 XCDs
   const uint64_t nwg = (uint64_t(num_seqs) * p.nsplit + 7) / 8 * 8 * nkv;
   const uint64_t nwg_v = (uint64_t(num_seqs) + 7) / 8 * 8 * nkv * p.vparts;
@@ -408,6 +410,7 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
   a.split_len = p.split_len;
   a.nsplit = p.nsplit;
   a.seg_cap = p.seg_cap;
+  a.segs = p.segs;
   a.vparts = p.vparts;
   a.k_stride = layout->k_block_stride_bytes;
   a.k_data = layout->k_data_section_bytes;
@@ -535,7 +538,7 @@ int prefill_as_decode(const kvq_layout* layout, const void* q, const void* k_cac
   const uint64_t rows = uint64_t(num_seqs) * max_query_len;
   if (rows >= (1ull << 31) || rows * num_q_heads >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const Plan p = make_plan(uint32_t(rows), nkv, G, hd, max_blocks_per_seq, layout->block_size, sliding_window, false,
-                           dense_pages(layout, false), wg_per_unit(layout, G, false));
+                           dense_pages(layout, false), wg_per_unit(layout, G, false), 0);
   const uint64_t nwg = (rows * p.nsplit + 7) / 8 * 8 * nkv;
   if (nwg >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   const uint64_t off_vrow = 0, off_vlen = up256(rows * 2 * sizeof(int32_t));

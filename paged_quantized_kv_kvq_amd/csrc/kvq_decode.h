@@ -421,7 +421,7 @@ struct PrologueSmem {
 
 // Page ids of the split, codebooks, and (turbo K) the rotated query in LDS;
 // then the lane's query registers.
-template <int KF, int VF, int HD, int G, int D>
+template <int KF, int VF, int HD, int G, int D, int NW = kWaves>
 __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, HD, G>& sm, uint32_t s,
                                          uint32_t g, int pb, int pe, int t, QReg<KF, D, G>& q) {
   const int tid = threadIdx.x;
@@ -444,20 +444,20 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
   // The page ids of the split (one per thread), the turbo K query rows (in
   // 16-byte pieces, rotated in LDS below) and the centroids are all requested
   // before any is stored: one round trip.
-  static_assert(kMaxPages <= kWaves * kWave, "a page id per thread");
+  static_assert(kMaxPages <= NW * kWave, "a page id per thread");
   const int first = pb >> a.log2_bs;
   const int n = ((pe - 1) >> a.log2_bs) - first + 1;
   const int32_t* bt = a.block_tables + uint64_t(row_table(a, s)) * a.max_blocks + first;
   const uint32_t page = tid < n ? uint32_t(bt[tid]) : 0u;
-  // (turbo K: query row h goes to wave h % kWaves, lane l taking elements
+  // (turbo K: query row h goes to wave h % NW, lane l taking elements
   // l * QE ... l * QE + QE - 1)
   const int lane = tid & 63, wq = tid >> 6;
-  constexpr int QE = HD / kWave, QR = Fmt<KF>::turbo ? (G + kWaves - 1) / kWaves : 1;
+  constexpr int QE = HD / kWave, QR = Fmt<KF>::turbo ? (G + NW - 1) / NW : 1;
   float qx[QR][QE];
   if constexpr (Fmt<KF>::turbo) {
 #pragma unroll
     for (int k = 0; k < QR; ++k) {
-      const int h = wq + k * kWaves;
+      const int h = wq + k * NW;
       const uint16_t* src = qg + (h < G ? h : 0) * HD + lane * QE;
       if constexpr (QE == 4) {
         const uint2 v = *reinterpret_cast<const uint2*>(src);
@@ -495,7 +495,7 @@ __device__ __forceinline__ void prologue(const DecodeArgs& a, PrologueSmem<KF, H
     // as it is
 #pragma unroll
     for (int k = 0; k < QR; ++k) {
-      const int h = wq + k * kWaves;
+      const int h = wq + k * NW;
       if constexpr (Fmt<KF>::rot) wave_wht<QE>(qx[k], lane, 1.0f);
       if (h < G) {
 #pragma unroll
@@ -856,10 +856,11 @@ namespace kvq {
 
 template <int KF, int HD, int G, bool MF>
 struct ScoreSmem {
+  static constexpr int NW = score_waves(MF);
   PrologueSmem<KF, HD, G> pro;
   float sc[kMaxSparseSplit * G];
-  float wm[kWaves][G];  // per-wave max and sum of exp2(score - max)
-  float wz[kWaves][G];
+  float wm[NW][G];  // per-wave max and sum of exp2(score - max)
+  float wz[NW][G];
   // matrix-core scores of a codebook K side: centroids of every pair of adjacent codes
   f32x2 kpair[MF && Fmt<KF>::cb ? 1 << (2 * Fmt<KF>::bits) : 1];
 };
@@ -882,12 +883,13 @@ struct ScoreSmem {
 // on turbo3 K at head_dim 256 (code unpacking, lookups, four heads' FMAs,
 // 16-lane sums).
 template <int KF, int HD, int G, bool MF>
-__global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(score_waves(MF) * kWave) void scores_kernel(const DecodeArgs a) {
   constexpr int D = LaneDims<G>::score;
   using GE = Geo<HD, D>;
   constexpr int T = GE::T;
   constexpr int RS = cand_record_words(G);
-  static_assert(!MF || (mfma_scores_ok(KF, HD, G) && kWaves * kChunk == 64), "matrix-core scores");
+  static_assert(!MF || mfma_scores_ok(KF, HD, G), "matrix-core scores");
+  constexpr int NW = int(score_waves(MF));  // waves, one record segment each
   __shared__ ScoreSmem<KF, HD, G, MF> sm;
   const Tile tl = unit_tile<KVQ_TILE_SCORES>(a, a.nsplit);
   if (!tl.valid) return;
@@ -897,20 +899,20 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int t = lane % T, r = lane / T;
   QReg<KF, D, G> q;
-  prologue<KF, KVQ_BF16, HD, G, D>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
+  prologue<KF, KVQ_BF16, HD, G, D, NW>(a, sm.pro, tl.s, tl.g, sp.pb, sp.pe, t, q);
   const float qscale = a.qk_scale * (Fmt<KF>::rot ? a.wht_scale : 1.0f);
   const int first = sp.pb >> a.log2_bs;
 
   float mloc[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
-  constexpr int step = kWaves * kChunk;
+  constexpr int step = NW * kChunk;
   const int cs = sp.pb & ~(kChunk - 1);
   if constexpr (MF) {
     using MG = MfmaGeo<KF, KVQ_BF16, HD, 4>;
     if constexpr (Fmt<KF>::cb) {  // from the centroids the prologue put in LDS
       constexpr int BITS = Fmt<KF>::bits;
-      for (int e = tid; e < (1 << (2 * BITS)); e += kWaves * kWave) {
+      for (int e = tid; e < (1 << (2 * BITS)); e += NW * kWave) {
         sm.kpair[e].x = sm.pro.kcen[e & ((1 << BITS) - 1)];
         sm.kpair[e].y = sm.pro.kcen[e >> BITS];
       }
@@ -1059,10 +1061,10 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
   for (int h = 0; h < G; ++h) {
     float m = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) m = fmaxf(m, sm.wm[ww][h]);
+    for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, sm.wm[ww][h]);
     float z = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       const float mk = sm.wm[ww][h];
       if (mk > -INFINITY) z += fast_exp2(mk - m) * sm.wz[ww][h];
     }
@@ -1075,7 +1077,7 @@ __global__ __launch_bounds__(kWaves * kWave) void scores_kernel(const DecodeArgs
     }
   }
   // candidates of this wave, compacted in its own segment
-  const uint64_t seg = ((uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split) * kWaves + w;
+  const uint64_t seg = ((uint64_t(tl.s) * a.num_kv_heads + tl.g) * a.nsplit + tl.split) * NW + w;
   uint32_t* rec = a.crec + seg * a.seg_cap * RS;
   int nw = 0;
   for (int cw = cs + w * kChunk; cw < sp.pe; cw += lap) {
@@ -1455,15 +1457,15 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = lane % T, r = lane / T;
-  const int nseg_all = ns * kWaves;  // (split, score wave) segments
+  const int nseg_all = ns * int(a.segs);  // (split, score wave) segments
   const int NW = int(a.vparts) * kVWaves, W = int(part) * kVWaves + w;
   const int nseg = nseg_all > W ? (nseg_all - W + NW - 1) / NW : 0;  // this wave's
   // requests that do not depend on each other go out first: the counts of the
   // wave's first batch of segments, a first record per lane, the statistics
-  const int myc0 = lane < nseg ? a.cnt[sbase * kWaves + W + NW * lane] : 0;
+  const int myc0 = lane < nseg ? a.cnt[sbase * a.segs + W + NW * lane] : 0;
   uint32_t spec[RS];
   if (W < nseg_all) {  // the wave's first segment exists (the last head's would lie past the workspace)
-    load_record<G>(a.crec + ((sbase * kWaves + W) * a.seg_cap + lane) * RS, spec);
+    load_record<G>(a.crec + ((sbase * a.segs + W) * a.seg_cap + lane) * RS, spec);
   } else {
 #pragma unroll
     for (int i = 0; i < RS; ++i) spec[i] = 0u;
@@ -1518,7 +1520,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
   // (split, score wave) number W + NW * i of the sequence and kv head)
   for (int sb = 0; sb < nseg; sb += kSegBatch) {
     const int nb = min(kSegBatch, nseg - sb);
-    const int myc = sb == 0 ? myc0 : (lane < nb ? a.cnt[sbase * kWaves + W + NW * (sb + lane)] : 0);
+    const int myc = sb == 0 ? myc0 : (lane < nb ? a.cnt[sbase * a.segs + W + NW * (sb + lane)] : 0);
     int pre = myc;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -1541,7 +1543,7 @@ __global__ __launch_bounds__(kVWaves * kWave) __attribute__((amdgpu_waves_per_eu
         for (int bb = kSegBatch / 2; bb > 0; bb >>= 1)
           if (k + bb < nb && sm.pre[w][k + bb - 1] <= gi) k += bb;
         const int off = gi - (k > 0 ? sm.pre[w][k - 1] : 0);
-        const uint64_t seg = sbase * kWaves + W + NW * (sb + k);
+        const uint64_t seg = sbase * a.segs + W + NW * (sb + k);
         load_record<G>(a.crec + (seg * a.seg_cap + off) * RS, rw);
       }
     };
@@ -1642,14 +1644,13 @@ hipError_t launch_split_k(int vf, int hd, int g, const DecodeArgs& a, uint32_t n
 // where they apply (block_size >= 16), else the VALU ones.
 template <int KF, int HD, int G>
 void launch_scores_one(const DecodeArgs& a, uint32_t nwg, hipStream_t st) {
-  const dim3 grid(nwg), block(kWaves * kWave);
   if constexpr (KVQ_SCORE_MFMA && mfma_scores_ok(KF, HD, G)) {
-    if (a.log2_bs >= 4) {
-      hipLaunchKernelGGL((scores_kernel<KF, HD, G, true>), grid, block, 0, st, a);
+    if (scores_on_mfma(KF, HD, G, 1u << a.log2_bs)) {
+      hipLaunchKernelGGL((scores_kernel<KF, HD, G, true>), dim3(nwg), dim3(score_waves(true) * kWave), 0, st, a);
       return;
     }
   }
-  hipLaunchKernelGGL((scores_kernel<KF, HD, G, false>), grid, block, 0, st, a);
+  hipLaunchKernelGGL((scores_kernel<KF, HD, G, false>), dim3(nwg), dim3(score_waves(false) * kWave), 0, st, a);
 }
 
 template <int KF, int HD>

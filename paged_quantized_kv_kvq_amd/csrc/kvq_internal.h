@@ -60,6 +60,9 @@
 #ifndef KVQ_SCORE_LOOKUPS
 #define KVQ_SCORE_LOOKUPS 16     // ... its code-pair lookups requested at once
 #endif
+#ifndef KVQ_SCORE_WAVES
+#define KVQ_SCORE_WAVES 8        // waves of the sparse score kernel's VALU form (its matrix-core form: 4)
+#endif
 #ifndef KVQ_SCORE_BUFS
 #define KVQ_SCORE_BUFS 2         // chunk buffers per wave in the sparse score kernel (loads run this - 1 ahead)
 #endif
@@ -120,6 +123,13 @@ __host__ __device__ constexpr bool mfma_scores_ok(int kf, int hd, int g) {
   return kf >= KVQ_TURBO2 && g <= 4 && kqb % 4 == 0 && kqb <= 32 && hd / 4 >= 16;
 }
 
+// Waves of the sparse score kernel, one record segment each: four for the
+// matrix-core form, KVQ_SCORE_WAVES for the VALU one.
+__host__ __device__ constexpr bool scores_on_mfma(int kf, int hd, int g, uint32_t bs) {
+  return KVQ_SCORE_MFMA && mfma_scores_ok(kf, hd, g) && bs >= 16;
+}
+__host__ __device__ constexpr uint32_t score_waves(bool mfma) { return mfma ? 4u : uint32_t(KVQ_SCORE_WAVES); }
+
 __host__ __device__ constexpr bool mfma_split_ok(int kf, int vf, int hd) {
   const int kbits = kf == KVQ_BF16 ? 16 : kf == KVQ_FP8_E4M3 ? 8 : kf == KVQ_NVFP4 ? 4 : kf;
   const int vbits = vf == KVQ_BF16 ? 16 : vf == KVQ_FP8_E4M3 ? 8 : vf == KVQ_NVFP4 ? 4 : vf;
@@ -166,12 +176,12 @@ struct WriteArgs {
 };
 
 // Sparse-V candidate lists hold one segment per (split, wave of the score
-// kernel).  A wave scores every KVQ_WAVES-th chunk of 16 positions of its
-// split, so a segment never holds more than cand_segment_cap records (at
-// least 64: the V pass reads one record per lane ahead of the counts).
-__host__ __device__ constexpr uint32_t cand_segment_cap(uint32_t split_len) {
-  return ((split_len + 15u) / (16u * KVQ_WAVES) + 1u) * 16u < 64u ? 64u
-                                                                 : ((split_len + 15u) / (16u * KVQ_WAVES) + 1u) * 16u;
+// kernel).  With `segs` waves, a wave scores every segs-th chunk of 16
+// positions of its split, so a segment never holds more than
+// cand_segment_cap records (at least 64: the V pass reads one record per
+// lane ahead of the counts).
+__host__ __device__ constexpr uint32_t cand_segment_cap(uint32_t split_len, uint32_t segs) {
+  return ((split_len + 15u) / (16u * segs) + 1u) * 16u < 64u ? 64u : ((split_len + 15u) / (16u * segs) + 1u) * 16u;
 }
 // Words per candidate record: page id, position, G scores, padded to 16 bytes.
 __host__ __device__ constexpr uint32_t cand_record_words(uint32_t g) { return (2u + g + 3u) / 4u * 4u; }
@@ -203,7 +213,8 @@ struct DecodeArgs {
   uint32_t window;
   uint32_t split_len;
   uint32_t nsplit;
-  uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len)
+  uint32_t seg_cap;  // sparse: records per segment, cand_segment_cap(split_len, segs)
+  uint32_t segs;     // sparse: record segments per split (the score kernel's waves)
   uint32_t vparts;   // sparse: V-pass workgroups per (sequence, kv head)
   uint32_t eq_split;  // 1: a sequence's splits share its span equally (split_span)
   uint64_t k_stride;
