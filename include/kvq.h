@@ -219,16 +219,15 @@ int kvq_paged_decode_noalloc(const kvq_layout* layout, const void* q, const void
  *                (per query: keys p - W < j <= p), k_scale, v_scale, workspace,
  *                workspace_bytes, stream: as for kvq_paged_decode.  No sparse-V
  *                threshold: the skip is a decode feature.
- * Tiles of queries run on the matrix cores where the operands allow it:
- * with a bf16 or fp8 K side and block_size >= 4, tiles of 128 (query, head)
- * rows (64 at head_dim 256) share each K/V chunk and write their rows
- * directly (the workspace is a nominal 256 bytes, still required); with
- * turbo / NVFP4 K, smaller tiles write per-split partials that a second
- * kernel merges.  Elsewhere (block_size < 4; turbo / NVFP4 K with
- * block_size < 16, V rows over 128 bytes or turbo3 K at head_dim 64) every
- * query runs as its own decode row through the decode kernels, which reads
- * the keys once per query; the workspace covers num_seqs * max_query_len
- * rows there. */
+ * With block_size >= 4, tiles of queries run on the matrix cores: tiles of
+ * 128 (query, head) rows (64 at head_dim 256 or with a rotated K side) share
+ * each dequantized K/V chunk and write their rows directly; the workspace
+ * holds the order in which the (sequence, kv head) units run, 4 bytes each
+ * (longest first), and, when a small grid splits the key ranges, the
+ * per-split partial rows that a second kernel merges.  With block_size < 4
+ * every query runs as its own decode row through the decode kernels, which
+ * reads the keys once per query; the workspace covers num_seqs *
+ * max_query_len rows there. */
 int kvq_paged_prefill(const kvq_layout* layout, const void* q, const void* k_cache, const void* v_cache, float* out,
                       const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start,
                       uint32_t max_blocks_per_seq, uint32_t num_seqs, uint32_t num_q_heads, uint32_t max_query_len,

@@ -618,8 +618,11 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
   }
   const uint64_t nwg = (base * nsplit / ntiles + 7) / 8 * 8 * ntiles;
   const uint64_t prow = base * nsplit * rows;  // partial rows
-  const uint64_t off_ml = 0, off_part = up256(prow * 2 * sizeof(float));
-  const uint64_t bytes = nsplit > 1 ? up256(off_part + prow * hd * sizeof(float)) : 256;
+  const uint64_t units = base / ntiles * nsplit;  // (sequence, kv head, split)
+  // the units' order, then (with splits) the partial rows' statistics and outputs
+  const uint64_t off_order = 0, off_ml = up256(units * sizeof(uint32_t));
+  const uint64_t off_part = up256(off_ml + prow * 2 * sizeof(float));
+  const uint64_t bytes = nsplit > 1 ? up256(off_part + prow * hd * sizeof(float)) : off_ml;
   if (nwg >= (1ull << 31) || base * nsplit * rows / 4 >= (1ull << 31)) return KVQ_ERR_UNSUPPORTED;
   if (!workspace) {
     *workspace_bytes = size_t(bytes);
@@ -641,8 +644,11 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.query_start = query_start;
-  a.ml = reinterpret_cast<float*>(ws + off_ml);
-  a.part = reinterpret_cast<float*>(ws + off_part);
+  if (nsplit > 1) {
+    a.ml = reinterpret_cast<float*>(ws + off_ml);
+    a.part = reinterpret_cast<float*>(ws + off_part);
+  }
+  if (KVQ_PREFILL_ORDER) a.order = reinterpret_cast<uint32_t*>(ws + off_order);
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -654,7 +660,11 @@ int prefill_tiles(const kvq_layout* layout, const void* q, const void* k_cache, 
   a.split_len = uint32_t(split_len);
   fill_common(a, layout, inv_sqrt_d, k_scale, v_scale);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_prefill_tiles(layout->k_format, layout->v_format, int(hd), int(G), a, uint32_t(nwg), st);
+  // buckets of the unit sort: 256 over the longest key range
+  const int width = int(std::max<uint64_t>(16, (nch * nk + 255) / 256));
+  hipError_t e = a.order ? launch_unit_order(a, st, 1, width) : hipSuccess;
+  if (e == hipSuccess)
+    e = launch_prefill_tiles(layout->k_format, layout->v_format, int(hd), int(G), a, uint32_t(nwg), st);
   if (e == hipSuccess && nsplit > 1) e = launch_prefill_tile_merge(layout->v_rotated != 0, int(hd), int(G), a, st);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

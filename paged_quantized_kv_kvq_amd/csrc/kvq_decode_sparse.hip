@@ -62,23 +62,36 @@ __global__ void prefill_rows_kernel(const int32_t* query_start, const int32_t* s
   vlen[v] = ok ? p + 1 : 0;
 }
 
-// A split kernel's units (split * S + sequence) in order of decreasing
-// length, bucketed by 16 positions (a counting sort in one workgroup; units
-// of one bucket in any order).  Started longest first, the units leave short
+// A split kernel's units in order of decreasing length, bucketed by `width`
+// positions (a counting sort in one workgroup; units of one bucket in any
+// order).  Decode units are (split * S + sequence) with the split's length;
+// prefill units (mode 1) are ((sequence * Hkv + kv head) * nsplit + split)
+// with the key range of the unit's last tile within the split.  Started longest first, the units leave short
 // ones for the end of the launch, when fewer workgroups share the memory
 // bandwidth: a unit's workgroup streams its K rows at a limited rate, so a
 // long unit started late would stretch the launch.
-__global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a, int mode, int width) {
   constexpr int NB = (KVQ_MAX_SPLIT > kMaxSparseSplit ? KVQ_MAX_SPLIT : kMaxSparseSplit) / kChunk + 1;
   constexpr int BPL = (NB + kWave - 1) / kWave;  // buckets per lane of the scan
   __shared__ uint32_t cnt[BPL * kWave];
-  const uint32_t n = a.num_seqs * a.nsplit;
+  const uint32_t n = a.num_seqs * a.nsplit * (mode ? a.num_kv_heads : 1u);
   for (int b = threadIdx.x; b < BPL * kWave; b += 1024) cnt[b] = 0u;
   __syncthreads();
   auto bucket = [&](uint32_t u) {
-    const SeqSpan sp = split_span(a, u % a.num_seqs, u / a.num_seqs);
-    const int len = sp.pe > sp.pb ? sp.pe - sp.pb : 0;
-    return min((len + kChunk - 1) / kChunk, NB - 1);
+    int len = 0;
+    if (mode == 0) {
+      const SeqSpan sp = split_span(a, u % a.num_seqs, u / a.num_seqs);
+      len = sp.pe > sp.pb ? sp.pe - sp.pb : 0;
+    } else {
+      const uint32_t s = u / (a.num_kv_heads * a.nsplit), split = u % a.nsplit;
+      const int nq = a.query_start[s + 1] - a.query_start[s];
+      if (nq > 0) {
+        const PrefillTile pt = prefill_tile(a, s, min(uint32_t(nq - 1) / a.qt, a.ntiles - 1u));
+        len = pt.nq > 0 ? pt.hi - pt.lo : 0;
+        if (a.nsplit > 1) len = max(0, min(int(a.split_len), len - int(split * a.split_len)));
+      }
+    }
+    return min((len + width - 1) / width, NB - 1);
   };
   for (uint32_t u = threadIdx.x; u < n; u += 1024) atomicAdd(&cnt[bucket(u)], 1u);
   __syncthreads();
@@ -109,8 +122,8 @@ __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a) {
 
 }  // namespace
 
-hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(1024), 0, st, a);
+hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st, int mode, int width) {
+  hipLaunchKernelGGL(unit_order_kernel, dim3(1), dim3(1024), 0, st, a, mode, width);
   return hipGetLastError();
 }
 

@@ -84,6 +84,9 @@
 #ifndef KVQ_PREFILL_TILES
 #define KVQ_PREFILL_TILES 1      // 1: chunked prefill on the tile kernel (kvq_prefill.h) where block_size >= 4
 #endif
+#ifndef KVQ_PREFILL_ORDER
+#define KVQ_PREFILL_ORDER 1      // 1: prefill units (sequence, kv head, split) start longest first
+#endif
 #ifndef KVQ_PREFILL_TILE_DESC
 #define KVQ_PREFILL_TILE_DESC 1  // 1: a unit's prefill tiles start from the last (longest key range)
 #endif
@@ -265,8 +268,9 @@ int prefill_tile_rows(int kf, int hd);
 hipError_t launch_prefill_tiles(int kf, int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the merge of its key splits (a.nsplit > 1)
 hipError_t launch_prefill_tile_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);
-// The order in which a split kernel takes its units (a.order)
-hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st);
+// The order in which a split kernel takes its units (a.order): decode units
+// (mode 0) or prefill tile units (mode 1), lengths bucketed by `width`
+hipError_t launch_unit_order(const DecodeArgs& a, hipStream_t st, int mode = 0, int width = 16);
 hipError_t launch_sparse_v(int vf, int hd, int g, const DecodeArgs& a, uint32_t nwg, hipStream_t st);
 // ... and the sum of its parts (a.vparts > 1), one workgroup per (sequence, kv head)
 hipError_t launch_sparse_v_merge(bool v_rotated, int hd, int g, const DecodeArgs& a, hipStream_t st);

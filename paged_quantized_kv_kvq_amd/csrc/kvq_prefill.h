@@ -261,14 +261,17 @@ __device__ __forceinline__ f32x4v mfma_bf16(u32x4 a, u32x4 b, f32x4v c) {
 // Workgroup -> (sequence, kv head, split of the key range, tile).  The
 // tiles of one (sequence, kv head, split) read the same keys at about the
 // same time: they go to one XCD (workgroup i runs on XCD i % 8), and groups
-// of 8 such units rotate over the XCDs.
+// of 8 such units rotate over the XCDs.  With a.order the units come longest
+// first, and a unit's tiles start from its last (longest key range), so
+// short tiles fill the end of the launch.
 struct TileId {
   uint32_t s, g, split, tile;
   bool valid;
 };
 __device__ __forceinline__ TileId tile_id(const DecodeArgs& a) {
   const uint32_t i = blockIdx.x, x = i & 7u, rest = i >> 3;
-  const uint32_t unit = (rest / a.ntiles) * 8u + x;
+  uint32_t unit = (rest / a.ntiles) * 8u + x;
+  if (a.order && unit < a.num_seqs * a.num_kv_heads * a.nsplit) unit = a.order[unit];  // longest units first
   const uint32_t sg = unit / a.nsplit;
   TileId t;
 #if KVQ_PREFILL_TILE_DESC

@@ -168,12 +168,14 @@ def test_status_strings(lib):
 def test_prefill_host_checks(lib):
     # sizes are computed on the host; unsupported shapes are refused before anything is launched
     # block_size >= 4 runs on the tile kernel, which writes its rows
-    # directly: a nominal 256-byte workspace, whatever the sizes
+    # directly: the workspace holds only the order of the (sequence, kv head)
+    # units, 4 bytes each, whatever the other sizes
+    up256 = lambda x: (x + 255) // 256 * 256
     lay = kvq.pool_layout("bf16", "turbo4", 16, 8, 128)
     lay_t = kvq.pool_layout("turbo4", "turbo3", 4, 8, 256)
     for lay_s in (lay, lay_t, kvq.pool_layout("nvfp4", "bf16", 512, 8, 64)):
-        assert kvq.prefill_workspace_bytes(lay_s, 400, 32, 64, 100) == 256
-        assert kvq.prefill_workspace_bytes(lay_s, 400, 64, 4096, 9000, sliding_window=128) == 256
+        assert kvq.prefill_workspace_bytes(lay_s, 400, 32, 64, 100) == up256(400 * 8 * 4)
+        assert kvq.prefill_workspace_bytes(lay_s, 400, 64, 4096, 9000, sliding_window=128) == up256(400 * 8 * 4)
     # ... and so does a small grid whose key ranges are short (1024 keys)
     assert kvq.prefill_workspace_bytes(lay, 4, 32, 64, 100) == 256
     # a grid of few tiles over long key ranges splits the ranges: partial rows
