@@ -93,7 +93,19 @@ __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a, in
     }
     return min((len + width - 1) / width, NB - 1);
   };
-  for (uint32_t u = threadIdx.x; u < n; u += 1024) atomicAdd(&cnt[bucket(u)], 1u);
+  // the first kKeep units of each thread keep their bucket in registers for
+  // the second pass (the rest are recomputed there)
+  constexpr int kKeep = 4;
+  int keep[kKeep];
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    const uint32_t u = threadIdx.x + 1024u * k;
+    keep[k] = u < n ? bucket(u) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k)
+    if (threadIdx.x + 1024u * k < n) atomicAdd(&cnt[keep[k]], 1u);
+  for (uint32_t u = threadIdx.x + 1024u * kKeep; u < n; u += 1024) atomicAdd(&cnt[bucket(u)], 1u);
   __syncthreads();
   if (threadIdx.x < kWave) {  // first slot of each bucket, the longest bucket first: one wave's scan
     const int lane = threadIdx.x;
@@ -117,7 +129,12 @@ __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a, in
     }
   }
   __syncthreads();
-  for (uint32_t u = threadIdx.x; u < n; u += 1024) a.order[atomicAdd(&cnt[bucket(u)], 1u)] = u;
+#pragma unroll
+  for (int k = 0; k < kKeep; ++k) {
+    const uint32_t u = threadIdx.x + 1024u * k;
+    if (u < n) a.order[atomicAdd(&cnt[keep[k]], 1u)] = u;
+  }
+  for (uint32_t u = threadIdx.x + 1024u * kKeep; u < n; u += 1024) a.order[atomicAdd(&cnt[bucket(u)], 1u)] = u;
 }
 
 }  // namespace
