@@ -102,9 +102,23 @@ __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a, in
     const uint32_t u = threadIdx.x + 1024u * k;
     keep[k] = u < n ? bucket(u) : 0;
   }
+  // a wave whose units all fall in one bucket (equal lengths: the common
+  // case) counts them with one atomic instead of 64 on the same address
+  const int lane = threadIdx.x & 63;
+  auto wave_uniform = [&](int k, uint64_t& valid) {
+    valid = __ballot(threadIdx.x + 1024u * k < n);
+    const int b0 = __shfl(keep[k], valid ? __builtin_ctzll(valid) : 0);
+    return valid != 0 && __ballot(threadIdx.x + 1024u * k < n && keep[k] == b0) == valid;
+  };
 #pragma unroll
-  for (int k = 0; k < kKeep; ++k)
-    if (threadIdx.x + 1024u * k < n) atomicAdd(&cnt[keep[k]], 1u);
+  for (int k = 0; k < kKeep; ++k) {
+    uint64_t valid;
+    if (wave_uniform(k, valid)) {
+      if (lane == __builtin_ctzll(valid)) atomicAdd(&cnt[keep[k]], uint32_t(__popcll(valid)));
+    } else if (threadIdx.x + 1024u * k < n) {
+      atomicAdd(&cnt[keep[k]], 1u);
+    }
+  }
   for (uint32_t u = threadIdx.x + 1024u * kKeep; u < n; u += 1024) atomicAdd(&cnt[bucket(u)], 1u);
   __syncthreads();
   if (threadIdx.x < kWave) {  // first slot of each bucket, the longest bucket first: one wave's scan
@@ -132,7 +146,16 @@ __global__ __launch_bounds__(1024) void unit_order_kernel(const DecodeArgs a, in
 #pragma unroll
   for (int k = 0; k < kKeep; ++k) {
     const uint32_t u = threadIdx.x + 1024u * k;
-    if (u < n) a.order[atomicAdd(&cnt[keep[k]], 1u)] = u;
+    uint64_t valid;
+    if (wave_uniform(k, valid)) {
+      const int lead = __builtin_ctzll(valid);
+      uint32_t base = 0;
+      if (lane == lead) base = atomicAdd(&cnt[keep[k]], uint32_t(__popcll(valid)));
+      base = __shfl(base, lead);
+      if (u < n) a.order[base + __popcll(valid & ((1ull << lane) - 1ull))] = u;
+    } else if (u < n) {
+      a.order[atomicAdd(&cnt[keep[k]], 1u)] = u;
+    }
   }
   for (uint32_t u = threadIdx.x + 1024u * kKeep; u < n; u += 1024) a.order[atomicAdd(&cnt[bucket(u)], 1u)] = u;
 }
