@@ -61,14 +61,15 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kUnitWaves = 8;  // most kv heads (waves) per workgroup
 
 // Waves (kv heads) per workgroup of one instance.  Decode with a grouped-scale
-// K side and G <= 4 is bound by its arithmetic and latency chain at 144
-// VGPRs, three waves per SIMD: workgroups of four kv heads let three of them
-// share a CU where one of eight fits (turbo8 / turbo8 and turbo4 / turbo8,
-// G = 4: 0.51 -> 0.46 ms and 0.57 -> 0.54 ms).  Everything else keeps whole
-// pages to one workgroup.
+// K side is bound by its arithmetic and latency chain (144 VGPRs at G = 4,
+// three waves per SIMD; 194 at G = 8, two): workgroups of four kv heads let
+// more of them share a CU than of eight (turbo8 / turbo8 and turbo4 / turbo8,
+// G = 4: 0.51 -> 0.46 ms and 0.57 -> 0.54 ms; turbo4 / turbo3, G = 8, once
+// its units are taken longest first: 0.310 -> 0.277 ms).  bf16 and fp8 K keep
+// whole pages to one workgroup.
 template <int KF, int G>
 constexpr int mfma_waves_cap() {
-  static_assert(mfma_waves_cap_of(KF, G) == ((Fmt<KF>::turbo && G <= 4) ? 4 : kUnitWaves), "host and device caps");
+  static_assert(mfma_waves_cap_of(KF, G) == (Fmt<KF>::turbo ? 4 : kUnitWaves), "host and device caps");
   return mfma_waves_cap_of(KF, G);
 }
 

@@ -109,9 +109,9 @@ __host__ __device__ constexpr int dense_max_pages(int kf) {
 }
 
 // Most kv heads (waves) per workgroup of the matrix-core split kernel: four
-// with a grouped-scale K side and G <= 4, else eight; and the heads per
-// workgroup for nkv kv heads (the largest divisor of nkv up to that cap).
-__host__ __device__ constexpr int mfma_waves_cap_of(int kf, int g) { return (kf >= KVQ_TURBO2 && g <= 4) ? 4 : 8; }
+// with a grouped-scale K side, else eight; and the heads per workgroup for
+// nkv kv heads (the largest divisor of nkv up to that cap).
+__host__ __device__ constexpr int mfma_waves_cap_of(int kf, int g) { return (kf >= KVQ_TURBO2 && g <= 8) ? 4 : 8; }
 __host__ __device__ constexpr uint32_t mfma_unit_waves(uint32_t nkv, uint32_t cap) {
   for (uint32_t d = cap; d > 1; --d)
     if (nkv % d == 0) return d;
