@@ -398,7 +398,15 @@ int decode_impl(const kvq_layout* layout, const void* q, const void* k_cache, co
     // lengths can differ: without a window.  With one, every sequence at least
     // as long as the window has the same span, and the extra launch (about 4 us)
     // costs more than it saves.
-    if (KVQ_SCORE_ORDER && sliding_window == 0) a.order = reinterpret_cast<uint32_t*>(ws + p.off_order);
+    if (KVQ_SCORE_ORDER && sliding_window == 0) {
+      // launches of few units (the VALU form's workgroup holds them all)
+      // order themselves in every workgroup instead of a sorting launch
+      if (KVQ_SCORE_ORDER_INLINE && segs == score_waves(false) &&
+          uint64_t(num_seqs) * p.nsplit <= uint64_t(score_waves(false)) * 64u)
+        a.lpt_inline = 1u;
+      else
+        a.order = reinterpret_cast<uint32_t*>(ws + p.off_order);
+    }
   }
   a.max_blocks = max_blocks_per_seq;
   a.num_seqs = num_seqs;

@@ -854,6 +854,73 @@ namespace kvq {
 
 // ------------------------------------------------------------------ sparse V
 
+// The unit (split * S + sequence) at rank r of the longest-first order of a
+// launch's units, computed by a whole workgroup of NW waves (every workgroup
+// of the launch computes the same order: a counting sort over 16-position
+// buckets, longest first, units of one bucket by increasing index), for
+// launches of at most NW * 64 units.  This replaces the sorting launch ahead
+// of the kernel.  `lds` holds at least 2 * NB + NW + 2 words and is free.
+template <int NW>
+__device__ uint32_t inline_unit_order(const DecodeArgs& a, uint32_t r, uint32_t* lds) {
+  constexpr int NB = kMaxSparseSplit / kChunk + 1;
+  uint32_t* cnt = lds;          // [NB] units per bucket
+  uint32_t* start = lds + NB;   // [NB] first rank of each bucket
+  uint32_t* wcnt = start + NB;  // [NW] units of the found bucket per wave
+  uint32_t* res = wcnt + NW;    // [0] the found bucket, [1] the unit
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t n = a.num_seqs * a.nsplit;
+  int b = -1;
+  if (uint32_t(tid) < n) {
+    const SeqSpan sp = split_span(a, uint32_t(tid) % a.num_seqs, uint32_t(tid) / a.num_seqs);
+    const int len = sp.pe > sp.pb ? sp.pe - sp.pb : 0;
+    b = min((len + kChunk - 1) / kChunk, NB - 1);
+  }
+  for (int i = tid; i < NB; i += NW * kWave) cnt[i] = 0u;
+  __syncthreads();
+  if (b >= 0) atomicAdd(&cnt[b], 1u);
+  __syncthreads();
+  if (tid < kWave) {  // first rank of each bucket, the longest bucket first (one wave's scan)
+    constexpr int BPL = (NB + kWave - 1) / kWave;
+    uint32_t c[BPL], sum = 0;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {  // lane l takes buckets NB - 1 - l * BPL - i
+      const int bb = NB - 1 - (lane * BPL + i);
+      c[i] = bb >= 0 ? cnt[bb] : 0u;
+      sum += c[i];
+    }
+    uint32_t pre = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t v = __shfl_up(pre, off);
+      if (lane >= off) pre += v;
+    }
+    uint32_t at = pre - sum;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      const int bb = NB - 1 - (lane * BPL + i);
+      if (bb >= 0) start[bb] = at;
+      at += c[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < NB; i += NW * kWave)
+    if (cnt[i] > 0u && start[i] <= r && r < start[i] + cnt[i]) res[0] = uint32_t(i);
+  __syncthreads();
+  const int bf = int(res[0]);
+  const uint64_t m = __ballot(b == bf);
+  if (lane == 0) wcnt[w] = uint32_t(__popcll(m));
+  __syncthreads();
+  if (b == bf) {
+    uint32_t k = uint32_t(__popcll(m & ((1ull << lane) - 1ull)));
+    for (int ww = 0; ww < w; ++ww) k += wcnt[ww];
+    if (start[bf] + k == r) res[1] = uint32_t(tid);
+  }
+  __syncthreads();
+  const uint32_t unit = res[1];
+  __syncthreads();  // the area is the score array, written next
+  return unit;
+}
+
 template <int KF, int HD, int G, bool MF>
 struct ScoreSmem {
   static constexpr int NW = score_waves(MF);
@@ -891,8 +958,13 @@ __global__ __launch_bounds__(score_waves(MF) * kWave) void scores_kernel(const D
   static_assert(!MF || mfma_scores_ok(KF, HD, G), "matrix-core scores");
   constexpr int NW = int(score_waves(MF));  // waves, one record segment each
   __shared__ ScoreSmem<KF, HD, G, MF> sm;
-  const Tile tl = unit_tile<KVQ_TILE_SCORES>(a, a.nsplit);
+  Tile tl = unit_tile<KVQ_TILE_SCORES>(a, a.nsplit);
   if (!tl.valid) return;
+  if (a.lpt_inline) {  // the unit of this rank in the longest-first order, found by the workgroup
+    const uint32_t unit = inline_unit_order<NW>(a, tl.split * a.num_seqs + tl.s, reinterpret_cast<uint32_t*>(sm.sc));
+    tl.s = unit % a.num_seqs;
+    tl.split = unit / a.num_seqs;
+  }
   const SeqSpan sp = split_span(a, tl.s, tl.split);
   if (sp.pb >= sp.L) return;
   const int tid = threadIdx.x, lane = tid & 63;

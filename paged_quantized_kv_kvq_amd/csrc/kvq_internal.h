@@ -54,6 +54,9 @@
 #ifndef KVQ_SCORE_MFMA
 #define KVQ_SCORE_MFMA 1         // 1: the sparse score kernel scores a grouped-scale K side on the matrix cores
 #endif
+#ifndef KVQ_SCORE_ORDER_INLINE
+#define KVQ_SCORE_ORDER_INLINE 1  // 1: small sparse launches order their units inside the score kernel
+#endif
 #ifndef KVQ_SCORE_MFMA_BUFS
 #define KVQ_SCORE_MFMA_BUFS 2    // ... its chunk buffers per wave
 #endif
@@ -207,6 +210,7 @@ struct DecodeArgs {
                    // of cand_record_words(G) words: page id, position, G log2 scores
   float* vpart;    // sparse, vparts > 1: [S][Hkv][vparts][G][hd] the V parts' sums
   uint32_t* order;  // [S * nsplit] units (split * S + sequence), longest first (null: in that order)
+  uint32_t lpt_inline;  // sparse VALU score kernel: each workgroup finds its unit of the longest-first order
   uint32_t max_blocks;
   uint32_t num_seqs;
   uint32_t num_q_heads;
