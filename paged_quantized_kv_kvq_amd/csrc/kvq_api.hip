@@ -178,10 +178,9 @@ uint32_t wg_per_unit(const kvq_layout* layout, uint32_t G, bool sparse) {
 // On the dense path, then halved while the split kernel would get fewer than
 // kMinWorkgroups workgroups (wpu per (sequence, split)) over the longest
 // possible window (the table's reach; shorter sequences leave some empty):
-// the matrix-core kernel with eight kv heads per workgroup and 194 VGPRs
-// (turbo4 K, G = 8) holds one workgroup per CU, and 32 sequences of
-// 4096-16384 positions in splits of 2048 left CUs idle (0.348 -> 0.311 ms
-// with splits of 1024).
+// with 194 VGPRs (turbo4 K, G = 8) the matrix-core kernel holds few waves
+// per CU, and 32 sequences of 4096-16384 positions in long splits left CUs
+// idle (0.35 -> 0.31 ms with shorter splits, the units longest first).
 Plan make_plan(uint32_t S, uint32_t nkv, uint32_t G, uint32_t hd, uint32_t max_blocks, uint32_t bs,
                uint32_t window, bool sparse, uint32_t max_pages, uint32_t wpu, uint32_t segs) {
   uint64_t span = uint64_t(max_blocks) * bs;

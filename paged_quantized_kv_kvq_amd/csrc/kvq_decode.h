@@ -9,13 +9,16 @@
 // decode query.  "spark_runtime/kv_cache.rs", is_wht_rotated: rotated K sides
 // are scored against WHT(q); rotated V sides give WHT(out), rotated back.
 //
-// Work decomposition (differs from the pages' one-block-per-(q head, seq)):
+// Work decomposition of the VALU kernels here (differs from the pages'
+// one-block-per-(q head, seq); the matrix-core split kernel is in
+// kvq_decode_mfma.h):
 //   * split-K over positions: a workgroup handles (sequence, kv head, split of
 //     split_len positions) and ALL G = Hq/Hkv query heads of that kv head, so
 //     every K/V byte is read once, not G times;
-//   * a wave walks 16-position chunks (wave w: chunks w, w + 4, ...); each
-//     lane finds its position's page in an LDS copy of the split's page table;
-//     chunk loads run one chunk ahead of their use, all issued inside the loop;
+//   * a wave walks 16-position chunks (wave w of NW: chunks w, w + NW, ...);
+//     each lane finds its position's page in an LDS copy of the split's page
+//     table; chunk loads run one chunk ahead of their use, all issued inside
+//     the loop;
 //   * inside a chunk, T = head_dim/D lanes share one position (D = 16 dims
 //     per lane, 8 for G = 8) and 64/T positions are side by side; a score is
 //     a T-lane DPP sum of bf16 dot products (v_dot2_f32_bf16 for bf16 K and
@@ -26,12 +29,16 @@
 //     combined by merge_kernel (which also applies the inverse rotation);
 //   * sparse (threshold > 0): scores_kernel keeps only candidate positions
 //     (split-local weight above thr: an upper bound on the global weight),
-//     each wave in its own segment; sparse_v_kernel, one workgroup per
+//     each wave in its own segment (a grouped-scale K side is scored on the
+//     matrix cores); sparse_v_kernel, one or more workgroups ("parts") per
 //     (sequence, kv head), recomputes each candidate's exact global weight,
 //     loads V only where some head of the group keeps it, and writes the
-//     output (fp8 V scale, inverse rotation);
+//     output (fp8 V scale, inverse rotation), or with several parts their
+//     sums, which sparse_v_merge_kernel adds;
 //   * workgroup ids are renumbered so the kv heads of one (sequence, split)
-//     run on the same XCD, and consecutive units rotate over the XCDs.
+//     run on the same XCD, and consecutive units rotate over the XCDs; the
+//     units can be taken longest first (unit_order_kernel, or
+//     inline_unit_order in the score kernel).
 #pragma once
 
 #include "kvq_device.h"
