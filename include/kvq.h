@@ -87,7 +87,8 @@ typedef enum kvq_status {
   KVQ_ERR_ALIGNMENT = -3,    /* a pointer or stride is not 16-byte aligned  */
   KVQ_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required  */
   KVQ_ERR_LAUNCH = -5,       /* the HIP runtime rejected a kernel launch    */
-  KVQ_ERR_EXHAUSTED = -6     /* the block manager has too few free blocks   */
+  KVQ_ERR_EXHAUSTED = -6,    /* the block manager has too few free blocks   */
+  KVQ_ERR_HOST_MEMORY = -7   /* a host allocation failed; nothing changed   */
 } kvq_status;
 
 /* Byte layout of the two pools of one attention layer.

@@ -46,6 +46,9 @@ extern "C" {
 
 typedef struct kvq_blocks kvq_blocks;  /* opaque */
 
+/* Any call that needs host memory it cannot get returns KVQ_ERR_HOST_MEMORY
+ * and leaves the manager as it was. */
+
 /* A manager of num_blocks blocks (1 <= num_blocks <= 2^31 - 1) of block_size
  * positions (>= 1).  *out receives the handle.  KVQ_ERR_INVALID_ARG on a bad
  * size or out == NULL. */

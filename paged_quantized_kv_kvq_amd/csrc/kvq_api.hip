@@ -790,6 +790,7 @@ const char* kvq_status_string(int status) {
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_LAUNCH: return "kernel launch failed";
     case KVQ_ERR_EXHAUSTED: return "no free block left";
+    case KVQ_ERR_HOST_MEMORY: return "host memory exhausted";
     default: return "unknown status";
   }
 }

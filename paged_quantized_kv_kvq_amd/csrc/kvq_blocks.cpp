@@ -4,10 +4,15 @@
 // "spark_runtime/kv_cache.rs", PagedKvCache (free_blocks, block_ref_counts);
 // "combs_models/kv.rs", PageAllocator (a stack of free ids, block 0 handed out
 // first), ensure_pages, popn, reset.  Plain host C++: no HIP calls.
+//
+// Every host allocation an entry point needs is made before the first change
+// to the manager's state, so a std::bad_alloc leaves that state as it was and
+// comes back as KVQ_ERR_HOST_MEMORY; no exception crosses the C interface.
 #include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "kvq_blocks.h"
@@ -51,17 +56,33 @@ struct kvq_blocks {
 
 namespace {
 constexpr uint32_t kMaxId = 0x7FFFFFFFu;
+
+template <class F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return KVQ_ERR_HOST_MEMORY;
+  }
 }
+}  // namespace
 
 extern "C" {
 
 int kvq_blocks_create(uint32_t num_blocks, uint32_t block_size, kvq_blocks** out) {
   if (!out || num_blocks == 0 || num_blocks > kMaxId || block_size == 0) return KVQ_ERR_INVALID_ARG;
   kvq_blocks* bm = new (std::nothrow) kvq_blocks;
-  if (!bm) return KVQ_ERR_INVALID_ARG;
+  if (!bm) return KVQ_ERR_HOST_MEMORY;
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
-  bm->reset();
+  const int st = guarded([&] {
+    bm->reset();
+    return int(KVQ_OK);
+  });
+  if (st != KVQ_OK) {
+    delete bm;
+    return st;
+  }
   *out = bm;
   return KVQ_OK;
 }
@@ -71,7 +92,7 @@ void kvq_blocks_destroy(kvq_blocks* bm) { delete bm; }
 int kvq_blocks_reset(kvq_blocks* bm) {
   if (!bm) return KVQ_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> g(bm->mu);
-  bm->reset();
+  bm->reset();  // the free stack and the counts keep their size: nothing is allocated
   return KVQ_OK;
 }
 
@@ -93,23 +114,27 @@ int kvq_blocks_ref_count(kvq_blocks* bm, uint32_t block, uint32_t* count) {
 int kvq_blocks_seq_new(kvq_blocks* bm, uint32_t* seq) {
   if (!bm || !seq) return KVQ_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> g(bm->mu);
-  const uint32_t id = bm->new_id();
-  bm->seqs[id] = kvq_blocks::Seq();
-  bm->seqs[id].live = true;
-  *seq = id;
-  return KVQ_OK;
+  return guarded([&] {
+    const uint32_t id = bm->new_id();  // the one allocation, made before any change
+    bm->seqs[id] = kvq_blocks::Seq();
+    bm->seqs[id].live = true;
+    *seq = id;
+    return int(KVQ_OK);
+  });
 }
 
 int kvq_blocks_seq_fork(kvq_blocks* bm, uint32_t parent, uint32_t* child) {
   if (!bm || !child) return KVQ_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> g(bm->mu);
   if (!bm->seq(parent)) return KVQ_ERR_INVALID_ARG;
-  const uint32_t id = bm->new_id();  // may grow seqs: look the parent up again
-  const kvq_blocks::Seq p = bm->seqs[parent];
-  for (uint32_t b : p.table) ++bm->count[b];
-  bm->seqs[id] = p;
-  *child = id;
-  return KVQ_OK;
+  return guarded([&] {
+    kvq_blocks::Seq p = bm->seqs[parent];  // both allocations come before any count changes
+    const uint32_t id = bm->new_id();
+    for (uint32_t b : p.table) ++bm->count[b];
+    bm->seqs[id] = std::move(p);
+    *child = id;
+    return int(KVQ_OK);
+  });
 }
 
 int kvq_blocks_seq_free(kvq_blocks* bm, uint32_t seq) {
@@ -144,6 +169,11 @@ int kvq_blocks_append(kvq_blocks* bm, uint32_t seq, uint32_t n, int64_t* slots, 
   const bool cow = n > 0 && s->len % bs != 0 && bm->count[s->table.back()] > 1;
   const uint64_t grow = bm->pages_for(uint64_t(s->len) + n) - s->table.size();
   if (grow + (cow ? 1 : 0) > bm->free.size()) return KVQ_ERR_EXHAUSTED;
+  const int st = guarded([&] {
+    s->table.reserve(s->table.size() + grow);  // the pushes below then cannot throw
+    return int(KVQ_OK);
+  });
+  if (st != KVQ_OK) return st;
   *cow_src = *cow_dst = -1;
   if (cow) {
     const uint32_t old = s->table.back();
@@ -168,7 +198,12 @@ int kvq_blocks_append_many(kvq_blocks* bm, const uint32_t* seqs, const uint32_t*
   std::lock_guard<std::mutex> g(bm->mu);
   const uint32_t bs = bm->block_size;
   uint64_t need = 0, total = 0;
-  std::vector<uint32_t> ids(seqs, seqs + num_seqs);
+  std::vector<uint32_t> ids;
+  const int st = guarded([&] {
+    ids.assign(seqs, seqs + num_seqs);
+    return int(KVQ_OK);
+  });
+  if (st != KVQ_OK) return st;
   std::sort(ids.begin(), ids.end());
   if (std::adjacent_find(ids.begin(), ids.end()) != ids.end()) return KVQ_ERR_INVALID_ARG;
   for (uint32_t i = 0; i < num_seqs; ++i) {
@@ -180,6 +215,15 @@ int kvq_blocks_append_many(kvq_blocks* bm, const uint32_t* seqs, const uint32_t*
   }
   if (total && !slots) return KVQ_ERR_INVALID_ARG;
   if (need > bm->free.size()) return KVQ_ERR_EXHAUSTED;
+  // every table gets its room first; extra capacity alone changes no state
+  const int room = guarded([&] {
+    for (uint32_t i = 0; i < num_seqs; ++i) {
+      kvq_blocks::Seq* s = bm->seq(seqs[i]);
+      s->table.reserve(bm->pages_for(uint64_t(s->len) + counts[i]));
+    }
+    return int(KVQ_OK);
+  });
+  if (room != KVQ_OK) return room;
   uint64_t o = 0;
   for (uint32_t i = 0; i < num_seqs; ++i) {
     kvq_blocks::Seq* s = bm->seq(seqs[i]);

@@ -2,6 +2,8 @@
 oracle model, call by call, on the host (no GPU)."""
 import ctypes
 import random
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -9,7 +11,7 @@ import pytest
 import paged_quantized_kv_kvq_amd as kvq
 from oracle.blocks import Blocks, Exhausted
 
-EXHAUSTED, INVALID = -6, -1
+EXHAUSTED, INVALID, HOST_MEMORY = -6, -1, -7
 
 
 def _same(bm: kvq.BlockManager, m: Blocks):
@@ -120,3 +122,25 @@ def test_append_many_rejects_repeats_and_unknown_ids():
     assert bm.num_free() == 8 and bm.seq_len(a) == (0, 0)
     slots, cow = bm.append_many([b, a], [5, 1])
     assert slots.tolist() == [0, 1, 2, 3, 4, 8] and cow.tolist() == [[-1, -1], [-1, -1]]
+
+
+def test_host_allocation_failure_is_a_status():
+    # a manager of 2^31 - 1 blocks needs 16 GiB of host tables; under a 3 GiB
+    # address-space limit its allocation fails, and the library must turn
+    # that into a status instead of letting the C++ exception cross the C
+    # interface (which would abort the process)
+    code = (
+        "import ctypes, resource, sys\n"
+        "resource.setrlimit(resource.RLIMIT_AS, (3 << 30, 3 << 30))\n"
+        "lib = ctypes.CDLL(sys.argv[1])\n"
+        "h = ctypes.c_void_p()\n"
+        "big = lib.kvq_blocks_create(ctypes.c_uint32(0x7FFFFFFF), ctypes.c_uint32(16), ctypes.byref(h))\n"
+        "ok = lib.kvq_blocks_create(ctypes.c_uint32(64), ctypes.c_uint32(16), ctypes.byref(h))\n"
+        "lib.kvq_blocks_destroy(h)\n"
+        "print(big, ok)\n")
+    kvq.load()
+    out = subprocess.run([sys.executable, "-c", code, kvq._LIB_PATH], capture_output=True, text=True,
+                         timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == [str(HOST_MEMORY), "0"]
+    assert kvq.load().kvq_status_string(HOST_MEMORY) == b"host memory exhausted"
